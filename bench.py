@@ -1,0 +1,169 @@
+"""Benchmark: conv2d forward (implicit GEMM, bf16 MFMA) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one conv2d_fwd call (the whole hot path: im2col gather, bf16 MFMA,
+fused bias, fp32 store) over the workload's batch, with every input already
+resident in device memory.  The default workload is the ResNet-style 3x3
+layer (N=16, 56x56, 64 -> 64 channels).  Prints ONE JSON line.
+
+Timing: K back-to-back calls on one stream between two HIP events (recorded
+on that stream), synchronised on both sides.  TFLOP/s = 2*M*OC*K / time with
+the real K = IC*KH*KW.  The roofline object prices the kernel against HBM
+bandwidth or dense bf16 MFMA peak, whichever bounds it at the workload's
+arithmetic intensity.  The CPU baseline is the fp64 oracle timed on this
+host's cores on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv2d fwd TFLOP/s (2·M·N·K/s) + % of bf16 MFMA peak, 1×MI355X"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
+
+# Measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+# scaled by the copy-kernel calibration) for the kernel as it stands; None
+# until counters are taken for the current kernel.
+TRAFFIC_BYTES = {}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="resnet3x3")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bound on the CPU-baseline sample (0 disables it)")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, wl, flops, seconds):
+    """The fp64 oracle on this host: whole-workload passes until `seconds`."""
+    import oracle
+    o = oracle.get()
+    threads = o.set_threads(0)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        o.conv2d_fwd(inp.x32, inp.w32, inp.bias, wl.stride, wl.pad, wl.dilation)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or runs >= 100:
+            break
+    per = el / runs
+    return {"value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d full pass(es) of the %s workload (fp64 direct 7-loop, also summing |x*w|), "
+                      "%.2f s each" % (runs, wl.name, per)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X "
+              "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from convolution_implicit_gemm_fwd_amd import abi
+    from convolution_implicit_gemm_fwd_amd.workloads import BF16, WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    abi.load()                      # fails loudly if the HIP library is not built
+    wl = WORKLOADS[args.workload]
+    inp = make_inputs(wl, seed=0)
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).cuda()
+
+    x, w, b = up(inp.x_store), up(inp.w_store), torch.from_numpy(inp.bias).cuda()
+    OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
+    OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
+    M, K = wl.N * OH * OW, wl.IC * wl.KH * wl.KW
+    out = torch.empty((wl.N, OH, OW, wl.OC), dtype=torch.float32, device="cuda")
+    rc, plan = abi.conv2d_fwd_plan(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride,
+                                   wl.pad, wl.dilation, wl.dtype, 0)
+    assert rc == 0, abi.conv2d_strerror(rc)
+
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    lib = abi.load()
+    call_args = (x.data_ptr(), w.data_ptr(), b.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC,
+                 wl.KH, wl.KW, wl.stride, wl.pad, wl.dilation, wl.dtype, out.data_ptr(), sptr)
+    fn = lib.conv2d_fwd
+
+    for _ in range(args.warmup):
+        rc = fn(*call_args)
+    assert rc == 0, abi.conv2d_strerror(rc)
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        fn(*call_args)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    assert abi.conv2d_fwd_status(sptr) == 0
+
+    flops = 2 * M * wl.OC * K
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    esz = 2 if wl.dtype == BF16 else 4
+    alg_bytes = (wl.N * wl.H * wl.W * wl.IC + wl.OC * K) * esz + wl.OC * 4 + M * wl.OC * 4
+    ai = flops / alg_bytes
+    peak_flops = PEAK_BF16_TFLOPS if wl.dtype == BF16 else PEAK_FP32_MFMA_TFLOPS
+    if ai < MACHINE_BALANCE:
+        achieved = alg_bytes / (ms_step * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": round(tflops / peak_flops, 4)}
+    roof["traffic"] = TRAFFIC_BYTES.get(wl.name)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == BF16 else "f32",
+        "data": "synthetic (seeded; x N(0,1), w N(0,1/sqrt(K)), bias N(0,0.01); bf16-rounded)",
+        "config": {"workload": wl.name, "N": wl.N, "H": wl.H, "W": wl.W, "IC": wl.IC,
+                   "OC": wl.OC, "KH": wl.KH, "KW": wl.KW, "stride": wl.stride, "pad": wl.pad,
+                   "dilation": wl.dilation, "M": M, "K": K,
+                   "plan": {k: plan[k] for k in ("tile_id", "BM", "BN", "BK", "loader",
+                                                 "splits", "grid")}},
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 6),
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(inp, wl, flops, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,69 @@
+"""MI355X-native 2-D convolution forward as an implicit GEMM.
+
+NHWC input, OHWI weight, fp32 bias and fp32 NHWC output; bf16 (or fp32)
+inputs; hand-written HIP kernels for gfx950 behind the C ABI of
+include/convimg.h.  ``abi`` is the ctypes binding of that ABI (same names);
+``conv2d_nhwc`` below wraps it for torch tensors, using torch only for device
+memory and the current stream.
+
+Importing the package loads nothing; the HIP library is loaded on first use
+and its absence is an error (there is no fallback path).
+"""
+from __future__ import annotations
+
+from . import abi
+from .abi import (CONVIMG_BF16, CONVIMG_FP32, LibraryMissing, conv2d_fwd, conv2d_fwd_force,
+                  conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
+                  conv2d_fwd_status, conv2d_release, conv2d_strerror)
+
+__all__ = ["abi", "conv2d_nhwc", "conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan",
+           "conv2d_strerror", "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_status",
+           "conv2d_release", "CONVIMG_BF16", "CONVIMG_FP32", "LibraryMissing"]
+
+
+def conv2d_nhwc(x, w, bias=None, stride=1, pad=0, dilation=1, out=None, stream=None):
+    """out[N,OH,OW,OC] (fp32) = conv2d(x[N,H,W,IC], w[OC,KH,KW,IC]) + bias[OC].
+
+    x and w: contiguous CUDA (HIP) tensors, both bfloat16 or both float32.
+    bias: contiguous float32 [OC] or None.  out: optional preallocated
+    float32 [N,OH,OW,OC].  Runs on ``stream`` (default: torch's current
+    stream of x's device) and returns without waiting.
+    """
+    import torch
+
+    if x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16:
+        dtype = CONVIMG_BF16
+    elif x.dtype == torch.float32 and w.dtype == torch.float32:
+        dtype = CONVIMG_FP32
+    else:
+        raise TypeError("x and w must both be bfloat16 or both float32")
+    if not (x.is_cuda and w.is_cuda):
+        raise ValueError("x and w must be device tensors")
+    if x.dim() != 4 or w.dim() != 4 or x.shape[3] != w.shape[3]:
+        raise ValueError("x must be [N,H,W,IC] and w [OC,KH,KW,IC]")
+    if not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous (NHWC / OHWI)")
+    N, H, W, IC = x.shape
+    OC, KH, KW, _ = w.shape
+    if bias is not None:
+        if bias.dtype != torch.float32 or not bias.is_cuda or bias.numel() != OC \
+                or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous float32 device tensor of OC values")
+    OH = conv2d_fwd_out_dim(H, KH, stride, pad, dilation)
+    OW = conv2d_fwd_out_dim(W, KW, stride, pad, dilation)
+    if OH <= 0 or OW <= 0:
+        raise ValueError("no output pixel for this shape")
+    if out is None:
+        out = torch.empty((N, OH, OW, OC), dtype=torch.float32, device=x.device)
+    elif (tuple(out.shape) != (N, OH, OW, OC) or out.dtype != torch.float32
+          or not out.is_contiguous() or not out.is_cuda):
+        raise ValueError("out must be a contiguous float32 [N,OH,OW,OC] device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        rc = conv2d_fwd(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                        N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out.data_ptr(),
+                        stream)
+    if rc != 0:
+        raise RuntimeError("conv2d_fwd failed: %s (status %d)" % (conv2d_strerror(rc), rc))
+    return out

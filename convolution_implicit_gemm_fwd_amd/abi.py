@@ -1,0 +1,123 @@
+"""ctypes binding of libconvimg's C ABI (include/convimg.h), same names.
+
+Argument marshalling only: every step of the convolution runs in the HIP
+library.  Loading fails loudly when the library has not been built; there is
+no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvimg.so")
+
+CONVIMG_BF16 = 0
+CONVIMG_FP32 = 1
+
+CONVIMG_OK = 0
+CONVIMG_ERR_NULL = 1
+CONVIMG_ERR_SHAPE = 2
+CONVIMG_ERR_DTYPE = 3
+CONVIMG_ERR_RANGE = 4
+CONVIMG_ERR_ALIAS = 5
+CONVIMG_ERR_ALLOC = 6
+CONVIMG_ERR_LAUNCH = 7
+CONVIMG_ERR_DEVICE = 8
+CONVIMG_ERR_TIMEOUT = 9
+
+CONVIMG_LOADER_TAP = 0
+CONVIMG_LOADER_VEC8 = 1
+CONVIMG_LOADER_SCALAR = 2
+CONVIMG_LOADER_FP32 = 3
+
+# Every symbol include/convimg.h declares.
+EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror",
+           "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_status", "conv2d_release")
+
+
+class convimg_plan(ctypes.Structure):
+    _fields_ = [("OH", ctypes.c_int), ("OW", ctypes.c_int), ("M", ctypes.c_longlong),
+                ("Ngemm", ctypes.c_int), ("K", ctypes.c_int), ("tile_id", ctypes.c_int),
+                ("BM", ctypes.c_int), ("BN", ctypes.c_int), ("BK", ctypes.c_int),
+                ("loader", ctypes.c_int), ("splits", ctypes.c_int), ("tiles_m", ctypes.c_int),
+                ("tiles_n", ctypes.c_int), ("ktiles", ctypes.c_int), ("grid", ctypes.c_int),
+                ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libconvimg.so (once).  Raises LibraryMissing if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise LibraryMissing(
+            "libconvimg.so is not built (%s); build it with "
+            "`python -m convolution_implicit_gemm_fwd_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    i, vp = ctypes.c_int, ctypes.c_void_p
+    lib.conv2d_fwd.argtypes = [vp, vp, vp] + [i] * 11 + [vp, vp]
+    lib.conv2d_fwd.restype = i
+    lib.conv2d_fwd_out_dim.argtypes = [i] * 5
+    lib.conv2d_fwd_out_dim.restype = i
+    lib.conv2d_fwd_plan.argtypes = [i] * 12 + [ctypes.POINTER(convimg_plan)]
+    lib.conv2d_fwd_plan.restype = i
+    lib.conv2d_strerror.argtypes = [i]
+    lib.conv2d_strerror.restype = ctypes.c_char_p
+    lib.conv2d_fwd_force.argtypes = [i, i, i]
+    lib.conv2d_fwd_force.restype = i
+    lib.conv2d_fwd_num_tiles.argtypes = []
+    lib.conv2d_fwd_num_tiles.restype = i
+    lib.conv2d_fwd_status.argtypes = [vp]
+    lib.conv2d_fwd_status.restype = i
+    lib.conv2d_release.argtypes = []
+    lib.conv2d_release.restype = None
+    _lib = lib
+    return lib
+
+
+def conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out, stream):
+    """Raw C call: pointers are integers (device addresses), returns a status."""
+    return load().conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation,
+                             dtype, out, stream)
+
+
+def conv2d_fwd_out_dim(size, k, stride, pad, dilation):
+    return load().conv2d_fwd_out_dim(size, k, stride, pad, dilation)
+
+
+def conv2d_fwd_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, num_cus):
+    """Returns (status, plan dict or None)."""
+    p = convimg_plan()
+    rc = load().conv2d_fwd_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, num_cus,
+                                ctypes.byref(p))
+    return rc, (p.as_dict() if rc == CONVIMG_OK else None)
+
+
+def conv2d_strerror(status):
+    return load().conv2d_strerror(status).decode()
+
+
+def conv2d_fwd_force(tile_id=-1, splits=-1, loader=-1):
+    return load().conv2d_fwd_force(tile_id, splits, loader)
+
+
+def conv2d_fwd_num_tiles():
+    return load().conv2d_fwd_num_tiles()
+
+
+def conv2d_fwd_status(stream):
+    return load().conv2d_fwd_status(stream)
+
+
+def conv2d_release():
+    load().conv2d_release()

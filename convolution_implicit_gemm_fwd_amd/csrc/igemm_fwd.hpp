@@ -1,0 +1,497 @@
+// igemm_fwd.hpp -- implicit-GEMM convolution forward kernels for gfx950.
+//
+// GEMM view (burn PR "Introduce autotuning to conv2d and conv_transpose2d
+// with a new im2col/GEMM algorithm", Changes): M = N*OH*OW output pixels,
+// N = OC output channels, K = IC*KH*KW, ordered k = (kh*KW + kw)*IC + ic so
+// that a row of the OHWI weight is a row of B (burn-cubecl
+// "kernel/conv/base.rs" listing, conv_forward: the weight is permuted to
+// channels-last before the NHWC kernel runs).
+//
+// One workgroup = 4 waves = 256 lanes computes a BM x BN output tile:
+//   * loader: gathers the A tile (BM pixels x 64 k) straight from NHWC x with
+//     stride / padding / dilation masking -- the im2col matrix only ever
+//     exists as registers and LDS -- and the B tile (BN x 64 k) from w;
+//   * LDS: two buffers; the global loads of K tile t+1 are in flight while the
+//     waves read K tile t from LDS and run MFMA on it, one barrier per K tile
+//     (the split of LDS reads and matrix ops into overlapping stages of the
+//     rocMLIR PR "Double buffering improvements");
+//   * LDS rows are 64 bf16 = 8 chunks of 16 bytes; chunk c of row r is stored
+//     at position c ^ (r & 7), so the eight lanes that read one 16-byte chunk
+//     column each hit a distinct group of four banks;
+//   * MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulators in registers;
+//   * epilogue: + fp32 bias, fp32 NHWC store; with split-K, the splits of one
+//     tile take turns on a per-tile semaphore and accumulate in place into
+//     the fp32 output, which serves as the reduction buffer (nvFuser issue
+//     "Split-K matmul is slow even for few partitions", section "Eliminating
+//     the workspace": serialised blocks, each waiting for its turn, with the
+//     output tensor reused as the work buffer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convimg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+enum : int { kLoaderTap = 0, kLoaderVec8 = 1, kLoaderScalar = 2 };
+
+constexpr int kThreads = 256;       // 4 waves of 64
+constexpr int kBK = 64;             // K per tile (bf16 path)
+constexpr int kChunks = kBK / 8;    // 16-byte chunks per LDS row
+constexpr int kSpinLimit = 1 << 20; // split-K wait bound (iterations of s_sleep)
+
+struct ConvArgs {
+    const void *x;
+    const void *w;
+    const float *bias;
+    float *out;
+    int *sem;       // split-K: one int per output tile, then one status word
+    int N, H, W, IC, OC, KH, KW, stride, pad, dil;
+    int OH, OW, M, K;
+    int tiles_m, tiles_n, ktiles, splits;
+    int tiles_pad;  // workgroup slots per split: tiles rounded up to a multiple of 8
+    int remap;      // 1: XCD-aware order of tiles (single split only)
+};
+
+// Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them
+// so each XCD works through a contiguous range of tiles: neighbouring M
+// tiles share input rows (the 3x3 halo) and every tile of one N column
+// shares its weights, so they should meet in the same L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg)
+{
+    const int q = nwg >> 3, r = nwg & 7;
+    const int xcd = bid & 7, idx = bid >> 3;
+    return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+__device__ __forceinline__ int swz(int row, int chunk)
+{
+    return row * kChunks + (chunk ^ (row & 7));
+}
+
+// ---------------------------------------------------------------------------
+// bf16 implicit GEMM.  BM x BN tile, WAVES_M x (4 / WAVES_M) waves.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WAVES_M, int LOADER>
+__global__ __launch_bounds__(kThreads) void igemm_fwd_bf16(ConvArgs a)
+{
+    constexpr int WAVES_N = 4 / WAVES_M;
+    constexpr int WTM = BM / WAVES_M;
+    constexpr int WTN = BN / WAVES_N;
+    constexpr int FM = WTM / 16;
+    constexpr int FN = WTN / 16;
+    constexpr int AR = BM / 32;     // A rows loaded per thread
+    constexpr int BR = BN / 32;     // B rows loaded per thread
+    static_assert(WAVES_M * WAVES_N == 4, "four waves");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must hold 16x16 blocks");
+    static_assert(BM % 32 == 0 && BN % 32 == 0, "loader covers 32 rows per pass");
+
+    __shared__ u32x4_t sA[2][BM * kChunks];
+    __shared__ u32x4_t sB[2][BN * kChunks];
+
+    const unsigned short *__restrict__ x = (const unsigned short *)a.x;
+    const unsigned short *__restrict__ w = (const unsigned short *)a.w;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave % WAVES_M;
+    const int wn = wave / WAVES_M;
+
+    // ---- which tile and which K range
+    // Split-major order with a stride of tiles_pad (a multiple of 8): the
+    // predecessor of split s of a tile has an id lower by tiles_pad, so it
+    // sits on the same XCD and was dispatched there before this workgroup.
+    const int tiles = a.tiles_m * a.tiles_n;
+    int bid = blockIdx.x;
+    if (a.remap)
+        bid = xcd_remap(bid, gridDim.x);
+    const int split = bid / a.tiles_pad;
+    const int tile = bid - split * a.tiles_pad;
+    if (tile >= tiles)
+        return;             // padding slot: the whole workgroup leaves together
+    const int tm = tile % a.tiles_m;
+    const int tn = tile / a.tiles_m;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int kt_begin = (int)(((long long)split * a.ktiles) / a.splits);
+    const int kt_end = (int)(((long long)(split + 1) * a.ktiles) / a.splits);
+
+    // ---- per-thread gather rows: decode m -> (n, oh, ow) once
+    const int cA = tid & 7;         // 16-byte chunk of the row this thread loads
+    const int rA = tid >> 3;        // first row (0..31), then +32 per pass
+    const int OHW = a.OH * a.OW;
+    int xoff[AR], ih0[AR], iw0[AR];
+    bool mok[AR];                   // row is a real output pixel (m < M)
+#pragma unroll
+    for (int j = 0; j < AR; ++j) {
+        const int m = m0 + rA + 32 * j;
+        mok[j] = m < a.M;
+        const int mm = mok[j] ? m : 0;
+        const int n = mm / OHW;
+        const int r = mm - n * OHW;
+        const int oh = r / a.OW;
+        const int ow = r - oh * a.OW;
+        xoff[j] = n * a.H * a.W * a.IC;
+        ih0[j] = oh * a.stride - a.pad;
+        iw0[j] = ow * a.stride - a.pad;
+    }
+    int woff[BR];
+    bool wok[BR];
+#pragma unroll
+    for (int j = 0; j < BR; ++j) {
+        const int oc = n0 + rA + 32 * j;
+        wok[j] = oc < a.OC;
+        woff[j] = wok[j] ? oc * a.K : 0;
+    }
+
+    // ---- tap-aligned loader state (IC % 64 == 0): tap (kh, kw), channel c0
+    int t_kh = 0, t_kw = 0, t_c0 = 0;
+    if (LOADER == kLoaderTap) {
+        const int kflat = kt_begin * kBK;
+        const int tap = kflat / a.IC;
+        t_c0 = kflat - tap * a.IC;
+        t_kh = tap / a.KW;
+        t_kw = tap - t_kh * a.KW;
+    }
+
+    u32x4_t ra[AR], rb[BR];
+    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+
+    auto load_tile = [&](int kt) {
+        if (LOADER == kLoaderTap) {
+            const int dh = t_kh * a.dil, dw = t_kw * a.dil;
+            const int cofs = t_c0 + cA * 8;
+#pragma unroll
+            for (int j = 0; j < AR; ++j) {
+                const int ih = ih0[j] + dh, iw = iw0[j] + dw;
+                const bool ok = mok[j] && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+                ra[j] = zero4;
+                if (ok)
+                    ra[j] = *(const u32x4_t *)(x + xoff[j] + (ih * a.W + iw) * a.IC + cofs);
+            }
+            const int k = kt * kBK + cA * 8;
+#pragma unroll
+            for (int j = 0; j < BR; ++j) {
+                rb[j] = zero4;
+                if (wok[j])
+                    rb[j] = *(const u32x4_t *)(w + woff[j] + k);
+            }
+            // advance to the next 64-channel slice / tap
+            t_c0 += kBK;
+            if (t_c0 == a.IC) {
+                t_c0 = 0;
+                if (++t_kw == a.KW) {
+                    t_kw = 0;
+                    ++t_kh;
+                }
+            }
+        } else if (LOADER == kLoaderVec8) {
+            const int k = kt * kBK + cA * 8;
+            const bool okk = k < a.K;
+            const int tap = k / a.IC;
+            const int ic = k - tap * a.IC;
+            const int kh = tap / a.KW;
+            const int kw = tap - kh * a.KW;
+            const int dh = kh * a.dil, dw = kw * a.dil;
+#pragma unroll
+            for (int j = 0; j < AR; ++j) {
+                const int ih = ih0[j] + dh, iw = iw0[j] + dw;
+                const bool ok = okk && mok[j] && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+                ra[j] = zero4;
+                if (ok)
+                    ra[j] = *(const u32x4_t *)(x + xoff[j] + (ih * a.W + iw) * a.IC + ic);
+            }
+#pragma unroll
+            for (int j = 0; j < BR; ++j) {
+                rb[j] = zero4;
+                if (okk && wok[j])
+                    rb[j] = *(const u32x4_t *)(w + woff[j] + k);
+            }
+        } else {
+            // element-wise gather: the 8 k values of this thread's chunk are
+            // decoded once and shared by all rows it loads
+            const int k0 = kt * kBK + cA * 8;
+            int tap = k0 / a.IC;
+            int ic = k0 - tap * a.IC;
+            int kh = tap / a.KW;
+            int kw = tap - kh * a.KW;
+            int koff[8], dh[8], dw[8];
+            bool okk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                okk[e] = (k0 + e) < a.K;
+                dh[e] = kh * a.dil;
+                dw[e] = kw * a.dil;
+                koff[e] = (dh[e] * a.W + dw[e]) * a.IC + ic;
+                if (++ic == a.IC) {
+                    ic = 0;
+                    if (++kw == a.KW) {
+                        kw = 0;
+                        ++kh;
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < AR; ++j) {
+                const int base = xoff[j] + (ih0[j] * a.W + iw0[j]) * a.IC;
+                unsigned int v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int ih = ih0[j] + dh[e], iw = iw0[j] + dw[e];
+                    const bool ok = okk[e] && mok[j] && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+                    const unsigned int h = ok ? (unsigned int)x[base + koff[e]] : 0u;
+                    v[e >> 1] |= h << (16 * (e & 1));
+                }
+                ra[j] = u32x4_t{v[0], v[1], v[2], v[3]};
+            }
+#pragma unroll
+            for (int j = 0; j < BR; ++j) {
+                unsigned int v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool ok = okk[e] && wok[j];
+                    const unsigned int h = ok ? (unsigned int)w[woff[j] + k0 + e] : 0u;
+                    v[e >> 1] |= h << (16 * (e & 1));
+                }
+                rb[j] = u32x4_t{v[0], v[1], v[2], v[3]};
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < AR; ++j)
+            sA[buf][swz(rA + 32 * j, cA)] = ra[j];
+#pragma unroll
+        for (int j = 0; j < BR; ++j)
+            sB[buf][swz(rA + 32 * j, cA)] = rb[j];
+    };
+
+    floatx4_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Lane l feeds row (l & 15) of a 16x16 block with the 8 consecutive k of
+    // chunk (l >> 4) of each 32-wide k step; A and B use the same k chunks,
+    // so every product pairs x and w at the same k.
+    const int lrow = lane & 15;
+    const int lchk = lane >> 4;
+
+    auto compute_tile = [&](int buf) {
+#pragma unroll
+        for (int ks = 0; ks < kBK / 32; ++ks) {
+            const int ck = ks * 4 + lchk;
+            bf16x8_t af[FM], bfg[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = __builtin_bit_cast(bf16x8_t, sA[buf][swz(wm * WTM + i * 16 + lrow, ck)]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bfg[j] = __builtin_bit_cast(bf16x8_t, sB[buf][swz(wn * WTN + j * 16 + lrow, ck)]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // ---- main loop: prefetch K tile t+1 into registers while tile t is
+    // consumed from LDS; one barrier per K tile
+    if (kt_begin < kt_end) {
+        load_tile(kt_begin);
+        store_tile(0);
+    }
+    __syncthreads();
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+        const int buf = (kt - kt_begin) & 1;
+        const bool more = kt + 1 < kt_end;
+        if (more)
+            load_tile(kt + 1);
+        compute_tile(buf);
+        if (more)
+            store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue.  Output block (i, j): lane holds column (lane & 15) of
+    // rows 4*(lane >> 4) + v, v = 0..3.
+    float bv[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int oc = n0 + wn * WTN + j * 16 + lrow;
+        bv[j] = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
+    }
+    const int row_base = m0 + wm * WTM + lchk * 4;
+    const int col_base = n0 + wn * WTN + lrow;
+
+    if (a.splits == 1) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int oc = col_base + j * 16;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = row_base + i * 16 + v;
+                    if (m < a.M && oc < a.OC)
+                        a.out[m * a.OC + oc] = acc[i][j][v] + bv[j];
+                }
+            }
+        return;
+    }
+
+    // ---- serial split-K: wait for this tile's turn, accumulate in place
+    int *sem = a.sem + tile;
+    if (tid == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(sem, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != split) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == kSpinLimit) {
+                __hip_atomic_store(a.sem + tiles, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int oc = col_base + j * 16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = row_base + i * 16 + v;
+                if (m < a.M && oc < a.OC) {
+                    float *o = a.out + m * a.OC + oc;
+                    *o = (split == 0) ? acc[i][j][v] + bv[j] : *o + acc[i][j][v];
+                }
+            }
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_store(sem, (split + 1 == a.splits) ? 0 : split + 1,
+                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 storage: the same implicit GEMM with fp32 tiles and
+// v_mfma_f32_16x16x4_f32 (products and sums in fp32).  64x64 tile, K tile 16,
+// element-wise gather, single LDS buffer, no split.
+// ---------------------------------------------------------------------------
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
+
+__global__ __launch_bounds__(kThreads) void igemm_fwd_f32(ConvArgs a)
+{
+    __shared__ float sA[kF32BM][kF32BK + 1];
+    __shared__ float sB[kF32BN][kF32BK + 1];
+    const float *__restrict__ x = (const float *)a.x;
+    const float *__restrict__ w = (const float *)a.w;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;   // 2 x 2 waves, 32 x 32 each
+    const int tm = blockIdx.x % a.tiles_m;
+    const int tn = blockIdx.x / a.tiles_m;
+    const int m0 = tm * kF32BM, n0 = tn * kF32BN;
+    const int OHW = a.OH * a.OW;
+
+    // each thread loads 4 elements of A and 4 of B per K tile: rows
+    // (tid >> 4) + 16*q, column k = tid & 15
+    const int lk = tid & 15;
+    int xoff[4], ih0[4], iw0[4], woff[4];
+    bool mok[4], wok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = m0 + (tid >> 4) + 16 * q;
+        mok[q] = m < a.M;
+        const int mm = mok[q] ? m : 0;
+        const int n = mm / OHW;
+        const int r = mm - n * OHW;
+        const int oh = r / a.OW;
+        const int ow = r - oh * a.OW;
+        xoff[q] = n * a.H * a.W * a.IC;
+        ih0[q] = oh * a.stride - a.pad;
+        iw0[q] = ow * a.stride - a.pad;
+        const int oc = n0 + (tid >> 4) + 16 * q;
+        wok[q] = oc < a.OC;
+        woff[q] = wok[q] ? oc * a.K : 0;
+    }
+
+    floatx4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int lrow = lane & 15, lchk = lane >> 4;
+    for (int kt = 0; kt < a.ktiles; ++kt) {
+        const int k = kt * kF32BK + lk;
+        const bool okk = k < a.K;
+        const int tap = k / a.IC;
+        const int ic = k - tap * a.IC;
+        const int kh = tap / a.KW;
+        const int kw = tap - kh * a.KW;
+        const int dh = kh * a.dil, dw = kw * a.dil;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ih = ih0[q] + dh, iw = iw0[q] + dw;
+            const bool ok = okk && mok[q] && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+            sA[(tid >> 4) + 16 * q][lk] = ok ? x[xoff[q] + (ih * a.W + iw) * a.IC + ic] : 0.f;
+            sB[(tid >> 4) + 16 * q][lk] = (okk && wok[q]) ? w[woff[q] + k] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < kF32BK / 4; ++ks) {
+            float af[2], bfg[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = sA[wm * 32 + i * 16 + lrow][ks * 4 + lchk];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bfg[j] = sB[wn * 32 + j * 16 + lrow][ks * 4 + lchk];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bfg[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int oc = n0 + wn * 32 + j * 16 + lrow;
+        const float bv = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + wm * 32 + i * 16 + lchk * 4 + v;
+                if (m < a.M && oc < a.OC)
+                    a.out[m * a.OC + oc] = acc[i][j][v] + bv;
+            }
+    }
+}
+
+// Zero an int array (semaphores); used instead of a memset so the call is a
+// plain kernel node if the caller captures the stream in a graph.
+__global__ void fill_zero_i32(int *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0;
+}
+
+}  // namespace convimg

@@ -1,0 +1,137 @@
+/*
+ * convimg.h -- C ABI of libconvimg: 2-D convolution forward computed as an
+ * implicit GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the forward convolution of the burn conv pages
+ * (burn-cubecl "kernel/conv/base.rs" listing, conv_forward_nhwc: NHWC input,
+ * weight permuted to [OC][KH][KW][IC], optional bias "added to each
+ * channel", groups = 1 on the implicit-GEMM route):
+ *
+ *   out[n][oh][ow][oc] = bias[oc] + sum_{kh,kw,ic}
+ *       X(n, oh*stride - pad + kh*dilation, ow*stride - pad + kw*dilation, ic)
+ *       * w[oc][kh][kw][ic]
+ *
+ * with X = x inside the image and 0 in the padding.  It is evaluated as a
+ * GEMM with M = N*OH*OW, N = OC, K = IC*KH*KW (burn PR "Introduce
+ * autotuning to conv2d and conv_transpose2d with a new im2col/GEMM
+ * algorithm", Changes: the implicit-GEMM dimensions batch*out_h*out_w,
+ * out_channels, in_channels*kernel_h*kernel_w).  The A operand is gathered
+ * from x on the fly; no im2col buffer is ever written.
+ *
+ * Every entry point is extern "C", takes plain pointers and sizes, and never
+ * throws.  Nothing is printed unless the environment sets CONVIMG_LOG=1.
+ */
+#ifndef CONVIMG_H
+#define CONVIMG_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of x and w.  The output and the bias are always fp32. */
+#define CONVIMG_BF16 0   /* bf16 inputs, bf16 MFMA products, fp32 accumulation */
+#define CONVIMG_FP32 1   /* fp32 inputs, fp32 MFMA products, fp32 accumulation */
+
+/* Status codes.  0 is success; every error is returned before any work is
+ * queued, and then `out` is untouched, except CONVIMG_ERR_LAUNCH. */
+#define CONVIMG_OK          0
+#define CONVIMG_ERR_NULL    1  /* x, w or out is NULL, or plan is NULL */
+#define CONVIMG_ERR_SHAPE   2  /* a size <= 0, stride/dilation < 1, pad < 0, or no output pixel */
+#define CONVIMG_ERR_DTYPE   3  /* dtype is neither CONVIMG_BF16 nor CONVIMG_FP32 */
+#define CONVIMG_ERR_RANGE   4  /* an element count of x, w or out reaches 2^31 */
+#define CONVIMG_ERR_ALIAS   5  /* out overlaps x, w or bias */
+#define CONVIMG_ERR_ALLOC   6  /* the library could not allocate its semaphores */
+#define CONVIMG_ERR_LAUNCH  7  /* the HIP runtime refused the launch */
+#define CONVIMG_ERR_DEVICE  8  /* no usable HIP device, or a device query failed */
+#define CONVIMG_ERR_TIMEOUT 9  /* a split-K wait gave up (reported by conv2d_fwd_status) */
+
+/* Loader variants used by the plan. */
+#define CONVIMG_LOADER_TAP    0  /* IC % 64 == 0: one 64-channel slice of one tap per K tile, 16-byte loads */
+#define CONVIMG_LOADER_VEC8   1  /* IC % 8 == 0: 16-byte loads of 8 channels, tap decoded per vector */
+#define CONVIMG_LOADER_SCALAR 2  /* any IC (the masked edge path): element-wise gather */
+#define CONVIMG_LOADER_FP32   3  /* fp32 storage: element-wise gather into fp32 tiles */
+
+/* What conv2d_fwd will launch for a problem (filled by conv2d_fwd_plan). */
+typedef struct convimg_plan {
+    int OH, OW;          /* output extent */
+    long long M;         /* N*OH*OW */
+    int Ngemm;           /* OC */
+    int K;               /* IC*KH*KW */
+    int tile_id;         /* index into the tile table */
+    int BM, BN, BK;      /* workgroup tile */
+    int loader;          /* CONVIMG_LOADER_* */
+    int splits;          /* split-K factor S (1 = no split) */
+    int tiles_m, tiles_n, ktiles;
+    int grid;            /* workgroups launched = tiles_m*tiles_n*splits */
+    int threads;         /* threads per workgroup */
+    int lds_bytes;       /* LDS per workgroup */
+} convimg_plan;
+
+/*
+ * conv2d_fwd -- out = conv2d(x, w) + bias, asynchronously on `stream`.
+ *
+ *   x     device pointer, [N][H][W][IC] contiguous (NHWC), bf16 or fp32 per dtype
+ *   w     device pointer, [OC][KH][KW][IC] contiguous (OHWI), same type as x
+ *   bias  device pointer to OC fp32 values, or NULL for zeros
+ *   out   device pointer, [N][OH][OW][OC] fp32 contiguous (NHWC); every element
+ *         is overwritten (nothing is accumulated into its previous contents)
+ *   stride >= 1, pad >= 0, dilation >= 1: the same for both spatial axes
+ *   OH = floor((H + 2*pad - dilation*(KH-1) - 1)/stride) + 1, likewise OW
+ *   stream  HIP stream on the device that owns all four buffers (0 = null stream)
+ *
+ * Ownership: the caller owns x, w, bias and out and keeps them alive until
+ * the stream has run the call.  The library owns only a small array of int32
+ * split-K semaphores per (device, stream), allocated on first need (that
+ * first call may block while it allocates) and freed by conv2d_release().
+ *
+ * Errors: CONVIMG_ERR_* as listed above; argument errors leave `out`
+ * untouched and queue nothing.  A fault inside the kernel surfaces at the
+ * caller's next synchronisation, as for any HIP kernel.  Calls on different
+ * streams may run concurrently; calls on one stream run in order.
+ */
+int conv2d_fwd(const void *x, const void *w, const float *bias,
+               int N, int H, int W, int IC, int OC, int KH, int KW,
+               int stride, int pad, int dilation, int dtype,
+               float *out, hipStream_t stream);
+
+/* Output extent along one axis, or -1 when an argument is out of range or no
+ * window fits.  Host only. */
+int conv2d_fwd_out_dim(int in, int k, int stride, int pad, int dilation);
+
+/* The plan conv2d_fwd would use for this problem with 16-byte aligned
+ * buffers, on a device with `num_cus` compute units (num_cus <= 0: query the
+ * current device).  Host only when num_cus > 0.  Returns a status code. */
+int conv2d_fwd_plan(int N, int H, int W, int IC, int OC, int KH, int KW,
+                    int stride, int pad, int dilation, int dtype, int num_cus,
+                    convimg_plan *plan);
+
+/* Static description of a status code (never NULL). */
+const char *conv2d_strerror(int status);
+
+/* Test knob: force the tile (-1 = automatic), the split-K factor (-1 =
+ * automatic) and the loader (-1 = automatic) of later calls in this process.
+ * A forced loader is honoured only when the shape allows it (the vector
+ * loaders need IC % 64 or IC % 8 and aligned buffers); a forced split is
+ * clipped to the number of K tiles.  Returns CONVIMG_OK or
+ * CONVIMG_ERR_SHAPE for an unknown tile or loader. */
+int conv2d_fwd_force(int tile_id, int splits, int loader);
+
+/* Number of entries in the tile table (valid tile_id values are 0..n-1). */
+int conv2d_fwd_num_tiles(void);
+
+/* Split-K health on `stream`: CONVIMG_OK, or CONVIMG_ERR_TIMEOUT if a
+ * workgroup gave up waiting for its turn since the last call of this
+ * function (the flag is then cleared).  Synchronises the stream. */
+int conv2d_fwd_status(hipStream_t stream);
+
+/* Free every library-owned buffer (synchronising each device that has
+ * one).  Later calls allocate again as needed. */
+void conv2d_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVIMG_H */
