@@ -31,10 +31,26 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
 
-# Measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE,
-# scaled by the copy-kernel calibration) for the kernel as it stands; None
-# until counters are taken for the current kernel.
-TRAFFIC_BYTES = {}
+# HBM traffic per launch measured with rocprofv3 (FETCH_SIZE then WRITE_SIZE,
+# each scaled by what the counter reads for a plain copy of known size, see
+# --copy-calibration), keyed by workload, with the hash of the kernel sources
+# the counters were taken on.  Reported only while the sources still hash to
+# that value; otherwise the kernel has changed since and traffic is null.
+TRAFFIC = {
+    # profiles/igemm_pipe_resnet3x3.md: 6.971 MB read + 12.845 MB written
+    "resnet3x3": {"bytes": 19983065, "kernel": "423d715466520959"},
+}
+
+
+def kernel_sources_hash():
+    import hashlib
+    csrc = os.path.join(ROOT, "convolution_implicit_gemm_fwd_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hpp", ".hip")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -45,7 +61,23 @@ def parse():
     ap.add_argument("--workload", default="resnet3x3")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline sample (0 disables it)")
+    ap.add_argument("--force", default=None,
+                    help="tile,splits,loader to force instead of the automatic plan (-1 = auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "copies": 5}), flush=True)
 
 
 def cpu_baseline(inp, wl, flops, seconds):
@@ -69,6 +101,9 @@ def cpu_baseline(inp, wl, flops, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X "
               "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
@@ -94,6 +129,8 @@ def main():
     OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
     M, K = wl.N * OH * OW, wl.IC * wl.KH * wl.KW
     out = torch.empty((wl.N, OH, OW, wl.OC), dtype=torch.float32, device="cuda")
+    if args.force:
+        abi.conv2d_fwd_force(*[int(v) for v in args.force.split(",")])
     rc, plan = abi.conv2d_fwd_plan(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride,
                                    wl.pad, wl.dilation, wl.dtype, 0)
     assert rc == 0, abi.conv2d_strerror(rc)
@@ -136,7 +173,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(tflops / peak_flops, 4)}
-    roof["traffic"] = TRAFFIC_BYTES.get(wl.name)
+    t = TRAFFIC.get(wl.name)
+    roof["traffic"] = t["bytes"] if t and t["kernel"] == kernel_sources_hash() else None
 
     line = {
         "metric": METRIC,
@@ -159,6 +197,7 @@ def main():
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 6),
+        "kernel_sources": kernel_sources_hash(),
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(inp, wl, flops, args.cpu_seconds)

@@ -2,8 +2,11 @@
 // argument checks, output extent, the tile plan, the split-K semaphore pool
 // and the kernel launch.  The kernels are in igemm_fwd.hpp.
 #include "convimg.h"
-#include "igemm_fwd.hpp"
+#include "igemm_patch.hpp"
+#include "igemm_pipe.hpp"
+#include "igemm_regs.hpp"
 
+#include <array>
 #include <atomic>
 #include <cstdint>
 #include <cstdio>
@@ -12,25 +15,56 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <type_traits>
 
 using namespace convimg;
 
 namespace {
 
 // ---------------------------------------------------------------------------
-// Tile table.  Every entry runs 4 waves; the loader variant is a second,
-// independent template argument.
+// Tile table.  kRegs entries use the register-staged kernel (every loader,
+// including the element-wise edge path); kPipe entries use the direct-to-LDS
+// pipelined kernel (vector loaders only).
 // ---------------------------------------------------------------------------
+enum Kind { kRegs = 0, kPipe = 1, kPatch = 2 };
+
 struct TileCfg {
-    int BM, BN, waves_m;
+    int kind, BM, BN, WM, WN, stages, ms;
     const char *name;
+    int patch_px;   // kPatch: input pixels the LDS patch holds
 };
 
 constexpr TileCfg kTiles[] = {
-    {128, 64, 2, "128x64"},     // 0: OC <= 64, large M (wave tile 64x32)
-    {128, 128, 2, "128x128"},   // 1: OC > 64 (wave tile 64x64)
-    {256, 128, 2, "256x128"},   // 2: OC > 64, very large M (wave tile 128x64)
-    {64, 64, 2, "64x64"},       // 3: small problems (wave tile 32x32)
+    {kRegs, 128, 64, 2, 2, 2, 16, "regs 128x64"},           // 0
+    {kRegs, 128, 128, 2, 2, 2, 16, "regs 128x128"},         // 1
+    {kRegs, 256, 128, 2, 2, 2, 16, "regs 256x128"},         // 2
+    {kRegs, 64, 64, 2, 2, 2, 16, "regs 64x64"},             // 3
+    {kPipe, 128, 64, 2, 2, 3, 16, "pipe16 128x64 s3"},      // 4
+    {kPipe, 128, 64, 2, 2, 4, 16, "pipe16 128x64 s4"},      // 5
+    {kPipe, 128, 128, 2, 2, 3, 16, "pipe16 128x128 s3"},    // 6
+    {kPipe, 256, 128, 4, 2, 3, 16, "pipe16 256x128 w8"},    // 7
+    {kPipe, 64, 64, 2, 2, 4, 16, "pipe16 64x64 s4"},        // 8
+    {kPipe, 256, 64, 4, 2, 3, 16, "pipe16 256x64 w8"},      // 9
+    {kPipe, 128, 128, 2, 4, 3, 16, "pipe16 128x128 w8"},    // 10
+    {kPipe, 128, 64, 4, 2, 3, 16, "pipe16 128x64 w8"},      // 11
+    {kPipe, 256, 128, 2, 2, 3, 32, "pipe32 256x128 w4"},    // 12: wave 128x64
+    {kPipe, 256, 128, 4, 2, 3, 32, "pipe32 256x128 w8"},    // 13: wave 64x64
+    {kPipe, 128, 128, 2, 2, 3, 32, "pipe32 128x128 s3"},    // 14: wave 64x64
+    {kPipe, 128, 128, 2, 2, 2, 32, "pipe32 128x128 s2"},    // 15: wave 64x64, 2 WG/CU
+    {kPipe, 128, 64, 2, 2, 3, 32, "pipe32 128x64 s3"},      // 16: wave 64x32
+    {kPipe, 256, 64, 4, 1, 3, 32, "pipe32 256x64 w4"},      // 17: wave 64x64
+    {kPipe, 128, 64, 4, 1, 3, 32, "pipe32 128x64 w4x1"},    // 18: wave 32x64
+    {kPipe, 128, 128, 2, 4, 3, 32, "pipe32 128x128 w8"},    // 19: wave 64x32
+    {kPipe, 64, 64, 2, 2, 4, 32, "pipe32 64x64 s4"},        // 20: wave 32x32
+    {kPipe, 128, 128, 2, 2, 4, 32, "pipe32 128x128 s4"},    // 21
+    {kPatch, 128, 64, 2, 2, 3, 32, "patch 128x64", 384},    // 22: wave 64x32
+    {kPatch, 256, 64, 4, 1, 3, 32, "patch 256x64", 512},    // 23: wave 64x64
+    {kPatch, 256, 128, 2, 2, 3, 32, "patch 256x128 w4", 768}, // 24: wave 128x64
+    {kPatch, 256, 128, 4, 2, 3, 32, "patch 256x128 w8", 768}, // 25: wave 64x64
+    {kPatch, 128, 128, 2, 2, 3, 32, "patch 128x128", 640},  // 26: wave 64x64
+    {kPatch, 128, 64, 4, 1, 3, 32, "patch 128x64 w4x1", 384}, // 27: wave 32x64
+    {kPatch, 256, 64, 4, 1, 9, 32, "patch 256x64 s9", 512},  // 28: all 3x3 weight taps in flight
+    {kPatch, 128, 64, 2, 2, 9, 32, "patch 128x64 s9", 384},  // 29
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kNumLoaders = 3;
@@ -40,19 +74,61 @@ typedef void (*KernelFn)(ConvArgs);
 template <int T, int L>
 constexpr KernelFn kfn()
 {
-    return &igemm_fwd_bf16<kTiles[T].BM, kTiles[T].BN, kTiles[T].waves_m, L>;
+    constexpr TileCfg c = kTiles[T];
+    if constexpr (c.kind == kRegs)
+        return &igemm_regs_bf16<c.BM, c.BN, c.WM, L>;
+    else if constexpr (c.kind == kPatch)
+        return L == kLoaderTap ? &igemm_patch_bf16<c.BM, c.BN, c.WM, c.WN, c.stages, c.patch_px>
+                               : nullptr;
+    else if constexpr (L == kLoaderScalar)
+        return nullptr;
+    else
+        return &igemm_pipe_bf16<c.BM, c.BN, c.WM, c.WN, c.stages, c.ms, L>;
 }
 
-const KernelFn kKernels[kNumTiles][kNumLoaders] = {
-    {kfn<0, 0>(), kfn<0, 1>(), kfn<0, 2>()},
-    {kfn<1, 0>(), kfn<1, 1>(), kfn<1, 2>()},
-    {kfn<2, 0>(), kfn<2, 1>(), kfn<2, 2>()},
-    {kfn<3, 0>(), kfn<3, 1>(), kfn<3, 2>()},
-};
+template <int T>
+constexpr std::array<KernelFn, kNumLoaders> krow()
+{
+    return {kfn<T, 0>(), kfn<T, 1>(), kfn<T, 2>()};
+}
+
+template <int... T>
+constexpr std::array<std::array<KernelFn, kNumLoaders>, sizeof...(T)> ktable(std::integer_sequence<int, T...>)
+{
+    return {krow<T>()...};
+}
+
+const std::array<std::array<KernelFn, kNumLoaders>, kNumTiles> kKernels =
+    ktable(std::make_integer_sequence<int, kNumTiles>{});
+
+int threads_of(int tile) { return kTiles[tile].WM * kTiles[tile].WN * 64; }
 
 int lds_bytes_of(int tile)
 {
-    return 2 * (kTiles[tile].BM + kTiles[tile].BN) * kChunks * 16;
+    const TileCfg &c = kTiles[tile];
+    if (c.kind == kPatch)
+        return (c.patch_px + 1) * kChunks * 16 + c.stages * c.BN * kChunks * 16;
+    return c.stages * (c.BM + c.BN) * kChunks * 16;
+}
+
+// Largest patch (input rows x W pixels) any BM-pixel tile of this problem
+// reads; -1 when there are too many tiles to check.
+long long max_patch_px(long long M, int BM, int H, int W, int OH, int OW, int KH, int s, int p,
+                       int d)
+{
+    const long long tiles = (M + BM - 1) / BM;
+    if (tiles > (1 << 20))
+        return -1;
+    long long best = 0;
+    for (long long t = 0; t < tiles; ++t) {
+        const int m0 = (int)(t * BM);
+        const int m1 = (int)(m0 + BM < M ? m0 + BM : M);
+        const PatchRows r = patch_rows(m0, m1, H, OH, OW, KH, s, p, d);
+        const long long px = (long long)(r.hi - r.lo + 1) * W;
+        if (px > best)
+            best = px;
+    }
+    return best;
 }
 
 // Workgroups of a tile config that can be resident on one CU, from its LDS
@@ -77,7 +153,7 @@ bool log_enabled()
 // Per-device facts that never change: CU count, occupancy per kernel.
 struct DeviceInfo {
     int num_cus = 0;
-    int occ[kNumTiles][kNumLoaders] = {};
+    std::array<int, kNumLoaders> occ[kNumTiles] = {};
 };
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_dev;
@@ -93,9 +169,11 @@ int device_info(int dev, DeviceInfo **out)
             return CONVIMG_ERR_DEVICE;
         for (int t = 0; t < kNumTiles; ++t)
             for (int l = 0; l < kNumLoaders; ++l) {
-                int nb = 0;
-                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kKernels[t][l], kThreads, 0) != hipSuccess
-                    || nb <= 0)
+                int nb = 1;
+                if (kKernels[t][l] != nullptr
+                    && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kKernels[t][l], threads_of(t), 0)
+                            != hipSuccess
+                        || nb <= 0))
                     nb = 1;
                 info.occ[t][l] = nb;
             }
@@ -156,11 +234,12 @@ int out_dim(int in, int k, int s, int p, int d)
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Problem -> plan.  `occ` (may be NULL) gives resident workgroups per CU for
-// each kernel; NULL uses the LDS-only estimate.
+// Problem -> plan.  `aligned`: x and w start on 16-byte boundaries (the
+// vector loaders need it).  `occ` (may be NULL) gives resident workgroups per
+// CU for each kernel; NULL uses the LDS-only estimate.
 int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
-              int dtype, int num_cus, bool aligned, const int (*occ)[kNumLoaders],
-              convimg_plan *pl)
+              int dtype, int num_cus, bool aligned,
+              const std::array<int, kNumLoaders> *occ, convimg_plan *pl)
 {
     if (N <= 0 || H <= 0 || W <= 0 || IC <= 0 || OC <= 0 || KH <= 0 || KW <= 0
         || s <= 0 || p < 0 || d <= 0)
@@ -184,7 +263,7 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     pl->M = M;
     pl->Ngemm = OC;
     pl->K = (int)K;
-    pl->threads = kThreads;
+    pl->threads = kRegsThreads;
 
     if (dtype == CONVIMG_FP32) {
         pl->tile_id = -1;
@@ -216,16 +295,35 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
             loader = fl;
     }
 
-    // tile: cover OC with as few N tiles as possible; shrink for small M
+    // The pipelined kernel addresses x and w through 32-bit buffer offsets
+    // with an out-of-range sentinel at 2^31 bytes.
+    const long long esz = 2;
+    const bool pipe_ok = loader != CONVIMG_LOADER_SCALAR
+        && (long long)N * H * W * IC * esz < lim && (long long)OC * K * esz < lim;
+
+    // Tile choice, from measured sweeps on MI355X (every table entry timed on
+    // each shape class): 128x64 with 8 waves wherever OC <= 64 or the M x N
+    // tiles cannot fill the CUs (then split-K fills them); 256x128 with 8
+    // waves when there are enough large tiles for every CU.
     int tile;
-    if (OC <= 64)
+    if (pipe_ok) {
+        const long long big = ((M + 255) / 256) * ((OC + 127) / 128);
+        tile = (OC > 64 && big >= num_cus) ? 7 : 11;
+    } else if (OC <= 64) {
         tile = (M <= 64LL * num_cus) ? 3 : 0;
-    else
+    } else {
         tile = 1;
+    }
     const int ft = g_force_tile.load();
     if (ft >= 0 && ft < kNumTiles)
         tile = ft;
-
+    if (kTiles[tile].kind == kPipe && !pipe_ok)
+        tile = 0;       // a forced pipelined tile the problem cannot use
+    if (kTiles[tile].kind == kPatch) {
+        const long long px = max_patch_px(M, kTiles[tile].BM, H, W, OH, OW, KH, s, p, d);
+        if (!pipe_ok || loader != CONVIMG_LOADER_TAP || px < 0 || px > kTiles[tile].patch_px)
+            tile = pipe_ok ? 4 : 0;   // the patch would not fit: the pipelined gather instead
+    }
     const int BM = kTiles[tile].BM, BN = kTiles[tile].BN;
     const int tiles_m = ceil_div(M, BM);
     const int tiles_n = ceil_div(OC, BN);
@@ -251,6 +349,8 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
         splits = fs;
     if (splits > ktiles)
         splits = ktiles;
+    if (M * OC * 4 >= lim || kTiles[tile].kind == kPatch)
+        splits = 1;     // the in-place reduction addresses out with 32-bit offsets
     if (splits > 1 && tiles * splits > resident) {
         splits = (int)(resident / tiles);
         if (splits < 1)
@@ -270,6 +370,7 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     pl->tiles_n = tiles_n;
     pl->ktiles = ktiles;
     pl->grid = (int)(tiles_pad * splits);
+    pl->threads = threads_of(tile);
     pl->lds_bytes = lds_bytes_of(tile);
     return CONVIMG_OK;
 }
@@ -307,7 +408,7 @@ int conv2d_fwd_plan(int N, int H, int W, int IC, int OC, int KH, int KW,
 {
     if (!plan)
         return CONVIMG_ERR_NULL;
-    const int(*occ)[kNumLoaders] = nullptr;
+    const std::array<int, kNumLoaders> *occ = nullptr;
     if (num_cus <= 0) {
         int dev = 0;
         DeviceInfo *info = nullptr;
@@ -362,6 +463,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.bias = bias;
     a.out = out;
     a.sem = nullptr;
+    a.x_bytes = (unsigned)(nx < 0xffffffffu ? nx : 0xffffffffu);
+    a.w_bytes = (unsigned)(nw < 0xffffffffu ? nw : 0xffffffffu);
+    a.out_bytes = (unsigned)(no < 0xffffffffu ? no : 0xffffffffu);
     a.N = N;
     a.H = H;
     a.W = W;
@@ -396,9 +500,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
                      pl.BK, pl.loader, pl.splits, pl.grid, pl.lds_bytes);
 
     if (dtype == CONVIMG_FP32)
-        hipLaunchKernelGGL(igemm_fwd_f32, dim3(pl.grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(igemm_fwd_f32, dim3(pl.grid), dim3(kRegsThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(kThreads), 0,
+        hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(pl.threads), 0,
                            stream, a);
     if (hipGetLastError() != hipSuccess)
         return CONVIMG_ERR_LAUNCH;

@@ -1,0 +1,220 @@
+// igemm_common.hpp -- pieces shared by the implicit-GEMM convolution kernels.
+//
+// GEMM view (burn PR "Introduce autotuning to conv2d and conv_transpose2d
+// with a new im2col/GEMM algorithm", Changes): M = N*OH*OW output pixels,
+// N = OC output channels, K = IC*KH*KW, ordered k = (kh*KW + kw)*IC + ic so
+// that a row of the OHWI weight is a row of B (burn-cubecl
+// "kernel/conv/base.rs" listing, conv_forward: the weight is permuted to
+// channels-last before the NHWC kernel runs).
+//
+// Common to every bf16 kernel:
+//   * LDS rows are 64 bf16 = 8 chunks of 16 bytes; logical chunk c of row r
+//     is stored at position c ^ (r & 7), so the eight lanes that read one
+//     chunk column of eight consecutive rows hit eight distinct 4-bank groups;
+//   * MFMA, two shapes.  v_mfma_f32_16x16x32_bf16: lane l feeds row (l & 15)
+//     of a 16x16 block with the 8 consecutive k of chunk (l >> 4) of each
+//     32-wide k step; its 4 results are column (l & 15), rows 4*(l >> 4) + v.
+//     v_mfma_f32_32x32x16_bf16: lane l feeds row (l & 31) of a 32x32 block
+//     with the 8 k of chunk (l >> 5) of each 16-wide k step; its 16 results
+//     are column (l & 31), rows 8*(v >> 2) + 4*(l >> 5) + (v & 3).  A and B
+//     always take the same chunks, so every product pairs x and w at one k;
+//   * epilogue: + fp32 bias, fp32 NHWC store; with split-K, the splits of one
+//     tile take turns on a per-tile semaphore and accumulate in place into the
+//     fp32 output, which is the reduction buffer (nvFuser issue "Split-K
+//     matmul is slow even for few partitions", section "Eliminating the
+//     workspace": blocks serialised by a semaphore, each waiting for its turn,
+//     and the output tensor reused as the work buffer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convimg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+enum : int { kLoaderTap = 0, kLoaderVec8 = 1, kLoaderScalar = 2 };
+
+constexpr int kBK = 64;              // K per tile (bf16 kernels)
+constexpr int kChunks = kBK / 8;     // 16-byte chunks per LDS row
+constexpr int kSpinLimit = 1 << 20;  // split-K wait bound (iterations of s_sleep)
+constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset past every buffer addressed so
+constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format
+constexpr int kCoherent = 16;                  // cache policy sc1: agent-coherent access
+
+struct ConvArgs {
+    const void *x;
+    const void *w;
+    const float *bias;
+    float *out;
+    int *sem;        // split-K: one int per output tile, then one status word
+    unsigned x_bytes, w_bytes;  // buffer extents for bounds-checked loads
+    unsigned out_bytes;         // extent of out (split-K only: below 2^31)
+    int N, H, W, IC, OC, KH, KW, stride, pad, dil;
+    int OH, OW, M, K;
+    int tiles_m, tiles_n, ktiles, splits;
+    int tiles_pad;   // workgroup slots per split: tiles rounded up to a multiple of 8
+    int remap;       // 1: XCD-aware order of tiles (single split only)
+};
+
+// Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them
+// so each XCD works through a contiguous range of tiles: neighbouring M tiles
+// share input rows (the kernel's halo) and all M tiles of one N column share
+// weights, so they should meet in the same L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg)
+{
+    const int q = nwg >> 3, r = nwg & 7;
+    const int xcd = bid & 7, idx = bid >> 3;
+    return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+__device__ __forceinline__ int swz(int row, int chunk)
+{
+    return row * kChunks + (chunk ^ (row & 7));
+}
+
+struct TileCoord {
+    int split, tile, m0, n0, kt_begin, kt_end;
+    bool valid;
+};
+
+// Workgroup -> (split, tile, K range).  Split-major with a stride of
+// tiles_pad (a multiple of 8): the predecessor of split s of a tile has an
+// id lower by tiles_pad, so it sits on the same XCD and was dispatched there
+// before this workgroup; a waiting workgroup never holds a slot its
+// predecessor needs.
+template <int BM, int BN>
+__device__ __forceinline__ TileCoord tile_coord(const ConvArgs &a)
+{
+    TileCoord t;
+    int bid = blockIdx.x;
+    if (a.remap)
+        bid = xcd_remap(bid, gridDim.x);
+    t.split = bid / a.tiles_pad;
+    t.tile = bid - t.split * a.tiles_pad;
+    const int tiles = a.tiles_m * a.tiles_n;
+    t.valid = t.tile < tiles;
+    const int tm = t.tile % a.tiles_m;
+    const int tn = t.tile / a.tiles_m;
+    t.m0 = tm * BM;
+    t.n0 = tn * BN;
+    t.kt_begin = (int)(((long long)t.split * a.ktiles) / a.splits);
+    t.kt_end = (int)(((long long)(t.split + 1) * a.ktiles) / a.splits);
+    return t;
+}
+
+// Write the accumulators of one wave.  Block (i, j) of this lane covers rows
+// row0 + i*16 + v (v = 0..3) and column col0 + j*16; bv[j] is that column's
+// bias (0 without bias).
+//
+// Serial split-K: split s waits until the tile's semaphore reads s, then
+// writes bias + partial (s = 0) or adds its partial to what is there, then
+// hands the tile to s + 1 (the last split resets the semaphore to 0, so the
+// array stays zeroed between calls).  The summation order is fixed:
+// ((bias + p0) + p1) + ..., so repeated runs agree bit for bit.
+//
+// The hand-off needs no cache maintenance: the partial sums and the
+// semaphore are read and written with sc1 (agent-coherent) accesses, the
+// instructions the gfx950 memory model uses for relaxed agent-scope atomics,
+// which are coherent across XCDs by themselves.  They are issued as plain
+// buffer loads/stores with the sc1 policy so that a thread's loads go out as
+// one batch.  A writer waits until all of its stores are acknowledged
+// (vmcnt 0) before the barrier that precedes the semaphore store, and a
+// reader loads only after the barrier that follows the semaphore load.
+// Row of value v of an S x S accumulator block, relative to the lane's row0.
+template <int S>
+__device__ __forceinline__ int acc_row(int v)
+{
+    return S == 16 ? v : 8 * (v >> 2) + (v & 3);
+}
+
+template <int S>
+__device__ __forceinline__ int acc_row0(int lane)
+{
+    return S == 16 ? 4 * (lane >> 4) : 4 * (lane >> 5);
+}
+
+template <int S>
+__device__ __forceinline__ int acc_col0(int lane)
+{
+    return S == 16 ? (lane & 15) : (lane & 31);
+}
+
+template <int S, int FM, int FN, typename AccT>
+__device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[FM][FN],
+                                           const float (&bv)[FN], int row0, int col0,
+                                           int split, int tile)
+{
+    constexpr int NV = S * S / 64;      // results per lane per block
+    if (a.splits == 1) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int oc = col0 + j * S;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int m = row0 + i * S + acc_row<S>(v);
+                    if (m < a.M && oc < a.OC)
+                        a.out[m * a.OC + oc] = acc[i][j][v] + bv[j];
+                }
+            }
+        return;
+    }
+
+    int *sem = a.sem + tile;
+    if (threadIdx.x == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(sem, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != split) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == kSpinLimit) {
+                const int tiles = a.tiles_m * a.tiles_n;
+                __hip_atomic_store(a.sem + tiles, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        // one block row at a time: its loads go out as one batch
+        unsigned off[FN][NV];
+        float prev[FN][NV];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int m = row0 + i * S + acc_row<S>(v), oc = col0 + j * S;
+                off[j][v] = (m < a.M && oc < a.OC) ? 4u * (unsigned)(m * a.OC + oc) : kOutOfRange;
+                prev[j][v] = split == 0 ? bv[j]
+                    : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ro, off[j][v], 0, kCoherent));
+            }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(unsigned, prev[j][v] + acc[i][j][v]), ro, off[j][v], 0,
+                    kCoherent);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(sem, (split + 1 == a.splits) ? 0 : split + 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Zero an int array (semaphores); a plain kernel, so the call is an ordinary
+// kernel node if the caller captures the stream in a graph.
+__global__ void fill_zero_i32(int *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0;
+}
+
+}  // namespace convimg

@@ -1,82 +1,25 @@
-// igemm_fwd.hpp -- implicit-GEMM convolution forward kernels for gfx950.
+// igemm_regs.hpp -- register-staged implicit-GEMM kernels.
 //
-// GEMM view (burn PR "Introduce autotuning to conv2d and conv_transpose2d
-// with a new im2col/GEMM algorithm", Changes): M = N*OH*OW output pixels,
-// N = OC output channels, K = IC*KH*KW, ordered k = (kh*KW + kw)*IC + ic so
-// that a row of the OHWI weight is a row of B (burn-cubecl
-// "kernel/conv/base.rs" listing, conv_forward: the weight is permuted to
-// channels-last before the NHWC kernel runs).
-//
-// One workgroup = 4 waves = 256 lanes computes a BM x BN output tile:
-//   * loader: gathers the A tile (BM pixels x 64 k) straight from NHWC x with
-//     stride / padding / dilation masking -- the im2col matrix only ever
-//     exists as registers and LDS -- and the B tile (BN x 64 k) from w;
-//   * LDS: two buffers; the global loads of K tile t+1 are in flight while the
-//     waves read K tile t from LDS and run MFMA on it, one barrier per K tile
-//     (the split of LDS reads and matrix ops into overlapping stages of the
-//     rocMLIR PR "Double buffering improvements");
-//   * LDS rows are 64 bf16 = 8 chunks of 16 bytes; chunk c of row r is stored
-//     at position c ^ (r & 7), so the eight lanes that read one 16-byte chunk
-//     column each hit a distinct group of four banks;
-//   * MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulators in registers;
-//   * epilogue: + fp32 bias, fp32 NHWC store; with split-K, the splits of one
-//     tile take turns on a per-tile semaphore and accumulate in place into
-//     the fp32 output, which serves as the reduction buffer (nvFuser issue
-//     "Split-K matmul is slow even for few partitions", section "Eliminating
-//     the workspace": serialised blocks, each waiting for its turn, with the
-//     output tensor reused as the work buffer).
+// The general kernel of the family: any channel count (including the
+// element-wise gather of the masked edge path, e.g. IC = 3 with K = 147),
+// any alignment, any buffer size.  Global loads of K tile t+1 go to
+// registers while the waves run MFMA on K tile t from LDS, then are written
+// to the other of two LDS buffers; one barrier per K tile (LDS reads and
+// matrix operations as overlapping stages, the structure of the rocMLIR PR
+// "Double buffering improvements").  Also the fp32-storage kernel.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "igemm_common.hpp"
 
 namespace convimg {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-enum : int { kLoaderTap = 0, kLoaderVec8 = 1, kLoaderScalar = 2 };
-
-constexpr int kThreads = 256;       // 4 waves of 64
-constexpr int kBK = 64;             // K per tile (bf16 path)
-constexpr int kChunks = kBK / 8;    // 16-byte chunks per LDS row
-constexpr int kSpinLimit = 1 << 20; // split-K wait bound (iterations of s_sleep)
-
-struct ConvArgs {
-    const void *x;
-    const void *w;
-    const float *bias;
-    float *out;
-    int *sem;       // split-K: one int per output tile, then one status word
-    int N, H, W, IC, OC, KH, KW, stride, pad, dil;
-    int OH, OW, M, K;
-    int tiles_m, tiles_n, ktiles, splits;
-    int tiles_pad;  // workgroup slots per split: tiles rounded up to a multiple of 8
-    int remap;      // 1: XCD-aware order of tiles (single split only)
-};
-
-// Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them
-// so each XCD works through a contiguous range of tiles: neighbouring M
-// tiles share input rows (the 3x3 halo) and every tile of one N column
-// shares its weights, so they should meet in the same L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nwg)
-{
-    const int q = nwg >> 3, r = nwg & 7;
-    const int xcd = bid & 7, idx = bid >> 3;
-    return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-}
-
-__device__ __forceinline__ int swz(int row, int chunk)
-{
-    return row * kChunks + (chunk ^ (row & 7));
-}
+constexpr int kRegsThreads = 256;   // 4 waves of 64
 
 // ---------------------------------------------------------------------------
 // bf16 implicit GEMM.  BM x BN tile, WAVES_M x (4 / WAVES_M) waves.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WAVES_M, int LOADER>
-__global__ __launch_bounds__(kThreads) void igemm_fwd_bf16(ConvArgs a)
+__global__ __launch_bounds__(kRegsThreads) void igemm_regs_bf16(ConvArgs a)
 {
     constexpr int WAVES_N = 4 / WAVES_M;
     constexpr int WTM = BM / WAVES_M;
@@ -102,23 +45,11 @@ __global__ __launch_bounds__(kThreads) void igemm_fwd_bf16(ConvArgs a)
     const int wn = wave / WAVES_M;
 
     // ---- which tile and which K range
-    // Split-major order with a stride of tiles_pad (a multiple of 8): the
-    // predecessor of split s of a tile has an id lower by tiles_pad, so it
-    // sits on the same XCD and was dispatched there before this workgroup.
-    const int tiles = a.tiles_m * a.tiles_n;
-    int bid = blockIdx.x;
-    if (a.remap)
-        bid = xcd_remap(bid, gridDim.x);
-    const int split = bid / a.tiles_pad;
-    const int tile = bid - split * a.tiles_pad;
-    if (tile >= tiles)
+    const TileCoord tc = tile_coord<BM, BN>(a);
+    if (!tc.valid)
         return;             // padding slot: the whole workgroup leaves together
-    const int tm = tile % a.tiles_m;
-    const int tn = tile / a.tiles_m;
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-    const int kt_begin = (int)(((long long)split * a.ktiles) / a.splits);
-    const int kt_end = (int)(((long long)(split + 1) * a.ktiles) / a.splits);
+    const int split = tc.split, tile = tc.tile, m0 = tc.m0, n0 = tc.n0;
+    const int kt_begin = tc.kt_begin, kt_end = tc.kt_end;
 
     // ---- per-thread gather rows: decode m -> (n, oh, ow) once
     const int cA = tid & 7;         // 16-byte chunk of the row this thread loads
@@ -262,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void igemm_fwd_bf16(ConvArgs a)
         }
     };
 
-    auto store_tile = [&](int buf) {
+    auto stage_tile = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < AR; ++j)
             sA[buf][swz(rA + 32 * j, cA)] = ra[j];
@@ -307,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void igemm_fwd_bf16(ConvArgs a)
     // consumed from LDS; one barrier per K tile
     if (kt_begin < kt_end) {
         load_tile(kt_begin);
-        store_tile(0);
+        stage_tile(0);
     }
     __syncthreads();
     for (int kt = kt_begin; kt < kt_end; ++kt) {
@@ -317,70 +248,19 @@ __global__ __launch_bounds__(kThreads) void igemm_fwd_bf16(ConvArgs a)
             load_tile(kt + 1);
         compute_tile(buf);
         if (more)
-            store_tile(buf ^ 1);
+            stage_tile(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue.  Output block (i, j): lane holds column (lane & 15) of
-    // rows 4*(lane >> 4) + v, v = 0..3.
+    // ---- epilogue
     float bv[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int oc = n0 + wn * WTN + j * 16 + lrow;
         bv[j] = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
     }
-    const int row_base = m0 + wm * WTM + lchk * 4;
-    const int col_base = n0 + wn * WTN + lrow;
-
-    if (a.splits == 1) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int oc = col_base + j * 16;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = row_base + i * 16 + v;
-                    if (m < a.M && oc < a.OC)
-                        a.out[m * a.OC + oc] = acc[i][j][v] + bv[j];
-                }
-            }
-        return;
-    }
-
-    // ---- serial split-K: wait for this tile's turn, accumulate in place
-    int *sem = a.sem + tile;
-    if (tid == 0) {
-        int spins = 0;
-        while (__hip_atomic_load(sem, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != split) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins == kSpinLimit) {
-                __hip_atomic_store(a.sem + tiles, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int oc = col_base + j * 16;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = row_base + i * 16 + v;
-                if (m < a.M && oc < a.OC) {
-                    float *o = a.out + m * a.OC + oc;
-                    *o = (split == 0) ? acc[i][j][v] + bv[j] : *o + acc[i][j][v];
-                }
-            }
-        }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (tid == 0)
-        __hip_atomic_store(sem, (split + 1 == a.splits) ? 0 : split + 1,
-                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    store_tile<16, FM, FN>(a, acc, bv, m0 + wm * WTM + acc_row0<16>(lane),
+                           n0 + wn * WTN + acc_col0<16>(lane), split, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -390,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void igemm_fwd_bf16(ConvArgs a)
 // ---------------------------------------------------------------------------
 constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 
-__global__ __launch_bounds__(kThreads) void igemm_fwd_f32(ConvArgs a)
+__global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
 {
     __shared__ float sA[kF32BM][kF32BK + 1];
     __shared__ float sB[kF32BN][kF32BK + 1];
@@ -483,15 +363,6 @@ __global__ __launch_bounds__(kThreads) void igemm_fwd_f32(ConvArgs a)
                     a.out[m * a.OC + oc] = acc[i][j][v] + bv;
             }
     }
-}
-
-// Zero an int array (semaphores); used instead of a memset so the call is a
-// plain kernel node if the caller captures the stream in a graph.
-__global__ void fill_zero_i32(int *p, int n)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n)
-        p[i] = 0;
 }
 
 }  // namespace convimg
