@@ -485,6 +485,7 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.ktiles = pl.ktiles;
     a.splits = pl.splits;
     a.tiles_pad = pl.grid / pl.splits;
+    a.vec_out = (((uintptr_t)out & 15) == 0 && OC % 4 == 0) ? 1 : 0;
     a.remap = pl.splits == 1 ? 1 : 0;
 
     if (pl.splits > 1) {

@@ -58,6 +58,7 @@ struct ConvArgs {
     int tiles_m, tiles_n, ktiles, splits;
     int tiles_pad;   // workgroup slots per split: tiles rounded up to a multiple of 8
     int remap;       // 1: XCD-aware order of tiles (single split only)
+    int vec_out;     // 1: out is 16-byte aligned and OC % 4 == 0 (16-byte stores allowed)
 };
 
 // Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them
@@ -206,6 +207,63 @@ __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[
     if (threadIdx.x == 0)
         __hip_atomic_store(sem, (split + 1 == a.splits) ? 0 : split + 1, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Floats per row of the epilogue scratch for a block row of C columns: C
+// plus a pad that puts the rows written by one store instruction into
+// disjoint bank groups (rows 4 apart for 32x32 blocks: stride = 8 mod 16;
+// rows 4, 8, 12 apart for 16x16 blocks: stride = 4 mod 16).
+template <int S, int C>
+struct EpiScratch {
+    static constexpr int stride = C + (S == 32 ? 8 : 4);
+    static constexpr int floats = S * stride;        // per wave
+};
+
+// Single-split epilogue with 16-byte stores: per block row i, each wave
+// writes acc + bias of its S x WTN sub-tile into its own LDS scratch in
+// row-major order, reads it back four consecutive output channels per lane
+// and stores them with one 16-byte store.  A store instruction then covers
+// whole row segments of WTN channels instead of 4-byte pieces.  The scratch
+// is private to the wave, and LDS accesses of one wave are performed in
+// order, so no barrier is needed between block rows.
+template <int S, int FM, int FN, int WTN, typename AccT>
+__device__ __forceinline__ void store_tile_vec(const ConvArgs &a, const AccT (&acc)[FM][FN],
+                                               const float (&bv)[FN], int m_wave0, int n_wave0,
+                                               float *scratch)
+{
+    constexpr int NV = S * S / 64;
+    constexpr int STRIDE = EpiScratch<S, WTN>::stride;
+    constexpr int C4 = WTN / 4;                      // float4 per scratch row
+    constexpr int F = S * C4;                        // float4 per block row
+    static_assert(F % 64 == 0, "whole float4 passes");
+    const int lane = threadIdx.x & 63;
+    const int r0 = acc_row0<S>(lane), c0 = acc_col0<S>(lane);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                scratch[(r0 + acc_row<S>(v)) * STRIDE + j * S + c0] = acc[i][j][v] + bv[j];
+#pragma unroll
+        for (int t = 0; t < F / 64; ++t) {
+            const int f = t * 64 + lane;
+            const int row = f / C4, c4 = (f % C4) * 4;
+            const floatx4_t val = *(const floatx4_t *)(scratch + row * STRIDE + c4);
+            const int m = m_wave0 + i * S + row, oc = n_wave0 + c4;
+            if (m < a.M) {
+                float *o = a.out + m * a.OC + oc;
+                if (oc + 3 < a.OC) {
+                    *(floatx4_t *)o = val;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (oc + e < a.OC)
+                            o[e] = val[e];
+                }
+            }
+        }
+    }
 }
 
 // Zero an int array (semaphores); a plain kernel, so the call is an ordinary

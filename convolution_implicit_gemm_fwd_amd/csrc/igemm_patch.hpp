@@ -248,6 +248,13 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_patch_bf16(ConvArgs a)
         }
     }
 
+    if (a.vec_out) {
+        static_assert(NW * EpiScratch<MS, WTN>::floats * 4 <= (int)sizeof(patch), "epilogue scratch");
+        __syncthreads();    // every wave is done reading the patch
+        store_tile_vec<MS, FM, FN, WTN>(a, acc, bv, m0 + wm * WTM, n0 + wn * WTN,
+                                        (float *)patch + wave * EpiScratch<MS, WTN>::floats);
+        return;
+    }
     store_tile<MS, FM, FN>(a, acc, bv, m0 + wm * WTM + acc_row0<MS>(lane),
                            n0 + wn * WTN + acc_col0<MS>(lane), 0, tc.tile);
 }

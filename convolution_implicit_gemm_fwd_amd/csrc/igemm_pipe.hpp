@@ -268,6 +268,13 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_pipe_bf16(ConvArgs a)
         compute(i % STAGES);
     }
 
+    if (a.splits == 1 && a.vec_out) {
+        static_assert(NW * EpiScratch<MS, WTN>::floats * 4 <= (int)sizeof(smem), "epilogue scratch");
+        __syncthreads();    // every wave is done reading the last stage
+        store_tile_vec<MS, FM, FN, WTN>(a, acc, bv, m0 + wm * WTM, n0 + wn * WTN,
+                                        (float *)smem + wave * EpiScratch<MS, WTN>::floats);
+        return;
+    }
     store_tile<MS, FM, FN>(a, acc, bv, m0 + wm * WTM + acc_row0<MS>(lane),
                            n0 + wn * WTN + acc_col0<MS>(lane), tc.split, tc.tile);
 }

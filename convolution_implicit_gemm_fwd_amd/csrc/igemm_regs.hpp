@@ -259,6 +259,13 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_regs_bf16(ConvArgs a)
         const int oc = n0 + wn * WTN + j * 16 + lrow;
         bv[j] = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
     }
+    if (a.splits == 1 && a.vec_out) {
+        // the loop's last barrier passed: every wave is done with sA / sB
+        static_assert(4 * EpiScratch<16, WTN>::floats * 4 <= (int)sizeof(sA), "epilogue scratch");
+        store_tile_vec<16, FM, FN, WTN>(a, acc, bv, m0 + wm * WTM, n0 + wn * WTN,
+                                        (float *)&sA[0][0] + wave * EpiScratch<16, WTN>::floats);
+        return;
+    }
     store_tile<16, FM, FN>(a, acc, bv, m0 + wm * WTM + acc_row0<16>(lane),
                            n0 + wn * WTN + acc_col0<16>(lane), split, tile);
 }
