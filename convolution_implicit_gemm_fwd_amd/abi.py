@@ -30,9 +30,15 @@ CONVIMG_LOADER_VEC8 = 1
 CONVIMG_LOADER_SCALAR = 2
 CONVIMG_LOADER_FP32 = 3
 
+CONVIMG_KIND_REGS = 0
+CONVIMG_KIND_PIPE = 1
+CONVIMG_KIND_PATCH = 2
+CONVIMG_KIND_STRIP = 3
+
 # Every symbol include/convimg.h declares.
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror",
-           "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_status", "conv2d_release")
+           "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_tile_kind", "conv2d_fwd_status",
+           "conv2d_release")
 
 
 class convimg_plan(ctypes.Structure):
@@ -77,6 +83,8 @@ def load(path: str = LIB_PATH):
     lib.conv2d_fwd_force.restype = i
     lib.conv2d_fwd_num_tiles.argtypes = []
     lib.conv2d_fwd_num_tiles.restype = i
+    lib.conv2d_fwd_tile_kind.argtypes = [i]
+    lib.conv2d_fwd_tile_kind.restype = i
     lib.conv2d_fwd_status.argtypes = [vp]
     lib.conv2d_fwd_status.restype = i
     lib.conv2d_release.argtypes = []
@@ -113,6 +121,10 @@ def conv2d_fwd_force(tile_id=-1, splits=-1, loader=-1):
 
 def conv2d_fwd_num_tiles():
     return load().conv2d_fwd_num_tiles()
+
+
+def conv2d_fwd_tile_kind(tile_id):
+    return load().conv2d_fwd_tile_kind(tile_id)
 
 
 def conv2d_fwd_status(stream):

@@ -5,6 +5,7 @@
 #include "igemm_patch.hpp"
 #include "igemm_pipe.hpp"
 #include "igemm_regs.hpp"
+#include "igemm_strip.hpp"
 
 #include <array>
 #include <atomic>
@@ -24,9 +25,11 @@ namespace {
 // ---------------------------------------------------------------------------
 // Tile table.  kRegs entries use the register-staged kernel (every loader,
 // including the element-wise edge path); kPipe entries use the direct-to-LDS
-// pipelined kernel (vector loaders only).
+// pipelined kernel (vector loaders only); kPatch entries the pipelined kernel
+// with an LDS patch of input rows; kStrip entries the strip kernel (BM is the
+// largest chunk of pixels: 4 waves x BM / 128 blocks of 32 rows).
 // ---------------------------------------------------------------------------
-enum Kind { kRegs = 0, kPipe = 1, kPatch = 2 };
+enum Kind { kRegs = 0, kPipe = 1, kPatch = 2, kStrip = 3 };
 
 struct TileCfg {
     int kind, BM, BN, WM, WN, stages, ms;
@@ -65,8 +68,13 @@ constexpr TileCfg kTiles[] = {
     {kPatch, 128, 64, 4, 1, 3, 32, "patch 128x64 w4x1", 384}, // 27: wave 32x64
     {kPatch, 256, 64, 4, 1, 9, 32, "patch 256x64 s9", 512},  // 28: all 3x3 weight taps in flight
     {kPatch, 128, 64, 2, 2, 9, 32, "patch 128x64 s9", 384},  // 29
+    {kStrip, 512, 64, 4, 1, 1, 32, "strip 512"},            // 30: chunks of up to 512 pixels
+    {kStrip, 384, 64, 4, 1, 1, 32, "strip 384"},            // 31
+    {kStrip, 256, 64, 4, 1, 1, 32, "strip 256"},            // 32
+    {kStrip, 128, 64, 4, 1, 1, 32, "strip 128"},            // 33
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+constexpr int kLdsBytes = 160 * 1024;     // LDS per CU (and per workgroup) on gfx950
 constexpr int kNumLoaders = 3;
 
 typedef void (*KernelFn)(ConvArgs);
@@ -77,6 +85,8 @@ constexpr KernelFn kfn()
     constexpr TileCfg c = kTiles[T];
     if constexpr (c.kind == kRegs)
         return &igemm_regs_bf16<c.BM, c.BN, c.WM, L>;
+    else if constexpr (c.kind == kStrip)
+        return L == kLoaderTap ? &igemm_strip_bf16<c.BM / 128> : nullptr;
     else if constexpr (c.kind == kPatch)
         return L == kLoaderTap ? &igemm_patch_bf16<c.BM, c.BN, c.WM, c.WN, c.stages, c.patch_px>
                                : nullptr;
@@ -108,6 +118,8 @@ int lds_bytes_of(int tile)
     const TileCfg &c = kTiles[tile];
     if (c.kind == kPatch)
         return (c.patch_px + 1) * kChunks * 16 + c.stages * c.BN * kChunks * 16;
+    if (c.kind == kStrip)
+        return kLdsBytes;       // sized per problem; one workgroup per CU
     return c.stages * (c.BM + c.BN) * kChunks * 16;
 }
 
@@ -135,7 +147,7 @@ long long max_patch_px(long long M, int BM, int H, int W, int OH, int OW, int KH
 // footprint alone (160 KB per CU on gfx950); used by the host-only plan.
 int lds_occupancy(int tile)
 {
-    int n = (160 * 1024) / lds_bytes_of(tile);
+    int n = kLdsBytes / lds_bytes_of(tile);
     return n < 1 ? 1 : (n > 8 ? 8 : n);
 }
 
@@ -167,6 +179,10 @@ int device_info(int dev, DeviceInfo **out)
         if (hipDeviceGetAttribute(&info.num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess
             || info.num_cus <= 0)
             return CONVIMG_ERR_DEVICE;
+        for (int t = 0; t < kNumTiles; ++t)
+            if (kTiles[t].kind == kStrip && kKernels[t][kLoaderTap] != nullptr)
+                (void)hipFuncSetAttribute((const void *)kKernels[t][kLoaderTap],
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         for (int t = 0; t < kNumTiles; ++t)
             for (int l = 0; l < kNumLoaders; ++l) {
                 int nb = 1;
@@ -234,12 +250,89 @@ int out_dim(int in, int k, int s, int p, int d)
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// Strip kernel plan: one workgroup per CU for each 64-channel slice, strips
+// of equal length, chunks of at most 256 pixels; LDS holds a zero block, the
+// slice's weights for the whole K, the largest patch any chunk needs and the
+// epilogue scratch.
+struct StripPlan {
+    int tile = -1;
+    int strip_px = 0, chunk_px = 0, tiles_m = 0, tiles_n = 0;
+    int cpp_shift = 0, lds_zero = 0, lds_patch = 0, lds_scratch = 0, lds_bytes = 0;
+};
+
+bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, int tiles_n,
+                int cpp, long long zero, long long wbytes, long long patch);
+
+bool plan_strip(long long M, int H, int W, int OH, int OW, int IC, int OC, int KH, int KW,
+                int s, int p, int d, long long K, int num_cus, StripPlan *sp)
+{
+    const int cpp = IC / 8;
+    if (IC % kBK != 0 || (cpp & (cpp - 1)) != 0)
+        return false;
+    const long long zero = ((IC * 2 > 1024 ? IC * 2 : 1024) + 1023) / 1024 * 1024;
+    if (cpp % kStripWaves != 0)
+        return false;
+    const long long wbytes = (long long)kStripBN * K * 2;
+    if (zero + wbytes + kStripScratchBytes >= kLdsBytes)
+        return false;
+    const int tiles_n = ceil_div(OC, kStripBN);
+    int gm = num_cus / tiles_n;
+    if (gm < 1)
+        gm = 1;
+    long long strip = (M + gm - 1) / gm;
+    if (strip < 32)
+        strip = 32;
+    const int tiles_m = ceil_div(M, strip);
+    // the largest chunk whose patch fits next to the weights
+    for (int cap = 512; cap >= 128; cap /= 2) {
+        const long long nc = (strip + cap - 1) / cap;
+        if ((long long)tiles_m * nc > (1 << 22))
+            return false;
+        const long long chunk = (strip + nc - 1) / nc;
+        long long patch = 0;
+        for (long long g = 0; g < tiles_m; ++g) {
+            const long long e = (g + 1) * strip < M ? (g + 1) * strip : M;
+            for (long long c0 = g * strip; c0 < e; c0 += chunk) {
+                const long long c1 = c0 + chunk < e ? c0 + chunk : e;
+                const StripSeg sg = strip_seg((int)c0, (int)c1, H, W, OH, OW, KH, s, p, d, cpp);
+                if (sg.total_chunks * 16 > patch)
+                    patch = sg.total_chunks * 16;
+            }
+        }
+        const long long total = zero + wbytes + patch + kStripScratchBytes;
+        if (total <= kLdsBytes)
+            return fill_strip(sp, strip, chunk, tiles_m, tiles_n, cpp, zero, wbytes, patch);
+    }
+    return false;
+}
+
+bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, int tiles_n,
+                int cpp, long long zero, long long wbytes, long long patch)
+{
+    const long long blocks = (chunk + 31) / 32;     // 32-row blocks, 4 waves
+    const int fm = (int)((blocks + 3) / 4);
+    int shift = 0;
+    while ((1 << shift) < cpp)
+        ++shift;
+    sp->tile = fm == 4 ? 30 : fm == 3 ? 31 : fm == 2 ? 32 : 33;
+    sp->strip_px = (int)strip;
+    sp->chunk_px = (int)chunk;
+    sp->tiles_m = tiles_m;
+    sp->tiles_n = tiles_n;
+    sp->cpp_shift = shift;
+    sp->lds_zero = (int)zero;
+    sp->lds_patch = (int)(zero + wbytes);
+    sp->lds_scratch = (int)(zero + wbytes + patch);
+    sp->lds_bytes = (int)(zero + wbytes + patch + kStripScratchBytes);
+    return true;
+}
+
 // Problem -> plan.  `aligned`: x and w start on 16-byte boundaries (the
 // vector loaders need it).  `occ` (may be NULL) gives resident workgroups per
 // CU for each kernel; NULL uses the LDS-only estimate.
 int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
               int dtype, int num_cus, bool aligned,
-              const std::array<int, kNumLoaders> *occ, convimg_plan *pl)
+              const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo = nullptr)
 {
     if (N <= 0 || H <= 0 || W <= 0 || IC <= 0 || OC <= 0 || KH <= 0 || KW <= 0
         || s <= 0 || p < 0 || d <= 0)
@@ -305,6 +398,9 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     // each shape class): 128x64 with 8 waves wherever OC <= 64 or the M x N
     // tiles cannot fill the CUs (then split-K fills them); 256x128 with 8
     // waves when there are enough large tiles for every CU.
+    StripPlan sp;
+    const bool strip_ok = pipe_ok && loader == CONVIMG_LOADER_TAP
+        && plan_strip(M, H, W, OH, OW, IC, OC, KH, KW, s, p, d, K, num_cus, &sp);
     int tile;
     if (pipe_ok) {
         const long long big = ((M + 255) / 256) * ((OC + 127) / 128);
@@ -317,6 +413,26 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     const int ft = g_force_tile.load();
     if (ft >= 0 && ft < kNumTiles)
         tile = ft;
+    if (kTiles[tile].kind == kStrip) {
+        if (strip_ok) {
+            pl->tile_id = sp.tile;
+            pl->BM = kTiles[sp.tile].BM;
+            pl->BN = kStripBN;
+            pl->BK = kBK;
+            pl->loader = loader;
+            pl->splits = 1;
+            pl->tiles_m = sp.tiles_m;
+            pl->tiles_n = sp.tiles_n;
+            pl->ktiles = ceil_div(K, kBK);
+            pl->grid = sp.tiles_m * sp.tiles_n;
+            pl->threads = kStripWaves * 64;
+            pl->lds_bytes = sp.lds_bytes;
+            if (spo)
+                *spo = sp;
+            return CONVIMG_OK;
+        }
+        tile = pipe_ok ? 11 : 0;    // a forced strip the problem cannot use
+    }
     if (kTiles[tile].kind == kPipe && !pipe_ok)
         tile = 0;       // a forced pipelined tile the problem cannot use
     if (kTiles[tile].kind == kPatch) {
@@ -392,6 +508,16 @@ int conv2d_fwd_out_dim(int in, int k, int stride, int pad, int dilation)
 
 int conv2d_fwd_num_tiles(void) { return kNumTiles; }
 
+int conv2d_fwd_tile_kind(int tile_id)
+{
+    if (tile_id < 0 || tile_id >= kNumTiles)
+        return -1;
+    static_assert(kRegs == CONVIMG_KIND_REGS && kPipe == CONVIMG_KIND_PIPE
+                      && kPatch == CONVIMG_KIND_PATCH && kStrip == CONVIMG_KIND_STRIP,
+                  "kind codes");
+    return kTiles[tile_id].kind;
+}
+
 int conv2d_fwd_force(int tile_id, int splits, int loader)
 {
     if (tile_id >= kNumTiles || loader >= kNumLoaders)
@@ -452,8 +578,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     if (rc != CONVIMG_OK)
         return rc;
     const bool aligned = (((uintptr_t)x | (uintptr_t)w) & 15) == 0;
+    StripPlan sp;
     rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned,
-                   info->occ, &pl);
+                   info->occ, &pl, &sp);
     if (rc != CONVIMG_OK)
         return rc;
 
@@ -487,6 +614,12 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.tiles_pad = pl.grid / pl.splits;
     a.vec_out = (((uintptr_t)out & 15) == 0 && OC % 4 == 0) ? 1 : 0;
     a.remap = pl.splits == 1 ? 1 : 0;
+    a.strip_px = sp.strip_px;
+    a.chunk_px = sp.chunk_px;
+    a.cpp_shift = sp.cpp_shift;
+    a.lds_zero = sp.lds_zero;
+    a.lds_patch = sp.lds_patch;
+    a.lds_scratch = sp.lds_scratch;
 
     if (pl.splits > 1) {
         rc = get_semaphores(dev, stream, pl.tiles_m * pl.tiles_n + 1, &a.sem);
@@ -502,6 +635,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
 
     if (dtype == CONVIMG_FP32)
         hipLaunchKernelGGL(igemm_fwd_f32, dim3(pl.grid), dim3(kRegsThreads), 0, stream, a);
+    else if (kTiles[pl.tile_id].kind == kStrip)
+        hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(pl.threads),
+                           (unsigned)pl.lds_bytes, stream, a);
     else
         hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(pl.threads), 0,
                            stream, a);

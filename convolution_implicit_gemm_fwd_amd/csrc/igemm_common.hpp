@@ -59,6 +59,11 @@ struct ConvArgs {
     int tiles_pad;   // workgroup slots per split: tiles rounded up to a multiple of 8
     int remap;       // 1: XCD-aware order of tiles (single split only)
     int vec_out;     // 1: out is 16-byte aligned and OC % 4 == 0 (16-byte stores allowed)
+    // strip kernel only
+    int strip_px;    // output pixels per workgroup
+    int chunk_px;    // output pixels per patch load
+    int cpp_shift;   // log2(IC / 8)
+    int lds_zero, lds_patch, lds_scratch;   // LDS byte offsets: patch, epilogue scratch; zero block size
 };
 
 // Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them
@@ -107,24 +112,6 @@ __device__ __forceinline__ TileCoord tile_coord(const ConvArgs &a)
     return t;
 }
 
-// Write the accumulators of one wave.  Block (i, j) of this lane covers rows
-// row0 + i*16 + v (v = 0..3) and column col0 + j*16; bv[j] is that column's
-// bias (0 without bias).
-//
-// Serial split-K: split s waits until the tile's semaphore reads s, then
-// writes bias + partial (s = 0) or adds its partial to what is there, then
-// hands the tile to s + 1 (the last split resets the semaphore to 0, so the
-// array stays zeroed between calls).  The summation order is fixed:
-// ((bias + p0) + p1) + ..., so repeated runs agree bit for bit.
-//
-// The hand-off needs no cache maintenance: the partial sums and the
-// semaphore are read and written with sc1 (agent-coherent) accesses, the
-// instructions the gfx950 memory model uses for relaxed agent-scope atomics,
-// which are coherent across XCDs by themselves.  They are issued as plain
-// buffer loads/stores with the sc1 policy so that a thread's loads go out as
-// one batch.  A writer waits until all of its stores are acknowledged
-// (vmcnt 0) before the barrier that precedes the semaphore store, and a
-// reader loads only after the barrier that follows the semaphore load.
 // Row of value v of an S x S accumulator block, relative to the lane's row0.
 template <int S>
 __device__ __forceinline__ int acc_row(int v)
@@ -144,6 +131,24 @@ __device__ __forceinline__ int acc_col0(int lane)
     return S == 16 ? (lane & 15) : (lane & 31);
 }
 
+// Write the accumulators of one wave.  Block (i, j) of this lane covers rows
+// row0 + i*16 + v (v = 0..3) and column col0 + j*16; bv[j] is that column's
+// bias (0 without bias).
+//
+// Serial split-K: split s waits until the tile's semaphore reads s, then
+// writes bias + partial (s = 0) or adds its partial to what is there, then
+// hands the tile to s + 1 (the last split resets the semaphore to 0, so the
+// array stays zeroed between calls).  The summation order is fixed:
+// ((bias + p0) + p1) + ..., so repeated runs agree bit for bit.
+//
+// The hand-off needs no cache maintenance: the partial sums and the
+// semaphore are read and written with sc1 (agent-coherent) accesses, the
+// instructions the gfx950 memory model uses for relaxed agent-scope atomics,
+// which are coherent across XCDs by themselves.  They are issued as plain
+// buffer loads/stores with the sc1 policy so that a thread's loads go out as
+// one batch.  A writer waits until all of its stores are acknowledged
+// (vmcnt 0) before the barrier that precedes the semaphore store, and a
+// reader loads only after the barrier that follows the semaphore load.
 template <int S, int FM, int FN, typename AccT>
 __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[FM][FN],
                                            const float (&bv)[FN], int row0, int col0,

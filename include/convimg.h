@@ -121,6 +121,23 @@ int conv2d_fwd_force(int tile_id, int splits, int loader);
 /* Number of entries in the tile table (valid tile_id values are 0..n-1). */
 int conv2d_fwd_num_tiles(void);
 
+/* Kernel family of a tile table entry, or -1 for an unknown tile_id:
+ *   CONVIMG_KIND_REGS  register-staged gather (every loader, incl. the edge path)
+ *   CONVIMG_KIND_PIPE  multi-stage direct-to-LDS pipeline (vector loaders)
+ *   CONVIMG_KIND_PATCH pipeline with an LDS patch of input rows (IC % 64 == 0)
+ *   CONVIMG_KIND_STRIP one workgroup per CU per 64 output channels: the
+ *                      weight slice for all of K and the input rows of a strip
+ *                      of output pixels held in LDS (IC a power of two >= 64,
+ *                      when they fit).  Forcing any strip entry selects this
+ *                      kernel with the chunk size the plan derives; a problem
+ *                      it cannot take falls back to the pipelined kernel.
+ * Host only. */
+#define CONVIMG_KIND_REGS  0
+#define CONVIMG_KIND_PIPE  1
+#define CONVIMG_KIND_PATCH 2
+#define CONVIMG_KIND_STRIP 3
+int conv2d_fwd_tile_kind(int tile_id);
+
 /* Split-K health on `stream`: CONVIMG_OK, or CONVIMG_ERR_TIMEOUT if a
  * workgroup gave up waiting for its turn since the last call of this
  * function (the flag is then cleared).  Synchronises the stream. */

@@ -81,12 +81,56 @@ def test_plans_of_named_workloads(lib):
     assert p["loader"] == abi.CONVIMG_LOADER_TAP and (p["OH"], p["OW"]) == (128, 128)
 
 
+def test_tile_kinds(lib):
+    kinds = [abi.conv2d_fwd_tile_kind(t) for t in range(abi.conv2d_fwd_num_tiles())]
+    assert set(kinds) == {abi.CONVIMG_KIND_REGS, abi.CONVIMG_KIND_PIPE, abi.CONVIMG_KIND_PATCH,
+                          abi.CONVIMG_KIND_STRIP}
+    assert abi.conv2d_fwd_tile_kind(-1) == -1
+    assert abi.conv2d_fwd_tile_kind(abi.conv2d_fwd_num_tiles()) == -1
+
+
+def strip_tiles():
+    return [t for t in range(abi.conv2d_fwd_num_tiles())
+            if abi.conv2d_fwd_tile_kind(t) == abi.CONVIMG_KIND_STRIP]
+
+
+def test_strip_plans(lib):
+    """A forced strip entry selects the strip kernel where the weight slice
+    and the patch fit in LDS, with one workgroup per CU per 64 channels and
+    strips that cover M; elsewhere the pipelined kernel."""
+    try:
+        for t in strip_tiles():
+            abi.conv2d_fwd_force(t, -1, -1)
+            for name, num_cus in (("resnet3x3", 256), ("resnet3x3", 80), ("dilated", 256)):
+                wl = WORKLOADS[name]
+                p = plan_of(wl, num_cus=num_cus)
+                if name == "dilated":
+                    # 64 x 1152 bf16 weights plus the patch do not fit next to each other
+                    assert abi.conv2d_fwd_tile_kind(p["tile_id"]) != abi.CONVIMG_KIND_STRIP
+                    continue
+                assert abi.conv2d_fwd_tile_kind(p["tile_id"]) == abi.CONVIMG_KIND_STRIP
+                assert p["splits"] == 1 and p["BN"] == 64 and p["threads"] == 256
+                assert p["tiles_n"] == 1 and p["grid"] == p["tiles_m"] <= num_cus
+                if num_cus == 256:      # 196 pixels per strip: one chunk of at most BM
+                    assert p["BM"] >= -(-p["M"] // p["tiles_m"])
+                assert p["lds_bytes"] <= 160 * 1024
+            # IC not a power of two, and a non-vector loader: never the strip kernel
+            for wl in (WORKLOADS["stem7x7"], WORKLOADS["resnet3x3"].scaled(IC=192)):
+                assert abi.conv2d_fwd_tile_kind(plan_of(wl)["tile_id"]) != abi.CONVIMG_KIND_STRIP
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+
+
 def test_forced_plans(lib):
     wl = WORKLOADS["largek"]
     try:
         for t in range(abi.conv2d_fwd_num_tiles()):
             assert abi.conv2d_fwd_force(t, 3, abi.CONVIMG_LOADER_VEC8) == 0
             p = plan_of(wl)
+            if abi.conv2d_fwd_tile_kind(t) == abi.CONVIMG_KIND_STRIP:
+                # 64 x 4608 bf16 weights do not fit in LDS: the pipelined kernel instead
+                assert abi.conv2d_fwd_tile_kind(p["tile_id"]) == abi.CONVIMG_KIND_PIPE
+                continue
             if p["tile_id"] != t:
                 # LDS-patch tiles take the tap-aligned loader only and do not split
                 abi.conv2d_fwd_force(t, 3, abi.CONVIMG_LOADER_TAP)
