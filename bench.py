@@ -33,23 +33,34 @@ MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per by
 
 # HBM traffic per launch measured with rocprofv3 (FETCH_SIZE then WRITE_SIZE,
 # each scaled by what the counter reads for a plain copy of known size, see
-# --copy-calibration), keyed by workload, with the hash of the kernel sources
-# the counters were taken on.  Reported only while the sources still hash to
-# that value; otherwise the kernel has changed since and traffic is null.
+# --copy-calibration), keyed by workload, with the tile the plan ran and the
+# hash of that kernel family's sources.  Reported only while the plan and
+# the sources are unchanged; otherwise traffic is null.
 TRAFFIC = {
-    # profiles/igemm_pipe_resnet3x3.md: 6.971 MB read + 12.845 MB written
-    "resnet3x3": {"bytes": 19983065, "kernel": "423d715466520959"},
+    # profiles/igemm_pipe_resnet3x3.md: 7.137 MB read + 12.845 MB written
+    "resnet3x3": {"bytes": 19981887, "tile": 11, "kernel": "48b8b53be02fd2ea"},
+    # profiles/igemm_pipe_largek.md: 89.977 MB read + 12.858 MB written
+    "largek": {"bytes": 102835250, "tile": 11, "kernel": "48b8b53be02fd2ea"},
+}
+
+# Sources each kernel family is compiled from (besides igemm_common.hpp).
+KIND_SOURCES = {
+    -1: ("igemm_regs.hpp",),                     # fp32 storage
+    0: ("igemm_regs.hpp",),                      # CONVIMG_KIND_REGS
+    1: ("igemm_pipe.hpp",),                      # CONVIMG_KIND_PIPE
+    2: ("igemm_patch.hpp", "igemm_pipe.hpp"),    # CONVIMG_KIND_PATCH
+    3: ("igemm_strip.hpp", "igemm_pipe.hpp"),    # CONVIMG_KIND_STRIP
 }
 
 
-def kernel_sources_hash():
+def kernel_sources_hash(kind):
+    """Hash of the sources of one kernel family (see KIND_SOURCES)."""
     import hashlib
     csrc = os.path.join(ROOT, "convolution_implicit_gemm_fwd_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hpp", ".hip")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in ("igemm_common.hpp",) + KIND_SOURCES[kind]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -173,8 +184,11 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(tflops / peak_flops, 4)}
+    kind = abi.conv2d_fwd_tile_kind(plan["tile_id"]) if plan["tile_id"] >= 0 else -1
+    ksrc = kernel_sources_hash(kind)
     t = TRAFFIC.get(wl.name)
-    roof["traffic"] = t["bytes"] if t and t["kernel"] == kernel_sources_hash() else None
+    roof["traffic"] = (t["bytes"] if t and t["tile"] == plan["tile_id"] and t["kernel"] == ksrc
+                       else None)
 
     line = {
         "metric": METRIC,
@@ -197,7 +211,7 @@ def main():
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 6),
-        "kernel_sources": kernel_sources_hash(),
+        "kernel_sources": ksrc,
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(inp, wl, flops, args.cpu_seconds)
