@@ -257,22 +257,21 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 struct StripPlan {
     int tile = -1;
     int strip_px = 0, chunk_px = 0, tiles_m = 0, tiles_n = 0;
-    int cpp_shift = 0, lds_zero = 0, lds_patch = 0, lds_scratch = 0, lds_bytes = 0;
+    int lds_zero = 0, lds_patch = 0, lds_scratch = 0, lds_bytes = 0;
 };
 
 bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, int tiles_n,
-                int cpp, long long zero, long long wbytes, long long patch);
+                long long zero, long long wbytes, long long patch);
 
 bool plan_strip(long long M, int H, int W, int OH, int OW, int IC, int OC, int KH, int KW,
                 int s, int p, int d, long long K, int num_cus, StripPlan *sp)
 {
     const int cpp = IC / 8;
-    if (IC % kBK != 0 || (cpp & (cpp - 1)) != 0)
+    if (IC % kBK != 0)
         return false;
     const long long zero = ((IC * 2 > 1024 ? IC * 2 : 1024) + 1023) / 1024 * 1024;
-    if (cpp % kStripWaves != 0)
-        return false;
-    const long long wbytes = (long long)kStripBN * K * 2;
+    const int rec = cpp + 1;                    // LDS record: cpp chunks and a spare
+    const long long wbytes = (long long)kStripBN * KH * KW * rec * 16;
     if (zero + wbytes + kStripScratchBytes >= kLdsBytes)
         return false;
     const int tiles_n = ceil_div(OC, kStripBN);
@@ -294,32 +293,28 @@ bool plan_strip(long long M, int H, int W, int OH, int OW, int IC, int OC, int K
             const long long e = (g + 1) * strip < M ? (g + 1) * strip : M;
             for (long long c0 = g * strip; c0 < e; c0 += chunk) {
                 const long long c1 = c0 + chunk < e ? c0 + chunk : e;
-                const StripSeg sg = strip_seg((int)c0, (int)c1, H, W, OH, OW, KH, s, p, d, cpp);
+                const StripSeg sg = strip_seg((int)c0, (int)c1, H, W, OH, OW, KH, s, p, d, rec);
                 if (sg.total_chunks * 16 > patch)
                     patch = sg.total_chunks * 16;
             }
         }
         const long long total = zero + wbytes + patch + kStripScratchBytes;
         if (total <= kLdsBytes)
-            return fill_strip(sp, strip, chunk, tiles_m, tiles_n, cpp, zero, wbytes, patch);
+            return fill_strip(sp, strip, chunk, tiles_m, tiles_n, zero, wbytes, patch);
     }
     return false;
 }
 
 bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, int tiles_n,
-                int cpp, long long zero, long long wbytes, long long patch)
+                long long zero, long long wbytes, long long patch)
 {
-    const long long blocks = (chunk + 31) / 32;     // 32-row blocks, 4 waves
+    const long long blocks = (chunk + 31) / 32;     // 32-row blocks over 4 M-groups
     const int fm = (int)((blocks + 3) / 4);
-    int shift = 0;
-    while ((1 << shift) < cpp)
-        ++shift;
     sp->tile = fm == 4 ? 30 : fm == 3 ? 31 : fm == 2 ? 32 : 33;
     sp->strip_px = (int)strip;
     sp->chunk_px = (int)chunk;
     sp->tiles_m = tiles_m;
     sp->tiles_n = tiles_n;
-    sp->cpp_shift = shift;
     sp->lds_zero = (int)zero;
     sp->lds_patch = (int)(zero + wbytes);
     sp->lds_scratch = (int)(zero + wbytes + patch);
@@ -614,9 +609,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.tiles_pad = pl.grid / pl.splits;
     a.vec_out = (((uintptr_t)out & 15) == 0 && OC % 4 == 0) ? 1 : 0;
     a.remap = pl.splits == 1 ? 1 : 0;
+    a.nfast = (pl.splits > 1 && nw > nx) ? 1 : 0;
     a.strip_px = sp.strip_px;
     a.chunk_px = sp.chunk_px;
-    a.cpp_shift = sp.cpp_shift;
     a.lds_zero = sp.lds_zero;
     a.lds_patch = sp.lds_patch;
     a.lds_scratch = sp.lds_scratch;

@@ -58,11 +58,11 @@ struct ConvArgs {
     int tiles_m, tiles_n, ktiles, splits;
     int tiles_pad;   // workgroup slots per split: tiles rounded up to a multiple of 8
     int remap;       // 1: XCD-aware order of tiles (single split only)
+    int nfast;       // 1: tiles numbered N-fastest (split-K with weights larger than x)
     int vec_out;     // 1: out is 16-byte aligned and OC % 4 == 0 (16-byte stores allowed)
     // strip kernel only
     int strip_px;    // output pixels per workgroup
     int chunk_px;    // output pixels per patch load
-    int cpp_shift;   // log2(IC / 8)
     int lds_zero, lds_patch, lds_scratch;   // LDS byte offsets: patch, epilogue scratch; zero block size
 };
 
@@ -103,8 +103,11 @@ __device__ __forceinline__ TileCoord tile_coord(const ConvArgs &a)
     t.tile = bid - t.split * a.tiles_pad;
     const int tiles = a.tiles_m * a.tiles_n;
     t.valid = t.tile < tiles;
-    const int tm = t.tile % a.tiles_m;
-    const int tn = t.tile / a.tiles_m;
+    // Split-K keeps ids round-robin over the XCDs (tile t on XCD t % 8).
+    // Numbering the tiles N-fastest then gives each XCD a fixed set of
+    // output-channel columns, so its L2 holds only those columns' weights.
+    const int tm = a.nfast ? t.tile / a.tiles_n : t.tile % a.tiles_m;
+    const int tn = a.nfast ? t.tile - tm * a.tiles_n : t.tile / a.tiles_m;
     t.m0 = tm * BM;
     t.n0 = tn * BN;
     t.kt_begin = (int)(((long long)t.split * a.ktiles) / a.splits);

@@ -1,7 +1,7 @@
 // igemm_strip.hpp -- implicit-GEMM kernel for layers whose weight slice fits
 // in LDS next to the input rows of a strip of output pixels.
 //
-// One workgroup (4 waves, one per SIMD) owns a contiguous strip of output
+// One workgroup (8 waves, two per SIMD) owns a contiguous strip of output
 // pixels (GEMM rows) and a 64-wide slice of the output channels.  It copies
 // the slice's weights for the whole K into LDS once, and for each chunk of
 // the strip every input row the chunk reads; the im2col gather then happens
@@ -13,16 +13,20 @@
 // work.
 //
 // The copies are direct-to-LDS (buffer_load ... lds, 1 KB per wave
-// instruction), so LDS areas are copied as contiguous runs of 16-byte
-// chunks:
-//   * weights: tap-major, [KH*KW][64 channel rows][IC]; chunk c of row r of
-//     a tap is stored at position c ^ (r & 7) within its group of 8;
+// instruction), so LDS areas are filled as contiguous runs of 16-byte chunks.
+// Both operands use records of cpp + 1 chunks (cpp = IC / 8): cpp chunks of
+// data and one spare, so that consecutive pixels (or channel rows) start 4
+// banks apart and the 8 lanes that read one chunk of 8 consecutive records hit
+// 8 distinct 4-bank groups, while the chunk a k step reads is a fixed byte
+// offset from the record start (an immediate of the LDS read, no per-step
+// address arithmetic):
+//   * weights: tap-major, [KH*KW][64 channel rows][cpp + 1 chunks];
 //   * patch: the input rows of each image the chunk touches, one contiguous
-//     run per image ("segment", rounded up to whole 1 KB blocks); chunk c of
-//     pixel p of a segment is stored at position c ^ (p & 7);
-// so the 8 lanes that read one chunk column of 8 consecutive pixels (or
-// channels) hit 8 distinct 4-bank groups.  Padding taps read a zero block at
-// LDS offset 0.
+//     run of pixel records per image ("segment", rounded up to whole 1 KB
+//     blocks);
+// a copy lane that lands on a spare chunk loads nothing (an out-of-range
+// offset, which writes zeros).  Padding taps read a zero block at LDS
+// offset 0.
 #pragma once
 
 #include "igemm_common.hpp"
@@ -31,9 +35,9 @@
 namespace convimg {
 
 constexpr int kStripBN = 64;      // output channels per workgroup
-constexpr int kStripWaves = 4;
+constexpr int kStripWaves = 8;    // 4 M-groups x 2 tap halves
 constexpr int kStripScratchStride = 68;   // floats per epilogue scratch row (64 + pad)
-constexpr int kStripScratchBytes = kStripWaves * 16 * kStripScratchStride * 4;
+constexpr int kStripScratchBytes = 4 * 16 * kStripScratchStride * 4;   // one 16-row tile per M-group
 
 // Input rows [lo, hi] that output rows oh_lo..oh_hi of one image read,
 // clipped to the image; returns the row count (0 if all of it is padding).
@@ -116,19 +120,31 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n)
     }
 }
 
-// FM: 32-row MFMA blocks per wave (a chunk is at most 128 * FM pixels).
-// v_mfma_f32_32x32x16_bf16 throughout: with one wave per SIMD it keeps the
-// matrix core busier than the 16x16x32 shape.
+// FM: 32-row MFMA blocks per M-group (a chunk is at most 128 * FM pixels).
+//
+// Waves: 8, two per SIMD.  Wave w computes M-group w & 3 (rows
+// [(w & 3) * FM * 32, ...) of the chunk, all 64 channels) over half of the
+// taps: w < 4 the first ceil(KH*KW / 2), w >= 4 the rest; the two waves of a
+// SIMD share one output block, so the SIMD interleaves two instruction
+// streams while LDS reads stay those of one wave per block, and the two
+// partial sums meet in LDS in the epilogue.  v_mfma_f32_32x32x16_bf16.
+//
+// Weights arrive in LDS tap by tap, in the order the tap iterations need
+// them (tap i of the first half, then tap nt0 + i of the second), copied two
+// iterations ahead of use; each iteration waits only for its own taps.
 template <int FM>
-__global__ __launch_bounds__(256) void igemm_strip_bf16(ConvArgs a)
+__global__ __launch_bounds__(kStripWaves * 64) void igemm_strip_bf16(ConvArgs a)
 {
     constexpr int FN = kStripBN / 32;
+    constexpr int NT = kStripWaves * 64;
     extern __shared__ u32x4_t dsm[];
     char *const lds = (char *)dsm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave & 3;      // M-group (and SIMD)
+    const int half = wave >> 2;    // tap half
     const int lk = lane >> 5;      // k chunk this lane feeds
     const int lr = lane & 31;      // row / column this lane feeds
 
@@ -146,15 +162,23 @@ __global__ __launch_bounds__(256) void igemm_strip_bf16(ConvArgs a)
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)a.w, 0, a.w_bytes, kRsrcWord3);
 
-    const int cpp = a.IC >> 3;              // 16-byte chunks per input pixel
-    const int cs = a.cpp_shift;             // log2(cpp)
+    const int cpp = a.IC >> 3;              // 16-byte data chunks per input pixel
+    const int rec = cpp + 1;                // chunks per LDS record (one spare)
+    const int recb = rec * 16;              // bytes per LDS record
+    const unsigned rmagic = 0xffffffffu / (unsigned)rec + 1u;   // P / rec == umulhi(P, rmagic) for P < 2^16
     const int KCH = a.K >> 3;               // 16-byte chunks per weight row
     const int zb = a.lds_zero;              // zero block bytes (at LDS offset 0)
     const int pb = a.lds_patch;             // patch offset (bytes)
     const int OHW = a.OH * a.OW;
+    const int ntaps = a.KH * a.KW;
+    const int nt0 = (ntaps + 1) >> 1;       // tap iterations (taps of the first half)
+    const int tapb = kStripBN * recb;       // bytes per tap of the weight slice
+    // weight copies per wave per tap: the tap's rec blocks of 1 KB dealt
+    // round-robin over the waves
+    const int wpt = (rec - wave + kStripWaves - 1) / kStripWaves;
 
     // ---- zero block
-    for (int i = tid; i < (zb >> 4); i += 256)
+    for (int i = tid; i < (zb >> 4); i += NT)
         dsm[i] = u32x4_t{0u, 0u, 0u, 0u};
 
     // bias of the columns this lane writes
@@ -165,26 +189,47 @@ __global__ __launch_bounds__(256) void igemm_strip_bf16(ConvArgs a)
         bv[j] = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
     }
 
+    // Weight copy of order position pos (2i: tap i, 2i + 1: tap nt0 + i):
+    // rec blocks of 1 KB per tap; chunk P of the tap's area is chunk P % rec
+    // of channel row P / rec.
+    auto issue_w = [&](int pos) {
+        if (pos >= ntaps)
+            return;
+        const int tap = (pos & 1) ? nt0 + (pos >> 1) : (pos >> 1);
+        for (int blk = wave; blk < rec; blk += kStripWaves) {
+            const int P = blk * 64 + lane;
+            const int row = (int)__umulhi((unsigned)P, rmagic), c = P - row * rec;
+            const int oc = n0 + row;
+            const unsigned off = (oc < a.OC && c < cpp)
+                ? 16u * (unsigned)(oc * KCH + tap * cpp + c) : kOutOfRange;
+            dma16(rw, (u32x4_t *)(lds + zb + tap * tapb) + blk * 64, off);
+        }
+    };
+    // Before tap iteration i: positions < min(2i + 2, ntaps) must have landed,
+    // and min(2 max(i, 1) + 4, ntaps) have been issued (the prologue issues
+    // 6, the boundary before iteration j >= 1 the 2 of iteration j + 2).
+    auto w_allowed = [&](int i) {
+        const int issued = min(2 * max(i, 1) + 4, ntaps);
+        return (issued - min(2 * i + 2, ntaps)) * wpt;
+    };
+
     // B fragment of channel row j*32 + lr, step t of tap tap (chunks 2t + lk):
-    // wrow[j] + tap * tapb + ((t << 5) ^ v16)
-    const int tapb = kStripBN * cpp * 16;       // bytes per tap of the weight slice
+    // wrow[j] + tap * tapb + 32 t
     int wrow[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-        wrow[j] = zb + (j * 32 + lr) * cpp * 16;
-    const int v16 = (lk ^ (lr & 7)) << 4;
-    const int ntaps = a.KH * a.KW;
-    const int wpt = cpp >> 2;                   // weight copies per wave per tap
+        wrow[j] = zb + (j * 32 + lr) * recb + lk * 16;
 
-    float *const scratch = (float *)(lds + a.lds_scratch) + wave * 16 * kStripScratchStride;
+    float *const scratch = (float *)(lds + a.lds_scratch) + grp * 16 * kStripScratchStride;
 
     for (int c0 = p_begin; c0 < p_end; c0 += a.chunk_px) {
         const int c1 = min(c0 + a.chunk_px, p_end);
-        if (c0 != p_begin)
+        const bool first = c0 == p_begin;
+        if (!first)
             __syncthreads();    // every wave is done with the previous patch
 
         // ---- patch: one contiguous run of input rows per image
-        const StripSeg g = strip_seg(c0, c1, a.H, a.W, a.OH, a.OW, a.KH, a.stride, a.pad, a.dil, cpp);
+        const StripSeg g = strip_seg(c0, c1, a.H, a.W, a.OH, a.OW, a.KH, a.stride, a.pad, a.dil, rec);
         {
             long long off_n = 0;
             for (int n = g.n_a; n <= g.n_b; ++n) {
@@ -196,45 +241,30 @@ __global__ __launch_bounds__(256) void igemm_strip_bf16(ConvArgs a)
                     rows = strip_rows(0, n == g.n_b ? g.oh_b : a.OH - 1, a.H, a.KH, a.stride,
                                       a.pad, a.dil, &ih_lo);
                 }
-                const int seg_chunks = rows * a.W * cpp;
+                const int seg_chunks = rows * a.W * rec;
                 const int gbase = ((n * a.H + ih_lo) * a.W) * cpp;
                 u32x4_t *dst = (u32x4_t *)(lds + pb) + off_n;
                 const int nblk = (seg_chunks + 63) >> 6;
                 for (int blk = wave; blk < nblk; blk += kStripWaves) {
                     const int P = blk * 64 + lane;
-                    const unsigned off = P < seg_chunks
-                        ? 16u * (unsigned)(gbase + (P ^ ((P >> cs) & 7))) : kOutOfRange;
+                    const int px = (int)__umulhi((unsigned)P, rmagic), c = P - px * rec;
+                    const unsigned off = (P < seg_chunks && c < cpp)
+                        ? 16u * (unsigned)(gbase + px * cpp + c) : kOutOfRange;
                     dma16(rx, dst + blk * 64, off);
                 }
                 off_n += (n == g.n_a) ? g.first_chunks : g.full_chunks;
             }
         }
+        if (first)
+            for (int pos = 0; pos < 6; ++pos)
+                issue_w(pos);
 
-        // ---- weights (first chunk only), after the patch, tap by tap: tap
-        // tau is cpp blocks of 1 KB; block b, lane l holds row (64b + l) >> cs,
-        // position (64b + l) & (cpp - 1).  Each wave issues wpt copies per tap,
-        // so before tap tau a wave waits until at most
-        // (ntaps - 1 - tau) * wpt of its copies are outstanding.
-        if (c0 == p_begin) {
-            for (int tap = 0; tap < ntaps; ++tap) {
-                for (int blk = wave; blk < cpp; blk += kStripWaves) {
-                    const int P = blk * 64 + lane;
-                    const int row = P >> cs, c = P & (cpp - 1);
-                    const int oc = n0 + row;
-                    const unsigned off = oc < a.OC
-                        ? 16u * (unsigned)(oc * KCH + tap * cpp + (c ^ (row & 7))) : kOutOfRange;
-                    dma16(rw, (u32x4_t *)(lds + zb + tap * tapb) + blk * 64, off);
-                }
-            }
-        }
-
-        // ---- per-block pixel geometry (block i of this wave: rows
-        // c0 + (wave * FM + i) * 32 + lr)
+        // ---- per-block pixel geometry (block i: rows c0 + (grp*FM + i)*32 + lr)
         int pix0[FM], ih0[FM], iw0[FM], segb[FM];
         bool vm[FM];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int m = c0 + (wave * FM + i) * 32 + lr;
+            const int m = c0 + (grp * FM + i) * 32 + lr;
             vm[i] = m < c1;
             const int mm = vm[i] ? m : c0;
             const int n = mm / OHW;
@@ -253,7 +283,7 @@ __global__ __launch_bounds__(256) void igemm_strip_bf16(ConvArgs a)
                 so = g.first_chunks + (long long)(n - g.n_a - 1) * g.full_chunks;
             }
             pix0[i] = (ih0[i] - ihl) * a.W + iw0[i];
-            segb[i] = pb + (int)so * 16;
+            segb[i] = pb + (int)so * 16 + lk * 16;
         }
 
         floatx16_t acc[FM][FN];
@@ -263,44 +293,42 @@ __global__ __launch_bounds__(256) void igemm_strip_bf16(ConvArgs a)
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = floatx16_t{};
 
-        // patch and the first tap's weights; on later chunks every weight
-        // copy is long complete and nothing newer than the patch is in flight
-        wait_vmcnt_rt(c0 == p_begin ? (ntaps - 1) * wpt : 0);
+        // patch and the first iteration's taps; on later chunks only the
+        // patch is in flight
+        wait_vmcnt_rt(first ? w_allowed(0) : 0);
         __syncthreads();
 
-        // ---- K loop: taps in (kh, kw) order, T = IC / 16 MFMA k steps per
-        // tap (a multiple of 4).  The fragments of step k + 1 are read from
-        // LDS while the MFMAs of step k run (two register sets, and a
-        // scheduling barrier that keeps the reads ahead of the MFMAs), so
-        // LDS latency hides behind matrix work with one wave per SIMD.
-        // A fragment of pixel pix, chunk 2t + lk of the tap: the tap's
-        // address (t = 0) ^ (t << 5), since the chunk's low 3 bits are XORed
-        // with pix & 7 and the pixel record is cpp * 16 bytes aligned.
-        const int T = a.IC >> 4;
-        int akh = 0, akw = 0;       // tap whose A addresses are computed next
+        // ---- K loop: tap iterations x 64-channel slices x 4 MFMA k steps.
+        // The fragments of step k + 1 are read from LDS while the MFMAs of
+        // step k run (two register sets, and a scheduling barrier that keeps
+        // the reads ahead of the MFMAs).  Step t of a slice reads chunk
+        // 2t + lk of the slice: the slice's address + 32 t, an immediate.
+        const int nsl = a.IC >> 6;
+        int abase[FM];              // record of the block's pixel at tap (0, 0), + lk chunk
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            abase[i] = segb[i] + pix0[i] * recb;
+        int tap_next = half ? nt0 : 0;      // tap whose A addresses are computed next
         auto tap_addr = [&](int (&aa)[FM]) {
-            const int dh = akh * a.dil, dw = akw * a.dil;
-            const int dpix = dh * a.W + dw;
+            const int kh = tap_next / a.KW, kw = tap_next - kh * a.KW;
+            const int dh = kh * a.dil, dw = kw * a.dil;
+            const int dofs = (dh * a.W + dw) * recb;
+            const bool tap_ok = tap_next < ntaps;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int pix = pix0[i] + dpix;
-                const bool ok = vm[i] && (unsigned)(ih0[i] + dh) < (unsigned)a.H
+                const bool ok = tap_ok && vm[i] && (unsigned)(ih0[i] + dh) < (unsigned)a.H
                     && (unsigned)(iw0[i] + dw) < (unsigned)a.W;
-                aa[i] = ok ? segb[i] + (pix << (cs + 4)) + (((pix & 7) ^ lk) << 4) : 0;
+                aa[i] = ok ? abase[i] + dofs : 0;
             }
-            if (++akw == a.KW) {
-                akw = 0;
-                ++akh;
-            }
+            ++tap_next;
         };
-        // wofs: tap * tapb + ((t << 5) ^ v16) of the step to read
-        auto load = [&](const int (&aa)[FM], int wofs, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
+        auto load = [&](const int (&aa)[FM], int wofs, int imm, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                fa[i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(lds + aa[i]));
+                fa[i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(lds + aa[i] + imm));
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                fb[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(lds + wrow[j] + wofs));
+                fb[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(lds + wrow[j] + wofs + imm));
         };
         auto mma = [&](const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) {
 #pragma unroll
@@ -310,76 +338,102 @@ __global__ __launch_bounds__(256) void igemm_strip_bf16(ConvArgs a)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         };
 
-        int a_cur[FM], a_nxt[FM], a_ld[FM];
-        tap_addr(a_cur);
+        int a_sl[FM], a_nxt[FM], a_nsl[FM];
+        tap_addr(a_sl);
         bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-        load(a_cur, v16, fa0, fb0);
-        for (int tap = 0; tap < ntaps; ++tap) {
-            const int tofs = tap * tapb;
-            if (tap + 1 < ntaps)
-                tap_addr(a_nxt);
-            else
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    a_nxt[i] = a_cur[i];    // harmless reads past the last step
-            for (int t = 0; t < T; t += 2) {
-                // fa0/fb0 hold step t of this tap
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    a_ld[i] = a_cur[i] ^ ((t + 1) << 5);
-                load(a_ld, tofs + (((t + 1) << 5) ^ v16), fa1, fb1);
+        int tap = half ? nt0 : 0;           // tap of this wave's current iteration
+        int w_sl = min(tap, ntaps - 1) * tapb;  // B offset of the current slice
+        load(a_sl, w_sl, 0, fa0, fb0);
+        for (int it = 0; it < nt0; ++it, ++tap) {
+            const bool act = tap < ntaps;   // the second half may have one tap fewer
+            const int nofs = min(tap + 1, ntaps - 1) * tapb;    // next tap (clamped)
+            tap_addr(a_nxt);
+            for (int sl = 0; sl < nsl; ++sl) {
+                const bool last_sl = sl + 1 == nsl;
+                // fa0/fb0 hold step 0 of this slice
+                load(a_sl, w_sl, 32, fa1, fb1);
                 __builtin_amdgcn_sched_barrier(0);  // the reads go out before the MFMAs
-                mma(fa0, fb0);
-                const bool last = t + 2 == T;
-                if (last && c0 == p_begin && tap + 1 < ntaps) {
-                    wait_vmcnt_rt((ntaps - 2 - tap) * wpt);   // next tap's weights
+                if (act)
+                    mma(fa0, fb0);
+                load(a_sl, w_sl, 64, fa0, fb0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (act)
+                    mma(fa1, fb1);
+                load(a_sl, w_sl, 96, fa1, fb1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (act)
+                    mma(fa0, fb0);
+                if (last_sl && first && it + 1 < nt0) {
+                    wait_vmcnt_rt(w_allowed(it + 1));   // next iteration's taps
                     __syncthreads();
+                    issue_w(2 * (it + 1) + 4);      // the taps of iteration it + 3
+                    issue_w(2 * (it + 1) + 5);
                 }
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
-                    a_ld[i] = last ? a_nxt[i] : (a_cur[i] ^ ((t + 2) << 5));
-                load(a_ld, last ? tofs + tapb + v16 : tofs + (((t + 2) << 5) ^ v16), fa0, fb0);
+                    a_nsl[i] = last_sl ? a_nxt[i] : a_sl[i] + 128;
+                const int w_nsl = last_sl ? nofs : w_sl + 128;
+                load(a_nsl, w_nsl, 0, fa0, fb0);
                 __builtin_amdgcn_sched_barrier(0);
-                mma(fa1, fb1);
-            }
+                if (act)
+                    mma(fa1, fb1);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                a_cur[i] = a_nxt[i];
+                for (int i = 0; i < FM; ++i)
+                    a_sl[i] = a_nsl[i];
+                w_sl = w_nsl;
+            }
         }
 
-        // ---- epilogue: + bias, through the wave's scratch (16 rows at a
-        // time) into 16-byte stores of whole 64-channel row segments.  Value
-        // v of block (i, j) is row 8*(v >> 2) + 4*lk + (v & 3), column
-        // j*32 + lr; half h holds v = 8h .. 8h + 7, rows 16h .. 16h + 15.
+        // ---- epilogue: the two partial sums of each block meet in the
+        // group's scratch (16 rows at a time); the owner of a round adds its
+        // own part and the bias and stores whole 64-channel row segments with
+        // 16-byte stores.  Value v of block (i, j) is row 8*(v >> 2) + 4*lk +
+        // (v & 3), column j*32 + lr; half h of a block holds v = 8h .. 8h + 7,
+        // rows 16h .. 16h + 15.  Rounds alternate the owner between the waves.
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                const bool owner = half == h;
+                if (!owner) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
+                    for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int v = 8 * h; v < 8 * h + 8; ++v)
-                        scratch[(8 * ((v >> 2) - 2 * h) + 4 * lk + (v & 3)) * kStripScratchStride
-                                + j * 32 + lr] = acc[i][j][v] + bv[j];
+                        for (int v = 8 * h; v < 8 * h + 8; ++v)
+                            scratch[(8 * ((v >> 2) - 2 * h) + 4 * lk + (v & 3)) * kStripScratchStride
+                                    + j * 32 + lr] = acc[i][j][v];
+                }
+                __syncthreads();
+                if (owner) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int f = t * 64 + lane;
-                    const int row = f >> 4, c4 = (f & 15) * 4;
-                    const floatx4_t val = *(const floatx4_t *)(scratch + row * kStripScratchStride + c4);
-                    const int m = c0 + (wave * FM + i) * 32 + 16 * h + row;
-                    const int oc = n0 + c4;
-                    if (m < c1) {
-                        float *o = a.out + (long long)m * a.OC + oc;
-                        if (a.vec_out && oc + 3 < a.OC) {
-                            *(floatx4_t *)o = val;
-                        } else {
+                    for (int j = 0; j < FN; ++j)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (oc + e < a.OC)
-                                    o[e] = val[e];
+                        for (int v = 8 * h; v < 8 * h + 8; ++v) {
+                            float *e = scratch + (8 * ((v >> 2) - 2 * h) + 4 * lk + (v & 3)) * kStripScratchStride
+                                + j * 32 + lr;
+                            *e = *e + acc[i][j][v] + bv[j];
+                        }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int f = t * 64 + lane;
+                        const int row = f >> 4, c4 = (f & 15) * 4;
+                        const floatx4_t val = *(const floatx4_t *)(scratch + row * kStripScratchStride + c4);
+                        const int m = c0 + (grp * FM + i) * 32 + 16 * h + row;
+                        const int oc = n0 + c4;
+                        if (m < c1) {
+                            float *o = a.out + (long long)m * a.OC + oc;
+                            if (a.vec_out && oc + 3 < a.OC) {
+                                *(floatx4_t *)o = val;
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (oc + e < a.OC)
+                                        o[e] = val[e];
+                            }
                         }
                     }
                 }
+                __syncthreads();
             }
         }
     }
