@@ -68,10 +68,8 @@ constexpr TileCfg kTiles[] = {
     {kPatch, 128, 64, 4, 1, 3, 32, "patch 128x64 w4x1", 384}, // 27: wave 32x64
     {kPatch, 256, 64, 4, 1, 9, 32, "patch 256x64 s9", 512},  // 28: all 3x3 weight taps in flight
     {kPatch, 128, 64, 2, 2, 9, 32, "patch 128x64 s9", 384},  // 29
-    {kStrip, 512, 64, 4, 1, 1, 32, "strip 512"},            // 30: chunks of up to 512 pixels
-    {kStrip, 384, 64, 4, 1, 1, 32, "strip 384"},            // 31
-    {kStrip, 256, 64, 4, 1, 1, 32, "strip 256"},            // 32
-    {kStrip, 128, 64, 4, 1, 1, 32, "strip 128"},            // 33
+    {kStrip, 256, 64, 4, 1, 1, 32, "strip 256"},            // 30: chunks of up to 256 pixels
+    {kStrip, 128, 64, 4, 1, 1, 32, "strip 128"},            // 31
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kLdsBytes = 160 * 1024;     // LDS per CU (and per workgroup) on gfx950
@@ -86,7 +84,7 @@ constexpr KernelFn kfn()
     if constexpr (c.kind == kRegs)
         return &igemm_regs_bf16<c.BM, c.BN, c.WM, L>;
     else if constexpr (c.kind == kStrip)
-        return L == kLoaderTap ? &igemm_strip_bf16<c.BM / 128> : nullptr;
+        return L == kLoaderTap ? &igemm_strip_bf16<c.BM / 128> : nullptr;   // FM
     else if constexpr (c.kind == kPatch)
         return L == kLoaderTap ? &igemm_patch_bf16<c.BM, c.BN, c.WM, c.WN, c.stages, c.patch_px>
                                : nullptr;
@@ -111,7 +109,10 @@ constexpr std::array<std::array<KernelFn, kNumLoaders>, sizeof...(T)> ktable(std
 const std::array<std::array<KernelFn, kNumLoaders>, kNumTiles> kKernels =
     ktable(std::make_integer_sequence<int, kNumTiles>{});
 
-int threads_of(int tile) { return kTiles[tile].WM * kTiles[tile].WN * 64; }
+int threads_of(int tile)
+{
+    return kTiles[tile].kind == kStrip ? kStripThreads : kTiles[tile].WM * kTiles[tile].WN * 64;
+}
 
 int lds_bytes_of(int tile)
 {
@@ -257,7 +258,7 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 struct StripPlan {
     int tile = -1;
     int strip_px = 0, chunk_px = 0, tiles_m = 0, tiles_n = 0;
-    int lds_zero = 0, lds_patch = 0, lds_scratch = 0, lds_bytes = 0;
+    int lds_zero = 0, lds_patch = 0, lds_scratch = 0, lds_flags = 0, lds_bytes = 0;
 };
 
 bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, int tiles_n,
@@ -282,8 +283,10 @@ bool plan_strip(long long M, int H, int W, int OH, int OW, int IC, int OC, int K
     if (strip < 32)
         strip = 32;
     const int tiles_m = ceil_div(M, strip);
-    // the largest chunk whose patch fits next to the weights
-    for (int cap = 512; cap >= 128; cap /= 2) {
+    // the largest chunk whose patch fits next to the weights (at most 256
+    // pixels: 2 blocks of 32 rows per M-group keep a compute wave within the
+    // registers of 3 waves per SIMD)
+    for (int cap = 256; cap >= 128; cap /= 2) {
         const long long nc = (strip + cap - 1) / cap;
         if ((long long)tiles_m * nc > (1 << 22))
             return false;
@@ -298,7 +301,7 @@ bool plan_strip(long long M, int H, int W, int OH, int OW, int IC, int OC, int K
                     patch = sg.total_chunks * 16;
             }
         }
-        const long long total = zero + wbytes + patch + kStripScratchBytes;
+        const long long total = zero + wbytes + patch + kStripScratchBytes + kStripTailBytes;
         if (total <= kLdsBytes)
             return fill_strip(sp, strip, chunk, tiles_m, tiles_n, zero, wbytes, patch);
     }
@@ -309,8 +312,7 @@ bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, in
                 long long zero, long long wbytes, long long patch)
 {
     const long long blocks = (chunk + 31) / 32;     // 32-row blocks over 4 M-groups
-    const int fm = (int)((blocks + 3) / 4);
-    sp->tile = fm == 4 ? 30 : fm == 3 ? 31 : fm == 2 ? 32 : 33;
+    sp->tile = blocks > 4 ? 30 : 31;
     sp->strip_px = (int)strip;
     sp->chunk_px = (int)chunk;
     sp->tiles_m = tiles_m;
@@ -318,7 +320,8 @@ bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, in
     sp->lds_zero = (int)zero;
     sp->lds_patch = (int)(zero + wbytes);
     sp->lds_scratch = (int)(zero + wbytes + patch);
-    sp->lds_bytes = (int)(zero + wbytes + patch + kStripScratchBytes);
+    sp->lds_flags = (int)(zero + wbytes + patch + kStripScratchBytes);
+    sp->lds_bytes = (int)(zero + wbytes + patch + kStripScratchBytes + kStripTailBytes);
     return true;
 }
 
@@ -420,7 +423,7 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
             pl->tiles_n = sp.tiles_n;
             pl->ktiles = ceil_div(K, kBK);
             pl->grid = sp.tiles_m * sp.tiles_n;
-            pl->threads = kStripWaves * 64;
+            pl->threads = kStripThreads;
             pl->lds_bytes = sp.lds_bytes;
             if (spo)
                 *spo = sp;
@@ -615,6 +618,7 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.lds_zero = sp.lds_zero;
     a.lds_patch = sp.lds_patch;
     a.lds_scratch = sp.lds_scratch;
+    a.lds_flags = sp.lds_flags;
 
     if (pl.splits > 1) {
         rc = get_semaphores(dev, stream, pl.tiles_m * pl.tiles_n + 1, &a.sem);

@@ -63,7 +63,7 @@ struct ConvArgs {
     // strip kernel only
     int strip_px;    // output pixels per workgroup
     int chunk_px;    // output pixels per patch load
-    int lds_zero, lds_patch, lds_scratch;   // LDS byte offsets: patch, epilogue scratch; zero block size
+    int lds_zero, lds_patch, lds_scratch, lds_flags;   // LDS: zero block size; offsets of patch, epilogue scratch, progress words
 };
 
 // Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them

@@ -127,8 +127,8 @@ int conv2d_fwd_num_tiles(void);
  *   CONVIMG_KIND_PATCH pipeline with an LDS patch of input rows (IC % 64 == 0)
  *   CONVIMG_KIND_STRIP one workgroup per CU per 64 output channels: the
  *                      weight slice for all of K and the input rows of a strip
- *                      of output pixels held in LDS (IC a power of two >= 64,
- *                      when they fit).  Forcing any strip entry selects this
+ *                      of output pixels held in LDS (IC % 64 == 0, when
+ *                      they fit).  Forcing any strip entry selects this
  *                      kernel with the chunk size the plan derives; a problem
  *                      it cannot take falls back to the pipelined kernel.
  * Host only. */
