@@ -50,6 +50,7 @@ KIND_SOURCES = {
     1: ("igemm_pipe.hpp",),                      # CONVIMG_KIND_PIPE
     2: ("igemm_patch.hpp", "igemm_pipe.hpp"),    # CONVIMG_KIND_PATCH
     3: ("igemm_strip.hpp", "igemm_pipe.hpp"),    # CONVIMG_KIND_STRIP
+    4: ("igemm_window.hpp", "igemm_pipe.hpp"),   # CONVIMG_KIND_WINDOW
 }
 
 

@@ -6,6 +6,7 @@
 #include "igemm_pipe.hpp"
 #include "igemm_regs.hpp"
 #include "igemm_strip.hpp"
+#include "igemm_window.hpp"
 
 #include <array>
 #include <atomic>
@@ -27,9 +28,10 @@ namespace {
 // including the element-wise edge path); kPipe entries use the direct-to-LDS
 // pipelined kernel (vector loaders only); kPatch entries the pipelined kernel
 // with an LDS patch of input rows; kStrip entries the strip kernel (BM is the
-// largest chunk of pixels: 4 waves x BM / 128 blocks of 32 rows).
+// largest chunk of pixels: 4 waves x BM / 128 blocks of 32 rows); the
+// kWindow entry the few-channel kernel (every loader slot).
 // ---------------------------------------------------------------------------
-enum Kind { kRegs = 0, kPipe = 1, kPatch = 2, kStrip = 3 };
+enum Kind { kRegs = 0, kPipe = 1, kPatch = 2, kStrip = 3, kWindow = 4 };
 
 struct TileCfg {
     int kind, BM, BN, WM, WN, stages, ms;
@@ -70,9 +72,11 @@ constexpr TileCfg kTiles[] = {
     {kPatch, 128, 64, 2, 2, 9, 32, "patch 128x64 s9", 384},  // 29
     {kStrip, 256, 64, 4, 1, 1, 32, "strip 256"},            // 30: chunks of up to 256 pixels
     {kStrip, 128, 64, 4, 1, 1, 32, "strip 128"},            // 31
+    {kWindow, 128, 64, 4, 1, 1, 32, "window"},              // 32: few input channels
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kLdsBytes = 160 * 1024;     // LDS per CU (and per workgroup) on gfx950
+constexpr int kWindowTile = 32;           // the kWindow entry
 constexpr int kNumLoaders = 3;
 
 typedef void (*KernelFn)(ConvArgs);
@@ -83,6 +87,8 @@ constexpr KernelFn kfn()
     constexpr TileCfg c = kTiles[T];
     if constexpr (c.kind == kRegs)
         return &igemm_regs_bf16<c.BM, c.BN, c.WM, L>;
+    else if constexpr (c.kind == kWindow)
+        return &igemm_window_bf16;
     else if constexpr (c.kind == kStrip)
         return L == kLoaderTap ? &igemm_strip_bf16<c.BM / 128> : nullptr;   // FM
     else if constexpr (c.kind == kPatch)
@@ -111,7 +117,9 @@ const std::array<std::array<KernelFn, kNumLoaders>, kNumTiles> kKernels =
 
 int threads_of(int tile)
 {
-    return kTiles[tile].kind == kStrip ? kStripThreads : kTiles[tile].WM * kTiles[tile].WN * 64;
+    return kTiles[tile].kind == kStrip ? kStripThreads
+         : kTiles[tile].kind == kWindow ? kWinThreads
+         : kTiles[tile].WM * kTiles[tile].WN * 64;
 }
 
 int lds_bytes_of(int tile)
@@ -119,7 +127,7 @@ int lds_bytes_of(int tile)
     const TileCfg &c = kTiles[tile];
     if (c.kind == kPatch)
         return (c.patch_px + 1) * kChunks * 16 + c.stages * c.BN * kChunks * 16;
-    if (c.kind == kStrip)
+    if (c.kind == kStrip || c.kind == kWindow)
         return kLdsBytes;       // sized per problem; one workgroup per CU
     return c.stages * (c.BM + c.BN) * kChunks * 16;
 }
@@ -181,9 +189,10 @@ int device_info(int dev, DeviceInfo **out)
             || info.num_cus <= 0)
             return CONVIMG_ERR_DEVICE;
         for (int t = 0; t < kNumTiles; ++t)
-            if (kTiles[t].kind == kStrip && kKernels[t][kLoaderTap] != nullptr)
-                (void)hipFuncSetAttribute((const void *)kKernels[t][kLoaderTap],
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+            for (int l = 0; l < kNumLoaders; ++l)
+                if ((kTiles[t].kind == kStrip || kTiles[t].kind == kWindow) && kKernels[t][l] != nullptr)
+                    (void)hipFuncSetAttribute((const void *)kKernels[t][l],
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         for (int t = 0; t < kNumTiles; ++t)
             for (int l = 0; l < kNumLoaders; ++l) {
                 int nb = 1;
@@ -264,6 +273,61 @@ struct StripPlan {
 bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, int tiles_n,
                 long long zero, long long wbytes, long long patch);
 
+// Window kernel plan (few input channels): one kernel row of the receptive
+// field fits in 32 k values, windows start at even elements for every pixel
+// and row (s*IC and W*IC even), x reached with 32-bit offsets in 16-byte
+// chunks, out with 32-bit store offsets.  (Odd s*IC or W*IC would need two
+// weight layouts; those shapes keep the element-wise gather.)  One workgroup per CU per 64
+// channels; units (up to 128 pixels of one output row) split evenly.
+struct WinPlan {
+    int seg = 0, segs = 0, per = 0, sh = 0, wp = 0, rb = 0;
+    int tiles_m = 0, tiles_n = 0, lds_rows = 0, lds_bytes = 0;
+};
+
+bool plan_window(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
+                 int OH, int OW, long long M, int num_cus, WinPlan *wp)
+{
+    const long long lim = 0x7fffffffLL;
+    const int sh = (p * IC) & 1;
+    const long long span = ((long long)(KW - 1) * d + 1) * IC;
+    if (KH > kWinMaxKH || span + sh > 32 || (s * IC) % 2 != 0 || (W * IC) % 2 != 0)
+        return false;
+    // (a 16-byte copy may run past the end of x: buffer loads check the
+    // range per dword, so the dwords inside x still arrive)
+    const long long xbytes = (long long)N * H * W * IC * 2;
+    if (xbytes % 4 != 0 || xbytes >= lim || M * OC * 4 >= lim)
+        return false;
+    const int segs = ceil_div(OW, kWinSeg);
+    const int seg = ceil_div(OW, segs);
+    // every wave reads its 32 pixels' windows, also past the unit's last
+    // pixel (those results are not stored): size the row buffers for 128.
+    // The run starts up to 14 bytes into its buffer (the copy starts at the
+    // 16-byte boundary below it) and ends 2 * jall bytes later.
+    const long long jall = (long long)(kWinSeg - 1) * s * IC + 32;
+    const long long rb = (16 + 2 * jall + 1023) / 1024 * 1024;
+    const int wrow = ((KH * 32 + 8) * 2 + 15) / 16 * 16;
+    const long long lds = 64LL * wrow + 2LL * KH * rb;
+    if (lds > kLdsBytes)
+        return false;
+    const int tiles_n = ceil_div(OC, 64);
+    int gm = num_cus / tiles_n;
+    if (gm < 1)
+        gm = 1;
+    const long long units = (long long)N * OH * segs;
+    const long long per = (units + gm - 1) / gm;
+    wp->seg = seg;
+    wp->segs = segs;
+    wp->per = (int)per;
+    wp->sh = sh;
+    wp->wp = wrow;
+    wp->rb = (int)rb;
+    wp->tiles_m = (int)((units + per - 1) / per);
+    wp->tiles_n = tiles_n;
+    wp->lds_rows = 64 * wrow;
+    wp->lds_bytes = (int)lds;
+    return true;
+}
+
 bool plan_strip(long long M, int H, int W, int OH, int OW, int IC, int OC, int KH, int KW,
                 int s, int p, int d, long long K, int num_cus, StripPlan *sp)
 {
@@ -330,7 +394,8 @@ bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, in
 // CU for each kernel; NULL uses the LDS-only estimate.
 int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
               int dtype, int num_cus, bool aligned,
-              const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo = nullptr)
+              const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo = nullptr,
+              WinPlan *wpo = nullptr)
 {
     if (N <= 0 || H <= 0 || W <= 0 || IC <= 0 || OC <= 0 || KH <= 0 || KW <= 0
         || s <= 0 || p < 0 || d <= 0)
@@ -399,6 +464,9 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     StripPlan sp;
     const bool strip_ok = pipe_ok && loader == CONVIMG_LOADER_TAP
         && plan_strip(M, H, W, OH, OW, IC, OC, KH, KW, s, p, d, K, num_cus, &sp);
+    WinPlan wnp;
+    const bool window_ok = aligned
+        && plan_window(N, H, W, IC, OC, KH, KW, s, p, d, OH, OW, M, num_cus, &wnp);
     int tile;
     if (pipe_ok) {
         const long long big = ((M + 255) / 256) * ((OC + 127) / 128);
@@ -408,9 +476,31 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     } else {
         tile = 1;
     }
+    if (window_ok && loader == CONVIMG_LOADER_SCALAR)
+        tile = kWindowTile;     // few channels: the window kernel instead of the element-wise gather
     const int ft = g_force_tile.load();
     if (ft >= 0 && ft < kNumTiles)
         tile = ft;
+    if (kTiles[tile].kind == kWindow) {
+        if (window_ok) {
+            pl->tile_id = tile;
+            pl->BM = wnp.seg;
+            pl->BN = 64;
+            pl->BK = 32;
+            pl->loader = loader;
+            pl->splits = 1;
+            pl->tiles_m = wnp.tiles_m;
+            pl->tiles_n = wnp.tiles_n;
+            pl->ktiles = KH;            // K laid out as KH steps of 32
+            pl->grid = wnp.tiles_m * wnp.tiles_n;
+            pl->threads = kWinThreads;
+            pl->lds_bytes = wnp.lds_bytes;
+            if (wpo)
+                *wpo = wnp;
+            return CONVIMG_OK;
+        }
+        tile = pipe_ok ? 11 : 0;    // a forced window the problem cannot use
+    }
     if (kTiles[tile].kind == kStrip) {
         if (strip_ok) {
             pl->tile_id = sp.tile;
@@ -511,8 +601,10 @@ int conv2d_fwd_tile_kind(int tile_id)
     if (tile_id < 0 || tile_id >= kNumTiles)
         return -1;
     static_assert(kRegs == CONVIMG_KIND_REGS && kPipe == CONVIMG_KIND_PIPE
-                      && kPatch == CONVIMG_KIND_PATCH && kStrip == CONVIMG_KIND_STRIP,
+                      && kPatch == CONVIMG_KIND_PATCH && kStrip == CONVIMG_KIND_STRIP
+                      && kWindow == CONVIMG_KIND_WINDOW,
                   "kind codes");
+    static_assert(kTiles[kWindowTile].kind == kWindow, "window tile index");
     return kTiles[tile_id].kind;
 }
 
@@ -577,8 +669,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
         return rc;
     const bool aligned = (((uintptr_t)x | (uintptr_t)w) & 15) == 0;
     StripPlan sp;
+    WinPlan wnp;
     rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned,
-                   info->occ, &pl, &sp);
+                   info->occ, &pl, &sp, &wnp);
     if (rc != CONVIMG_OK)
         return rc;
 
@@ -619,6 +712,13 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.lds_patch = sp.lds_patch;
     a.lds_scratch = sp.lds_scratch;
     a.lds_flags = sp.lds_flags;
+    a.win_seg = wnp.seg;
+    a.win_segs = wnp.segs;
+    a.win_per = wnp.per;
+    a.win_sh = wnp.sh;
+    a.win_wp = wnp.wp;
+    a.win_rb = wnp.rb;
+    a.lds_rows = wnp.lds_rows;
 
     if (pl.splits > 1) {
         rc = get_semaphores(dev, stream, pl.tiles_m * pl.tiles_n + 1, &a.sem);
@@ -634,7 +734,7 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
 
     if (dtype == CONVIMG_FP32)
         hipLaunchKernelGGL(igemm_fwd_f32, dim3(pl.grid), dim3(kRegsThreads), 0, stream, a);
-    else if (kTiles[pl.tile_id].kind == kStrip)
+    else if (kTiles[pl.tile_id].kind == kStrip || kTiles[pl.tile_id].kind == kWindow)
         hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(pl.threads),
                            (unsigned)pl.lds_bytes, stream, a);
     else

@@ -131,11 +131,17 @@ int conv2d_fwd_num_tiles(void);
  *                      they fit).  Forcing any strip entry selects this
  *                      kernel with the chunk size the plan derives; a problem
  *                      it cannot take falls back to the pipelined kernel.
+ *   CONVIMG_KIND_WINDOW few input channels (the fast edge path, e.g. IC = 3):
+ *                      one kernel row of the receptive field, ((KW-1)*d+1)*IC
+ *                      elements, fits in 32 k values; input rows copied to
+ *                      LDS, weights in registers.  Chosen automatically where
+ *                      the element-wise gather would run and it applies.
  * Host only. */
-#define CONVIMG_KIND_REGS  0
-#define CONVIMG_KIND_PIPE  1
-#define CONVIMG_KIND_PATCH 2
-#define CONVIMG_KIND_STRIP 3
+#define CONVIMG_KIND_REGS   0
+#define CONVIMG_KIND_PIPE   1
+#define CONVIMG_KIND_PATCH  2
+#define CONVIMG_KIND_STRIP  3
+#define CONVIMG_KIND_WINDOW 4
 int conv2d_fwd_tile_kind(int tile_id);
 
 /* Split-K health on `stream`: CONVIMG_OK, or CONVIMG_ERR_TIMEOUT if a

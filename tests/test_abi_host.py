@@ -76,7 +76,10 @@ def test_plans_of_named_workloads(lib):
     assert p["grid"] == (tiles + 7) // 8 * 8 * p["splits"]      # slots per split padded to 8
     p = plan_of(WORKLOADS["stem7x7"])
     assert p["loader"] == abi.CONVIMG_LOADER_SCALAR and (p["OH"], p["OW"]) == (112, 112)
-    assert p["K"] == 147 and p["ktiles"] == 3
+    # 3 channels: the window kernel (7 kernel rows of 21 <= 32 k values each)
+    assert abi.conv2d_fwd_tile_kind(p["tile_id"]) == abi.CONVIMG_KIND_WINDOW
+    assert p["K"] == 147 and p["ktiles"] == 7 and p["BK"] == 32
+    assert p["grid"] == p["tiles_m"] * p["tiles_n"] <= 256 and p["BM"] == 112
     p = plan_of(WORKLOADS["dilated"])
     assert p["loader"] == abi.CONVIMG_LOADER_TAP and (p["OH"], p["OW"]) == (128, 128)
 
@@ -84,7 +87,7 @@ def test_plans_of_named_workloads(lib):
 def test_tile_kinds(lib):
     kinds = [abi.conv2d_fwd_tile_kind(t) for t in range(abi.conv2d_fwd_num_tiles())]
     assert set(kinds) == {abi.CONVIMG_KIND_REGS, abi.CONVIMG_KIND_PIPE, abi.CONVIMG_KIND_PATCH,
-                          abi.CONVIMG_KIND_STRIP}
+                          abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW}
     assert abi.conv2d_fwd_tile_kind(-1) == -1
     assert abi.conv2d_fwd_tile_kind(abi.conv2d_fwd_num_tiles()) == -1
 
@@ -128,8 +131,9 @@ def test_forced_plans(lib):
         for t in range(abi.conv2d_fwd_num_tiles()):
             assert abi.conv2d_fwd_force(t, 3, abi.CONVIMG_LOADER_VEC8) == 0
             p = plan_of(wl)
-            if abi.conv2d_fwd_tile_kind(t) == abi.CONVIMG_KIND_STRIP:
-                # 64 x 4608 bf16 weights do not fit in LDS: the pipelined kernel instead
+            if abi.conv2d_fwd_tile_kind(t) in (abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW):
+                # 64 x 4608 bf16 weights do not fit in LDS, and 512 channels are
+                # far more than a window holds: the pipelined kernel instead
                 assert abi.conv2d_fwd_tile_kind(p["tile_id"]) == abi.CONVIMG_KIND_PIPE
                 continue
             if p["tile_id"] != t:

@@ -114,6 +114,29 @@ def test_forced_variants(wl):
                 parity(wl, seed=5, force=(tile, splits, loader), ref=ref)
 
 
+WINDOW_SHAPES = [
+    shape(2, 40, 36, 3, 64, 7, 7, 2, 3, 1, name="stem-like"),
+    shape(1, 17, 300, 3, 16, 7, 7, 2, 3, 1, name="rows of 2 units"),   # OW 150; x ends mid-chunk
+    shape(2, 20, 22, 3, 70, 3, 3, 2, 1, 1, name="3x3 s2, OC tail"),
+    shape(1, 15, 15, 4, 64, 5, 5, 1, 2, 1, name="IC 4 s1"),
+    shape(1, 19, 18, 2, 33, 5, 3, 1, 3, 2, name="IC 2 dilated"),
+    shape(2, 9, 10, 1, 64, 7, 7, 2, 3, 1, name="IC 1 s2"),
+    shape(1, 12, 14, 6, 129, 3, 5, 2, 0, 1, name="IC 6 no pad, 3 slices"),
+    shape(3, 5, 6, 3, 8, 3, 3, 2, 4, 1, name="padding beyond window"),
+]
+
+
+@pytest.mark.parametrize("wl", WINDOW_SHAPES, ids=lambda w: w.name)
+def test_window_kernel(wl):
+    """Few-channel layers take the window kernel; parity with the oracle,
+    masked rows and channels, rows split into several units."""
+    rc, plan = abi.conv2d_fwd_plan(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride,
+                                   wl.pad, wl.dilation, BF16, 0)
+    assert abi.conv2d_fwd_tile_kind(plan["tile_id"]) == abi.CONVIMG_KIND_WINDOW, plan
+    log("window %s plan %s" % (wl.name, plan))
+    parity(wl, seed=7)
+
+
 DEGENERATE = [
     shape(3, 7, 5, 8, 9, 1, 1, 1, 0, 1, name="1x1"),
     shape(2, 6, 6, 16, 16, 1, 1, 2, 0, 1, name="1x1 stride 2"),
