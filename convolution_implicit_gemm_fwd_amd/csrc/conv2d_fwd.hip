@@ -88,7 +88,7 @@ constexpr KernelFn kfn()
     if constexpr (c.kind == kRegs)
         return &igemm_regs_bf16<c.BM, c.BN, c.WM, L>;
     else if constexpr (c.kind == kWindow)
-        return &igemm_window_bf16;
+        return &igemm_window_bf16<kWinMaxKH>;      // stands for the family; launches pick by KH
     else if constexpr (c.kind == kStrip)
         return L == kLoaderTap ? &igemm_strip_bf16<c.BM / 128> : nullptr;   // FM
     else if constexpr (c.kind == kPatch)
@@ -114,6 +114,13 @@ constexpr std::array<std::array<KernelFn, kNumLoaders>, sizeof...(T)> ktable(std
 
 const std::array<std::array<KernelFn, kNumLoaders>, kNumTiles> kKernels =
     ktable(std::make_integer_sequence<int, kNumTiles>{});
+
+// Window kernels by kernel height (1 .. kWinMaxKH).
+const KernelFn kWinKernels[kWinMaxKH + 1] = {
+    nullptr, &igemm_window_bf16<1>, &igemm_window_bf16<2>, &igemm_window_bf16<3>,
+    &igemm_window_bf16<4>, &igemm_window_bf16<5>, &igemm_window_bf16<6>, &igemm_window_bf16<7>,
+};
+static_assert(kWinMaxKH == 7, "window kernel table");
 
 int threads_of(int tile)
 {
@@ -193,6 +200,9 @@ int device_info(int dev, DeviceInfo **out)
                 if ((kTiles[t].kind == kStrip || kTiles[t].kind == kWindow) && kKernels[t][l] != nullptr)
                     (void)hipFuncSetAttribute((const void *)kKernels[t][l],
                                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        for (int kh = 1; kh <= kWinMaxKH; ++kh)
+            (void)hipFuncSetAttribute((const void *)kWinKernels[kh],
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         for (int t = 0; t < kNumTiles; ++t)
             for (int l = 0; l < kNumLoaders; ++l) {
                 int nb = 1;
@@ -280,7 +290,7 @@ bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, in
 // weight layouts; those shapes keep the element-wise gather.)  One workgroup per CU per 64
 // channels; units (up to 128 pixels of one output row) split evenly.
 struct WinPlan {
-    int seg = 0, segs = 0, per = 0, sh = 0, wp = 0, rb = 0;
+    int seg = 0, segs = 0, sh = 0, wp = 0, rb = 0, sets = 0;
     int tiles_m = 0, tiles_n = 0, lds_rows = 0, lds_bytes = 0;
 };
 
@@ -295,7 +305,8 @@ bool plan_window(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int
     // (a 16-byte copy may run past the end of x: buffer loads check the
     // range per dword, so the dwords inside x still arrive)
     const long long xbytes = (long long)N * H * W * IC * 2;
-    if (xbytes % 4 != 0 || xbytes >= lim || M * OC * 4 >= lim)
+    const long long wbytes = (long long)OC * KH * KW * IC * 2;
+    if (xbytes % 4 != 0 || xbytes >= lim || wbytes >= lim || M * OC * 4 >= lim)
         return false;
     const int segs = ceil_div(OW, kWinSeg);
     const int seg = ceil_div(OW, segs);
@@ -305,26 +316,35 @@ bool plan_window(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int
     // 16-byte boundary below it) and ends 2 * jall bytes later.
     const long long jall = (long long)(kWinSeg - 1) * s * IC + 32;
     const long long rb = (16 + 2 * jall + 1023) / 1024 * 1024;
+    // LDS: the weight staging rows (later the epilogue scratch), then the
+    // row-buffer sets.  Prefer kWinOcc workgroups per CU, then 3 sets (rows
+    // of two units in flight) over 2.
     const int wrow = ((KH * 32 + 8) * 2 + 15) / 16 * 16;
-    const long long lds = 64LL * wrow + 2LL * KH * rb;
-    if (lds > kLdsBytes)
+    const int rows_at = 64 * wrow > kWinScrBytes ? 64 * wrow : kWinScrBytes;
+    int occ = 0, sets = 0;
+    for (int o = kWinOcc; o >= 1 && sets == 0; --o)
+        for (int st = 3; st >= 2 && sets == 0; --st)
+            if ((rows_at + (long long)st * KH * rb) * o <= kLdsBytes) {
+                occ = o;
+                sets = st;
+            }
+    if (sets == 0)
         return false;
     const int tiles_n = ceil_div(OC, 64);
-    int gm = num_cus / tiles_n;
+    long long gm = (long long)occ * num_cus / tiles_n;
     if (gm < 1)
         gm = 1;
     const long long units = (long long)N * OH * segs;
-    const long long per = (units + gm - 1) / gm;
     wp->seg = seg;
     wp->segs = segs;
-    wp->per = (int)per;
     wp->sh = sh;
     wp->wp = wrow;
     wp->rb = (int)rb;
-    wp->tiles_m = (int)((units + per - 1) / per);
+    wp->sets = sets;
+    wp->tiles_m = (int)(units < gm ? units : gm);      // groups of units (an even split)
     wp->tiles_n = tiles_n;
-    wp->lds_rows = 64 * wrow;
-    wp->lds_bytes = (int)lds;
+    wp->lds_rows = rows_at;
+    wp->lds_bytes = (int)(rows_at + (long long)sets * KH * rb);
     return true;
 }
 
@@ -714,7 +734,7 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.lds_flags = sp.lds_flags;
     a.win_seg = wnp.seg;
     a.win_segs = wnp.segs;
-    a.win_per = wnp.per;
+    a.win_sets = wnp.sets;
     a.win_sh = wnp.sh;
     a.win_wp = wnp.wp;
     a.win_rb = wnp.rb;
@@ -734,7 +754,10 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
 
     if (dtype == CONVIMG_FP32)
         hipLaunchKernelGGL(igemm_fwd_f32, dim3(pl.grid), dim3(kRegsThreads), 0, stream, a);
-    else if (kTiles[pl.tile_id].kind == kStrip || kTiles[pl.tile_id].kind == kWindow)
+    else if (kTiles[pl.tile_id].kind == kWindow)
+        hipLaunchKernelGGL(kWinKernels[KH], dim3(pl.grid), dim3(pl.threads), (unsigned)pl.lds_bytes,
+                           stream, a);
+    else if (kTiles[pl.tile_id].kind == kStrip)
         hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(pl.threads),
                            (unsigned)pl.lds_bytes, stream, a);
     else

@@ -66,10 +66,10 @@ struct ConvArgs {
     int lds_zero, lds_patch, lds_scratch, lds_flags;   // LDS: zero block size; offsets of patch, epilogue scratch, progress words
     // window kernel only
     int win_seg, win_segs;   // pixels per unit, units per output row
-    int win_per;             // units per workgroup
     int win_sh;              // k positions before a window (0 or 1)
     int win_wp, win_rb;      // LDS bytes per weight row, per input-row buffer
     int lds_rows;            // LDS offset of the input-row buffers
+    int win_sets;            // input-row buffer sets (units in flight + 1)
 };
 
 // Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them

@@ -103,26 +103,6 @@ __host__ __device__ inline StripSeg strip_seg(int c0, int c1, int H, int W, int 
     return g;
 }
 
-// s_waitcnt vmcnt(n) for a count known only at run time (the instruction
-// takes an immediate); n >= 63 needs no wait, since at most 63 vector memory
-// instructions of a wave are ever outstanding.
-__device__ __forceinline__ void wait_vmcnt_rt(int n)
-{
-    switch (n) {
-#define CONVIMG_W(k) case k: wait_vmcnt<k>(); break;
-#define CONVIMG_W8(k) CONVIMG_W(k) CONVIMG_W(k + 1) CONVIMG_W(k + 2) CONVIMG_W(k + 3) \
-                      CONVIMG_W(k + 4) CONVIMG_W(k + 5) CONVIMG_W(k + 6) CONVIMG_W(k + 7)
-        CONVIMG_W8(0) CONVIMG_W8(8) CONVIMG_W8(16) CONVIMG_W8(24)
-        CONVIMG_W8(32) CONVIMG_W8(40) CONVIMG_W8(48)
-        CONVIMG_W(56) CONVIMG_W(57) CONVIMG_W(58) CONVIMG_W(59) CONVIMG_W(60) CONVIMG_W(61)
-        CONVIMG_W(62)
-#undef CONVIMG_W8
-#undef CONVIMG_W
-    default:
-        break;
-    }
-}
-
 // FM: 32-row MFMA blocks per M-group (a chunk is at most 128 * FM pixels).
 //
 // Waves: 4 copy waves (0-3) and 8 compute waves (4-11), two per SIMD.

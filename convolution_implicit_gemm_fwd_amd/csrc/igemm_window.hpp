@@ -15,13 +15,20 @@
 // A workgroup (4 waves) keeps the 64-channel weight slice in registers (each
 // lane holds the B fragments of every k step) and walks a contiguous range
 // of "units": up to 128 pixels of one output row.  Per unit the KH input rows
-// it reads are copied into LDS (direct-to-LDS, 16-byte chunks, double
-// buffered: the next unit's rows are in flight while this unit computes);
-// elements outside the image row are then zeroed in LDS.  Wave w computes
-// pixels [32w, 32w + 32) of the unit against all 64 channels with
-// v_mfma_f32_32x32x16_bf16 (A from LDS, B from registers) and stores the
-// results straight from the accumulators (fixed count of buffer stores; a
-// masked element's offset is out of range, so the store is dropped).
+// it reads are copied into LDS (direct-to-LDS, 16-byte chunks) into one of
+// `win_sets` buffer sets, so the rows of the next win_sets - 1 units are in
+// flight while this unit computes; elements outside the image row are then
+// zeroed in LDS.  Wave w computes pixels [32w, 32w + 32) of the unit against
+// all 64 channels with v_mfma_f32_32x32x16_bf16 (A from LDS, B from
+// registers).  The results go out as 16-byte stores after a transpose
+// through a per-wave LDS scratch (over the weight staging area, free once
+// the weights are in registers), or as 4-byte stores straight from the
+// accumulators when out is not 16-byte aligned or OC % 4 != 0.  Every store
+// is issued unconditionally: a masked element's offset is out of range, so
+// the store is dropped and each wave's count of memory instructions per unit
+// is fixed.  Two workgroups share a CU, so one's per-unit bookkeeping
+// overlaps the other's MFMAs and stores; KH is a template argument so the
+// MFMA loop has no branches.
 #pragma once
 
 #include "igemm_common.hpp"
@@ -31,10 +38,15 @@ namespace convimg {
 
 constexpr int kWinThreads = 256;
 constexpr int kWinMaxKH = 7;                   // B fragments of up to 14 k steps in registers
+constexpr int kWinOcc = 2;                     // workgroups per CU the plan aims for
 constexpr int kWinSeg = 128;                   // pixels per unit at most (4 waves x 32)
-constexpr int kWinStores = 2 * 16;             // buffer stores per wave per unit
+constexpr int kWinStores = 2 * 16;             // 4-byte stores per wave per unit
+constexpr int kWinVecStores = 8;               // 16-byte stores per wave per unit
+constexpr int kWinScrRow = 72;                 // floats per pixel row of the epilogue scratch
+constexpr int kWinScrBytes = 4 * 32 * kWinScrRow * 4;   // epilogue scratch of the 4 waves
 
-__global__ __launch_bounds__(kWinThreads) void igemm_window_bf16(ConvArgs a)
+template <int KH>
+__global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvArgs a)
 {
     extern __shared__ u32x4_t dsm[];
     char *const lds = (char *)dsm;
@@ -45,69 +57,33 @@ __global__ __launch_bounds__(kWinThreads) void igemm_window_bf16(ConvArgs a)
     const int lk = lane >> 5;      // k chunk this lane feeds
     const int lr = lane & 31;      // pixel row / channel column this lane feeds
 
-    int bid = blockIdx.x;
-    if (a.remap)
-        bid = xcd_remap(bid, gridDim.x);
-    const int gn = bid / a.tiles_m;
-    const int gm = bid - gn * a.tiles_m;
+    // Workgroups in launch order: the first tiles_m (one per CU slot, the
+    // dispatcher fills every CU once before it doubles up) take the larger
+    // shares of an even split, so the two workgroups of a CU sum to about
+    // the same count on every CU.
+    const int gn = blockIdx.x / a.tiles_m;
+    const int gm = blockIdx.x - gn * a.tiles_m;
     const int n0 = gn * 64;
-    const int nunits = a.N * a.OH * a.win_segs;
-    const int u_begin = gm * a.win_per;
-    if (u_begin >= nunits)
+    const int units = a.N * a.OH * a.win_segs;
+    const int per = units / a.tiles_m, extra = units - per * a.tiles_m;
+    const int u_begin = gm * per + min(gm, extra);
+    const int u_end = u_begin + per + (gm < extra ? 1 : 0);
+    if (u_begin >= u_end)
         return;
-    const int u_end = min(u_begin + a.win_per, nunits);
 
-    const int IC = a.IC, KH = a.KH, KW = a.KW;
+    const int IC = a.IC, KW = a.KW;
     const int sic = a.stride * IC;          // elements between neighbouring pixels' windows
     const int WIC = a.W * IC;               // elements per input row
     const int sh = a.win_sh;
     const int wp = a.win_wp;                // LDS bytes per weight row
     const int rb = a.win_rb;                // LDS bytes per input-row buffer
-    const int nsteps = 2 * KH;              // 16-wide MFMA k steps
+    const int nsets = a.win_sets;
+    constexpr int nsteps = 2 * KH;          // 16-wide MFMA k steps
     const int jcap = (a.win_seg - 1) * sic + 32;    // row elements a unit reads
 
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
     char *const rows = lds + a.lds_rows;
-
-    // ---- weight slice -> LDS (zeros off the window grid), then registers
-    for (int i = tid; i < 64 * wp / 16; i += kWinThreads)
-        dsm[i] = u32x4_t{0u, 0u, 0u, 0u};
-    __syncthreads();
-    {
-        // thread tid handles k = tid, tid + 256, ... of every channel row
-        const unsigned short *w = (const unsigned short *)a.w;
-        const int kwic = KW * IC;
-        for (int k = tid; k < a.K; k += kWinThreads) {
-            const int kh = k / kwic;
-            const int rem = k - kh * kwic;
-            const int kw = rem / IC;
-            const int c = rem - kw * IC;
-            const int pos = 2 * (kh * 32 + sh + kw * a.dil * IC + c);
-#pragma unroll 8
-            for (int r = 0; r < 64; ++r) {
-                const int oc = n0 + r;
-                const unsigned short v = oc < a.OC ? w[(long long)oc * a.K + k] : (unsigned short)0;
-                *(unsigned short *)(lds + r * wp + pos) = v;
-            }
-        }
-    }
-    float bv[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int oc = n0 + j * 32 + lr;
-        bv[j] = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
-    }
-    __syncthreads();
-    // B fragment of step t, block j: channel row j*32 + lr, positions 16t + 8lk .. + 8
-    bf16x8_t breg[2 * kWinMaxKH][2];
-#pragma unroll
-    for (int t = 0; t < 2 * kWinMaxKH; ++t)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            breg[t][j] = t < nsteps
-                ? __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(lds + (j * 32 + lr) * wp + 2 * (16 * t + 8 * lk)))
-                : bf16x8_t{};
 
     // Geometry of unit u: output row q = n*OH + oh, first pixel ow0, and the
     // first element e_lo of the run of each input row it reads.
@@ -124,15 +100,18 @@ __global__ __launch_bounds__(kWinThreads) void igemm_window_bf16(ConvArgs a)
         g.e_lo = (g.ow0 * a.stride - a.pad) * IC - sh;      // even
         return g;
     };
-    // Byte offset within the row buffer of the run's first element: the
-    // copy starts at the 16-byte boundary below it.
-    auto row_delta = [&](const Unit &g, int ih) {
-        const long long gb = 2LL * (((long long)(g.n * a.H + ih) * a.W) * IC + g.e_lo);
-        return (int)(gb & 15);
+    // Byte offset within the row buffer of the run's first element of row
+    // kh: the copy starts at the 16-byte boundary below it (only the low
+    // four bits of the byte address matter, so unsigned wrap-around is fine).
+    auto row_delta = [&](const Unit &g, int kh) {
+        const unsigned ih = (unsigned)(g.oh * a.stride - a.pad + kh * a.dil);
+        return (int)((2u * (((unsigned)g.n * a.H + ih) * (unsigned)WIC + (unsigned)g.e_lo)) & 15u);
     };
     // Copy the KH input rows of unit u into buffer set `set`: per row
     // rb / 1024 instructions of 64 16-byte chunks, dealt round-robin over
     // the waves; rows outside the image and chunks outside x read zeros.
+    // Lanes past the run the unit reads get an out-of-range offset (no
+    // memory request); the instruction count per wave stays fixed.
     const int bpr = rb >> 10;               // 1 KB copies per row
     auto issue_rows = [&](int u, int set) {
         const Unit g = unit_of(u);
@@ -140,52 +119,109 @@ __global__ __launch_bounds__(kWinThreads) void igemm_window_bf16(ConvArgs a)
             const int kh = idx / bpr, b = idx - kh * bpr;
             const int ih = g.oh * a.stride - a.pad + kh * a.dil;
             const long long gb = 2LL * (((long long)(g.n * a.H + ih) * a.W) * IC + g.e_lo);
-            const long long src = (gb & ~15LL) + 16LL * (b * 64 + lane);
+            const int chunk = b * 64 + lane;
+            const long long src = (gb & ~15LL) + 16LL * chunk;
             // a chunk that runs past the end of x still brings its dwords
             // inside x (the buffer range check is per dword)
-            const bool ok = (unsigned)ih < (unsigned)a.H && src >= 0 && src < (long long)a.x_bytes;
+            const bool ok = (unsigned)ih < (unsigned)a.H && src >= 0 && src < (long long)a.x_bytes
+                && 16 * chunk < (int)(gb & 15) + 2 * jcap;
             dma16(rx, (u32x4_t *)(rows + (set * KH + kh) * rb) + b * 64, ok ? (unsigned)src : kOutOfRange);
         }
     };
+    // vector memory instructions of this wave per unit: row copies, stores
+    const int ndma = wave < KH * bpr ? (KH * bpr - 1 - wave) / 4 + 1 : 0;
+    const int nst = a.vec_out ? kWinVecStores : kWinStores;
+    const int ahead = nsets - 1;            // units whose rows are in flight
+
+    // the rows of the first units are in flight while the weights load
+    for (int i = 0; i < ahead && u_begin + i < u_end; ++i)
+        issue_rows(u_begin + i, i);
+
+    // ---- weight slice -> LDS (zeros off the window grid), then registers.
+    // Thread k (K <= KH * 32 <= 256) reads column k of the 64 channel rows
+    // (one wave's 64 loads of a row are one contiguous run of w), every
+    // load issued before the first is waited for; rows past OC read zeros.
+    // Column-per-thread keeps the LDS writes below on neighbouring banks.
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)a.w, 0, a.w_bytes, kRsrcWord3);
+    unsigned short wcol[64];
+    if (tid < a.K) {
+#pragma unroll
+        for (int r = 0; r < 64; ++r) {
+            const int oc = n0 + r;
+            const unsigned off = oc < a.OC ? 2u * (unsigned)(oc * a.K + tid) : kOutOfRange;
+            wcol[r] = __builtin_amdgcn_raw_buffer_load_b16(rw, off, 0, 0);
+        }
+    }
+    for (int i = tid; i < 64 * wp / 16; i += kWinThreads)
+        dsm[i] = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+    if (tid < a.K) {
+        const int kwic = KW * IC;
+        const int kh = tid / kwic;
+        const int rem = tid - kh * kwic;
+        const int kw = rem / IC;
+        const int c = rem - kw * IC;
+        char *const col = lds + 2 * (kh * 32 + sh + kw * a.dil * IC + c);
+#pragma unroll
+        for (int r = 0; r < 64; ++r)
+            *(unsigned short *)(col + r * wp) = wcol[r];
+    }
+    float bv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int oc = n0 + j * 32 + lr;
+        bv[j] = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
+    }
+    __syncthreads();
+    // B fragment of step t, block j: channel row j*32 + lr, positions 16t + 8lk .. + 8
+    bf16x8_t breg[2 * KH][2];
+#pragma unroll
+    for (int t = 0; t < 2 * KH; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            breg[t][j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(lds + (j * 32 + lr) * wp + 2 * (16 * t + 8 * lk)));
 
     floatx16_t acc[2];
-    issue_rows(u_begin, 0);
+    int set = 0;
     for (int u = u_begin; u < u_end; ++u) {
-        const int set = (u - u_begin) & 1;
         const Unit g = unit_of(u);
-        // this unit's rows have landed (the previous unit's stores may not)
-        if (u == u_begin)
-            wait_vmcnt<0>();
-        else
-            wait_vmcnt<kWinStores>();
-        __syncthreads();
-        // zero the elements of each row run that lie outside the image row
+        // Unit u's rows have landed once at most this many of this wave's
+        // later instructions are outstanding: the copies of units u+1 ..
+        // u+ahead-1 and the stores of the last `ahead` units (vector memory
+        // instructions complete in order; a smaller count only waits longer).
+        // The barriers here carry no memory fence: a fence would also wait
+        // for the rows still in flight for later units.  Each wave's waits
+        // give the order instead.
         {
-            const int left = min(max(-g.e_lo, 0), jcap);        // j < -e_lo
-            const int right0 = max(min(WIC - g.e_lo, jcap), 0);  // j >= WIC - e_lo
+            const int later = min(u + ahead - 1, u_end - 1) - u;
+            const int done = u - max(u - ahead, u_begin);
+            wait_vmcnt_rt(min(later * ndma + done * nst, 63));
+        }
+        lds_barrier();
+        // zero the elements of each row run that lie outside the image row
+        // (left: j < -e_lo, right: j >= WIC - e_lo), all rows in one pass
+        {
+            const int left = min(max(-g.e_lo, 0), jcap);
+            const int right0 = max(min(WIC - g.e_lo, jcap), 0);
             const int nfix = left + (jcap - right0);
-            for (int kh = 0; kh < KH; ++kh) {
-                const int ih = g.oh * a.stride - a.pad + kh * a.dil;
-                char *const row = rows + (set * KH + kh) * rb + row_delta(g, ih);
-                for (int f = tid; f < nfix; f += kWinThreads) {
-                    const int j = f < left ? f : right0 + (f - left);
-                    *(unsigned short *)(row + 2 * j) = 0;
-                }
+            for (int f = tid; f < KH * nfix; f += kWinThreads) {
+                const int kh = f / nfix;
+                const int e = f - kh * nfix;
+                const int j = e < left ? e : right0 + (e - left);
+                *(unsigned short *)(rows + (set * KH + kh) * rb + row_delta(g, kh) + 2 * j) = 0;
             }
         }
-        __syncthreads();
-        if (u + 1 < u_end)
-            issue_rows(u + 1, set ^ 1);
+        wait_lgkmcnt0();
+        lds_barrier();
+        if (u + ahead < u_end)
+            issue_rows(u + ahead, set == 0 ? ahead : set - 1);
 
         // A fragment of step t: row buffer t >> 1, bytes
         // delta + 2 * (pixel * sic + 16 (t & 1) + 8 lk), 4-byte aligned
-        int abase[kWinMaxKH];
+        int abase[KH];
 #pragma unroll
-        for (int kh = 0; kh < kWinMaxKH; ++kh) {
-            const int ih = g.oh * a.stride - a.pad + min(kh, KH - 1) * a.dil;
-            abase[kh] = (set * KH + min(kh, KH - 1)) * rb + row_delta(g, ih)
-                + 2 * ((32 * wave + lr) * sic + 8 * lk);
-        }
+        for (int kh = 0; kh < KH; ++kh)
+            abase[kh] = (set * KH + kh) * rb + row_delta(g, kh) + 2 * ((32 * wave + lr) * sic + 8 * lk);
         auto aload = [&](int t) {
             const unsigned *p = (const unsigned *)(rows + abase[t >> 1] + 32 * (t & 1));
             return __builtin_bit_cast(bf16x8_t, u32x4_t{p[0], p[1], p[2], p[3]});
@@ -194,35 +230,58 @@ __global__ __launch_bounds__(kWinThreads) void igemm_window_bf16(ConvArgs a)
         acc[1] = floatx16_t{};
         bf16x8_t fa0 = aload(0), fa1;
 #pragma unroll
-        for (int t = 0; t < 2 * kWinMaxKH; t += 2) {
-            if (t < nsteps) {
-                fa1 = aload(t + 1);
-                __builtin_amdgcn_sched_barrier(0);
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, breg[t][0], acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, breg[t][1], acc[1], 0, 0, 0);
-                if (t + 2 < nsteps)
-                    fa0 = aload(t + 2);
-                __builtin_amdgcn_sched_barrier(0);
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, breg[t + 1][0], acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, breg[t + 1][1], acc[1], 0, 0, 0);
-            }
+        for (int t = 0; t < nsteps; t += 2) {
+            fa1 = aload(t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, breg[t][0], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, breg[t][1], acc[1], 0, 0, 0);
+            if (t + 2 < nsteps)
+                fa0 = aload(t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, breg[t + 1][0], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, breg[t + 1][1], acc[1], 0, 0, 0);
         }
 
         // ---- stores: value v of block j is pixel 32*wave + 8*(v >> 2) +
-        // 4*lk + (v & 3), channel n0 + j*32 + lr; always kWinStores stores
+        // 4*lk + (v & 3), channel n0 + j*32 + lr
         const int ow_end = min(g.ow0 + a.win_seg, a.OW);
+        if (a.vec_out) {
+            // transpose through this wave's scratch rows (pixel-major, 72
+            // floats apart so the two lane halves hit different banks), then
+            // lane l stores channels 4(l & 15) .. +4 of pixel 4i + (l >> 4)
+            float *const scr = (float *)lds + wave * (32 * kWinScrRow);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int oc = n0 + j * 32 + lr;
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int ow = g.ow0 + 32 * wave + 8 * (v >> 2) + 4 * lk + (v & 3);
-                const int m = g.q * a.OW + ow;
-                const unsigned off = (ow < ow_end && oc < a.OC) ? 4u * (unsigned)(m * a.OC + oc) : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc[j][v] + bv[j]), ro,
-                                                      off, 0, 0);
+                for (int v = 0; v < 16; ++v)
+                    scr[(8 * (v >> 2) + 4 * lk + (v & 3)) * kWinScrRow + j * 32 + lr] = acc[j][v] + bv[j];
+            // (the LDS operations of one wave complete in order)
+            const int c4 = 4 * (lane & 15);
+            const int oc = n0 + c4;
+#pragma unroll
+            for (int i = 0; i < kWinVecStores; ++i) {
+                const int px = 4 * i + (lane >> 4);
+                const u32x4_t val = *(const u32x4_t *)(scr + px * kWinScrRow + c4);
+                const int ow = g.ow0 + 32 * wave + px;
+                const unsigned off = (ow < ow_end && oc < a.OC)
+                    ? 4u * (unsigned)((g.q * a.OW + ow) * a.OC + oc) : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b128(val, ro, off, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int oc = n0 + j * 32 + lr;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int ow = g.ow0 + 32 * wave + 8 * (v >> 2) + 4 * lk + (v & 3);
+                    const int m = g.q * a.OW + ow;
+                    const unsigned off = (ow < ow_end && oc < a.OC) ? 4u * (unsigned)(m * a.OC + oc) : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc[j][v] + bv[j]), ro,
+                                                          off, 0, 0);
+                }
             }
         }
+        set = set == ahead ? 0 : set + 1;
     }
 }
 
