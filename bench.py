@@ -51,6 +51,7 @@ KIND_SOURCES = {
     2: ("igemm_patch.hpp", "igemm_pipe.hpp"),    # CONVIMG_KIND_PATCH
     3: ("igemm_strip.hpp", "igemm_pipe.hpp"),    # CONVIMG_KIND_STRIP
     4: ("igemm_window.hpp", "igemm_pipe.hpp"),   # CONVIMG_KIND_WINDOW
+    5: ("igemm_resident.hpp", "igemm_pipe.hpp"), # CONVIMG_KIND_RESIDENT
 }
 
 

@@ -35,6 +35,7 @@ CONVIMG_KIND_PIPE = 1
 CONVIMG_KIND_PATCH = 2
 CONVIMG_KIND_STRIP = 3
 CONVIMG_KIND_WINDOW = 4
+CONVIMG_KIND_RESIDENT = 5
 
 # Every symbol include/convimg.h declares.
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror",

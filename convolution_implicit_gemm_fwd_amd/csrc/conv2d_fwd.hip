@@ -5,9 +5,11 @@
 #include "igemm_patch.hpp"
 #include "igemm_pipe.hpp"
 #include "igemm_regs.hpp"
+#include "igemm_resident.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_window.hpp"
 
+#include <algorithm>
 #include <array>
 #include <atomic>
 #include <cstdint>
@@ -29,9 +31,10 @@ namespace {
 // pipelined kernel (vector loaders only); kPatch entries the pipelined kernel
 // with an LDS patch of input rows; kStrip entries the strip kernel (BM is the
 // largest chunk of pixels: 4 waves x BM / 128 blocks of 32 rows); the
-// kWindow entry the few-channel kernel (every loader slot).
+// kWindow entry the few-channel kernel (every loader slot); the kResident
+// entry the kernel with weights and input rows resident in LDS (tap loader).
 // ---------------------------------------------------------------------------
-enum Kind { kRegs = 0, kPipe = 1, kPatch = 2, kStrip = 3, kWindow = 4 };
+enum Kind { kRegs = 0, kPipe = 1, kPatch = 2, kStrip = 3, kWindow = 4, kResident = 5 };
 
 struct TileCfg {
     int kind, BM, BN, WM, WN, stages, ms;
@@ -73,10 +76,12 @@ constexpr TileCfg kTiles[] = {
     {kStrip, 256, 64, 4, 1, 1, 32, "strip 256"},            // 30: chunks of up to 256 pixels
     {kStrip, 128, 64, 4, 1, 1, 32, "strip 128"},            // 31
     {kWindow, 128, 64, 4, 1, 1, 32, "window"},              // 32: few input channels
+    {kResident, 32, 64, 8, 1, 1, 32, "resident"},           // 33: weights + input rows in LDS
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kLdsBytes = 160 * 1024;     // LDS per CU (and per workgroup) on gfx950
 constexpr int kWindowTile = 32;           // the kWindow entry
+constexpr int kResidentTile = 33;         // the kResident entry
 constexpr int kNumLoaders = 3;
 
 typedef void (*KernelFn)(ConvArgs);
@@ -89,6 +94,8 @@ constexpr KernelFn kfn()
         return &igemm_regs_bf16<c.BM, c.BN, c.WM, L>;
     else if constexpr (c.kind == kWindow)
         return &igemm_window_bf16<kWinMaxKH>;      // stands for the family; launches pick by KH
+    else if constexpr (c.kind == kResident)
+        return &igemm_resident_bf16<9, 4>;         // stands for the family; launches pick by IC
     else if constexpr (c.kind == kStrip)
         return L == kLoaderTap ? &igemm_strip_bf16<c.BM / 128> : nullptr;   // FM
     else if constexpr (c.kind == kPatch)
@@ -122,10 +129,21 @@ const KernelFn kWinKernels[kWinMaxKH + 1] = {
 };
 static_assert(kWinMaxKH == 7, "window kernel table");
 
+// Resident kernels (3x3) by IC / 16 = 1, 2, 4, 8.
+const KernelFn kResKernels[4] = {
+    &igemm_resident_bf16<9, 1>, &igemm_resident_bf16<9, 2>, &igemm_resident_bf16<9, 4>,
+    &igemm_resident_bf16<9, 8>,
+};
+int res_index(int IC)
+{
+    return IC == 16 ? 0 : IC == 32 ? 1 : IC == 64 ? 2 : IC == 128 ? 3 : -1;
+}
+
 int threads_of(int tile)
 {
     return kTiles[tile].kind == kStrip ? kStripThreads
          : kTiles[tile].kind == kWindow ? kWinThreads
+         : kTiles[tile].kind == kResident ? kResThreads
          : kTiles[tile].WM * kTiles[tile].WN * 64;
 }
 
@@ -134,7 +152,7 @@ int lds_bytes_of(int tile)
     const TileCfg &c = kTiles[tile];
     if (c.kind == kPatch)
         return (c.patch_px + 1) * kChunks * 16 + c.stages * c.BN * kChunks * 16;
-    if (c.kind == kStrip || c.kind == kWindow)
+    if (c.kind == kStrip || c.kind == kWindow || c.kind == kResident)
         return kLdsBytes;       // sized per problem; one workgroup per CU
     return c.stages * (c.BM + c.BN) * kChunks * 16;
 }
@@ -203,6 +221,8 @@ int device_info(int dev, DeviceInfo **out)
         for (int kh = 1; kh <= kWinMaxKH; ++kh)
             (void)hipFuncSetAttribute((const void *)kWinKernels[kh],
                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        for (KernelFn f : kResKernels)
+            (void)hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         for (int t = 0; t < kNumTiles; ++t)
             for (int l = 0; l < kNumLoaders; ++l) {
                 int nb = 1;
@@ -348,6 +368,59 @@ bool plan_window(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int
     return true;
 }
 
+struct ResPlan {
+    int tiles_m = 0, tiles_n = 0, lds_rows = 0, zero = 0, lds_bytes = 0, rows = 0;
+};
+
+// Resident kernel plan (3x3, IC = 16, 32, 64 or 128, x and w 16-byte
+// aligned): the 64-channel weight slice (K bf16 + one spare chunk per
+// record) and the input rows of the largest of the tiles_m pixel ranges
+// (IC bf16 + one spare chunk per pixel) must fit in LDS with one zero
+// record.  The ranges split M evenly, larger shares first, as the kernel
+// does.
+bool plan_resident(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
+                   int OH, int OW, long long M, int num_cus, ResPlan *rp)
+{
+    const long long lim = 0x7fffffffLL;
+    if (KH * KW != 9 || res_index(IC) < 0)
+        return false;
+    if ((long long)N * H * W * IC * 2 >= lim || (long long)OC * KH * KW * IC * 2 >= lim || M * OC * 4 >= lim)
+        return false;
+    const long long prec = IC * 2 + 16;
+    const long long wbytes = 64 * ((long long)KH * KW * IC * 2 + 16);
+    if (wbytes + 1024 + prec > kLdsBytes)
+        return false;
+    const int tiles_n = ceil_div(OC, 64);
+    long long tm = num_cus / tiles_n;
+    if (tm < 1)
+        tm = 1;
+    if (tm > M)
+        tm = M;
+    const long long per = M / tm, extra = M - per * tm;
+    const long long ohw = (long long)OH * OW;
+    long long max_rows = 0;
+    for (long long g = 0; g < tm; ++g) {
+        const long long m_a = g * per + (g < extra ? g : extra);
+        const long long m_b = m_a + per + (g < extra ? 1 : 0);
+        const long long n_a = m_a / ohw, oh_a = (m_a - n_a * ohw) / OW;
+        const long long n_b = (m_b - 1) / ohw, oh_b = (m_b - 1 - n_b * ohw) / OW;
+        const long long lo = n_a * H + std::max<long long>(oh_a * s - p, 0);
+        const long long hi = n_b * H + std::min<long long>(oh_b * s - p + (long long)(KH - 1) * d, H - 1);
+        max_rows = std::max(max_rows, hi - lo + 1);
+    }
+    const long long rows_bytes = (max_rows * W * prec + 1023) / 1024 * 1024;
+    const long long lds = wbytes + rows_bytes + prec;
+    if (lds > kLdsBytes)
+        return false;
+    rp->tiles_m = (int)tm;
+    rp->tiles_n = tiles_n;
+    rp->lds_rows = (int)wbytes;
+    rp->zero = (int)(wbytes + rows_bytes);
+    rp->lds_bytes = (int)lds;
+    rp->rows = (int)max_rows;
+    return true;
+}
+
 bool plan_strip(long long M, int H, int W, int OH, int OW, int IC, int OC, int KH, int KW,
                 int s, int p, int d, long long K, int num_cus, StripPlan *sp)
 {
@@ -415,7 +488,7 @@ bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, in
 int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
               int dtype, int num_cus, bool aligned,
               const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo = nullptr,
-              WinPlan *wpo = nullptr)
+              WinPlan *wpo = nullptr, ResPlan *rpo = nullptr)
 {
     if (N <= 0 || H <= 0 || W <= 0 || IC <= 0 || OC <= 0 || KH <= 0 || KW <= 0
         || s <= 0 || p < 0 || d <= 0)
@@ -478,15 +551,20 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
         && (long long)N * H * W * IC * esz < lim && (long long)OC * K * esz < lim;
 
     // Tile choice, from measured sweeps on MI355X (every table entry timed on
-    // each shape class): 128x64 with 8 waves wherever OC <= 64 or the M x N
-    // tiles cannot fill the CUs (then split-K fills them); 256x128 with 8
-    // waves when there are enough large tiles for every CU.
+    // each shape class): the resident kernel wherever its weights and input
+    // rows fit in LDS (3x3, IC 16 .. 128); else 128x64 with 8 waves wherever
+    // OC <= 64 or the M x N tiles cannot fill the CUs (then split-K fills
+    // them); 256x128 with 8 waves when there are enough large tiles for
+    // every CU; the window kernel for few input channels.
     StripPlan sp;
     const bool strip_ok = pipe_ok && loader == CONVIMG_LOADER_TAP
         && plan_strip(M, H, W, OH, OW, IC, OC, KH, KW, s, p, d, K, num_cus, &sp);
     WinPlan wnp;
     const bool window_ok = aligned
         && plan_window(N, H, W, IC, OC, KH, KW, s, p, d, OH, OW, M, num_cus, &wnp);
+    ResPlan rsp;
+    const bool resident_ok = pipe_ok && aligned
+        && plan_resident(N, H, W, IC, OC, KH, KW, s, p, d, OH, OW, M, num_cus, &rsp);
     int tile;
     if (pipe_ok) {
         const long long big = ((M + 255) / 256) * ((OC + 127) / 128);
@@ -496,6 +574,8 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     } else {
         tile = 1;
     }
+    if (resident_ok)
+        tile = kResidentTile;   // weights and input rows fit in LDS: measured faster on every such shape
     if (window_ok && loader == CONVIMG_LOADER_SCALAR)
         tile = kWindowTile;     // few channels: the window kernel instead of the element-wise gather
     const int ft = g_force_tile.load();
@@ -520,6 +600,26 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
             return CONVIMG_OK;
         }
         tile = pipe_ok ? 11 : 0;    // a forced window the problem cannot use
+    }
+    if (kTiles[tile].kind == kResident) {
+        if (resident_ok) {
+            pl->tile_id = tile;
+            pl->BM = 32;                // pixels per wave unit
+            pl->BN = 64;
+            pl->BK = 16;
+            pl->loader = loader;
+            pl->splits = 1;
+            pl->tiles_m = rsp.tiles_m;
+            pl->tiles_n = rsp.tiles_n;
+            pl->ktiles = (int)(K / 16);
+            pl->grid = rsp.tiles_m * rsp.tiles_n;
+            pl->threads = kResThreads;
+            pl->lds_bytes = rsp.lds_bytes;
+            if (rpo)
+                *rpo = rsp;
+            return CONVIMG_OK;
+        }
+        tile = pipe_ok ? 11 : 0;    // a forced resident tile the problem cannot use
     }
     if (kTiles[tile].kind == kStrip) {
         if (strip_ok) {
@@ -622,9 +722,10 @@ int conv2d_fwd_tile_kind(int tile_id)
         return -1;
     static_assert(kRegs == CONVIMG_KIND_REGS && kPipe == CONVIMG_KIND_PIPE
                       && kPatch == CONVIMG_KIND_PATCH && kStrip == CONVIMG_KIND_STRIP
-                      && kWindow == CONVIMG_KIND_WINDOW,
+                      && kWindow == CONVIMG_KIND_WINDOW && kResident == CONVIMG_KIND_RESIDENT,
                   "kind codes");
     static_assert(kTiles[kWindowTile].kind == kWindow, "window tile index");
+    static_assert(kTiles[kResidentTile].kind == kResident, "resident tile index");
     return kTiles[tile_id].kind;
 }
 
@@ -690,8 +791,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     const bool aligned = (((uintptr_t)x | (uintptr_t)w) & 15) == 0;
     StripPlan sp;
     WinPlan wnp;
+    ResPlan rsp;
     rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned,
-                   info->occ, &pl, &sp, &wnp);
+                   info->occ, &pl, &sp, &wnp, &rsp);
     if (rc != CONVIMG_OK)
         return rc;
 
@@ -738,7 +840,8 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.win_sh = wnp.sh;
     a.win_wp = wnp.wp;
     a.win_rb = wnp.rb;
-    a.lds_rows = wnp.lds_rows;
+    a.res_zero = rsp.zero;
+    a.lds_rows = pl.tile_id >= 0 && kTiles[pl.tile_id].kind == kResident ? rsp.lds_rows : wnp.lds_rows;
 
     if (pl.splits > 1) {
         rc = get_semaphores(dev, stream, pl.tiles_m * pl.tiles_n + 1, &a.sem);
@@ -757,6 +860,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     else if (kTiles[pl.tile_id].kind == kWindow)
         hipLaunchKernelGGL(kWinKernels[KH], dim3(pl.grid), dim3(pl.threads), (unsigned)pl.lds_bytes,
                            stream, a);
+    else if (kTiles[pl.tile_id].kind == kResident)
+        hipLaunchKernelGGL(kResKernels[res_index(IC)], dim3(pl.grid), dim3(pl.threads),
+                           (unsigned)pl.lds_bytes, stream, a);
     else if (kTiles[pl.tile_id].kind == kStrip)
         hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(pl.threads),
                            (unsigned)pl.lds_bytes, stream, a);

@@ -70,6 +70,8 @@ struct ConvArgs {
     int win_wp, win_rb;      // LDS bytes per weight row, per input-row buffer
     int lds_rows;            // LDS offset of the input-row buffers
     int win_sets;            // input-row buffer sets (units in flight + 1)
+    // resident kernel only (also lds_rows: LDS offset of the input rows)
+    int res_zero;            // LDS offset of the zero pixel record
 };
 
 // Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them

@@ -57,17 +57,35 @@ __global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvAr
     const int lk = lane >> 5;      // k chunk this lane feeds
     const int lr = lane & 31;      // pixel row / channel column this lane feeds
 
-    // Workgroups in launch order: the first tiles_m (one per CU slot, the
-    // dispatcher fills every CU once before it doubles up) take the larger
-    // shares of an even split, so the two workgroups of a CU sum to about
-    // the same count on every CU.
-    const int gn = blockIdx.x / a.tiles_m;
-    const int gm = blockIdx.x - gn * a.tiles_m;
-    const int n0 = gn * 64;
+    // Unit ranges.  With one 64-channel slice, XCD x (workgroups b with
+    // b % 8 == x, the order the dispatcher deals them in) takes a contiguous
+    // block of units, so input rows that neighbouring units share meet in
+    // its L2; within the XCD the first half of its workgroups (the first
+    // slot of each of its CUs: every CU is filled once before any takes a
+    // second workgroup) take the larger shares of an even split, so the two
+    // workgroups of a CU sum to about the same count on every CU.  With
+    // several slices: an even split in launch order, larger shares first.
     const int units = a.N * a.OH * a.win_segs;
-    const int per = units / a.tiles_m, extra = units - per * a.tiles_m;
-    const int u_begin = gm * per + min(gm, extra);
-    const int u_end = u_begin + per + (gm < extra ? 1 : 0);
+    int gn, u_begin, u_end;
+    if (a.tiles_n == 1) {
+        const int G = gridDim.x, q = G >> 3, r = G & 7;
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        const int cnt = q + (x < r ? 1 : 0);                      // workgroups of XCD x
+        const int base = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+        const int ux0 = (int)((long long)units * base / G);
+        const int ux1 = (int)((long long)units * (base + cnt) / G);
+        const int per = (ux1 - ux0) / cnt, extra = (ux1 - ux0) - per * cnt;
+        gn = 0;
+        u_begin = ux0 + j * per + min(j, extra);
+        u_end = u_begin + per + (j < extra ? 1 : 0);
+    } else {
+        gn = blockIdx.x / a.tiles_m;
+        const int gm = blockIdx.x - gn * a.tiles_m;
+        const int per = units / a.tiles_m, extra = units - per * a.tiles_m;
+        u_begin = gm * per + min(gm, extra);
+        u_end = u_begin + per + (gm < extra ? 1 : 0);
+    }
+    const int n0 = gn * 64;
     if (u_begin >= u_end)
         return;
 

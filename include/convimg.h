@@ -136,12 +136,18 @@ int conv2d_fwd_num_tiles(void);
  *                      elements, fits in 32 k values; input rows copied to
  *                      LDS, weights in registers.  Chosen automatically where
  *                      the element-wise gather would run and it applies.
+ *   CONVIMG_KIND_RESIDENT one workgroup per CU per 64 output channels holds the
+ *                      weight slice and every input row of its share of the
+ *                      output pixels in LDS, then its waves work through
+ *                      32-pixel units with no further copies (3x3, IC = 16,
+ *                      32, 64 or 128, when they fit).
  * Host only. */
 #define CONVIMG_KIND_REGS   0
 #define CONVIMG_KIND_PIPE   1
 #define CONVIMG_KIND_PATCH  2
 #define CONVIMG_KIND_STRIP  3
 #define CONVIMG_KIND_WINDOW 4
+#define CONVIMG_KIND_RESIDENT 5
 int conv2d_fwd_tile_kind(int tile_id);
 
 /* Split-K health on `stream`: CONVIMG_OK, or CONVIMG_ERR_TIMEOUT if a

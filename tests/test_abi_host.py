@@ -11,7 +11,7 @@ import re
 import pytest
 
 from convolution_implicit_gemm_fwd_amd import abi
-from convolution_implicit_gemm_fwd_amd.workloads import WORKLOADS
+from convolution_implicit_gemm_fwd_amd.workloads import BF16, WORKLOADS, Workload
 
 from pins import read_table
 
@@ -88,7 +88,7 @@ def test_plans_of_named_workloads(lib):
 def test_tile_kinds(lib):
     kinds = [abi.conv2d_fwd_tile_kind(t) for t in range(abi.conv2d_fwd_num_tiles())]
     assert set(kinds) == {abi.CONVIMG_KIND_REGS, abi.CONVIMG_KIND_PIPE, abi.CONVIMG_KIND_PATCH,
-                          abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW}
+                          abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW, abi.CONVIMG_KIND_RESIDENT}
     assert abi.conv2d_fwd_tile_kind(-1) == -1
     assert abi.conv2d_fwd_tile_kind(abi.conv2d_fwd_num_tiles()) == -1
 
@@ -126,13 +126,50 @@ def test_strip_plans(lib):
         abi.conv2d_fwd_force(-1, -1, -1)
 
 
+def shape(N, H, W, IC, OC, KH, KW, s, p, d):
+    dist = ("normal", 0.0, 1.0)
+    return Workload("case", N, IC, H, W, OC, KH, KW, s, p, d, BF16, dist, dist, dist)
+
+
+def resident_tile():
+    (t,) = [t for t in range(abi.conv2d_fwd_num_tiles())
+            if abi.conv2d_fwd_tile_kind(t) == abi.CONVIMG_KIND_RESIDENT]
+    return t
+
+
+def test_resident_plans(lib):
+    """The resident entry holds the 64-channel weight slice and the input rows
+    of one CU's share of the pixels in LDS: one 8-wave workgroup per CU per 64
+    channels where they fit; elsewhere the pipelined kernel."""
+    t = resident_tile()
+    try:
+        abi.conv2d_fwd_force(t, -1, -1)
+        p = plan_of(WORKLOADS["resnet3x3"])
+        assert p["tile_id"] == t and p["threads"] == 512 and p["splits"] == 1
+        assert p["grid"] == p["tiles_m"] * p["tiles_n"] == 256
+        # 64 records of 576 bf16 + 16 bytes; 196 pixels span at most 4 output
+        # rows, so 6 input rows of 56 pixels of 144 bytes; one zero record
+        assert p["lds_bytes"] == 64 * 1168 + (6 * 56 * 144 + 1023) // 1024 * 1024 + 144
+        # two 64-channel slices: half the CUs per slice
+        wl = shape(2, 20, 20, 32, 100, 3, 3, 1, 1, 1)
+        p = plan_of(wl)
+        assert p["tile_id"] == t and p["tiles_n"] == 2 and p["tiles_m"] == 128
+        for wl in (WORKLOADS["largek"],                           # weights do not fit
+                   shape(1, 9, 9, 48, 64, 3, 3, 1, 1, 1),          # IC not 16, 32, 64 or 128
+                   shape(1, 9, 9, 64, 64, 5, 5, 1, 2, 1)):         # not 3x3
+            assert abi.conv2d_fwd_tile_kind(plan_of(wl)["tile_id"]) == abi.CONVIMG_KIND_PIPE
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+
+
 def test_forced_plans(lib):
     wl = WORKLOADS["largek"]
     try:
         for t in range(abi.conv2d_fwd_num_tiles()):
             assert abi.conv2d_fwd_force(t, 3, abi.CONVIMG_LOADER_VEC8) == 0
             p = plan_of(wl)
-            if abi.conv2d_fwd_tile_kind(t) in (abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW):
+            if abi.conv2d_fwd_tile_kind(t) in (abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW,
+                                               abi.CONVIMG_KIND_RESIDENT):
                 # 64 x 4608 bf16 weights do not fit in LDS, and 512 channels are
                 # far more than a window holds: the pipelined kernel instead
                 assert abi.conv2d_fwd_tile_kind(p["tile_id"]) == abi.CONVIMG_KIND_PIPE
@@ -152,9 +189,11 @@ def test_forced_plans(lib):
         # a vector loader is not honoured where the channels do not allow it
         abi.conv2d_fwd_force(-1, -1, abi.CONVIMG_LOADER_TAP)
         assert plan_of(WORKLOADS["stem7x7"])["loader"] == abi.CONVIMG_LOADER_SCALAR
-        # splits are clipped to the K tiles (tiny in bf16: one tile, 3 K tiles)
-        abi.conv2d_fwd_force(-1, 50, -1)
+        # splits of the pipelined kernel are clipped to the K tiles (tiny in
+        # bf16: one tile, 3 K tiles)
+        abi.conv2d_fwd_force(11, 50, -1)
         assert plan_of(WORKLOADS["tiny"], dtype=abi.CONVIMG_BF16)["splits"] == 3
+        abi.conv2d_fwd_force(-1, 50, -1)
         # ... and to what stays resident at once: 1568 tiles leave no room
         assert plan_of(WORKLOADS["stem7x7"])["splits"] == 1
         assert abi.conv2d_fwd_force(abi.conv2d_fwd_num_tiles(), -1, -1) == abi.CONVIMG_ERR_SHAPE

@@ -137,6 +137,36 @@ def test_window_kernel(wl):
     parity(wl, seed=7)
 
 
+RESIDENT_SHAPES = [
+    shape(2, 14, 14, 64, 64, 3, 3, 1, 1, 1, name="resnet-like"),
+    shape(8, 5, 6, 32, 64, 3, 3, 1, 1, 1, name="ranges over several images"),
+    shape(1, 9, 40, 16, 40, 3, 3, 1, 1, 1, name="IC 16, OC tail"),
+    shape(2, 9, 9, 128, 100, 3, 3, 1, 1, 1, name="IC 128, two slices"),
+    shape(2, 17, 15, 64, 64, 3, 3, 2, 1, 1, name="stride 2"),
+    shape(1, 16, 16, 32, 64, 3, 3, 1, 2, 2, name="dilation 2"),
+    shape(3, 8, 7, 64, 8, 3, 3, 1, 0, 1, name="no padding, OC 8"),
+    shape(1, 3, 3, 64, 64, 3, 3, 1, 3, 1, name="padding beyond window"),
+]
+
+
+@pytest.mark.parametrize("wl", RESIDENT_SHAPES, ids=lambda w: w.name)
+def test_resident_kernel(wl):
+    """Forced onto the kernel with weights and input rows resident in LDS:
+    parity with the oracle for ranges crossing rows and images, channel
+    tails and several 64-channel slices, strides, dilation and padding."""
+    (t,) = [t for t in range(abi.conv2d_fwd_num_tiles())
+            if abi.conv2d_fwd_tile_kind(t) == abi.CONVIMG_KIND_RESIDENT]
+    abi.conv2d_fwd_force(t, -1, -1)
+    try:
+        rc, plan = abi.conv2d_fwd_plan(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride,
+                                       wl.pad, wl.dilation, BF16, 0)
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+    assert plan["tile_id"] == t, plan
+    log("resident %s plan %s" % (wl.name, plan))
+    parity(wl, seed=11, force=(t, -1, -1))
+
+
 DEGENERATE = [
     shape(3, 7, 5, 8, 9, 1, 1, 1, 0, 1, name="1x1"),
     shape(2, 6, 6, 16, 16, 1, 1, 2, 0, 1, name="1x1 stride 2"),
