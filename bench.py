@@ -56,6 +56,7 @@ KIND_SOURCES = {
     3: ("igemm_strip.hpp", "igemm_pipe.hpp"),    # CONVIMG_KIND_STRIP
     4: ("igemm_window.hpp", "igemm_pipe.hpp"),   # CONVIMG_KIND_WINDOW
     5: ("igemm_resident.hpp", "igemm_pipe.hpp"), # CONVIMG_KIND_RESIDENT
+    6: ("igemm_image.hpp", "igemm_pipe.hpp"),    # CONVIMG_KIND_IMAGE
 }
 
 

@@ -36,6 +36,7 @@ CONVIMG_KIND_PATCH = 2
 CONVIMG_KIND_STRIP = 3
 CONVIMG_KIND_WINDOW = 4
 CONVIMG_KIND_RESIDENT = 5
+CONVIMG_KIND_IMAGE = 6
 
 # Every symbol include/convimg.h declares.
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror",

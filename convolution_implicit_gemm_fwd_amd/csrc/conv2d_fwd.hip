@@ -2,6 +2,7 @@
 // argument checks, output extent, the tile plan, the split-K semaphore pool
 // and the kernel launch.  The kernels are in igemm_fwd.hpp.
 #include "convimg.h"
+#include "igemm_image.hpp"
 #include "igemm_patch.hpp"
 #include "igemm_pipe.hpp"
 #include "igemm_regs.hpp"
@@ -32,9 +33,11 @@ namespace {
 // with an LDS patch of input rows; kStrip entries the strip kernel (BM is the
 // largest chunk of pixels: 4 waves x BM / 128 blocks of 32 rows); the
 // kWindow entry the few-channel kernel (every loader slot); the kResident
-// entry the kernel with weights and input rows resident in LDS (tap loader).
+// entry the kernel with weights and input rows resident in LDS; the kImage
+// entry the kernel for deep layers on small images (one workgroup per image
+// and 32 output channels, K in chunks of 64 channels).
 // ---------------------------------------------------------------------------
-enum Kind { kRegs = 0, kPipe = 1, kPatch = 2, kStrip = 3, kWindow = 4, kResident = 5 };
+enum Kind { kRegs = 0, kPipe = 1, kPatch = 2, kStrip = 3, kWindow = 4, kResident = 5, kImage = 6 };
 
 struct TileCfg {
     int kind, BM, BN, WM, WN, stages, ms;
@@ -77,11 +80,14 @@ constexpr TileCfg kTiles[] = {
     {kStrip, 128, 64, 4, 1, 1, 32, "strip 128"},            // 31
     {kWindow, 128, 64, 4, 1, 1, 32, "window"},              // 32: few input channels
     {kResident, 32, 64, 8, 1, 1, 32, "resident"},           // 33: weights + input rows in LDS
+    {kImage, 32, 32, 8, 1, 2, 32, "image"},                 // 34: one image x 32 channels per workgroup
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kLdsBytes = 160 * 1024;     // LDS per CU (and per workgroup) on gfx950
 constexpr int kWindowTile = 32;           // the kWindow entry
 constexpr int kResidentTile = 33;         // the kResident entry
+constexpr int kImageTile = 34;            // the kImage entry
+constexpr int kImgMaxMB = 8;              // image kernel: at most 8 blocks of 32 output pixels
 constexpr int kNumLoaders = 3;
 
 typedef void (*KernelFn)(ConvArgs);
@@ -96,6 +102,8 @@ constexpr KernelFn kfn()
         return &igemm_window_bf16<kWinMaxKH>;      // stands for the family; launches pick by KH
     else if constexpr (c.kind == kResident)
         return &igemm_resident_bf16<9, 4>;         // stands for the family; launches pick by IC
+    else if constexpr (c.kind == kImage)
+        return &igemm_image_bf16<kImgMaxMB>;       // stands for the family; launches pick by MB
     else if constexpr (c.kind == kStrip)
         return L == kLoaderTap ? &igemm_strip_bf16<c.BM / 128> : nullptr;   // FM
     else if constexpr (c.kind == kPatch)
@@ -134,6 +142,13 @@ const KernelFn kResKernels[4] = {
     &igemm_resident_bf16<9, 1>, &igemm_resident_bf16<9, 2>, &igemm_resident_bf16<9, 4>,
     &igemm_resident_bf16<9, 8>,
 };
+// Image kernels by blocks of 32 output pixels per image (1 .. kImgMaxMB).
+const KernelFn kImgKernels[kImgMaxMB + 1] = {
+    nullptr, &igemm_image_bf16<1>, &igemm_image_bf16<2>, &igemm_image_bf16<3>, &igemm_image_bf16<4>,
+    &igemm_image_bf16<5>, &igemm_image_bf16<6>, &igemm_image_bf16<7>, &igemm_image_bf16<8>,
+};
+static_assert(kImgMaxMB == 8, "image kernel table");
+
 int res_index(int IC)
 {
     return IC == 16 ? 0 : IC == 32 ? 1 : IC == 64 ? 2 : IC == 128 ? 3 : -1;
@@ -144,6 +159,7 @@ int threads_of(int tile)
     return kTiles[tile].kind == kStrip ? kStripThreads
          : kTiles[tile].kind == kWindow ? kWinThreads
          : kTiles[tile].kind == kResident ? kResThreads
+         : kTiles[tile].kind == kImage ? kImgThreads
          : kTiles[tile].WM * kTiles[tile].WN * 64;
 }
 
@@ -152,7 +168,7 @@ int lds_bytes_of(int tile)
     const TileCfg &c = kTiles[tile];
     if (c.kind == kPatch)
         return (c.patch_px + 1) * kChunks * 16 + c.stages * c.BN * kChunks * 16;
-    if (c.kind == kStrip || c.kind == kWindow || c.kind == kResident)
+    if (c.kind == kStrip || c.kind == kWindow || c.kind == kResident || c.kind == kImage)
         return kLdsBytes;       // sized per problem; one workgroup per CU
     return c.stages * (c.BM + c.BN) * kChunks * 16;
 }
@@ -223,6 +239,9 @@ int device_info(int dev, DeviceInfo **out)
                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         for (KernelFn f : kResKernels)
             (void)hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        for (int mb = 1; mb <= kImgMaxMB; ++mb)
+            (void)hipFuncSetAttribute((const void *)kImgKernels[mb],
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         for (int t = 0; t < kNumTiles; ++t)
             for (int l = 0; l < kNumLoaders; ++l) {
                 int nb = 1;
@@ -421,6 +440,58 @@ bool plan_resident(int N, int H, int W, int IC, int OC, int KH, int KW, int s, i
     return true;
 }
 
+struct ImgPlan {
+    int mb = 0, set = 0, wofs = 0, lds_bytes = 0, tiles_n = 0, ti = 1, ts = 1;
+};
+
+// Image kernel plan (3x3, IC % 64 == 0, x and w 16-byte aligned): one
+// image's output (at most kImgMaxMB blocks of 32 pixels) per workgroup;
+// two buffer sets of (zero-padded image, 64 records of 144 bytes per pixel;
+// 9 x 32 weight records) must fit in LDS, as must the 4 partial tiles of
+// the final reduction.
+bool plan_image(int N, int H, int W, int IC, int OC, int KH, int KW, int p, int OH, int OW,
+                ImgPlan *ip)
+{
+    const long long lim = 0x7fffffffLL;
+    if (KH != 3 || KW != 3 || IC % 64 != 0)
+        return false;
+    if ((long long)N * H * W * IC * 2 >= lim || (long long)OC * 9 * IC * 2 >= lim
+        || (long long)N * OH * OW * OC * 4 >= lim)
+        return false;
+    const int mb = ceil_div(OH * OW, 32);
+    if (mb > kImgMaxMB)
+        return false;
+    const long long patch = ((long long)(H + 2 * p) * (W + 2 * p) * kImgRec + 1023) / 1024 * 1024;
+    const long long wts = ((long long)kImgNT * kImgBN * kImgRec + 1023) / 1024 * 1024;
+    const long long set = patch + wts;
+    long long lds = 2 * set;
+    const long long red = 4LL * mb * 16 * 64 * 4;
+    if (red > lds)
+        lds = red;
+    if (lds > kLdsBytes)
+        return false;
+    const long long copies = ((H + 2LL * p) * (W + 2 * p) * 9 + 63) / 64 + (kImgNT * kImgBN * 9 + 63) / 64;
+    if ((copies + kImgWaves - 1) / kImgWaves > kImgMaxCopies)
+        return false;
+    ip->mb = mb;
+    ip->set = (int)set;
+    ip->wofs = (int)patch;
+    ip->lds_bytes = (int)lds;
+    ip->tiles_n = ceil_div(OC, kImgBN);
+    // workgroup blocks of ti images x ts slices (about one XCD's 32 workgroups)
+    for (int g : {4, 2, 1})
+        if (N % g == 0) {
+            ip->ti = g;
+            break;
+        }
+    for (int g : {8, 4, 2, 1})
+        if (ip->tiles_n % g == 0) {
+            ip->ts = g;
+            break;
+        }
+    return true;
+}
+
 bool plan_strip(long long M, int H, int W, int OH, int OW, int IC, int OC, int KH, int KW,
                 int s, int p, int d, long long K, int num_cus, StripPlan *sp)
 {
@@ -488,7 +559,7 @@ bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, in
 int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
               int dtype, int num_cus, bool aligned,
               const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo = nullptr,
-              WinPlan *wpo = nullptr, ResPlan *rpo = nullptr)
+              WinPlan *wpo = nullptr, ResPlan *rpo = nullptr, ImgPlan *ipo = nullptr)
 {
     if (N <= 0 || H <= 0 || W <= 0 || IC <= 0 || OC <= 0 || KH <= 0 || KW <= 0
         || s <= 0 || p < 0 || d <= 0)
@@ -552,7 +623,9 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
 
     // Tile choice, from measured sweeps on MI355X (every table entry timed on
     // each shape class): the resident kernel wherever its weights and input
-    // rows fit in LDS (3x3, IC 16 .. 128); else 128x64 with 8 waves wherever
+    // rows fit in LDS (3x3, IC 16 .. 128); else the image kernel for 3x3
+    // layers on images of at most 256 output pixels (IC % 64 == 0, the
+    // padded image fits twice in LDS); else 128x64 with 8 waves wherever
     // OC <= 64 or the M x N tiles cannot fill the CUs (then split-K fills
     // them); 256x128 with 8 waves when there are enough large tiles for
     // every CU; the window kernel for few input channels.
@@ -565,6 +638,8 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     ResPlan rsp;
     const bool resident_ok = pipe_ok && aligned
         && plan_resident(N, H, W, IC, OC, KH, KW, s, p, d, OH, OW, M, num_cus, &rsp);
+    ImgPlan imp;
+    const bool image_ok = pipe_ok && aligned && plan_image(N, H, W, IC, OC, KH, KW, p, OH, OW, &imp);
     int tile;
     if (pipe_ok) {
         const long long big = ((M + 255) / 256) * ((OC + 127) / 128);
@@ -574,6 +649,8 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     } else {
         tile = 1;
     }
+    if (image_ok)
+        tile = kImageTile;      // deep layer on small images: measured faster on every such shape
     if (resident_ok)
         tile = kResidentTile;   // weights and input rows fit in LDS: measured faster on every such shape
     if (window_ok && loader == CONVIMG_LOADER_SCALAR)
@@ -600,6 +677,26 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
             return CONVIMG_OK;
         }
         tile = pipe_ok ? 11 : 0;    // a forced window the problem cannot use
+    }
+    if (kTiles[tile].kind == kImage) {
+        if (image_ok) {
+            pl->tile_id = tile;
+            pl->BM = 32 * imp.mb;           // one image's output pixels
+            pl->BN = kImgBN;
+            pl->BK = 64;
+            pl->loader = loader;
+            pl->splits = 1;
+            pl->tiles_m = N;
+            pl->tiles_n = imp.tiles_n;
+            pl->ktiles = IC / 64;
+            pl->grid = N * imp.tiles_n;
+            pl->threads = kImgThreads;
+            pl->lds_bytes = imp.lds_bytes;
+            if (ipo)
+                *ipo = imp;
+            return CONVIMG_OK;
+        }
+        tile = pipe_ok ? 11 : 0;    // a forced image tile the problem cannot use
     }
     if (kTiles[tile].kind == kResident) {
         if (resident_ok) {
@@ -722,10 +819,12 @@ int conv2d_fwd_tile_kind(int tile_id)
         return -1;
     static_assert(kRegs == CONVIMG_KIND_REGS && kPipe == CONVIMG_KIND_PIPE
                       && kPatch == CONVIMG_KIND_PATCH && kStrip == CONVIMG_KIND_STRIP
-                      && kWindow == CONVIMG_KIND_WINDOW && kResident == CONVIMG_KIND_RESIDENT,
+                      && kWindow == CONVIMG_KIND_WINDOW && kResident == CONVIMG_KIND_RESIDENT
+                      && kImage == CONVIMG_KIND_IMAGE,
                   "kind codes");
     static_assert(kTiles[kWindowTile].kind == kWindow, "window tile index");
     static_assert(kTiles[kResidentTile].kind == kResident, "resident tile index");
+    static_assert(kTiles[kImageTile].kind == kImage, "image tile index");
     return kTiles[tile_id].kind;
 }
 
@@ -792,8 +891,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     StripPlan sp;
     WinPlan wnp;
     ResPlan rsp;
+    ImgPlan imp;
     rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned,
-                   info->occ, &pl, &sp, &wnp, &rsp);
+                   info->occ, &pl, &sp, &wnp, &rsp, &imp);
     if (rc != CONVIMG_OK)
         return rc;
 
@@ -841,6 +941,10 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.win_wp = wnp.wp;
     a.win_rb = wnp.rb;
     a.res_zero = rsp.zero;
+    a.img_set = imp.set;
+    a.img_wofs = imp.wofs;
+    a.img_ti = imp.ti;
+    a.img_ts = imp.ts;
     a.lds_rows = pl.tile_id >= 0 && kTiles[pl.tile_id].kind == kResident ? rsp.lds_rows : wnp.lds_rows;
 
     if (pl.splits > 1) {
@@ -863,6 +967,9 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     else if (kTiles[pl.tile_id].kind == kResident)
         hipLaunchKernelGGL(kResKernels[res_index(IC)], dim3(pl.grid), dim3(pl.threads),
                            (unsigned)pl.lds_bytes, stream, a);
+    else if (kTiles[pl.tile_id].kind == kImage)
+        hipLaunchKernelGGL(kImgKernels[imp.mb], dim3(pl.grid), dim3(pl.threads), (unsigned)pl.lds_bytes,
+                           stream, a);
     else if (kTiles[pl.tile_id].kind == kStrip)
         hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(pl.threads),
                            (unsigned)pl.lds_bytes, stream, a);

@@ -72,6 +72,9 @@ struct ConvArgs {
     int win_sets;            // input-row buffer sets (units in flight + 1)
     // resident kernel only (also lds_rows: LDS offset of the input rows)
     int res_zero;            // LDS offset of the zero pixel record
+    // image kernel only
+    int img_set, img_wofs;   // LDS bytes per buffer set; weights' offset within a set
+    int img_ti, img_ts;      // workgroup blocks: images x channel slices (dividing N and tiles_n)
 };
 
 // Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them

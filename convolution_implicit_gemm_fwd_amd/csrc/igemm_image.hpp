@@ -1,0 +1,243 @@
+// igemm_image.hpp -- implicit-GEMM kernel for deep layers on small images
+// (the large-K case: 512 -> 512 channels on 14x14 maps, K = 4608), where the
+// output tile of one image is small and K is long.
+//
+// One workgroup (8 waves) computes one image's output pixels (MB blocks of
+// 32) against 32 output channels, over all of K, with no split-K.  K is
+// walked in chunks of 64 input channels.  Per chunk, direct-to-LDS copies
+// bring in
+//   * the image zero-padded by p on every side, each pixel a record of the
+//     chunk's 64 channels plus a spare 16-byte chunk (copy lanes that fall
+//     on the frame or the spare chunk read zeros), so every tap of every
+//     output pixel addresses a record with no bounds test;
+//   * the chunk's weights: per tap, 32 records of 64 channels plus a spare
+//     chunk;
+// into one of two buffer sets, so chunk c+1 is in flight while chunk c is
+// multiplied.  Waves 0-3 take the first ceil(MB/2) pixel blocks and waves
+// 4-7 the rest (each SIMD holds one wave of each group, so every SIMD does
+// the same MFMA work); within a group, wave w takes channels 16 (w & 3) ..
+// +16 of every chunk, for all taps, with v_mfma_f32_32x32x16_bf16 (A and B
+// from LDS; each B fragment serves the group's blocks).  Each wave's code is
+// straight-line over the taps (no branch around an MFMA: the compiler
+// duplicates the accumulators across such branches).  After the last chunk
+// the 4 partial tiles of each block are summed through LDS, bias added, and
+// stored.
+#pragma once
+
+#include <type_traits>
+
+#include "igemm_common.hpp"
+#include "igemm_pipe.hpp"
+
+namespace convimg {
+
+constexpr int kImgThreads = 512;
+constexpr int kImgWaves = 8;
+constexpr int kImgNT = 9;                      // taps (3x3)
+constexpr int kImgRec = 144;                   // LDS record: 64 bf16 + a spare 16-byte chunk
+constexpr int kImgBN = 32;                     // output channels per workgroup
+constexpr int kImgMaxCopies = 11;              // copies per wave per chunk at most (the plan checks)
+
+// MB: 32-pixel blocks per image (OH * OW <= 32 MB).
+template <int MB>
+__global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
+{
+    extern __shared__ u32x4_t dsm[];
+    char *const lds = (char *)dsm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lk = lane >> 5;
+    const int lr = lane & 31;
+
+    // workgroups in XCD order (each XCD runs a contiguous range), tiled in
+    // blocks of img_ti images x img_ts channel slices (about one XCD's
+    // share), so the images and the weight slices a block reads are shared
+    // within one L2
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int ti = a.img_ti, ts = a.img_ts;
+    const int blk = bid / (ti * ts), inb = bid - blk * (ti * ts);
+    const int nbs = a.tiles_n / ts;                 // blocks along the slices
+    const int bi = blk / nbs, bs = blk - bi * nbs;
+    const int n = bi * ti + inb % ti;
+    const int ot = bs * ts + inb / ti;
+    const int n0 = ot * kImgBN;
+
+    const int H = a.H, W = a.W, IC = a.IC, p = a.pad;
+    const int PW = W + 2 * p;                       // padded row width
+    const int PR = (H + 2 * p) * PW;                // padded pixels
+    const int ohw = a.OH * a.OW;
+    const int nchunks = IC / 64;
+    // LDS: buffer set b at b * a.img_set: patch (PR records), then weights
+    const int set_bytes = a.img_set;
+    const int wofs = a.img_wofs;                    // weights' offset within a set
+
+    // ---- copies of chunk c into set b: instruction j of the chunk's
+    // patch instructions then weight instructions; wave w issues j = w, w+8, ...
+    // Each lane's source offsets are worked out once: chunk c only adds
+    // c * 128 bytes (64 channels) to every one, and an out-of-range offset
+    // stays out of range.
+    const int pins = (PR * 9 + 63) / 64;
+    const int wins = (kImgNT * kImgBN * 9 + 63) / 64;
+    const int cins = pins + wins;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)a.w, 0, a.w_bytes, kRsrcWord3);
+    // (rec / PW through a float reciprocal: exact, rec + 0.5 is at least 0.5
+    // away from every multiple of PW and the quotient is small); chunk 0 is
+    // copied as soon as each offset is known
+    const float inv_pw = 1.0f / (float)PW;
+    unsigned soff[kImgMaxCopies];
+#pragma unroll
+    for (int k = 0; k < kImgMaxCopies; ++k) {
+        const int j = wave + kImgWaves * k;
+        unsigned off = kOutOfRange;
+        if (j < pins) {
+            const int q = j * 64 + lane;
+            const int rec = q / 9, sub = q - rec * 9;
+            const int pr = (int)(((float)rec + 0.5f) * inv_pw), pc = rec - pr * PW;
+            const int ih = pr - p, iw = pc - p;
+            if (sub < 8 && rec < PR && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W)
+                off = 16u * (unsigned)(((n * H + ih) * W + iw) * (IC / 8) + sub);
+        } else if (j < cins) {
+            const int q = (j - pins) * 64 + lane;
+            const int rec = q / 9, sub = q - rec * 9;             // rec = tap * 32 + r
+            const int t = rec >> 5, r = rec & 31;
+            if (sub < 8 && t < kImgNT && n0 + r < a.OC)
+                off = 16u * (unsigned)(((n0 + r) * kImgNT + t) * (IC / 8) + sub);
+        }
+        soff[k] = off;
+        if (j < pins)
+            dma16(rx, dsm + j * 64, off);
+        else if (j < cins)
+            dma16(rw, (u32x4_t *)(lds + wofs) + (j - pins) * 64, off);
+    }
+    const int mine = (cins - wave + kImgWaves - 1) / kImgWaves;   // this wave's copies per chunk
+    auto issue = [&](int c, int b) {
+        char *const base = lds + b * set_bytes;
+#pragma unroll
+        for (int k = 0; k < kImgMaxCopies; ++k) {
+            const int j = wave + kImgWaves * k;
+            if (j < pins)
+                dma16(rx, (u32x4_t *)base + j * 64, soff[k] + 128u * c);
+            else if (j < cins)
+                dma16(rw, (u32x4_t *)(base + wofs) + (j - pins) * 64, soff[k] + 128u * c);
+        }
+    };
+
+    if (nchunks > 1)
+        issue(1, 1);
+
+    auto tap_off = [&](int t) { return ((t / 3) * a.dil * PW + (t % 3) * a.dil) * kImgRec; };
+    // this wave's 16-channel slice (w & 3) and k half lk
+    const int sub16 = 32 * (wave & 3) + 16 * lk;
+    // B fragment of tap t: weight record t*32 + lr of the set, same slice
+    const int brec = wofs + lr * kImgRec + sub16;
+    float *const red = (float *)lds;
+
+    // Blocks [I0, I1) (compile time) for the whole K loop, then the partial
+    // sums to LDS: wave slice s, block i, value v, lane l at float index
+    // ((s * MB + i) * 16 + v) * 64 + l.
+    auto body = [&](auto i0_tag, auto i1_tag) {
+        constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value, NB = I1 - I0;
+        constexpr int NA = NB > 0 ? NB : 1;         // (a group with no block still copies and meets)
+        // per lane: padded-patch record of each block's output pixel at tap
+        // (0, 0); tap (kh, kw) adds the same (kh*d*PW + kw*d) records for
+        // every lane
+        int abase[NA];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int m = min(32 * (I0 + i) + lr, ohw - 1);   // past the image: any pixel, never stored
+            const int oh = m / a.OW, ow = m - (m / a.OW) * a.OW;
+            abase[i] = (oh * a.stride * PW + ow * a.stride) * kImgRec + sub16;
+        }
+        floatx16_t acc[NA];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            acc[i] = floatx16_t{};
+        // all taps of the chunk in buffer set B.  Each block's A fragment
+        // for the next tap loads right after its MFMA has read the current
+        // one; the next B fragment loads at the start of the tap.
+        auto run = [&](auto b_tag) {
+            constexpr int B = decltype(b_tag)::value;
+            const char *const sb = lds + B * set_bytes;
+            auto af = [&](int i, int t) {
+                return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(sb + abase[i] + tap_off(t)));
+            };
+            auto bf = [&](int t) {
+                return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(sb + brec + t * 32 * kImgRec));
+            };
+            if constexpr (NB == 0)
+                return;
+            bf16x8_t fb = bf(0), fa[NA];
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                fa[i] = af(i, 0);
+#pragma unroll
+            for (int t = 0; t < kImgNT; ++t) {
+                bf16x8_t nb;
+                if (t + 1 < kImgNT)
+                    nb = bf(t + 1);
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i], 0, 0, 0);
+                    if (t + 1 < kImgNT)
+                        fa[i] = af(i, t + 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (t + 1 < kImgNT)
+                    fb = nb;
+            }
+        };
+        auto chunk = [&](int c, auto b_tag) {
+            // chunk c has landed once at most the next chunk's copies of this
+            // wave are outstanding (copies complete in order); then all meet
+            wait_vmcnt_rt(c + 1 < nchunks ? min(mine, 63) : 0);
+            lds_barrier();
+            run(b_tag);
+            // every wave is done with this set before it is refilled
+            wait_lgkmcnt0();
+            lds_barrier();
+            if (c + 2 < nchunks)
+                issue(c + 2, decltype(b_tag)::value);
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(c, std::integral_constant<int, 0>{});
+            if (c + 1 < nchunks)
+                chunk(c + 1, std::integral_constant<int, 1>{});
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                red[(((wave & 3) * MB + I0 + i) * 16 + v) * 64 + lane] = acc[i][v];
+        (void)abase;
+    };
+    constexpr int MB0 = (MB + 1) / 2;
+    if (wave < 4)
+        body(std::integral_constant<int, 0>{}, std::integral_constant<int, MB0>{});
+    else
+        body(std::integral_constant<int, MB0>{}, std::integral_constant<int, MB>{});
+    wait_lgkmcnt0();
+    lds_barrier();
+
+    // block i: summed by wave i % 8 from its 4 partials, + bias, stored
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
+    const int oc = n0 + lr;
+    const float bv = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
+    for (int i = wave; i < MB; i += kImgWaves) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float sum = bv;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                sum += red[((w * MB + i) * 16 + v) * 64 + lane];
+            const int m = 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
+            const unsigned off = (m < ohw && oc < a.OC) ? 4u * (unsigned)((n * ohw + m) * a.OC + oc) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, sum), ro, off, 0, 0);
+        }
+    }
+}
+
+}  // namespace convimg

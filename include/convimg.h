@@ -141,6 +141,11 @@ int conv2d_fwd_num_tiles(void);
  *                      output pixels in LDS, then its waves work through
  *                      32-pixel units with no further copies (3x3, IC = 16,
  *                      32, 64 or 128, when they fit).
+ *   CONVIMG_KIND_IMAGE deep layers on small images: one workgroup per image
+ *                      and 32 output channels over all of K, K in chunks of
+ *                      64 input channels with the zero-padded image and the
+ *                      chunk's weights double-buffered in LDS (3x3,
+ *                      IC % 64 == 0, at most 256 output pixels per image).
  * Host only. */
 #define CONVIMG_KIND_REGS   0
 #define CONVIMG_KIND_PIPE   1
@@ -148,6 +153,7 @@ int conv2d_fwd_num_tiles(void);
 #define CONVIMG_KIND_STRIP  3
 #define CONVIMG_KIND_WINDOW 4
 #define CONVIMG_KIND_RESIDENT 5
+#define CONVIMG_KIND_IMAGE 6
 int conv2d_fwd_tile_kind(int tile_id);
 
 /* Split-K health on `stream`: CONVIMG_OK, or CONVIMG_ERR_TIMEOUT if a

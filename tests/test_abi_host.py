@@ -71,6 +71,15 @@ def test_plans_of_named_workloads(lib):
     assert p["splits"] == 1 and p["grid"] == p["tiles_m"] * p["tiles_n"]
     p = plan_of(WORKLOADS["largek"])
     assert p["loader"] == abi.CONVIMG_LOADER_TAP and p["K"] == 4608
+    # 14x14 images: the image kernel, one workgroup per image and 32 channels
+    assert abi.conv2d_fwd_tile_kind(p["tile_id"]) == abi.CONVIMG_KIND_IMAGE
+    assert p["splits"] == 1 and p["grid"] == 16 * 16
+    # the pipelined 128x64 tile on it: long K with few tiles must split
+    abi.conv2d_fwd_force(11, -1, -1)
+    try:
+        p = plan_of(WORKLOADS["largek"])
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
     assert p["splits"] > 1, "long K with few tiles must split"
     tiles = p["tiles_m"] * p["tiles_n"]
     assert p["grid"] == (tiles + 7) // 8 * 8 * p["splits"]      # slots per split padded to 8
@@ -88,7 +97,8 @@ def test_plans_of_named_workloads(lib):
 def test_tile_kinds(lib):
     kinds = [abi.conv2d_fwd_tile_kind(t) for t in range(abi.conv2d_fwd_num_tiles())]
     assert set(kinds) == {abi.CONVIMG_KIND_REGS, abi.CONVIMG_KIND_PIPE, abi.CONVIMG_KIND_PATCH,
-                          abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW, abi.CONVIMG_KIND_RESIDENT}
+                          abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW, abi.CONVIMG_KIND_RESIDENT,
+                          abi.CONVIMG_KIND_IMAGE}
     assert abi.conv2d_fwd_tile_kind(-1) == -1
     assert abi.conv2d_fwd_tile_kind(abi.conv2d_fwd_num_tiles()) == -1
 
@@ -162,12 +172,36 @@ def test_resident_plans(lib):
         abi.conv2d_fwd_force(-1, -1, -1)
 
 
+def test_image_plans(lib):
+    """The image entry: one workgroup per image and 32 output channels over
+    all of K; two buffer sets of (padded image, 9 x 32 weight records) in LDS;
+    elsewhere the pipelined kernel."""
+    (t,) = [t for t in range(abi.conv2d_fwd_num_tiles())
+            if abi.conv2d_fwd_tile_kind(t) == abi.CONVIMG_KIND_IMAGE]
+    try:
+        abi.conv2d_fwd_force(t, -1, -1)
+        p = plan_of(WORKLOADS["largek"])
+        assert p["tile_id"] == t and p["threads"] == 512 and p["splits"] == 1
+        assert p["grid"] == 16 * (512 // 32) and p["BM"] == 7 * 32 and p["BN"] == 32
+        # padded 16x16 image of 144-byte records, 288 weight records rounded to 1 KB, twice
+        assert p["lds_bytes"] == 2 * (16 * 16 * 144 + 41 * 1024)
+        for wl in (WORKLOADS["resnet3x3"],                         # 56x56: 98 blocks of 32 pixels
+                   shape(2, 14, 14, 96, 64, 3, 3, 1, 1, 1),         # IC not a multiple of 64
+                   shape(2, 14, 14, 64, 64, 5, 5, 1, 2, 1)):        # not 3x3
+            assert abi.conv2d_fwd_tile_kind(plan_of(wl)["tile_id"]) == abi.CONVIMG_KIND_PIPE
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+
+
 def test_forced_plans(lib):
     wl = WORKLOADS["largek"]
     try:
         for t in range(abi.conv2d_fwd_num_tiles()):
             assert abi.conv2d_fwd_force(t, 3, abi.CONVIMG_LOADER_VEC8) == 0
             p = plan_of(wl)
+            if abi.conv2d_fwd_tile_kind(t) == abi.CONVIMG_KIND_IMAGE:
+                assert p["tile_id"] == t and p["splits"] == 1     # 14x14 images fit
+                continue
             if abi.conv2d_fwd_tile_kind(t) in (abi.CONVIMG_KIND_STRIP, abi.CONVIMG_KIND_WINDOW,
                                                abi.CONVIMG_KIND_RESIDENT):
                 # 64 x 4608 bf16 weights do not fit in LDS, and 512 channels are

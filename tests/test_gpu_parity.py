@@ -167,6 +167,35 @@ def test_resident_kernel(wl):
     parity(wl, seed=11, force=(t, -1, -1))
 
 
+IMAGE_SHAPES = [
+    shape(2, 14, 14, 128, 64, 3, 3, 1, 1, 1, name="largek-like, 2 chunks"),
+    shape(3, 7, 7, 256, 100, 3, 3, 1, 1, 1, name="7x7, 4 chunks, OC tail"),
+    shape(2, 13, 13, 64, 32, 3, 3, 2, 1, 1, name="stride 2"),
+    shape(1, 12, 12, 128, 64, 3, 3, 1, 2, 2, name="dilation 2"),
+    shape(2, 16, 16, 64, 32, 3, 3, 1, 0, 1, name="no padding, 7 blocks"),
+    shape(5, 4, 4, 64, 64, 3, 3, 1, 1, 1, name="one block per image"),
+    shape(1, 9, 11, 192, 40, 3, 3, 1, 1, 1, name="3 chunks, odd sizes"),
+]
+
+
+@pytest.mark.parametrize("wl", IMAGE_SHAPES, ids=lambda w: w.name)
+def test_image_kernel(wl):
+    """Forced onto the kernel with one image x 32 channels per workgroup:
+    parity with the oracle over chunk counts, channel tails, strides,
+    dilation, padding and the block counts (one wave group idle)."""
+    (t,) = [t for t in range(abi.conv2d_fwd_num_tiles())
+            if abi.conv2d_fwd_tile_kind(t) == abi.CONVIMG_KIND_IMAGE]
+    abi.conv2d_fwd_force(t, -1, -1)
+    try:
+        rc, plan = abi.conv2d_fwd_plan(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride,
+                                       wl.pad, wl.dilation, BF16, 0)
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+    assert plan["tile_id"] == t, plan
+    log("image %s plan %s" % (wl.name, plan))
+    parity(wl, seed=13, force=(t, -1, -1))
+
+
 DEGENERATE = [
     shape(3, 7, 5, 8, 9, 1, 1, 1, 0, 1, name="1x1"),
     shape(2, 6, 6, 16, 16, 1, 1, 2, 0, 1, name="1x1 stride 2"),
@@ -194,18 +223,38 @@ def test_padding_only_outputs_equal_bias():
     assert np.array_equal(y[0, 0, 0], inp.bias)
 
 
+# The large-K workload's own plan is the image kernel (no split-K); these
+# tests force the pipelined 128x64 tile with split-K on it.
+SPLITK_FORCE = (11, 4, -1)
+
+
+def forced_splits(wl):
+    abi.conv2d_fwd_force(*SPLITK_FORCE)
+    try:
+        rc, plan = abi.conv2d_fwd_plan(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride,
+                                       wl.pad, wl.dilation, BF16, 0)
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+    return plan["splits"]
+
+
 def test_splitk_deterministic():
     wl = WORKLOADS["largek"]
+    assert forced_splits(wl) > 1
     inp = make_inputs(wl, seed=0)
     x, w, b = to_device(inp)
     first = None
-    for rep in range(10):
-        out, dims = run_hip(wl, x, w, b, wl.dtype)
-        y = fetch(out, dims, wl)
-        if first is None:
-            first = y.copy()
-        else:
-            assert np.array_equal(y, first), "split-K result changed on repeat %d" % rep
+    abi.conv2d_fwd_force(*SPLITK_FORCE)
+    try:
+        for rep in range(10):
+            out, dims = run_hip(wl, x, w, b, wl.dtype)
+            y = fetch(out, dims, wl)
+            if first is None:
+                first = y.copy()
+            else:
+                assert np.array_equal(y, first), "split-K result changed on repeat %d" % rep
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
     assert abi.conv2d_fwd_status(torch.cuda.current_stream().cuda_stream) == 0
     yref, S = oracle_full(inp, wl)
     check(first, yref, S, "largek")
@@ -216,10 +265,25 @@ def test_splitk_concurrent_streams():
     # grids of 56 and 144 workgroups: both fit on the chip at once
     wls = [shape(4, 14, 14, 256, 256, 3, 3, 1, 1, 1, name="s256"),
            shape(2, 14, 14, 512, 512, 3, 3, 1, 1, 1, name="s512")]
+    assert all(forced_splits(wl) > 1 for wl in wls)
     ins = [make_inputs(wl, seed=3) for wl in wls]
     devs = [to_device(i) for i in ins]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = []
+    abi.conv2d_fwd_force(*SPLITK_FORCE)
+    try:
+        _splitk_streams_run(wls, devs, streams, outs)
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+    for st in streams:
+        assert abi.conv2d_fwd_status(st.cuda_stream) == 0
+    for wl, inp, (out, dims) in zip(wls, ins, outs):
+        y = fetch(out, dims, wl)
+        yref, S = oracle_full(inp, wl)
+        check(y, yref, S, wl.name)
+
+
+def _splitk_streams_run(wls, devs, streams, outs):
     for rep in range(3):
         bufs = []
         for wl in wls:
@@ -229,15 +293,9 @@ def test_splitk_concurrent_streams():
             buf[n_out:] = SENTINEL
             bufs.append(buf)
         torch.cuda.synchronize()            # prefills done before the other streams start
-        outs = [run_hip(wl, x, w, b, BF16, stream=st.cuda_stream, out=buf)
-                for wl, (x, w, b), st, buf in zip(wls, devs, streams, bufs)]
+        outs[:] = [run_hip(wl, x, w, b, BF16, stream=st.cuda_stream, out=buf)
+                   for wl, (x, w, b), st, buf in zip(wls, devs, streams, bufs)]
         torch.cuda.synchronize()
-    for st in streams:
-        assert abi.conv2d_fwd_status(st.cuda_stream) == 0
-    for wl, inp, (out, dims) in zip(wls, ins, outs):
-        y = fetch(out, dims, wl)
-        yref, S = oracle_full(inp, wl)
-        check(y, yref, S, wl.name)
 
 
 def test_largest_int32_output_sampled():
