@@ -38,13 +38,13 @@ MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per by
 # the sources are unchanged; otherwise traffic is null.
 TRAFFIC = {
     # profiles/igemm_resident_resnet3x3.md: 7.140 MB read + 12.845 MB written
-    "resnet3x3": {"bytes": 19984881, "tile": 33, "kernel": "9f1b2f6a965b3d25"},
-    # profiles/igemm_pipe_largek.md: 36.980 MB read + 12.858 MB written
-    "largek": {"bytes": 49837925, "tile": 11, "kernel": "a3b7f14988d11c61"},
-    # profiles/igemm_window_stem7x7.md: 5.216 MB read + 51.380 MB written
-    "stem7x7": {"bytes": 56596461, "tile": 32, "kernel": "cc0d385100793a93"},
-    # profiles/igemm_pipe_dilated.md: 19.853 MB read + 33.554 MB written
-    "dilated": {"bytes": 53407648, "tile": 7, "kernel": "a3b7f14988d11c61"},
+    "resnet3x3": {"bytes": 19984878, "tile": 33, "kernel": "5ddcc88d92d042a3"},
+    # profiles/igemm_image_largek.md: 25.742 MB read + 6.423 MB written
+    "largek": {"bytes": 32164623, "tile": 34, "kernel": "3ef1fdb178195380"},
+    # profiles/igemm_window_stem7x7.md: 5.223 MB read + 51.380 MB written
+    "stem7x7": {"bytes": 56603605, "tile": 32, "kernel": "f0abf8b48debc0ac"},
+    # profiles/igemm_pipe_dilated.md: 19.859 MB read + 33.554 MB written
+    "dilated": {"bytes": 53413786, "tile": 7, "kernel": "441e70d786f31c7f"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
