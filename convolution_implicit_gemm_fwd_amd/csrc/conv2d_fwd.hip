@@ -374,6 +374,9 @@ bool plan_window(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int
     if (gm < 1)
         gm = 1;
     const long long units = (long long)N * OH * segs;
+    // the kernel's 32-bit row offsets and float-reciprocal unit divisions
+    if (xbytes >= (1LL << 30) || units >= (1LL << 21))
+        return false;
     wp->seg = seg;
     wp->segs = segs;
     wp->sh = sh;
@@ -404,6 +407,8 @@ bool plan_resident(int N, int H, int W, int IC, int OC, int KH, int KW, int s, i
     if (KH * KW != 9 || res_index(IC) < 0)
         return false;
     if ((long long)N * H * W * IC * 2 >= lim || (long long)OC * KH * KW * IC * 2 >= lim || M * OC * 4 >= lim)
+        return false;
+    if (M >= (1LL << 21))           // the kernel's float-reciprocal divisions of pixel indices
         return false;
     const long long prec = IC * 2 + 16;
     const long long wbytes = 64 * ((long long)KH * KW * IC * 2 + 16);
@@ -461,8 +466,18 @@ bool plan_image(int N, int H, int W, int IC, int OC, int KH, int KW, int p, int 
     const int mb = ceil_div(OH * OW, 32);
     if (mb > kImgMaxMB)
         return false;
-    const long long patch = ((long long)(H + 2 * p) * (W + 2 * p) * kImgRec + 1023) / 1024 * 1024;
-    const long long wts = ((long long)kImgNT * kImgBN * kImgRec + 1023) / 1024 * 1024;
+    // the kernel's 24-bit products and float-reciprocal divisions
+    if (IC > 65536 || (long long)N * ceil_div(OC, kImgBN) >= (1LL << 21))
+        return false;
+    // padded rows of img_row_units chunks (at least one copy instruction's
+    // 64 chunks), then the weight chunks; no copy writes past its region
+    if (W + 2LL * p > 4096 || H + 2LL * p > 4096)
+        return false;
+    long long pchunks = (long long)(H + 2 * p) * img_row_units(W + 2 * p, OW);
+    if (pchunks < 64)
+        pchunks = 64;
+    const long long patch = pchunks * 16;
+    const long long wts = (long long)kImgWChunks * 16;
     const long long set = patch + wts;
     long long lds = 2 * set;
     const long long red = 4LL * mb * 16 * 64 * 4;
@@ -470,7 +485,7 @@ bool plan_image(int N, int H, int W, int IC, int OC, int KH, int KW, int p, int 
         lds = red;
     if (lds > kLdsBytes)
         return false;
-    const long long copies = ((H + 2LL * p) * (W + 2 * p) * 9 + 63) / 64 + (kImgNT * kImgBN * 9 + 63) / 64;
+    const long long copies = (pchunks + 63) / 64 + (kImgWChunks + 63) / 64;
     if ((copies + kImgWaves - 1) / kImgWaves > kImgMaxCopies)
         return false;
     ip->mb = mb;

@@ -9,7 +9,11 @@
 //   * the image zero-padded by p on every side, each pixel a record of the
 //     chunk's 64 channels plus a spare 16-byte chunk (copy lanes that fall
 //     on the frame or the spare chunk read zeros), so every tap of every
-//     output pixel addresses a record with no bounds test;
+//     output pixel addresses a record with no bounds test.  Each padded row
+//     ends in a gap that makes the row stride, in 16-byte units, congruent
+//     to 9 OW mod 16: the 16 lanes an LDS 128-bit read serves together then
+//     cover all 64 banks even where their output pixels wrap to the next
+//     row (without the gap, pixel (oh+1, 0) shares banks with (oh, 0));
 //   * the chunk's weights: per tap, 32 records of 64 channels plus a spare
 //     chunk;
 // into one of two buffer sets, so chunk c+1 is in flight while chunk c is
@@ -37,6 +41,18 @@ constexpr int kImgNT = 9;                      // taps (3x3)
 constexpr int kImgRec = 144;                   // LDS record: 64 bf16 + a spare 16-byte chunk
 constexpr int kImgBN = 32;                     // output channels per workgroup
 constexpr int kImgMaxCopies = 11;              // copies per wave per chunk at most (the plan checks)
+constexpr int kImgWChunks = kImgNT * kImgBN * 9;  // 16-byte chunks of a chunk's weights
+#ifndef CONVIMG_IMG_SPREAD
+#define CONVIMG_IMG_SPREAD 22
+#endif
+constexpr int kImgCopySpread = CONVIMG_IMG_SPREAD;  // MFMA slots a chunk's copies are spread over
+
+// Padded-image row stride in 16-byte units: PW records of 9 units, then a
+// gap of 0..15 units so that the stride is congruent to 9 * OW modulo 16.
+__host__ __device__ constexpr int img_row_units(int PW, int OW)
+{
+    return 9 * PW + ((9 * OW - 9 * PW) & 15);
+}
 
 // MB: 32-pixel blocks per image (OH * OW <= 32 MB).
 template <int MB>
@@ -55,85 +71,94 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
     // blocks of img_ti images x img_ts channel slices (about one XCD's
     // share), so the images and the weight slices a block reads are shared
     // within one L2
+    // (ti and ts are powers of two; the few divisions left go through
+    // small_div: the prologue runs before any copy is in flight, so every
+    // instruction in it is on the critical path)
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int ti = a.img_ti, ts = a.img_ts;
-    const int blk = bid / (ti * ts), inb = bid - blk * (ti * ts);
-    const int nbs = a.tiles_n / ts;                 // blocks along the slices
-    const int bi = blk / nbs, bs = blk - bi * nbs;
-    const int n = bi * ti + inb % ti;
-    const int ot = bs * ts + inb / ti;
+    const int lti = __builtin_ctz(a.img_ti), lts = __builtin_ctz(a.img_ts);
+    const int blk = bid >> (lti + lts), inb = bid & ((1 << (lti + lts)) - 1);
+    const int nbs = a.tiles_n >> lts;               // blocks along the slices
+    const int bi = small_div(blk, __builtin_amdgcn_rcpf((float)nbs)), bs = blk - bi * nbs;
+    const int n = (bi << lti) + (inb & ((1 << lti) - 1));
+    const int ot = (bs << lts) + (inb >> lti);
     const int n0 = ot * kImgBN;
 
     const int H = a.H, W = a.W, IC = a.IC, p = a.pad;
     const int PW = W + 2 * p;                       // padded row width
-    const int PR = (H + 2 * p) * PW;                // padded pixels
+    const int RU = img_row_units(PW, a.OW);         // padded row stride, 16-byte units
+    const int PC = (H + 2 * p) * RU;                // patch chunks
     const int ohw = a.OH * a.OW;
     const int nchunks = IC / 64;
-    // LDS: buffer set b at b * a.img_set: patch (PR records), then weights
+    // LDS: buffer set b at b * a.img_set: patch (PC chunks), then weights
     const int set_bytes = a.img_set;
     const int wofs = a.img_wofs;                    // weights' offset within a set
 
     // ---- copies of chunk c into set b: instruction j of the chunk's
     // patch instructions then weight instructions; wave w issues j = w, w+8, ...
-    // Each lane's source offsets are worked out once: chunk c only adds
-    // c * 128 bytes (64 channels) to every one, and an out-of-range offset
-    // stays out of range.
-    const int pins = (PR * 9 + 63) / 64;
-    const int wins = (kImgNT * kImgBN * 9 + 63) / 64;
+    // Instruction j of a region copies its chunks 64 j .. 64 j + 63, the last
+    // one moved back to end on the region's last chunk (its first lanes copy
+    // again what the one before copied: the same bytes), so no copy writes
+    // past its region.  Each lane's source offsets are worked out once:
+    // chunk c only adds c * 128 bytes (64 channels) to every one, and an
+    // out-of-range offset stays out of range.
+    const int pins = (PC + 63) / 64;
+    const int wins = (kImgWChunks + 63) / 64;
     const int cins = pins + wins;
+    auto first = [&](int j, int n) { return min(64 * j, max(n - 64, 0)); };
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)a.w, 0, a.w_bytes, kRsrcWord3);
-    // (rec / PW through a float reciprocal: exact, rec + 0.5 is at least 0.5
-    // away from every multiple of PW and the quotient is small); chunk 0 is
-    // copied as soon as each offset is known
-    const float inv_pw = 1.0f / (float)PW;
+    // Byte offsets: pixel (ih, iw) of image n at xbase + (ih W + iw) IC2,
+    // weight row oc, tap t at oc K2 + t IC2.  All 24-bit products (the plan
+    // keeps x and w under 2 GB and the image under 2^24 pixels).  A weight
+    // row at or past OC lies past the end of w and reads zeros.  Chunk 0 is
+    // copied as soon as each offset is known.
+    const unsigned IC2 = 2u * (unsigned)IC, K2 = (unsigned)kImgNT * IC2;
+    const unsigned xbase = (unsigned)n * (unsigned)(H * W) * IC2, wbase = (unsigned)n0 * K2;
+    const float inv_ru = __builtin_amdgcn_rcpf((float)RU);
     unsigned soff[kImgMaxCopies];
 #pragma unroll
     for (int k = 0; k < kImgMaxCopies; ++k) {
         const int j = wave + kImgWaves * k;
         unsigned off = kOutOfRange;
         if (j < pins) {
-            const int q = j * 64 + lane;
-            const int rec = q / 9, sub = q - rec * 9;
-            const int pr = (int)(((float)rec + 0.5f) * inv_pw), pc = rec - pr * PW;
+            // chunk q: padded row q / RU, record (q mod RU) / 9 of it (past
+            // the row's PW records: the gap), 16-byte part (q mod RU) mod 9
+            const int q = first(j, PC) + lane;
+            const int pr = small_div(q, inv_ru), within = q - (int)__umul24(pr, RU);
+            const int pc = div9(within), sub = within - 9 * pc;
             const int ih = pr - p, iw = pc - p;
-            if (sub < 8 && rec < PR && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W)
-                off = 16u * (unsigned)(((n * H + ih) * W + iw) * (IC / 8) + sub);
+            if (sub < 8 && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W)
+                off = xbase + __umul24(__umul24(ih, W) + iw, IC2) + 16u * sub;
         } else if (j < cins) {
-            const int q = (j - pins) * 64 + lane;
-            const int rec = q / 9, sub = q - rec * 9;             // rec = tap * 32 + r
+            const int q = first(j - pins, kImgWChunks) + lane;
+            const int rec = div9(q), sub = q - 9 * rec;             // rec = tap * 32 + r
             const int t = rec >> 5, r = rec & 31;
-            if (sub < 8 && t < kImgNT && n0 + r < a.OC)
-                off = 16u * (unsigned)(((n0 + r) * kImgNT + t) * (IC / 8) + sub);
+            if (sub < 8)
+                off = wbase + __umul24(r, K2) + __umul24(t, IC2) + 16u * sub;
         }
         soff[k] = off;
         if (j < pins)
-            dma16(rx, dsm + j * 64, off);
+            dma16(rx, dsm + first(j, PC), off);
         else if (j < cins)
-            dma16(rw, (u32x4_t *)(lds + wofs) + (j - pins) * 64, off);
+            dma16(rw, (u32x4_t *)(lds + wofs) + first(j - pins, kImgWChunks), off);
     }
-    const int mine = (cins - wave + kImgWaves - 1) / kImgWaves;   // this wave's copies per chunk
-    auto issue = [&](int c, int b) {
+    // copy k of chunk c into set b
+    auto issue_one = [&](int k, int c, int b) {
+        const int j = wave + kImgWaves * k;
         char *const base = lds + b * set_bytes;
-#pragma unroll
-        for (int k = 0; k < kImgMaxCopies; ++k) {
-            const int j = wave + kImgWaves * k;
-            if (j < pins)
-                dma16(rx, (u32x4_t *)base + j * 64, soff[k] + 128u * c);
-            else if (j < cins)
-                dma16(rw, (u32x4_t *)(base + wofs) + (j - pins) * 64, soff[k] + 128u * c);
-        }
+        if (j < pins)
+            dma16(rx, (u32x4_t *)base + first(j, PC), soff[k] + 128u * c);
+        else if (j < cins)
+            dma16(rw, (u32x4_t *)(base + wofs) + first(j - pins, kImgWChunks), soff[k] + 128u * c);
     };
 
-    if (nchunks > 1)
-        issue(1, 1);
-
-    auto tap_off = [&](int t) { return ((t / 3) * a.dil * PW + (t % 3) * a.dil) * kImgRec; };
+    auto tap_off = [&](int t) { return ((t / 3) * a.dil * RU + (t % 3) * a.dil * 9) * 16; };
     // this wave's 16-channel slice (w & 3) and k half lk
     const int sub16 = 32 * (wave & 3) + 16 * lk;
     // B fragment of tap t: weight record t*32 + lr of the set, same slice
     const int brec = wofs + lr * kImgRec + sub16;
     float *const red = (float *)lds;
+    const float inv_ow = __builtin_amdgcn_rcpf((float)a.OW);
 
     // Blocks [I0, I1) (compile time) for the whole K loop, then the partial
     // sums to LDS: wave slice s, block i, value v, lane l at float index
@@ -142,24 +167,39 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
         constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value, NB = I1 - I0;
         constexpr int NA = NB > 0 ? NB : 1;         // (a group with no block still copies and meets)
         // per lane: padded-patch record of each block's output pixel at tap
-        // (0, 0); tap (kh, kw) adds the same (kh*d*PW + kw*d) records for
+        // (0, 0); tap (kh, kw) adds the same kh*d rows and kw*d records for
         // every lane
         int abase[NA];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int m = min(32 * (I0 + i) + lr, ohw - 1);   // past the image: any pixel, never stored
-            const int oh = m / a.OW, ow = m - (m / a.OW) * a.OW;
-            abase[i] = (oh * a.stride * PW + ow * a.stride) * kImgRec + sub16;
+            const int oh = small_div(m, inv_ow), ow = m - oh * a.OW;
+            abase[i] = (int)(__umul24(__umul24(oh, a.stride), RU) + __umul24(ow, 9 * a.stride)) * 16 + sub16;
         }
         floatx16_t acc[NA];
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             acc[i] = floatx16_t{};
-        // all taps of the chunk in buffer set B.  Each block's A fragment
-        // for the next tap loads right after its MFMA has read the current
-        // one; the next B fragment loads at the start of the tap.
-        auto run = [&](auto b_tag) {
+        // all taps of the chunk in buffer set B, while chunk cn's copies go
+        // into the other set (when cn < nchunks), spread over the first
+        // MFMAs so that the copy unit works beside the matrix cores instead
+        // of holding the waves at a burst of copies.  Each block's A
+        // fragment for the next tap loads right after its MFMA has read the
+        // current one; the next B fragment loads at the start of the tap.
+        auto run = [&](auto b_tag, int cn) {
             constexpr int B = decltype(b_tag)::value;
+            constexpr int M = kImgNT * NB;                              // MFMAs of the chunk
+            constexpr int S = M < kImgCopySpread ? M : kImgCopySpread;  // MFMA slots the copies use
+            const bool more = cn < nchunks;
+            // copies k with slot(k) == m follow MFMA m (slot(k) = k S / K)
+            auto copies_after = [&](int m) {
+                if (!more)
+                    return;
+#pragma unroll
+                for (int k = 0; k < kImgMaxCopies; ++k)
+                    if ((k * S) / kImgMaxCopies == m)
+                        issue_one(k, cn, B ^ 1);
+            };
             const char *const sb = lds + B * set_bytes;
             auto af = [&](int i, int t) {
                 return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(sb + abase[i] + tap_off(t)));
@@ -167,8 +207,14 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
             auto bf = [&](int t) {
                 return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(sb + brec + t * 32 * kImgRec));
             };
-            if constexpr (NB == 0)
+            if constexpr (NB == 0) {
+                if (more) {
+#pragma unroll
+                    for (int k = 0; k < kImgMaxCopies; ++k)
+                        issue_one(k, cn, B ^ 1);
+                }
                 return;
+            }
             bf16x8_t fb = bf(0), fa[NA];
 #pragma unroll
             for (int i = 0; i < NB; ++i)
@@ -184,6 +230,7 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i], 0, 0, 0);
                     if (t + 1 < kImgNT)
                         fa[i] = af(i, t + 1);
+                    copies_after(t * NB + i);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (t + 1 < kImgNT)
@@ -191,22 +238,22 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
             }
         };
         auto chunk = [&](int c, auto b_tag) {
-            // chunk c has landed once at most the next chunk's copies of this
-            // wave are outstanding (copies complete in order); then all meet
-            wait_vmcnt_rt(c + 1 < nchunks ? min(mine, 63) : 0);
+            // this wave's copies of chunk c (the only ones in flight) have
+            // landed; after the barrier all of chunk c has, and every wave
+            // is done with the other set (chunk c - 1), which chunk c + 1
+            // then refills
+            wait_vmcnt<0>();
             lds_barrier();
-            run(b_tag);
-            // every wave is done with this set before it is refilled
-            wait_lgkmcnt0();
-            lds_barrier();
-            if (c + 2 < nchunks)
-                issue(c + 2, decltype(b_tag)::value);
+            run(b_tag, c + 1);
         };
         for (int c = 0; c < nchunks; c += 2) {
             chunk(c, std::integral_constant<int, 0>{});
             if (c + 1 < nchunks)
                 chunk(c + 1, std::integral_constant<int, 1>{});
         }
+        // the partial sums overwrite both sets: every wave's reads first
+        wait_lgkmcnt0();
+        lds_barrier();
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll

@@ -71,6 +71,21 @@ __device__ __forceinline__ void lds_barrier()
 }
 
 
+// floor(x / d) for 0 <= x < 2^21, inv = v_rcp_f32(d): the quotient of
+// x + 0.5 is at least 0.5 / d from an integer, and its float error is below
+// that for such x.
+__device__ __forceinline__ int small_div(int x, float inv)
+{
+    return (int)(((float)x + 0.5f) * inv);
+}
+
+// floor(x / 9) for 0 <= x < 16384 (7282 / 65536 exceeds 1/9 by under
+// 1/16384 per unit of x).
+__device__ __forceinline__ int div9(int x)
+{
+    return (int)(__umul24(x, 7282u) >> 16);
+}
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, u32x4_t *lds, unsigned off)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds,

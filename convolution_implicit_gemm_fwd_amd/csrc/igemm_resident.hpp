@@ -78,25 +78,31 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
     char *const rows = lds + a.lds_rows;
     char *const zero = lds + a.res_zero;
     // ---- prologue: weight records, then pixel records; slot q of a region
-    // is its q-th 16-byte chunk (copy instruction q / 64, lane q % 64)
+    // is its q-th 16-byte chunk (copy instruction q / 64, lane q % 64).  The
+    // address arithmetic uses float-reciprocal divisions and 24-bit products
+    // (the plan keeps x and w under 2 GB): the copies wait on it.  A weight
+    // row at or past OC lies past the end of w and reads zeros.
     {
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)a.w, 0, a.w_bytes, kRsrcWord3);
         const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
         const int wins = wchunks;
         const int rins = (nrows * W * pchunks + 63) / 64;
+        const float inv_wch = __builtin_amdgcn_rcpf((float)wchunks);
+        const float inv_pch = __builtin_amdgcn_rcpf((float)pchunks);
+        const unsigned wbase = (unsigned)n0 * (unsigned)K * 2u;
+        const unsigned xbase = (unsigned)g_lo * (unsigned)W * (unsigned)IC * 2u;
+        const int npx = nrows * W;
         for (int i = wave; i < wins + rins; i += kResWaves) {
             if (i < wins) {
                 const int q = i * 64 + lane;
-                const int r = q / wchunks, c = q - r * wchunks;
-                const bool ok = c < K / 8 && n0 + r < a.OC;
-                dma16(rw, dsm + i * 64, ok ? 16u * (unsigned)((n0 + r) * (K / 8) + c) : kOutOfRange);
+                const int r = small_div(q, inv_wch), c = q - (int)__umul24(r, wchunks);
+                dma16(rw, dsm + i * 64, c < K / 8 ? wbase + __umul24(r, 2u * K) + 16u * c : kOutOfRange);
             } else {
                 const int j = i - wins;
                 const int q = j * 64 + lane;
-                const int px = q / pchunks, c = q - px * pchunks;
-                const bool ok = c < IC / 8 && px < nrows * W;
-                dma16(rx, (u32x4_t *)rows + j * 64,
-                      ok ? 16u * (unsigned)((g_lo * W + px) * (IC / 8) + c) : kOutOfRange);
+                const int px = small_div(q, inv_pch), c = q - (int)__umul24(px, pchunks);
+                const bool ok = c < IC / 8 && px < npx;
+                dma16(rx, (u32x4_t *)rows + j * 64, ok ? xbase + __umul24(px, 2u * IC) + 16u * c : kOutOfRange);
             }
         }
         if (tid < pchunks)
@@ -112,6 +118,9 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
     __syncthreads();
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
     const int nunits = (m_b - m_a + 31) / 32;
+    const float inv_ohw = __builtin_amdgcn_rcpf((float)ohw), inv_ow = __builtin_amdgcn_rcpf((float)a.OW);
+    // this lane's part of each output offset: row 4 lk of a unit, channel lr
+    const unsigned lane_out = 4u * (__umul24(4 * lk, a.OC) + (unsigned)lr);
     // B fragment of step st = tap * CPS + c: weight record j*32 + lr, bytes 32 st + 16 lk
     const char *const b0 = lds + lr * wrec + 16 * lk;
     const char *const b1 = b0 + 32 * wrec;
@@ -119,17 +128,17 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
         const int m0 = m_a + 32 * u;
         // this lane's output pixel (past the range: any pixel, never stored)
         const int m = min(m0 + lr, m_b - 1);
-        const int n = m / ohw;
-        const int rem = m - n * ohw;
-        const int oh = rem / a.OW;
-        const int ow = rem - oh * a.OW;
+        const int n = small_div(m, inv_ohw);
+        const int rem = m - (int)__umul24(n, ohw);
+        const int oh = small_div(rem, inv_ow);
+        const int ow = rem - (int)__umul24(oh, a.OW);
         int tap[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int kh = t / a.KW, kw = t - kh * a.KW;
             const int ih = oh * s - p + kh * d, iw = ow * s - p + kw * d;
             const bool ok = (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
-            tap[t] = (int)((ok ? rows + ((n * H + ih - g_lo) * W + iw) * prec : zero) - lds) + 16 * lk;
+            tap[t] = (ok ? a.lds_rows + (int)__umul24(__umul24(n * H + ih - g_lo, W) + iw, prec) : a.res_zero) + 16 * lk;
         }
         floatx16_t acc0 = floatx16_t{}, acc1 = floatx16_t{};
         // step st = t * CPS + c: A at tap record t + 32 c, B at 32 st; the
@@ -159,14 +168,17 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
                 fb1 = nb1;
             }
         }
-        // value v of block j: pixel m0 + 8*(v >> 2) + 4*lk + (v & 3), channel n0 + j*32 + lr
+        // value v of block j: pixel m0 + 8*(v >> 2) + 4*lk + (v & 3), channel
+        // n0 + j*32 + lr, at ubase + lane_out + 4 ((8 (v >> 2) + (v & 3)) OC + 32 j)
+        const unsigned ubase = 4u * ((unsigned)m0 * (unsigned)a.OC + (unsigned)n0) + lane_out;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int mv = m0 + 8 * (v >> 2) + 4 * lk + (v & 3);
+            const unsigned vofs = 4u * (unsigned)((8 * (v >> 2) + (v & 3)) * a.OC);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int oc = n0 + j * 32 + lr;
-                const unsigned off = (mv < m_b && oc < a.OC) ? 4u * (unsigned)(mv * a.OC + oc) : kOutOfRange;
+                const unsigned off = (mv < m_b && oc < a.OC) ? ubase + vofs + 128u * j : kOutOfRange;
                 const float val = (j == 0 ? acc0[v] : acc1[v]) + bv[j];
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, val), ro, off, 0, 0);
             }

@@ -103,46 +103,51 @@ __global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvAr
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
     char *const rows = lds + a.lds_rows;
 
-    // Geometry of unit u: output row q = n*OH + oh, first pixel ow0, and the
-    // first element e_lo of the run of each input row it reads.
+    // Geometry of unit u: output row q = n*OH + oh, first pixel ow0, the
+    // first element e_lo of the run of each input row it reads, and gb0, the
+    // byte offset in x of element e_lo of input row oh*s - p of image n
+    // (negative at the top-left corner); kernel row kh adds kh * rowstep.
+    // Divisions go through float reciprocals (the plan keeps the unit count
+    // under 2^21): this bookkeeping runs once per unit on every wave.
     struct Unit {
-        int n, oh, ow0, q, e_lo;
+        int n, oh, ow0, q, e_lo, gb0;
     };
+    const float inv_segs = __builtin_amdgcn_rcpf((float)a.win_segs);
+    const float inv_oh = __builtin_amdgcn_rcpf((float)a.OH);
+    const int rowstep = 2 * a.dil * WIC;
     auto unit_of = [&](int u) {
         Unit g;
-        g.q = u / a.win_segs;
+        g.q = small_div(u, inv_segs);
         const int seg = u - g.q * a.win_segs;
-        g.n = g.q / a.OH;
+        g.n = small_div(g.q, inv_oh);
         g.oh = g.q - g.n * a.OH;
         g.ow0 = seg * a.win_seg;
         g.e_lo = (g.ow0 * a.stride - a.pad) * IC - sh;      // even
+        g.gb0 = 2 * ((g.n * a.H + g.oh * a.stride - a.pad) * WIC + g.e_lo);
         return g;
     };
     // Byte offset within the row buffer of the run's first element of row
-    // kh: the copy starts at the 16-byte boundary below it (only the low
-    // four bits of the byte address matter, so unsigned wrap-around is fine).
-    auto row_delta = [&](const Unit &g, int kh) {
-        const unsigned ih = (unsigned)(g.oh * a.stride - a.pad + kh * a.dil);
-        return (int)((2u * (((unsigned)g.n * a.H + ih) * (unsigned)WIC + (unsigned)g.e_lo)) & 15u);
-    };
+    // kh: the copy starts at the 16-byte boundary below it.
+    auto row_delta = [&](const Unit &g, int kh) { return (g.gb0 + kh * rowstep) & 15; };
     // Copy the KH input rows of unit u into buffer set `set`: per row
     // rb / 1024 instructions of 64 16-byte chunks, dealt round-robin over
     // the waves; rows outside the image and chunks outside x read zeros.
     // Lanes past the run the unit reads get an out-of-range offset (no
     // memory request); the instruction count per wave stays fixed.
     const int bpr = rb >> 10;               // 1 KB copies per row
+    const float inv_bpr = __builtin_amdgcn_rcpf((float)bpr);
     auto issue_rows = [&](int u, int set) {
         const Unit g = unit_of(u);
         for (int idx = wave; idx < KH * bpr; idx += 4) {
-            const int kh = idx / bpr, b = idx - kh * bpr;
+            const int kh = small_div(idx, inv_bpr), b = idx - kh * bpr;
             const int ih = g.oh * a.stride - a.pad + kh * a.dil;
-            const long long gb = 2LL * (((long long)(g.n * a.H + ih) * a.W) * IC + g.e_lo);
+            const int gb = g.gb0 + kh * rowstep;
             const int chunk = b * 64 + lane;
-            const long long src = (gb & ~15LL) + 16LL * chunk;
+            const int src = (gb & ~15) + 16 * chunk;
             // a chunk that runs past the end of x still brings its dwords
             // inside x (the buffer range check is per dword)
-            const bool ok = (unsigned)ih < (unsigned)a.H && src >= 0 && src < (long long)a.x_bytes
-                && 16 * chunk < (int)(gb & 15) + 2 * jcap;
+            const bool ok = (unsigned)ih < (unsigned)a.H && src >= 0 && (unsigned)src < a.x_bytes
+                && 16 * chunk < (gb & 15) + 2 * jcap;
             dma16(rx, (u32x4_t *)(rows + (set * KH + kh) * rb) + b * 64, ok ? (unsigned)src : kOutOfRange);
         }
     };
@@ -222,11 +227,15 @@ __global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvAr
             const int left = min(max(-g.e_lo, 0), jcap);
             const int right0 = max(min(WIC - g.e_lo, jcap), 0);
             const int nfix = left + (jcap - right0);
-            for (int f = tid; f < KH * nfix; f += kWinThreads) {
-                const int kh = f / nfix;
-                const int e = f - kh * nfix;
-                const int j = e < left ? e : right0 + (e - left);
-                *(unsigned short *)(rows + (set * KH + kh) * rb + row_delta(g, kh) + 2 * j) = 0;
+            if (nfix > 0) {
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh) {
+                    char *const rowp = rows + (set * KH + kh) * rb + row_delta(g, kh);
+                    for (int e = tid; e < nfix; e += kWinThreads) {
+                        const int j = e < left ? e : right0 + (e - left);
+                        *(unsigned short *)(rowp + 2 * j) = 0;
+                    }
+                }
             }
         }
         wait_lgkmcnt0();

@@ -183,8 +183,9 @@ def test_image_plans(lib):
         p = plan_of(WORKLOADS["largek"])
         assert p["tile_id"] == t and p["threads"] == 512 and p["splits"] == 1
         assert p["grid"] == 16 * (512 // 32) and p["BM"] == 7 * 32 and p["BN"] == 32
-        # padded 16x16 image of 144-byte records, 288 weight records rounded to 1 KB, twice
-        assert p["lds_bytes"] == 2 * (16 * 16 * 144 + 41 * 1024)
+        # padded 16x16 image of 144-byte records with a 224-byte gap per row
+        # (row stride 158 units of 16 bytes = 9 * 14 mod 16), 288 weight records, twice
+        assert p["lds_bytes"] == 2 * (16 * (16 * 144 + 224) + 288 * 144) == 160 * 1024
         for wl in (WORKLOADS["resnet3x3"],                         # 56x56: 98 blocks of 32 pixels
                    shape(2, 14, 14, 96, 64, 3, 3, 1, 1, 1),         # IC not a multiple of 64
                    shape(2, 14, 14, 64, 64, 5, 5, 1, 2, 1)):        # not 3x3
