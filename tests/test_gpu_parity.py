@@ -146,6 +146,7 @@ RESIDENT_SHAPES = [
     shape(1, 16, 16, 32, 64, 3, 3, 1, 2, 2, name="dilation 2"),
     shape(3, 8, 7, 64, 8, 3, 3, 1, 0, 1, name="no padding, OC 8"),
     shape(1, 3, 3, 64, 64, 3, 3, 1, 3, 1, name="padding beyond window"),
+    shape(2, 9, 9, 32, 50, 3, 3, 1, 1, 1, name="OC 50, dword stores"),
 ]
 
 
