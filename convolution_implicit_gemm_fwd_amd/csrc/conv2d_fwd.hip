@@ -485,7 +485,7 @@ bool plan_image(int N, int H, int W, int IC, int OC, int KH, int KW, int p, int 
     const long long wts = (long long)kImgWChunks * 16;
     const long long set = patch + wts;
     long long lds = 2 * set;
-    const long long red = 4LL * mb * 16 * 64 * 4;
+    const long long red = 4LL * 32 * mb * kImgRedRow * 4;
     if (red > lds)
         lds = red;
     if (lds > kLdsBytes)

@@ -42,6 +42,7 @@ constexpr int kImgRec = 144;                   // LDS record: 64 bf16 + a spare 
 constexpr int kImgBN = 32;                     // output channels per workgroup
 constexpr int kImgMaxCopies = 11;              // copies per wave per chunk at most (the plan checks)
 constexpr int kImgWChunks = kImgNT * kImgBN * 9;  // 16-byte chunks of a chunk's weights
+constexpr int kImgRedRow = 40;                     // floats per pixel of the partial sums in LDS
 #ifndef CONVIMG_IMG_SPREAD
 #define CONVIMG_IMG_SPREAD 22
 #endif
@@ -161,8 +162,9 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
     const float inv_ow = __builtin_amdgcn_rcpf((float)a.OW);
 
     // Blocks [I0, I1) (compile time) for the whole K loop, then the partial
-    // sums to LDS: wave slice s, block i, value v, lane l at float index
-    // ((s * MB + i) * 16 + v) * 64 + l.
+    // sums to LDS: wave slice s, pixel m, channel c at float index
+    // (s * 32 MB + m) * kImgRedRow + c (40 floats a pixel: the two lane
+    // halves of a write, 4 pixels apart, fall on disjoint banks).
     auto body = [&](auto i0_tag, auto i1_tag) {
         constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value, NB = I1 - I0;
         constexpr int NA = NB > 0 ? NB : 1;         // (a group with no block still copies and meets)
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
         for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                red[(((wave & 3) * MB + I0 + i) * 16 + v) * 64 + lane] = acc[i][v];
+                red[((wave & 3) * 32 * MB + 32 * (I0 + i) + 8 * (v >> 2) + 4 * lk + (v & 3)) * kImgRedRow + lr] = acc[i][v];
         (void)abase;
     };
     constexpr int MB0 = (MB + 1) / 2;
@@ -269,19 +271,34 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
     wait_lgkmcnt0();
     lds_barrier();
 
-    // block i: summed by wave i % 8 from its 4 partials, + bias, stored
+    // every output pixel m of the image: the 4 partials + bias, stored by
+    // all 512 threads; four channels (16 bytes) a thread where the output
+    // allows 16-byte stores, else one
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
-    const int oc = n0 + lr;
-    const float bv = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
-    for (int i = wave; i < MB; i += kImgWaves) {
+    const unsigned obase = 4u * ((unsigned)n * (unsigned)ohw * (unsigned)a.OC + (unsigned)n0);
+    if (a.vec_out) {
+        const int q4 = 4 * (tid & 7);
+        floatx4_t b4;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int e = 0; e < 4; ++e)
+            b4[e] = (a.bias != nullptr && n0 + q4 + e < a.OC) ? a.bias[n0 + q4 + e] : 0.f;
+        for (int m = tid >> 3; m < ohw; m += kImgThreads / 8) {
+            floatx4_t sum = b4;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                sum += *(const floatx4_t *)(red + (w * 32 * MB + m) * kImgRedRow + q4);
+            const unsigned off = n0 + q4 < a.OC ? obase + 4u * (unsigned)(m * a.OC + q4) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sum), ro, off, 0, kOutAux);
+        }
+    } else {
+        const int c = tid & 31;
+        const float bv = (a.bias != nullptr && n0 + c < a.OC) ? a.bias[n0 + c] : 0.f;
+        for (int m = tid >> 5; m < ohw; m += kImgThreads / 32) {
             float sum = bv;
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                sum += red[((w * MB + i) * 16 + v) * 64 + lane];
-            const int m = 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
-            const unsigned off = (m < ohw && oc < a.OC) ? 4u * (unsigned)((n * ohw + m) * a.OC + oc) : kOutOfRange;
+                sum += red[(w * 32 * MB + m) * kImgRedRow + c];
+            const unsigned off = n0 + c < a.OC ? obase + 4u * (unsigned)(m * a.OC + c) : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, sum), ro, off, 0, kOutAux);
         }
     }

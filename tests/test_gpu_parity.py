@@ -176,6 +176,7 @@ IMAGE_SHAPES = [
     shape(2, 16, 16, 64, 32, 3, 3, 1, 0, 1, name="no padding, 7 blocks"),
     shape(5, 4, 4, 64, 64, 3, 3, 1, 1, 1, name="one block per image"),
     shape(1, 9, 11, 192, 40, 3, 3, 1, 1, 1, name="3 chunks, odd sizes"),
+    shape(2, 10, 10, 64, 50, 3, 3, 1, 1, 1, name="OC 50, dword stores"),
 ]
 
 
