@@ -87,6 +87,7 @@ constexpr int kLdsBytes = 160 * 1024;     // LDS per CU (and per workgroup) on g
 constexpr int kWindowTile = 32;           // the kWindow entry
 constexpr int kResidentTile = 33;         // the kResident entry
 constexpr int kImageTile = 34;            // the kImage entry
+constexpr int kTwoPerCuTile = 15;         // pipe32 128x128, 2 stages: two workgroups per CU
 constexpr int kImgMaxMB = 8;              // image kernel: at most 8 blocks of 32 output pixels
 constexpr int kNumLoaders = 3;
 
@@ -662,8 +663,13 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     const bool image_ok = pipe_ok && aligned && plan_image(N, H, W, IC, OC, KH, KW, p, OH, OW, &imp);
     int tile;
     if (pipe_ok) {
+        // 128x128 tiles two per CU when there are enough for that (one
+        // workgroup's copies overlap the other's MFMAs: measured 7 % faster
+        // than 256x128 on the dilated layer), else 256x128 one per CU, else
+        // 128x64 (with split-K where K is large)
         const long long big = ((M + 255) / 256) * ((OC + 127) / 128);
-        tile = (OC > 64 && big >= num_cus) ? 7 : 11;
+        const long long mid = ((M + 127) / 128) * ((OC + 127) / 128);
+        tile = (OC > 64 && mid >= 2LL * num_cus) ? kTwoPerCuTile : (OC > 64 && big >= num_cus) ? 7 : 11;
     } else if (OC <= 64) {
         tile = (M <= 64LL * num_cus) ? 3 : 0;
     } else {

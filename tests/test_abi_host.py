@@ -92,6 +92,8 @@ def test_plans_of_named_workloads(lib):
     assert p["grid"] == p["tiles_m"] * p["tiles_n"] <= 2 * 256 and p["BM"] == 112
     p = plan_of(WORKLOADS["dilated"])
     assert p["loader"] == abi.CONVIMG_LOADER_TAP and (p["OH"], p["OW"]) == (128, 128)
+    # 512 tiles of 128x128: two workgroups per CU
+    assert p["BM"] == 128 and p["BN"] == 128 and p["grid"] == 512 and p["splits"] == 1
 
 
 def test_tile_kinds(lib):
