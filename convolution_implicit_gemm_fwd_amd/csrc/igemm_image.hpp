@@ -67,6 +67,12 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lk = lane >> 5;
     const int lr = lane & 31;
+    // the arguments the set-up reads, loaded in one batch: the compiler
+    // otherwise loads them as they are needed, one dependent round trip
+    // after another
+    asm volatile("" ::"s"(a.img_ti), "s"(a.img_ts), "s"(a.tiles_n), "s"(a.N), "s"(a.H), "s"(a.W), "s"(a.IC), "s"(a.pad),
+                 "s"(a.OW), "s"(a.OH), "s"(a.img_set), "s"(a.img_wofs), "s"(a.x), "s"(a.w), "s"(a.x_bytes),
+                 "s"(a.w_bytes), "s"(a.dil), "s"(a.stride));
 
     // workgroups in XCD order (each XCD runs a contiguous range), tiled in
     // blocks of img_ti images x img_ts channel slices (about one XCD's
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
     // (ti and ts are powers of two; the few divisions left go through
     // small_div: the prologue runs before any copy is in flight, so every
     // instruction in it is on the critical path)
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int bid = xcd_remap(blockIdx.x, a.N * a.tiles_n);   // (the grid: one workgroup per image and slice)
     const int lti = __builtin_ctz(a.img_ti), lts = __builtin_ctz(a.img_ts);
     const int blk = bid >> (lti + lts), inb = bid & ((1 << (lti + lts)) - 1);
     const int nbs = a.tiles_n >> lts;               // blocks along the slices

@@ -53,9 +53,15 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lk = lane >> 5;
     const int lr = lane & 31;
+    // the arguments the set-up reads, loaded in one batch: the compiler
+    // otherwise loads them as they are needed, one dependent round trip
+    // after another
+    asm volatile("" ::"s"(a.tiles_m), "s"(a.tiles_n), "s"(a.M), "s"(a.IC), "s"(a.H), "s"(a.W), "s"(a.K),
+                 "s"(a.stride), "s"(a.pad), "s"(a.dil), "s"(a.OH), "s"(a.OW), "s"(a.KH), "s"(a.x), "s"(a.w),
+                 "s"(a.x_bytes), "s"(a.w_bytes), "s"(a.lds_rows), "s"(a.res_zero), "s"(a.OC), "s"(a.bias));
     // ranges in XCD order: neighbouring ranges share input rows, which then
-    // meet in one L2
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    // meet in one L2 (the grid: tiles_m ranges per 64-channel slice)
+    const int bid = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
     const int gn = bid / a.tiles_m;
     const int gm = bid - gn * a.tiles_m;
     const int n0 = gn * 64;

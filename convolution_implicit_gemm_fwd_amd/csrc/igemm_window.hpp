@@ -65,10 +65,17 @@ __global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvAr
     // second workgroup) take the larger shares of an even split, so the two
     // workgroups of a CU sum to about the same count on every CU.  With
     // several slices: an even split in launch order, larger shares first.
+    // the arguments the set-up reads, loaded in one batch: the compiler
+    // otherwise loads them as they are needed, one dependent round trip
+    // after another
+    asm volatile("" ::"s"(a.N), "s"(a.OH), "s"(a.OW), "s"(a.win_segs), "s"(a.win_seg), "s"(a.tiles_n),
+                 "s"(a.tiles_m), "s"(a.IC), "s"(a.KW), "s"(a.stride), "s"(a.pad), "s"(a.dil), "s"(a.H), "s"(a.W),
+                 "s"(a.win_sh), "s"(a.win_wp), "s"(a.win_rb), "s"(a.win_sets), "s"(a.x), "s"(a.x_bytes),
+                 "s"(a.lds_rows), "s"(a.K));
     const int units = a.N * a.OH * a.win_segs;
     int gn, u_begin, u_end;
     if (a.tiles_n == 1) {
-        const int G = gridDim.x, q = G >> 3, r = G & 7;
+        const int G = a.tiles_m, q = G >> 3, r = G & 7;      // (the grid: tiles_m groups of units)
         const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
         const int cnt = q + (x < r ? 1 : 0);                      // workgroups of XCD x
         const int base = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
