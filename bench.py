@@ -37,14 +37,14 @@ MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per by
 # hash of that kernel family's sources.  Reported only while the plan and
 # the sources are unchanged; otherwise traffic is null.
 TRAFFIC = {
-    # profiles/igemm_resident_resnet3x3.md: 7.143 MB read + 12.845 MB written
-    "resnet3x3": {"bytes": 19987799, "tile": 33, "kernel": "ea59ce70ee35293f"},
-    # profiles/igemm_image_largek.md: 25.605 MB read + 6.423 MB written
-    "largek": {"bytes": 32027866, "tile": 34, "kernel": "3d3da43a173e9fd5"},
-    # profiles/igemm_window_stem7x7.md: 5.298 MB read + 51.380 MB written
-    "stem7x7": {"bytes": 56678228, "tile": 32, "kernel": "55da977536ac0e07"},
-    # profiles/igemm_pipe_dilated.md: 19.908 MB read + 33.554 MB written
-    "dilated": {"bytes": 53462546, "tile": 7, "kernel": "967f9af2851f572e"},
+    # profiles/igemm_resident_resnet3x3.md: 7.147 MB read + 12.845 MB written
+    "resnet3x3": {"bytes": 19992049, "tile": 33, "kernel": "59acd9361b6bc264"},
+    # profiles/igemm_image_largek.md: 25.604 MB read + 6.423 MB written
+    "largek": {"bytes": 32026353, "tile": 34, "kernel": "c13d94dd0324654a"},
+    # profiles/igemm_window_stem7x7.md: 5.316 MB read + 51.380 MB written
+    "stem7x7": {"bytes": 56695731, "tile": 32, "kernel": "38c0bae53d9aeee5"},
+    # profiles/igemm_pipe_dilated.md: 19.912 MB read + 33.554 MB written
+    "dilated": {"bytes": 53466019, "tile": 15, "kernel": "967f9af2851f572e"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
