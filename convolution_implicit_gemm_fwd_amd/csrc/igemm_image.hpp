@@ -16,16 +16,17 @@
 //     row (without the gap, pixel (oh+1, 0) shares banks with (oh, 0));
 //   * the chunk's weights: per tap, 32 records of 64 channels plus a spare
 //     chunk;
-// into one of two buffer sets, so chunk c+1 is in flight while chunk c is
-// multiplied.  Waves 0-3 take the first ceil(MB/2) pixel blocks and waves
+// into one of two buffer sets: chunk c+1's copies are issued between chunk
+// c's MFMAs, after the one barrier per chunk that tells every wave chunk c
+// has landed and the other set is free.  Waves 0-3 take the first ceil(MB/2) pixel blocks and waves
 // 4-7 the rest (each SIMD holds one wave of each group, so every SIMD does
 // the same MFMA work); within a group, wave w takes channels 16 (w & 3) ..
 // +16 of every chunk, for all taps, with v_mfma_f32_32x32x16_bf16 (A and B
 // from LDS; each B fragment serves the group's blocks).  Each wave's code is
 // straight-line over the taps (no branch around an MFMA: the compiler
 // duplicates the accumulators across such branches).  After the last chunk
-// the 4 partial tiles of each block are summed through LDS, bias added, and
-// stored.
+// the 4 partial sums of each output are added through LDS by all threads,
+// bias added, and stored 16 bytes a thread where the output allows.
 #pragma once
 
 #include <type_traits>

@@ -17,15 +17,16 @@
 // K loop runs over all taps, IC/16 MFMA steps per tap, with
 // v_mfma_f32_32x32x16_bf16 against both 32-channel halves of the slice
 // (A and B from LDS, next step's fragments loaded during this step's
-// MFMAs).  Results (+ bias) are stored straight from the accumulators; no
-// copy or barrier follows the prologue, so one wave's stores overlap the
-// other waves' MFMAs.
+// MFMAs; even and odd steps into separate accumulators).  Results (+ bias)
+// leave through a per-wave LDS scratch as 16-byte stores (or one dword a
+// lane where the output does not allow them); no copy or barrier follows
+// the prologue, so one wave's stores overlap the other waves' MFMAs.
 //
 // Measured on MI355X (ResNet 3x3 layer above), this order beat the
 // alternatives tried: copying the rows before the weights, tap-major weight
-// records with a barrier per tap (MFMAs starting before the later taps have
-// landed), and 64-pixel units (one wave per SIMD cannot hide the LDS and
-// MFMA latencies that two waves per SIMD do).
+// records with a barrier per tap or per kernel row (MFMAs starting before
+// the later taps have landed), 16 waves, and 64-pixel units (one wave per
+// SIMD cannot hide the LDS and MFMA latencies that two waves per SIMD do).
 #pragma once
 
 #include "igemm_common.hpp"
