@@ -68,6 +68,8 @@ class Oracle:
             [dp, dp, dp] + [ip] * 10
             + [ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, dp, dp])
         lib.oracle_conv2d_fwd_pixels.restype = ip
+        lib.oracle_conv2d_bwd_data.argtypes = [dp, dp] + [ip] * 10 + [dp, dp]
+        lib.oracle_conv2d_bwd_data.restype = ip
         lib.oracle_set_threads.argtypes = [ip]
         lib.oracle_set_threads.restype = ip
         self.lib = lib
@@ -129,6 +131,29 @@ class Oracle:
             raise ValueError("oracle rejected the shape or a pixel index")
         return y, S
 
+    def conv2d_bwd_data(self, dy, w, H, W, stride=1, pad=0, dilation=1):
+        """Gradient of the forward convolution with respect to its input.
+
+        dy: [N][OH][OW][OC] (OH, OW the forward extents of H, W), w:
+        [OC][KH][KW][IC].  Returns (dx, S), float64 [N][H][W][IC]; S = sum
+        |dy*w| over the terms of each element.
+        """
+        dy = _as_f64(dy, 4, "dy")
+        w = _as_f64(w, 4, "w")
+        N, OH, OW, OC = dy.shape
+        OC2, KH, KW, IC = w.shape
+        if OC2 != OC:
+            raise ValueError("channel mismatch: dy has %d, w has %d" % (OC, OC2))
+        if (self.out_dim(H, KH, stride, pad, dilation), self.out_dim(W, KW, stride, pad, dilation)) != (OH, OW):
+            raise ValueError("dy extent does not match the forward output of H, W")
+        dx = np.empty((N, H, W, IC), np.float64)
+        S = np.empty((N, H, W, IC), np.float64)
+        rc = self.lib.oracle_conv2d_bwd_data(_dptr(dy), _dptr(w), N, H, W, IC, OC, KH, KW,
+                                             stride, pad, dilation, _dptr(dx), _dptr(S))
+        if rc != 0:
+            raise ValueError("oracle rejected the shape")
+        return dx, S
+
 
 _default = None
 
@@ -157,3 +182,7 @@ def conv2d_fwd(x, w, bias=None, stride=1, pad=0, dilation=1):
 
 def conv2d_fwd_pixels(x, w, bias, stride, pad, dilation, pixels):
     return get().conv2d_fwd_pixels(x, w, bias, stride, pad, dilation, pixels)
+
+
+def conv2d_bwd_data(dy, w, H, W, stride=1, pad=0, dilation=1):
+    return get().conv2d_bwd_data(dy, w, H, W, stride, pad, dilation)

@@ -1,5 +1,6 @@
 /*
- * conv_ref.c -- CPU oracle for 2-D convolution forward, NHWC / OHWI / NHWC.
+ * conv_ref.c -- CPU oracle for 2-D convolution forward, NHWC / OHWI / NHWC,
+ * and for its data-backward pass.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The HIP library and
@@ -147,6 +148,66 @@ int oracle_conv2d_fwd_pixels(const double *x, const double *w, const double *bia
         conv_pixel(x, w, bias, H, W, IC, OC, KH, KW, s, p, d, n, oh, ow,
                    y + i * OC, S ? S + i * OC : NULL);
     }
+    return 0;
+}
+
+/* Gradient of the forward convolution with respect to its input x (the
+ * data-backward pass of the burn-cubecl "kernel/conv/base.rs" listing,
+ * conv_data_backward: it takes the output gradient and the weights and
+ * returns a tensor of the input's shape).  Since y is linear in x,
+ *
+ *   dx[n][ih][iw][ic] = sum over (oh, ow, kh, kw, oc) with
+ *                         oh*s - p + kh*d == ih and ow*s - p + kw*d == iw
+ *                       of dy[n][oh][ow][oc] * w[oc][kh][kw][ic]
+ *   S[n][ih][iw][ic]  = the same sum of |dy * w|
+ *
+ * dy is N x OH x OW x OC with OH, OW the forward output extents of (H, W);
+ * dx and S are N x H x W x IC.  For each input pixel the terms are taken in
+ * the order kh, kw, oc, with oh = (ih + p - kh*d) / s where that division
+ * is exact and 0 <= oh < OH (likewise ow); any stride.  Returns 0, or -1 on
+ * bad shapes. */
+int oracle_conv2d_bwd_data(const double *dy, const double *w,
+                           int N, int H, int W, int IC, int OC, int KH, int KW,
+                           int s, int p, int d, double *dx, double *S)
+{
+    int OH, OW;
+    if (check_args(N, H, W, IC, OC, KH, KW, s, p, d, &OH, &OW))
+        return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int n = 0; n < N; ++n)
+        for (int ih = 0; ih < H; ++ih)
+            for (int iw = 0; iw < W; ++iw) {
+                size_t px = ((size_t)n * H + ih) * W + iw;
+                double *g = dx + px * IC;
+                double *a = S ? S + px * IC : NULL;
+                for (int ic = 0; ic < IC; ++ic) {
+                    g[ic] = 0.0;
+                    if (a)
+                        a[ic] = 0.0;
+                }
+                for (int kh = 0; kh < KH; ++kh) {
+                    int th = ih + p - kh * d;          /* = oh * s */
+                    if (th < 0 || th % s != 0 || th / s >= OH)
+                        continue;
+                    int oh = th / s;
+                    for (int kw = 0; kw < KW; ++kw) {
+                        int tw = iw + p - kw * d;      /* = ow * s */
+                        if (tw < 0 || tw % s != 0 || tw / s >= OW)
+                            continue;
+                        int ow = tw / s;
+                        const double *gy = dy + (((size_t)n * OH + oh) * OW + ow) * OC;
+                        for (int oc = 0; oc < OC; ++oc) {
+                            const double *wr = w + ((size_t)(oc * KH + kh) * KW + kw) * IC;
+                            for (int ic = 0; ic < IC; ++ic) {
+                                double t = gy[oc] * wr[ic];
+                                g[ic] += t;
+                                if (a)
+                                    a[ic] += fabs(t);
+                            }
+                        }
+                    }
+                }
+            }
     return 0;
 }
 

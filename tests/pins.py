@@ -244,5 +244,78 @@ def pin_pixels(o):
     assert np.array_equal(py, flat_y[pix]) and np.array_equal(pS, flat_S[pix])
 
 
+# ---- data backward (the gradient with respect to x)
+
+def pin_bwd_adjoint(o, cases=30, seed=19):
+    """B1: the data-backward pass is the adjoint of the forward map x -> y - b:
+    sum(conv(x, w) * dy) == sum(x * dx(dy, w)) for every dy, x, w.  Small
+    integers make both sides exact in fp64, so the check is equality; random
+    strides, paddings (also past the window), dilations, non-square kernels."""
+    rng = np.random.default_rng(seed)
+    done = 0
+    while done < cases:
+        N, H, W = int(rng.integers(1, 3)), int(rng.integers(1, 10)), int(rng.integers(1, 10))
+        IC, OC = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        KH, KW = int(rng.choice([1, 2, 3, 5])), int(rng.choice([1, 2, 3]))
+        s, p, d = int(rng.integers(1, 4)), int(rng.integers(0, 4)), int(rng.integers(1, 3))
+        OH, OW = o.out_dim(H, KH, s, p, d), o.out_dim(W, KW, s, p, d)
+        if OH <= 0 or OW <= 0:
+            continue
+        x = int_data(rng, (N, H, W, IC))
+        w = int_data(rng, (OC, KH, KW, IC))
+        dy = int_data(rng, (N, OH, OW, OC))
+        y, _ = o.conv2d_fwd(x, w, None, s, p, d)
+        dx, S = o.conv2d_bwd_data(dy, w, H, W, s, p, d)
+        assert dx.shape == x.shape
+        lhs, rhs = float(np.sum(y * dy)), float(np.sum(x * dx))
+        assert lhs == rhs, "adjoint identity fails: %r vs %r at %s" % (lhs, rhs, (N, H, W, IC, OC, KH, KW, s, p, d))
+        done += 1
+
+
+def pin_bwd_torch(o):
+    """B2: torch.nn.grad.conv2d_input in fp64 on NCHW views (an independent
+    library implementation of the same gradient)."""
+    import torch
+    rng = np.random.default_rng(20)
+    for (N, H, W, IC, OC, KH, KW, s, p, d) in [(2, 11, 9, 6, 5, 3, 3, 1, 1, 1),
+                                                (1, 16, 16, 3, 8, 7, 7, 2, 3, 1),
+                                                (2, 13, 12, 8, 4, 3, 3, 1, 2, 2),
+                                                (1, 10, 7, 5, 6, 2, 4, 3, 2, 2)]:
+        OH, OW = o.out_dim(H, KH, s, p, d), o.out_dim(W, KW, s, p, d)
+        dy = rng.standard_normal((N, OH, OW, OC))
+        w = rng.standard_normal((OC, KH, KW, IC))
+        dx, _ = o.conv2d_bwd_data(dy, w, H, W, s, p, d)
+        t = torch.nn.grad.conv2d_input((N, IC, H, W), torch.from_numpy(w).permute(0, 3, 1, 2),
+                                       torch.from_numpy(dy).permute(0, 3, 1, 2),
+                                       stride=s, padding=p, dilation=d)
+        assert_close(dx, t.permute(0, 2, 3, 1).numpy(), 1e-12, 1e-12, "torch conv2d_input")
+
+
+def pin_bwd_delta(o):
+    """B3: with a centred identity kernel and 'same' padding (stride 1) the
+    forward map is the identity, so its gradient is too: dx == dy exactly."""
+    rng = np.random.default_rng(21)
+    for K, d in ((3, 1), (5, 2), (1, 1)):
+        C = 4
+        w = np.zeros((C, K, K, C))
+        for c in range(C):
+            w[c, K // 2, K // 2, c] = 1.0
+        dy = rng.standard_normal((2, 7, 6, C))
+        dx, _ = o.conv2d_bwd_data(dy, w, 7, 6, 1, d * (K - 1) // 2, d)
+        assert np.array_equal(dx, dy), "identity kernel: dx != dy (K=%d, d=%d)" % (K, d)
+
+
+def pin_bwd_magnitude(o):
+    """B4: S >= |dx| everywhere, and S equals the gradient of |dy| through |w|."""
+    rng = np.random.default_rng(22)
+    dy = rng.standard_normal((2, 8, 8, 5))
+    w = rng.standard_normal((5, 3, 3, 4))
+    dx, S = o.conv2d_bwd_data(dy, w, 8, 8, 1, 1, 1)
+    assert (S >= np.abs(dx) - 1e-12).all(), "triangle inequality"
+    da, _ = o.conv2d_bwd_data(np.abs(dy), np.abs(w), 8, 8, 1, 1, 1)
+    assert_close(S, da, 1e-12, 1e-12, "S equals the gradient of magnitudes")
+
+
 ALL_PINS = [pin_out_dims, pin_matmul_1x1, pin_centered_delta, pin_offcenter_delta,
-            pin_all_ones, pin_bruteforce, pin_linearity, pin_torch, pin_magnitude, pin_pixels]
+            pin_all_ones, pin_bruteforce, pin_linearity, pin_torch, pin_magnitude, pin_pixels,
+            pin_bwd_adjoint, pin_bwd_torch, pin_bwd_delta, pin_bwd_magnitude]

@@ -63,6 +63,18 @@ MUTANTS = [
      "double acc = 0.0;", "float acc = 0.0f;"),
     ("output extent rounded up",
      "return (int)((padded - span) / s + 1);", "return (int)((padded - span + s - 1) / s + 1);"),
+    ("data backward: padding sign flipped",
+     "int th = ih + p - kh * d;", "int th = ih - p - kh * d;"),
+    ("data backward: stride remainder ignored",
+     "if (th < 0 || th % s != 0 || th / s >= OH)", "if (th < 0 || th / s >= OH)"),
+    ("data backward: kernel flipped",
+     "((size_t)(oc * KH + kh) * KW + kw) * IC", "((size_t)(oc * KH + (KH - 1 - kh)) * KW + (KW - 1 - kw)) * IC"),
+    ("data backward: input channels reversed",
+     "double t = gy[oc] * wr[ic];", "double t = gy[oc] * wr[IC - 1 - ic];"),
+    ("data backward: column dilation dropped",
+     "int tw = iw + p - kw * d;", "int tw = iw + p - kw;"),
+    ("data backward: magnitude without abs",
+     "a[ic] += fabs(t);", "a[ic] += t;"),
 ]
 
 
