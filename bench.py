@@ -1,11 +1,16 @@
 """Benchmark: conv2d forward (implicit GEMM, bf16 MFMA) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op fwd|dgrad]
 
 A step is one conv2d_fwd call (the whole hot path: im2col gather, bf16 MFMA,
 fused bias, fp32 store) over the workload's batch, with every input already
 resident in device memory.  The default workload is the ResNet-style 3x3
 layer (N=16, 56x56, 64 -> 64 channels).  Prints ONE JSON line.
+
+--op dgrad times conv2d_bwd_data instead (the gradient with respect to the
+input, stride-1 workloads only): a step is the weight flip-transpose plus
+the forward implicit GEMM it maps to; the roofline object then prices that
+GEMM kernel alone (timed in its own loop on the same buffers).
 
 Timing: K back-to-back calls on one stream between two HIP events (recorded
 on that stream), synchronised on both sides.  TFLOP/s = 2*M*OC*K / time with
@@ -26,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "conv2d fwd TFLOP/s (2·M·N·K/s) + % of bf16 MFMA peak, 1×MI355X"
+METRIC_DGRAD = "conv2d bwd-data TFLOP/s (2·N·H·W·IC·OC·KH·KW/s) + % of bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
@@ -77,6 +83,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="resnet3x3")
+    ap.add_argument("--op", choices=("fwd", "dgrad"), default="fwd")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline sample (0 disables it)")
     ap.add_argument("--force", default=None,
@@ -98,14 +105,17 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_mib": mib, "copies": 5}), flush=True)
 
 
-def cpu_baseline(inp, wl, flops, seconds):
+def cpu_baseline(inp, wl, flops, seconds, op="fwd"):
     """The fp64 oracle on this host: whole-workload passes until `seconds`."""
     import oracle
     o = oracle.get()
     threads = o.set_threads(0)
     runs, t0 = 0, time.perf_counter()
     while True:
-        o.conv2d_fwd(inp.x32, inp.w32, inp.bias, wl.stride, wl.pad, wl.dilation)
+        if op == "fwd":
+            o.conv2d_fwd(inp.x32, inp.w32, inp.bias, wl.stride, wl.pad, wl.dilation)
+        else:
+            o.conv2d_bwd_data(inp.x32, inp.w32, wl.H, wl.W, wl.stride, wl.pad, wl.dilation)
         runs += 1
         el = time.perf_counter() - t0
         if el >= seconds or runs >= 100:
@@ -113,8 +123,37 @@ def cpu_baseline(inp, wl, flops, seconds):
     per = el / runs
     return {"value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d full pass(es) of the %s workload (fp64 direct 7-loop, also summing |x*w|), "
-                      "%.2f s each" % (runs, wl.name, per)}
+            "sample": "%d full pass(es) of the %s workload's %s (fp64 direct 7-loop, also "
+                      "summing |x*w|), %.2f s each" % (runs, wl.name, op, per)}
+
+
+def dist_text(dist):
+    if dist[0] == "normal":
+        return "N(%g, sd %g)" % (dist[1], dist[2])
+    if dist[0] == "uniform":
+        return "U(%g, %g)" % (dist[1], dist[2])
+    return dist[0]
+
+
+def timed(fn, call_args, steps, warmup, stream):
+    """ms per call of fn(*call_args): warmup calls, then `steps` calls
+    between two events recorded on `stream`, synchronised on both sides."""
+    import torch
+    rc = fn(*call_args)
+    assert rc == 0, rc
+    for _ in range(warmup):
+        fn(*call_args)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn(*call_args)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall * 1e3 / steps
 
 
 def main():
@@ -131,74 +170,83 @@ def main():
     import torch
 
     from convolution_implicit_gemm_fwd_amd import abi
-    from convolution_implicit_gemm_fwd_amd.workloads import BF16, WORKLOADS, make_inputs
+    from convolution_implicit_gemm_fwd_amd.workloads import (BF16, WORKLOADS, make_grad_inputs,
+                                                             make_inputs)
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
-    abi.load()                      # fails loudly if the HIP library is not built
+    lib = abi.load()                # fails loudly if the HIP library is not built
     wl = WORKLOADS[args.workload]
-    inp = make_inputs(wl, seed=0)
+    dgrad = args.op == "dgrad"
+    if dgrad and wl.stride != 1:
+        print("--op dgrad needs a stride-1 workload (%s has stride %d)" % (wl.name, wl.stride),
+              file=sys.stderr)
+        sys.exit(2)
+    OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
+    OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
+    M, K = wl.N * OH * OW, wl.IC * wl.KH * wl.KW
+    inp = make_grad_inputs(wl, OH, OW, seed=0) if dgrad else make_inputs(wl, seed=0)
 
     def up(a):
         t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
         return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).cuda()
 
     x, w, b = up(inp.x_store), up(inp.w_store), torch.from_numpy(inp.bias).cuda()
-    OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
-    OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
-    M, K = wl.N * OH * OW, wl.IC * wl.KH * wl.KW
-    out = torch.empty((wl.N, OH, OW, wl.OC), dtype=torch.float32, device="cuda")
     if args.force:
         abi.conv2d_fwd_force(*[int(v) for v in args.force.split(",")])
-    rc, plan = abi.conv2d_fwd_plan(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride,
-                                   wl.pad, wl.dilation, wl.dtype, 0)
-    assert rc == 0, abi.conv2d_strerror(rc)
-
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    lib = abi.load()
-    call_args = (x.data_ptr(), w.data_ptr(), b.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC,
-                 wl.KH, wl.KW, wl.stride, wl.pad, wl.dilation, wl.dtype, out.data_ptr(), sptr)
-    fn = lib.conv2d_fwd
-
-    for _ in range(args.warmup):
-        rc = fn(*call_args)
-    assert rc == 0, abi.conv2d_strerror(rc)
-    torch.cuda.synchronize()
-
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        fn(*call_args)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
-    assert abi.conv2d_fwd_status(sptr) == 0
-
-    flops = 2 * M * wl.OC * K
-    tflops = flops / (ms_step * 1e-3) / 1e12
     esz = 2 if wl.dtype == BF16 else 4
-    alg_bytes = (wl.N * wl.H * wl.W * wl.IC + wl.OC * K) * esz + wl.OC * 4 + M * wl.OC * 4
+    if not dgrad:
+        out = torch.empty((wl.N, OH, OW, wl.OC), dtype=torch.float32, device="cuda")
+        gemm = (wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride, wl.pad, wl.dilation)
+        call_args = ((x.data_ptr(), w.data_ptr(), b.data_ptr()) + gemm
+                     + (wl.dtype, out.data_ptr(), sptr))
+        fn = lib.conv2d_fwd
+        alg_bytes = (wl.N * wl.H * wl.W * wl.IC + wl.OC * K) * esz + wl.OC * 4 + M * wl.OC * 4
+    else:
+        # x holds dy [N,OH,OW,OC]; the data backward maps to a forward
+        # convolution of dy with the flipped, transposed weights
+        out = torch.empty((wl.N, wl.H, wl.W, wl.IC), dtype=torch.float32, device="cuda")
+        wt = torch.empty_like(w)
+        call_args = (x.data_ptr(), w.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
+                     1, wl.pad, wl.dilation, wl.dtype, wt.data_ptr(), out.data_ptr(), sptr)
+        fn = lib.conv2d_bwd_data
+        gemm = (wl.N, OH, OW, wl.OC, wl.IC, wl.KH, wl.KW, 1,
+                wl.dilation * (wl.KH - 1) - wl.pad, wl.dilation)
+        alg_bytes = (M * wl.OC + wl.OC * K) * esz + wl.N * wl.H * wl.W * wl.IC * 4
+    rc, plan = abi.conv2d_fwd_plan(*gemm, wl.dtype, 0)
+    assert rc == 0, abi.conv2d_strerror(rc)
+
+    ms_step, wall_ms = timed(fn, call_args, args.steps, args.warmup, stream)
+    assert abi.conv2d_fwd_status(sptr) == 0
+    if dgrad:
+        # the implicit-GEMM kernel alone, on the weights the steps left in wt
+        gemm_args = (x.data_ptr(), wt.data_ptr(), None) + gemm + (wl.dtype, out.data_ptr(), sptr)
+        ms_gemm, _ = timed(lib.conv2d_fwd, gemm_args, args.steps, args.warmup, stream)
+        assert abi.conv2d_fwd_status(sptr) == 0
+    else:
+        ms_gemm = ms_step
+
+    flops = 2 * M * wl.OC * K          # = 2*N*H*W*IC*OC*KH*KW for the stride-1 data backward
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
     ai = flops / alg_bytes
     peak_flops = PEAK_BF16_TFLOPS if wl.dtype == BF16 else PEAK_FP32_MFMA_TFLOPS
     if ai < MACHINE_BALANCE:
-        achieved = alg_bytes / (ms_step * 1e-3) / 1e9
+        achieved = alg_bytes / (ms_gemm * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_flops,
-                "unit": "TFLOP/s", "frac": round(tflops / peak_flops, 4)}
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / peak_flops, 4)}
     kind = abi.conv2d_fwd_tile_kind(plan["tile_id"]) if plan["tile_id"] >= 0 else -1
     ksrc = kernel_sources_hash(kind)
-    t = TRAFFIC.get(wl.name)
+    t = TRAFFIC.get(wl.name if not dgrad else "dgrad:" + wl.name)
     roof["traffic"] = (t["bytes"] if t and t["tile"] == plan["tile_id"] and t["kernel"] == ksrc
                        else None)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC_DGRAD if dgrad else METRIC,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -209,19 +257,24 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == BF16 else "f32",
-        "data": "synthetic (seeded; x N(0,1), w N(0,1/sqrt(K)), bias N(0,0.01); bf16-rounded)",
-        "config": {"workload": wl.name, "N": wl.N, "H": wl.H, "W": wl.W, "IC": wl.IC,
+        "data": "synthetic (seeded; %s %s, w %s%s; bf16-rounded)" % (
+            "dy" if dgrad else "x", dist_text(wl.x_dist), dist_text(wl.w_dist),
+            "" if dgrad else ", bias " + dist_text(wl.bias_dist)),
+        "config": {"workload": wl.name + (" data backward" if dgrad else ""), "N": wl.N,
+                   "H": wl.H, "W": wl.W, "IC": wl.IC,
                    "OC": wl.OC, "KH": wl.KH, "KW": wl.KW, "stride": wl.stride, "pad": wl.pad,
                    "dilation": wl.dilation, "M": M, "K": K,
                    "plan": {k: plan[k] for k in ("tile_id", "BM", "BN", "BK", "loader",
                                                  "splits", "grid")}},
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
-        "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 6),
+        "host_wall_ms_per_step": round(wall_ms, 6),
         "kernel_sources": ksrc,
     }
+    if dgrad:
+        line["gemm_ms"] = round(ms_gemm, 6)
     if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(inp, wl, flops, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inp, wl, flops, args.cpu_seconds, args.op)
     print(json.dumps(line), flush=True)
 
 

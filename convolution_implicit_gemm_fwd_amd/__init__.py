@@ -4,7 +4,8 @@ NHWC input, OHWI weight, fp32 bias and fp32 NHWC output; bf16 (or fp32)
 inputs; hand-written HIP kernels for gfx950 behind the C ABI of
 include/convimg.h.  ``abi`` is the ctypes binding of that ABI (same names);
 ``conv2d_nhwc`` below wraps it for torch tensors, using torch only for device
-memory and the current stream.
+memory and the current stream; ``conv2d_bwd_data_nhwc`` does the same for the
+gradient with respect to the input (stride 1).
 
 Importing the package loads nothing; the HIP library is loaded on first use
 and its absence is an error (there is no fallback path).
@@ -12,13 +13,24 @@ and its absence is an error (there is no fallback path).
 from __future__ import annotations
 
 from . import abi
-from .abi import (CONVIMG_BF16, CONVIMG_FP32, LibraryMissing, conv2d_fwd, conv2d_fwd_force,
-                  conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
+from .abi import (CONVIMG_BF16, CONVIMG_FP32, LibraryMissing, conv2d_bwd_data,
+                  conv2d_bwd_data_weights, conv2d_fwd, conv2d_fwd_force, conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
                   conv2d_fwd_status, conv2d_release, conv2d_strerror)
 
-__all__ = ["abi", "conv2d_nhwc", "conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan",
-           "conv2d_strerror", "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_status",
-           "conv2d_release", "CONVIMG_BF16", "CONVIMG_FP32", "LibraryMissing"]
+__all__ = ["abi", "conv2d_nhwc", "conv2d_bwd_data_nhwc", "conv2d_bwd_data",
+           "conv2d_bwd_data_weights", "conv2d_fwd",
+           "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror", "conv2d_fwd_force",
+           "conv2d_fwd_num_tiles", "conv2d_fwd_status", "conv2d_release", "CONVIMG_BF16", "CONVIMG_FP32", "LibraryMissing"]
+
+
+def _dtype_of(a, b, what):
+    import torch
+
+    if a.dtype == torch.bfloat16 and b.dtype == torch.bfloat16:
+        return CONVIMG_BF16
+    if a.dtype == torch.float32 and b.dtype == torch.float32:
+        return CONVIMG_FP32
+    raise TypeError("%s must both be bfloat16 or both float32" % what)
 
 
 def conv2d_nhwc(x, w, bias=None, stride=1, pad=0, dilation=1, out=None, stream=None):
@@ -31,12 +43,7 @@ def conv2d_nhwc(x, w, bias=None, stride=1, pad=0, dilation=1, out=None, stream=N
     """
     import torch
 
-    if x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16:
-        dtype = CONVIMG_BF16
-    elif x.dtype == torch.float32 and w.dtype == torch.float32:
-        dtype = CONVIMG_FP32
-    else:
-        raise TypeError("x and w must both be bfloat16 or both float32")
+    dtype = _dtype_of(x, w, "x and w")
     if not (x.is_cuda and w.is_cuda):
         raise ValueError("x and w must be device tensors")
     if x.dim() != 4 or w.dim() != 4 or x.shape[3] != w.shape[3]:
@@ -67,3 +74,48 @@ def conv2d_nhwc(x, w, bias=None, stride=1, pad=0, dilation=1, out=None, stream=N
     if rc != 0:
         raise RuntimeError("conv2d_fwd failed: %s (status %d)" % (conv2d_strerror(rc), rc))
     return out
+
+
+def conv2d_bwd_data_nhwc(dy, w, H, W, stride=1, pad=0, dilation=1, dx=None, wt=None,
+                         stream=None):
+    """dx[N,H,W,IC] (fp32): gradient of conv2d_nhwc's output with respect to x.
+
+    dy: contiguous [N,OH,OW,OC] device tensor (the output gradient), w: the
+    forward weights [OC,KH,KW,IC]; both bfloat16 or both float32.  H, W,
+    stride, pad, dilation: the forward problem (stride must be 1 and KH == KW).
+    wt: optional workspace of w's numel and dtype that receives the flipped,
+    transposed weights [IC,KH,KW,OC]; dx: optional preallocated output.  Runs
+    on ``stream`` (default: torch's current stream) without waiting.
+    """
+    import torch
+
+    dtype = _dtype_of(dy, w, "dy and w")
+    if not (dy.is_cuda and w.is_cuda):
+        raise ValueError("dy and w must be device tensors")
+    if dy.dim() != 4 or w.dim() != 4 or dy.shape[3] != w.shape[0]:
+        raise ValueError("dy must be [N,OH,OW,OC] and w [OC,KH,KW,IC]")
+    if not (dy.is_contiguous() and w.is_contiguous()):
+        raise ValueError("dy and w must be contiguous (NHWC / OHWI)")
+    N, OH, OW, OC = dy.shape
+    _, KH, KW, IC = w.shape
+    if (conv2d_fwd_out_dim(H, KH, stride, pad, dilation) != OH
+            or conv2d_fwd_out_dim(W, KW, stride, pad, dilation) != OW):
+        raise ValueError("dy's extent is not the forward output extent of H x W")
+    if wt is None:
+        wt = torch.empty(w.numel(), dtype=w.dtype, device=w.device)
+    elif (wt.numel() != w.numel() or wt.dtype != w.dtype or not wt.is_contiguous()
+          or not wt.is_cuda):
+        raise ValueError("wt must be a contiguous device tensor of w's size and dtype")
+    if dx is None:
+        dx = torch.empty((N, H, W, IC), dtype=torch.float32, device=dy.device)
+    elif (tuple(dx.shape) != (N, H, W, IC) or dx.dtype != torch.float32
+          or not dx.is_contiguous() or not dx.is_cuda):
+        raise ValueError("dx must be a contiguous float32 [N,H,W,IC] device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(dy.device).cuda_stream
+    with torch.cuda.device(dy.device):
+        rc = conv2d_bwd_data(dy.data_ptr(), w.data_ptr(), N, H, W, IC, OC, KH, KW, stride, pad,
+                             dilation, dtype, wt.data_ptr(), dx.data_ptr(), stream)
+    if rc != 0:
+        raise RuntimeError("conv2d_bwd_data failed: %s (status %d)" % (conv2d_strerror(rc), rc))
+    return dx

@@ -24,6 +24,7 @@ CONVIMG_ERR_ALLOC = 6
 CONVIMG_ERR_LAUNCH = 7
 CONVIMG_ERR_DEVICE = 8
 CONVIMG_ERR_TIMEOUT = 9
+CONVIMG_ERR_UNSUPPORTED = 10
 
 CONVIMG_LOADER_TAP = 0
 CONVIMG_LOADER_VEC8 = 1
@@ -41,7 +42,7 @@ CONVIMG_KIND_IMAGE = 6
 # Every symbol include/convimg.h declares.
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror",
            "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_tile_kind", "conv2d_fwd_status",
-           "conv2d_release")
+           "conv2d_release", "conv2d_bwd_data", "conv2d_bwd_data_weights")
 
 
 class convimg_plan(ctypes.Structure):
@@ -92,6 +93,10 @@ def load(path: str = LIB_PATH):
     lib.conv2d_fwd_status.restype = i
     lib.conv2d_release.argtypes = []
     lib.conv2d_release.restype = None
+    lib.conv2d_bwd_data.argtypes = [vp, vp] + [i] * 11 + [vp, vp, vp]
+    lib.conv2d_bwd_data.restype = i
+    lib.conv2d_bwd_data_weights.argtypes = [vp] + [i] * 5 + [vp, vp]
+    lib.conv2d_bwd_data_weights.restype = i
     _lib = lib
     return lib
 
@@ -100,6 +105,17 @@ def conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype
     """Raw C call: pointers are integers (device addresses), returns a status."""
     return load().conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation,
                              dtype, out, stream)
+
+
+def conv2d_bwd_data(dy, w, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, wt, dx, stream):
+    """Raw C call of the data backward (device addresses as integers), returns a status."""
+    return load().conv2d_bwd_data(dy, w, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype,
+                                  wt, dx, stream)
+
+
+def conv2d_bwd_data_weights(w, OC, KH, KW, IC, dtype, wt, stream):
+    """Raw C call of the data backward's weight transform, returns a status."""
+    return load().conv2d_bwd_data_weights(w, OC, KH, KW, IC, dtype, wt, stream)
 
 
 def conv2d_fwd_out_dim(size, k, stride, pad, dilation):

@@ -7,6 +7,7 @@
 #include "igemm_pipe.hpp"
 #include "igemm_regs.hpp"
 #include "igemm_resident.hpp"
+#include "igemm_dgrad.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_window.hpp"
 
@@ -577,10 +578,10 @@ bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, in
 // Problem -> plan.  `aligned`: x and w start on 16-byte boundaries (the
 // vector loaders need it).  `occ` (may be NULL) gives resident workgroups per
 // CU for each kernel; NULL uses the LDS-only estimate.
-int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
-              int dtype, int num_cus, bool aligned,
-              const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo = nullptr,
-              WinPlan *wpo = nullptr, ResPlan *rpo = nullptr, ImgPlan *ipo = nullptr)
+int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
+                       int dtype, int num_cus, bool aligned,
+                       const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo,
+                       WinPlan *wpo, ResPlan *rpo, ImgPlan *ipo)
 {
     if (N <= 0 || H <= 0 || W <= 0 || IC <= 0 || OC <= 0 || KH <= 0 || KW <= 0
         || s <= 0 || p < 0 || d <= 0)
@@ -820,6 +821,65 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     pl->threads = threads_of(tile);
     pl->lds_bytes = lds_bytes_of(tile);
     return CONVIMG_OK;
+}
+
+// Plans of recent problems, per host thread (no lock): planning evaluates
+// every kernel family (several microseconds for some shapes), which would
+// otherwise be paid on each call of a layer that is run over and over.  The
+// key holds every input of the planner, the forced settings included.
+constexpr int kPlanCacheWays = 8;
+struct PlanCacheEntry {
+    int key[16] = {};
+    const void *occ = nullptr;
+    bool valid = false;
+    int rc = 0;
+    convimg_plan pl = {};
+    StripPlan sp;
+    WinPlan wp;
+    ResPlan rp;
+    ImgPlan ip;
+};
+thread_local PlanCacheEntry t_plans[kPlanCacheWays];
+thread_local unsigned t_plan_next = 0;
+
+int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
+              int dtype, int num_cus, bool aligned,
+              const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo = nullptr,
+              WinPlan *wpo = nullptr, ResPlan *rpo = nullptr, ImgPlan *ipo = nullptr)
+{
+    const int key[16] = {N, H, W, IC, OC, KH, KW, s, p, d, dtype, num_cus, aligned ? 1 : 0,
+                         g_force_tile.load(), g_force_splits.load(), g_force_loader.load()};
+    PlanCacheEntry *e = nullptr;
+    for (PlanCacheEntry &c : t_plans)
+        if (c.valid && c.occ == (const void *)occ && std::memcmp(c.key, key, sizeof(key)) == 0) {
+            e = &c;
+            break;
+        }
+    if (!e) {
+        e = &t_plans[t_plan_next++ % kPlanCacheWays];
+        e->valid = false;
+        e->sp = StripPlan();
+        e->wp = WinPlan();
+        e->rp = ResPlan();
+        e->ip = ImgPlan();
+        e->rc = make_plan_uncached(N, H, W, IC, OC, KH, KW, s, p, d, dtype, num_cus, aligned, occ,
+                                   &e->pl, &e->sp, &e->wp, &e->rp, &e->ip);
+        std::memcpy(e->key, key, sizeof(key));
+        e->occ = occ;
+        e->valid = true;
+    }
+    if (e->rc == CONVIMG_OK) {
+        *pl = e->pl;
+        if (spo)
+            *spo = e->sp;
+        if (wpo)
+            *wpo = e->wp;
+        if (rpo)
+            *rpo = e->rp;
+        if (ipo)
+            *ipo = e->ip;
+    }
+    return e->rc;
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -1065,6 +1125,72 @@ void conv2d_release(void)
     g_sems.clear();
 }
 
+int conv2d_bwd_data_weights(const void *w, int OC, int KH, int KW, int IC, int dtype, void *wt,
+                            hipStream_t stream)
+{
+    if (!w || !wt)
+        return CONVIMG_ERR_NULL;
+    if (OC <= 0 || KH <= 0 || KW <= 0 || IC <= 0)
+        return CONVIMG_ERR_SHAPE;
+    if (dtype != CONVIMG_BF16 && dtype != CONVIMG_FP32)
+        return CONVIMG_ERR_DTYPE;
+    if ((long long)OC * KH * KW * IC >= 0x7fffffffLL)
+        return CONVIMG_ERR_RANGE;
+    const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
+    const size_t nw = (size_t)OC * KH * KW * IC * esz;
+    if (overlaps(wt, nw, w, nw))
+        return CONVIMG_ERR_ALIAS;
+    const dim3 grid((IC + kFlipTile - 1) / kFlipTile, (OC + kFlipTile - 1) / kFlipTile, KH * KW);
+    if (grid.y > 65535u || grid.z > 65535u)
+        return CONVIMG_ERR_RANGE;
+    const int vlen = (int)(16 / esz);
+    const int vec_in = (IC % vlen == 0 && ((uintptr_t)w & 15) == 0) ? 1 : 0;
+    const int vec_out = (OC % vlen == 0 && ((uintptr_t)wt & 15) == 0) ? 1 : 0;
+    if (dtype == CONVIMG_BF16)
+        hipLaunchKernelGGL(flip_transpose<unsigned short>, grid, dim3(kFlipThreads), 0, stream,
+                           (const unsigned short *)w, (unsigned short *)wt, OC, KH * KW, IC,
+                           vec_in, vec_out);
+    else
+        hipLaunchKernelGGL(flip_transpose<unsigned>, grid, dim3(kFlipThreads), 0, stream,
+                           (const unsigned *)w, (unsigned *)wt, OC, KH * KW, IC, vec_in, vec_out);
+    if (hipGetLastError() != hipSuccess)
+        return CONVIMG_ERR_LAUNCH;
+    return CONVIMG_OK;
+}
+
+int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, int OC, int KH, int KW,
+                    int stride, int pad, int dilation, int dtype, void *wt, float *dx, hipStream_t stream)
+{
+    if (!dy || !w || !wt || !dx)
+        return CONVIMG_ERR_NULL;
+    // the forward problem this maps to: first every check conv2d_fwd makes
+    // on the shapes (the output extent OH x OW of dy included)
+    convimg_plan fwd;
+    int rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, true, nullptr, &fwd);
+    if (rc != CONVIMG_OK)
+        return rc;
+    if (stride != 1 || KH != KW || pad > dilation * (KH - 1))
+        return CONVIMG_ERR_UNSUPPORTED;
+    const int pt = dilation * (KH - 1) - pad;
+    convimg_plan pl;
+    rc = make_plan(N, fwd.OH, fwd.OW, OC, IC, KH, KW, 1, pt, dilation, dtype, 1, true, nullptr, &pl);
+    if (rc != CONVIMG_OK)
+        return rc;
+    if (pl.OH != H || pl.OW != W)      // (cannot happen for stride 1)
+        return CONVIMG_ERR_SHAPE;
+    const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
+    const size_t nw = (size_t)OC * KH * KW * IC * esz;
+    const size_t ny = (size_t)N * fwd.OH * fwd.OW * OC * esz;
+    const size_t nx = (size_t)N * H * W * IC * 4;
+    if (overlaps(wt, nw, dy, ny) || overlaps(dx, nx, w, nw) || overlaps(dx, nx, dy, ny)
+        || overlaps(dx, nx, wt, nw))
+        return CONVIMG_ERR_ALIAS;
+    rc = conv2d_bwd_data_weights(w, OC, KH, KW, IC, dtype, wt, stream);
+    if (rc != CONVIMG_OK)
+        return rc;
+    return conv2d_fwd(dy, wt, nullptr, N, fwd.OH, fwd.OW, OC, IC, KH, KW, 1, pt, dilation, dtype, dx, stream);
+}
+
 const char *conv2d_strerror(int status)
 {
     switch (status) {
@@ -1078,6 +1204,7 @@ const char *conv2d_strerror(int status)
     case CONVIMG_ERR_LAUNCH: return "kernel launch failed";
     case CONVIMG_ERR_DEVICE: return "no usable HIP device";
     case CONVIMG_ERR_TIMEOUT: return "a split-K workgroup timed out waiting for its turn";
+    case CONVIMG_ERR_UNSUPPORTED: return "data backward needs stride 1, KH == KW and pad <= dilation*(KH-1)";
     default: return "unknown status";
     }
 }

@@ -147,3 +147,23 @@ def make_inputs(wl: Workload, seed: int = 0, round_bf16: bool = True,
     else:
         x_store, w_store = x, w
     return Inputs(wl, x, w, b, x_store, w_store, round_bf16)
+
+
+def make_grad_inputs(wl: Workload, OH: int, OW: int, seed: int = 0,
+                     dtype: int | None = None) -> Inputs:
+    """Draw the data-backward inputs of a workload: dy [N,OH,OW,OC] from the
+    workload's x distribution, then w [OC,KH,KW,IC] as in ``make_inputs``.
+
+    OH, OW: the forward output extent, given by the caller (this module
+    computes nothing of the convolution).  The result's x32/x_store hold dy;
+    bias is drawn but unused.  Values are bf16-rounded.
+    """
+    dtype = wl.dtype if dtype is None else dtype
+    rng = np.random.default_rng(seed)
+    dy = round_to_bf16_bits(_draw(rng, wl.x_dist, (wl.N, OH, OW, wl.OC)))
+    w = round_to_bf16_bits(_draw(rng, wl.w_dist, (wl.OC, wl.KH, wl.KW, wl.IC)))
+    b = _draw(rng, wl.bias_dist, (wl.OC,))
+    dy32, w32 = bf16_bits_to_f32(dy), bf16_bits_to_f32(w)
+    if dtype == BF16:
+        return Inputs(wl, dy32, w32, b, dy, w, True)
+    return Inputs(wl, dy32, w32, b, dy32, w32, True)

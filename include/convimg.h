@@ -46,6 +46,7 @@ extern "C" {
 #define CONVIMG_ERR_LAUNCH  7  /* the HIP runtime refused the launch */
 #define CONVIMG_ERR_DEVICE  8  /* no usable HIP device, or a device query failed */
 #define CONVIMG_ERR_TIMEOUT 9  /* a split-K wait gave up (reported by conv2d_fwd_status) */
+#define CONVIMG_ERR_UNSUPPORTED 10 /* conv2d_bwd_data: stride != 1, KH != KW or pad > dilation*(KH-1) */
 
 /* Loader variants used by the plan. */
 #define CONVIMG_LOADER_TAP    0  /* IC % 64 == 0: one 64-channel slice of one tap per K tile, 16-byte loads */
@@ -160,6 +161,54 @@ int conv2d_fwd_tile_kind(int tile_id);
  * workgroup gave up waiting for its turn since the last call of this
  * function (the flag is then cleared).  Synchronises the stream. */
 int conv2d_fwd_status(hipStream_t stream);
+
+/* Data backward: the gradient of conv2d_fwd's output with respect to its
+ * input x (burn-cubecl "kernel/conv/base.rs" listing, conv_data_backward,
+ * whose implicit-GEMM route serves groups = 1 and stride 1):
+ *
+ *   dx[n][ih][iw][ic] = sum_{kh,kw,oc} dY(n, ih + pad - kh*dilation,
+ *                                         iw + pad - kw*dilation, oc)
+ *                       * w[oc][kh][kw][ic]
+ *
+ * with dY = dy inside [0,OH) x [0,OW) and 0 outside.  For stride 1 this is
+ * the forward convolution of dy with the weights flipped in both spatial
+ * axes and transposed OC <-> IC, padding dilation*(KH-1) - pad: the call
+ * writes those weights to `wt` (conv2d_bwd_data_weights), then runs
+ * conv2d_fwd(dy, wt, NULL, N, OH, OW, OC, IC, KH, KW, 1,
+ * dilation*(KH-1) - pad, dilation, dtype, dx, stream) -- same plans, same
+ * kernels, no bias.  A caller whose weights do not change between calls
+ * may transform them once and make that conv2d_fwd call itself.
+ *
+ *   dy    device, N x OH x OW x OC (NHWC) in `dtype`, OH/OW the forward
+ *         output extents of H/W (the formula under conv2d_fwd)
+ *   w     device, OC x KH x KW x IC (OHWI) in `dtype`: the forward weights
+ *   wt    device, OC*KH*KW*IC elements of `dtype`, caller-owned workspace;
+ *         receives IC x KH x KW x OC, the flipped and transposed weights
+ *   dx    device, fp32 N x H x W x IC (NHWC), fully overwritten
+ *   N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype: the forward
+ *         problem's arguments
+ *
+ * Errors: CONVIMG_ERR_UNSUPPORTED unless stride == 1, KH == KW and
+ * pad <= dilation*(KH-1); the argument errors of conv2d_fwd for the forward
+ * problem and for the one it maps to; CONVIMG_ERR_ALIAS if wt or dx overlaps
+ * another buffer.  These are returned before any work is queued.  After the
+ * transform is queued, CONVIMG_ERR_LAUNCH / CONVIMG_ERR_ALLOC may still come
+ * back (wt then holds the transform).  Asynchronous on `stream`. */
+int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, int OC, int KH, int KW,
+                    int stride, int pad, int dilation, int dtype, void *wt, float *dx, hipStream_t stream);
+
+/* The weight transform of conv2d_bwd_data alone (same passage):
+ *
+ *   wt[ic][KH-1-kh][KW-1-kw][oc] = w[oc][kh][kw][ic]
+ *
+ * for any KH, KW.  w: device, OC x KH x KW x IC in `dtype`; wt: device,
+ * the same number of elements, caller-owned, must not overlap w.  Errors
+ * (returned before any work is queued): CONVIMG_ERR_NULL, _SHAPE (a size
+ * <= 0), _DTYPE, _RANGE (2^31 elements or more, or more than 65535
+ * 64-channel tiles of OC or kernel taps), _ALIAS; _LAUNCH if the launch
+ * fails.  Asynchronous on `stream`. */
+int conv2d_bwd_data_weights(const void *w, int OC, int KH, int KW, int IC, int dtype, void *wt,
+                            hipStream_t stream);
 
 /* Free every library-owned buffer (synchronising each device that has
  * one).  Later calls allocate again as needed. */

@@ -46,7 +46,7 @@ def test_out_dim_table(lib):
 
 
 def test_strerror(lib):
-    for code in range(10):
+    for code in range(11):
         msg = abi.conv2d_strerror(code)
         assert msg and msg != "unknown status"
     assert abi.conv2d_strerror(1234) == "unknown status"
@@ -274,3 +274,62 @@ def test_argument_errors_before_any_device_work(lib, kw, code):
 
 def test_plan_null(lib):
     assert lib.conv2d_fwd_plan(1, 8, 8, 16, 16, 3, 3, 1, 1, 1, 0, 256, None) == abi.CONVIMG_ERR_NULL
+
+
+def call_bwd(**kw):
+    a = dict(BASE, dy=0x1000000, w=0x2000000, wt=0x4000000, dx=0x3000000, stream=None)
+    a.update(kw)
+    return abi.conv2d_bwd_data(a["dy"], a["w"], a["N"], a["H"], a["W"], a["IC"], a["OC"],
+                               a["KH"], a["KW"], a["stride"], a["pad"], a["dilation"], a["dtype"],
+                               a["wt"], a["dx"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dy=None), abi.CONVIMG_ERR_NULL),
+    (dict(w=None), abi.CONVIMG_ERR_NULL),
+    (dict(wt=None), abi.CONVIMG_ERR_NULL),
+    (dict(dx=None), abi.CONVIMG_ERR_NULL),
+    (dict(N=0), abi.CONVIMG_ERR_SHAPE),
+    (dict(H=2, pad=0), abi.CONVIMG_ERR_SHAPE),
+    (dict(dtype=2), abi.CONVIMG_ERR_DTYPE),
+    (dict(stride=2), abi.CONVIMG_ERR_UNSUPPORTED),
+    (dict(KW=5, pad=2), abi.CONVIMG_ERR_UNSUPPORTED),
+    (dict(pad=3), abi.CONVIMG_ERR_UNSUPPORTED),                # pad > dilation*(KH-1)
+    (dict(pad=5, dilation=2), abi.CONVIMG_ERR_UNSUPPORTED),
+    (dict(N=1 << 12, H=1 << 10, W=1 << 10), abi.CONVIMG_ERR_RANGE),
+    # 90000 taps: more transform workgroups along one grid axis than HIP allows
+    (dict(N=1, H=300, W=300, IC=1, OC=1, KH=300, KW=300, pad=0), abi.CONVIMG_ERR_RANGE),
+    (dict(dx=0x1000000 + 64), abi.CONVIMG_ERR_ALIAS),          # dx inside dy
+    (dict(wt=0x2000000 + 2), abi.CONVIMG_ERR_ALIAS),           # wt overlaps w
+    (dict(wt=0x3000000 + 32), abi.CONVIMG_ERR_ALIAS),          # wt inside dx
+])
+def test_bwd_data_errors_before_any_device_work(lib, kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_data_accepts_the_edge_pads(lib):
+    """pad = dilation*(KH-1) maps to pad 0 and pad 0 to full padding: both are
+    planned (checked through the forward plans they map to)."""
+    for pad, dil in ((2, 1), (0, 1), (4, 2), (0, 3)):
+        rc, fwd = abi.conv2d_fwd_plan(2, 9, 9, 24, 40, 3, 3, 1, pad, dil, 0, 256)
+        assert rc == abi.CONVIMG_OK
+        rc, p = abi.conv2d_fwd_plan(2, fwd["OH"], fwd["OW"], 40, 24, 3, 3, 1,
+                                    dil * 2 - pad, dil, 0, 256)
+        assert rc == abi.CONVIMG_OK and (p["OH"], p["OW"]) == (9, 9)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), abi.CONVIMG_ERR_NULL),
+    (dict(wt=None), abi.CONVIMG_ERR_NULL),
+    (dict(OC=0), abi.CONVIMG_ERR_SHAPE),
+    (dict(KW=-1), abi.CONVIMG_ERR_SHAPE),
+    (dict(dtype=5), abi.CONVIMG_ERR_DTYPE),
+    (dict(OC=1 << 16, IC=1 << 16), abi.CONVIMG_ERR_RANGE),
+    (dict(OC=1, IC=1, KH=300, KW=300), abi.CONVIMG_ERR_RANGE),
+    (dict(wt=0x2000000 + 16 * 9 * 16 * 2 - 2), abi.CONVIMG_ERR_ALIAS),   # last element of w
+])
+def test_bwd_data_weights_errors_before_any_device_work(lib, kw, code):
+    a = dict(w=0x2000000, OC=16, KH=3, KW=3, IC=16, dtype=0, wt=0x4000000, stream=None)
+    a.update(kw)
+    assert abi.conv2d_bwd_data_weights(a["w"], a["OC"], a["KH"], a["KW"], a["IC"], a["dtype"],
+                                       a["wt"], a["stream"]) == code

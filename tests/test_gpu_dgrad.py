@@ -1,0 +1,148 @@
+"""GPU parity of the data backward (conv2d_bwd_data, stride 1) against the
+fp64 oracle's definition of the input gradient, element by element with the
+forward's bound |err| <= 1e-3*S + 1e-5 (S: the oracle's sum of |dy*w| over
+each element's terms).
+
+The flipped, transposed weights the call leaves in its workspace are checked
+bit-exactly against a numpy index permutation of w (a pure data movement).
+dx is pre-filled with NaN (an element never written fails) and followed by a
+sentinel guard (a write past the end fails).  Covered: the ResNet-style 3x3
+layer and the deep 14x14 layer at full size, a dilated layer, IC != OC with
+channel tails, 1x1, 5x5, edge paddings (0 and dilation*(K-1)), IC = 3 with a
+7x7 window, fp32 storage, and the torch wrapper; the weight transform alone
+on non-square windows, channel tails and misaligned buffers (element path).
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_implicit_gemm_fwd_amd as cig
+from convolution_implicit_gemm_fwd_amd import abi
+from convolution_implicit_gemm_fwd_amd.workloads import BF16, FP32, WORKLOADS, make_grad_inputs
+
+import oracle
+from gpu_harness import GUARD, SENTINEL, check, log, need_gpu, shape
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    abi.conv2d_fwd_force(-1, -1, -1)
+
+
+def upload(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bwd_parity(wl, dtype=None, seed=0):
+    dtype = wl.dtype if dtype is None else dtype
+    OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, 1, wl.pad, wl.dilation)
+    OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, 1, wl.pad, wl.dilation)
+    assert OH > 0 and OW > 0
+    inp = make_grad_inputs(wl, OH, OW, seed=seed, dtype=dtype)
+    dy, w = upload(inp.x_store), upload(inp.w_store)
+    wt = torch.empty_like(w.reshape(-1))
+    n_dx = wl.N * wl.H * wl.W * wl.IC
+    dx = torch.full((n_dx + GUARD,), float("nan"), dtype=torch.float32, device="cuda")
+    dx[n_dx:] = SENTINEL
+    log("dgrad %s dtype=%d" % (wl, dtype))
+    rc = abi.conv2d_bwd_data(dy.data_ptr(), w.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH,
+                             wl.KW, 1, wl.pad, wl.dilation, dtype, wt.data_ptr(), dx.data_ptr(),
+                             torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, abi.conv2d_strerror(rc)
+    torch.cuda.synchronize()
+    host = dx.cpu().numpy()
+    assert (host[n_dx:] == SENTINEL).all(), "write past the end of dx"
+    y = host[:n_dx].reshape(wl.N, wl.H, wl.W, wl.IC)
+    # the workspace: w[oc][kh][kw][ic] -> wt[ic][KH-1-kh][KW-1-kw][oc], bit for bit
+    want = np.ascontiguousarray(inp.w_store[:, ::-1, ::-1, :].transpose(3, 1, 2, 0))
+    got = wt.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == BF16 \
+        else wt.cpu().numpy()
+    assert np.array_equal(got.reshape(want.shape), want), "flipped weights differ"
+    yref, S = oracle.conv2d_bwd_data(inp.x32, inp.w32, wl.H, wl.W, 1, wl.pad, wl.dilation)
+    ratio = check(y, yref, S, "dgrad %s" % (wl,))
+    log("dgrad %s worst err/tol %.3g" % (wl.name, ratio))
+    return y, yref
+
+
+FULL = [WORKLOADS["resnet3x3"], WORKLOADS["largek"].scaled(N=4, name="largek N=4"),
+        WORKLOADS["dilated"].scaled(N=1, H=64, W=64, name="dilated 64x64")]
+
+SMALL = [
+    shape(2, 13, 11, 24, 40, 3, 3, 1, 1, 1, name="IC 24 OC 40 tails"),
+    shape(2, 9, 17, 40, 24, 3, 3, 1, 1, 1, name="IC 40 OC 24 tails"),
+    shape(3, 10, 10, 64, 96, 1, 1, 1, 0, 1, name="1x1"),
+    shape(2, 12, 12, 32, 48, 5, 5, 1, 2, 1, name="5x5 pad 2"),
+    shape(2, 12, 12, 32, 48, 5, 5, 1, 0, 1, name="5x5 pad 0 (full pad after mapping)"),
+    shape(2, 11, 11, 64, 64, 3, 3, 1, 2, 1, name="pad = K-1 (no pad after mapping)"),
+    shape(1, 20, 20, 64, 64, 3, 3, 1, 0, 2, name="dilation 2 pad 0"),
+    shape(1, 21, 19, 16, 72, 3, 3, 1, 6, 3, name="dilation 3 full pad"),
+    shape(2, 30, 30, 3, 64, 7, 7, 1, 3, 1, name="IC 3 7x7"),
+    shape(1, 8, 8, 1, 1, 3, 3, 1, 1, 1, name="IC 1 OC 1"),
+    shape(1, 3, 3, 8, 8, 3, 3, 1, 0, 1, name="single output pixel"),
+]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
+def test_dgrad_full_size(wl):
+    bwd_parity(wl)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_dgrad_shapes(wl):
+    bwd_parity(wl)
+
+
+@pytest.mark.parametrize("wl", SMALL[:3] + SMALL[6:7], ids=lambda w: w.name)
+def test_dgrad_fp32_storage(wl):
+    bwd_parity(wl, dtype=FP32)
+
+
+def test_dgrad_torch_wrapper():
+    wl = shape(2, 14, 14, 48, 80, 3, 3, 1, 1, 1)
+    inp = make_grad_inputs(wl, 14, 14, seed=3)
+    dy, w = upload(inp.x_store), upload(inp.w_store)
+    dx = cig.conv2d_bwd_data_nhwc(dy, w, 14, 14, stride=1, pad=1)
+    torch.cuda.synchronize()
+    yref, S = oracle.conv2d_bwd_data(inp.x32, inp.w32, 14, 14, 1, 1, 1)
+    check(dx.cpu().numpy(), yref, S, "wrapper")
+    with pytest.raises(RuntimeError, match="stride 1"):
+        cig.conv2d_bwd_data_nhwc(upload(inp.x_store[:, ::2, ::2].copy()), w, 14, 14, stride=2,
+                                 pad=1)
+
+
+@pytest.mark.parametrize("OC,KH,KW,IC,dtype,misalign", [
+    (512, 3, 3, 512, BF16, False),      # 16-byte loads and stores
+    (40, 3, 5, 24, BF16, False),        # non-square window
+    (70, 2, 3, 45, BF16, False),        # channel counts off the vector: element path
+    (64, 3, 3, 64, BF16, True),         # misaligned w and wt: element path
+    (36, 5, 1, 20, FP32, False),
+    (33, 3, 3, 7, FP32, True),
+])
+def test_weight_transform_alone(OC, KH, KW, IC, dtype, misalign):
+    rng = np.random.default_rng(7)
+    n = OC * KH * KW * IC
+    if dtype == BF16:
+        host = rng.integers(0, 1 << 16, size=n, dtype=np.uint16)   # any bit pattern moves
+        dev_t, pad_val = torch.int16, 0x7F7F
+    else:
+        host = rng.standard_normal(n).astype(np.float32)
+        dev_t, pad_val = torch.float32, 1234.5
+    off = 1 if misalign else 0
+    src = torch.full((n + off,), pad_val, dtype=dev_t, device="cuda")
+    src[off:] = torch.from_numpy(host.view(np.int16) if dtype == BF16 else host).cuda()
+    dst = torch.full((n + off + GUARD,), pad_val, dtype=dev_t, device="cuda")
+    rc = abi.conv2d_bwd_data_weights(src[off:].data_ptr(), OC, KH, KW, IC, dtype,
+                                     dst[off:].data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, abi.conv2d_strerror(rc)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    got = got.view(np.uint16) if dtype == BF16 else got
+    pad = np.uint16(pad_val) if dtype == BF16 else np.float32(pad_val)
+    assert (got[:off] == pad).all() and (got[off + n:] == pad).all(), "write outside wt"
+    want = host.reshape(OC, KH, KW, IC)[:, ::-1, ::-1, :].transpose(3, 1, 2, 0)
+    assert np.array_equal(got[off:off + n].reshape(IC, KH, KW, OC), want)
