@@ -1,4 +1,5 @@
-"""CPU oracle for 2-D convolution forward (NHWC input, OHWI weight).
+"""CPU oracle for 2-D convolution forward (NHWC input, OHWI weight) and its
+two backward passes (gradients with respect to the input and the weights).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package.  The HIP
@@ -70,6 +71,8 @@ class Oracle:
         lib.oracle_conv2d_fwd_pixels.restype = ip
         lib.oracle_conv2d_bwd_data.argtypes = [dp, dp] + [ip] * 10 + [dp, dp]
         lib.oracle_conv2d_bwd_data.restype = ip
+        lib.oracle_conv2d_bwd_weight.argtypes = [dp, dp] + [ip] * 10 + [dp, dp]
+        lib.oracle_conv2d_bwd_weight.restype = ip
         lib.oracle_set_threads.argtypes = [ip]
         lib.oracle_set_threads.restype = ip
         self.lib = lib
@@ -154,6 +157,29 @@ class Oracle:
             raise ValueError("oracle rejected the shape")
         return dx, S
 
+    def conv2d_bwd_weight(self, x, dy, KH, KW, stride=1, pad=0, dilation=1):
+        """Gradient of the forward convolution with respect to its weights.
+
+        x: [N][H][W][IC], dy: [N][OH][OW][OC] (OH, OW the forward extents).
+        Returns (dw, S), float64 [OC][KH][KW][IC]; S = sum |dy*x| over the
+        terms of each element.
+        """
+        x = _as_f64(x, 4, "x")
+        dy = _as_f64(dy, 4, "dy")
+        N, H, W, IC = x.shape
+        N2, OH, OW, OC = dy.shape
+        if N2 != N:
+            raise ValueError("batch mismatch: x has %d, dy has %d" % (N, N2))
+        if (self.out_dim(H, KH, stride, pad, dilation), self.out_dim(W, KW, stride, pad, dilation)) != (OH, OW):
+            raise ValueError("dy extent does not match the forward output of H, W")
+        dw = np.empty((OC, KH, KW, IC), np.float64)
+        S = np.empty((OC, KH, KW, IC), np.float64)
+        rc = self.lib.oracle_conv2d_bwd_weight(_dptr(x), _dptr(dy), N, H, W, IC, OC, KH, KW,
+                                               stride, pad, dilation, _dptr(dw), _dptr(S))
+        if rc != 0:
+            raise ValueError("oracle rejected the shape")
+        return dw, S
+
 
 _default = None
 
@@ -186,3 +212,7 @@ def conv2d_fwd_pixels(x, w, bias, stride, pad, dilation, pixels):
 
 def conv2d_bwd_data(dy, w, H, W, stride=1, pad=0, dilation=1):
     return get().conv2d_bwd_data(dy, w, H, W, stride, pad, dilation)
+
+
+def conv2d_bwd_weight(x, dy, KH, KW, stride=1, pad=0, dilation=1):
+    return get().conv2d_bwd_weight(x, dy, KH, KW, stride, pad, dilation)

@@ -1,6 +1,6 @@
 /*
  * conv_ref.c -- CPU oracle for 2-D convolution forward, NHWC / OHWI / NHWC,
- * and for its data-backward pass.
+ * and for its data-backward and weight-backward passes.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The HIP library and
@@ -207,6 +207,61 @@ int oracle_conv2d_bwd_data(const double *dy, const double *w,
                         }
                     }
                 }
+            }
+    return 0;
+}
+
+/* Gradient of the forward convolution with respect to its weights (the
+ * weight-backward pass of the burn-cubecl "kernel/conv/base.rs" listing,
+ * conv_weight_backward: it takes the input and the output gradient and
+ * returns a tensor of the weights' shape).  Since y is linear in w,
+ *
+ *   dw[oc][kh][kw][ic] = sum_{n<N} sum_{oh<OH} sum_{ow<OW}
+ *                          dy[n][oh][ow][oc] * X(n, oh*s - p + kh*d, ow*s - p + kw*d, ic)
+ *   S[oc][kh][kw][ic]  = the same sum of |dy * X|
+ *
+ * with X as for the forward (0 in the padding).  x is N x H x W x IC, dy is
+ * N x OH x OW x OC with OH, OW the forward output extents; dw and S are
+ * OC x KH x KW x IC.  The terms are taken in the order n, oh, ow; any
+ * stride, padding and dilation.  Returns 0, or -1 on bad shapes. */
+int oracle_conv2d_bwd_weight(const double *x, const double *dy,
+                             int N, int H, int W, int IC, int OC, int KH, int KW,
+                             int s, int p, int d, double *dw, double *S)
+{
+    int OH, OW;
+    if (check_args(N, H, W, IC, OC, KH, KW, s, p, d, &OH, &OW))
+        return -1;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int oc = 0; oc < OC; ++oc)
+        for (int kh = 0; kh < KH; ++kh)
+            for (int kw = 0; kw < KW; ++kw) {
+                const size_t wrow = (size_t)oc * KH * KW + (size_t)kh * KW + kw;
+                double *g = dw + wrow * IC;
+                double *m = S ? S + wrow * IC : NULL;
+                for (int ic = 0; ic < IC; ++ic) {
+                    g[ic] = 0.0;
+                    if (m)
+                        m[ic] = 0.0;
+                }
+                for (int n = 0; n < N; ++n)
+                    for (int oh = 0; oh < OH; ++oh) {
+                        int jh = oh * s - p + kh * d;     /* input row of this tap */
+                        if (jh < 0 || jh >= H)
+                            continue;
+                        for (int ow = 0; ow < OW; ++ow) {
+                            int jw = ow * s - p + kw * d; /* input column */
+                            if (jw < 0 || jw >= W)
+                                continue;
+                            double gy = dy[(((size_t)n * OH + oh) * OW + ow) * OC + oc];
+                            const double *xr = x + (((size_t)n * H + jh) * W + jw) * IC;
+                            for (int ic = 0; ic < IC; ++ic) {
+                                double t = gy * xr[ic];
+                                g[ic] += t;
+                                if (m)
+                                    m[ic] += fabs(t);
+                            }
+                        }
+                    }
             }
     return 0;
 }

@@ -316,6 +316,78 @@ def pin_bwd_magnitude(o):
     assert_close(S, da, 1e-12, 1e-12, "S equals the gradient of magnitudes")
 
 
+def pin_wgt_adjoint(o, cases=30, seed=23):
+    """G1: the weight-backward pass is the adjoint of the forward map w -> y - b:
+    sum(conv(x, w) * dy) == sum(w * dw(x, dy)) for every x, w, dy.  Small
+    integers make both sides exact in fp64; random strides, paddings (also
+    past the window), dilations, non-square kernels."""
+    rng = np.random.default_rng(seed)
+    done = 0
+    while done < cases:
+        N, H, W = int(rng.integers(1, 3)), int(rng.integers(1, 10)), int(rng.integers(1, 10))
+        IC, OC = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        KH, KW = int(rng.choice([1, 2, 3, 5])), int(rng.choice([1, 2, 3]))
+        s, p, d = int(rng.integers(1, 4)), int(rng.integers(0, 4)), int(rng.integers(1, 3))
+        OH, OW = o.out_dim(H, KH, s, p, d), o.out_dim(W, KW, s, p, d)
+        if OH <= 0 or OW <= 0:
+            continue
+        x = int_data(rng, (N, H, W, IC))
+        w = int_data(rng, (OC, KH, KW, IC))
+        dy = int_data(rng, (N, OH, OW, OC))
+        y, _ = o.conv2d_fwd(x, w, None, s, p, d)
+        dw, S = o.conv2d_bwd_weight(x, dy, KH, KW, s, p, d)
+        assert dw.shape == w.shape
+        lhs, rhs = float(np.sum(y * dy)), float(np.sum(w * dw))
+        assert lhs == rhs, "adjoint identity fails: %r vs %r at %s" % (lhs, rhs, (N, H, W, IC, OC, KH, KW, s, p, d))
+        done += 1
+
+
+def pin_wgt_torch(o):
+    """G2: torch.nn.grad.conv2d_weight in fp64 on NCHW views (an independent
+    library implementation of the same gradient)."""
+    import torch
+    rng = np.random.default_rng(24)
+    for (N, H, W, IC, OC, KH, KW, s, p, d) in [(2, 11, 9, 6, 5, 3, 3, 1, 1, 1),
+                                                (1, 16, 16, 3, 8, 7, 7, 2, 3, 1),
+                                                (2, 13, 12, 8, 4, 3, 3, 1, 2, 2),
+                                                (1, 10, 7, 5, 6, 2, 4, 3, 2, 2)]:
+        OH, OW = o.out_dim(H, KH, s, p, d), o.out_dim(W, KW, s, p, d)
+        x = rng.standard_normal((N, H, W, IC))
+        dy = rng.standard_normal((N, OH, OW, OC))
+        dw, _ = o.conv2d_bwd_weight(x, dy, KH, KW, s, p, d)
+        t = torch.nn.grad.conv2d_weight(torch.from_numpy(x).permute(0, 3, 1, 2), (OC, IC, KH, KW),
+                                        torch.from_numpy(dy).permute(0, 3, 1, 2),
+                                        stride=s, padding=p, dilation=d)
+        assert_close(dw, t.permute(0, 2, 3, 1).numpy(), 1e-12, 1e-12, "torch conv2d_weight")
+
+
+def pin_wgt_matmul_1x1(o):
+    """G3: a 1x1 window without padding makes the weight gradient a plain
+    product over pixels, dw[oc][0][0][:] = dy^T x (x subsampled by the
+    stride), checked against numpy's matmul in fp64."""
+    rng = np.random.default_rng(25)
+    for s in (1, 2, 3):
+        x = rng.standard_normal((2, 9, 8, 7))
+        OH, OW = o.out_dim(9, 1, s, 0, 1), o.out_dim(8, 1, s, 0, 1)
+        dy = rng.standard_normal((2, OH, OW, 5))
+        dw, _ = o.conv2d_bwd_weight(x, dy, 1, 1, s, 0, 1)
+        xs = x[:, ::s, ::s, :][:, :OH, :OW, :].reshape(-1, 7)
+        want = dy.reshape(-1, 5).T @ xs
+        assert_close(dw[:, 0, 0, :], want, 1e-12, 1e-12, "1x1 weight gradient, stride %d" % s)
+
+
+def pin_wgt_magnitude(o):
+    """G4: S >= |dw| everywhere, and S equals the weight gradient of |x| and |dy|."""
+    rng = np.random.default_rng(26)
+    x = rng.standard_normal((2, 8, 8, 4))
+    dy = rng.standard_normal((2, 8, 8, 5))
+    dw, S = o.conv2d_bwd_weight(x, dy, 3, 3, 1, 1, 1)
+    assert (S >= np.abs(dw) - 1e-12).all(), "triangle inequality"
+    da, _ = o.conv2d_bwd_weight(np.abs(x), np.abs(dy), 3, 3, 1, 1, 1)
+    assert_close(S, da, 1e-12, 1e-12, "S equals the gradient of magnitudes")
+
+
 ALL_PINS = [pin_out_dims, pin_matmul_1x1, pin_centered_delta, pin_offcenter_delta,
             pin_all_ones, pin_bruteforce, pin_linearity, pin_torch, pin_magnitude, pin_pixels,
-            pin_bwd_adjoint, pin_bwd_torch, pin_bwd_delta, pin_bwd_magnitude]
+            pin_bwd_adjoint, pin_bwd_torch, pin_bwd_delta, pin_bwd_magnitude,
+            pin_wgt_adjoint, pin_wgt_torch, pin_wgt_matmul_1x1, pin_wgt_magnitude]

@@ -75,6 +75,19 @@ MUTANTS = [
      "int tw = iw + p - kw * d;", "int tw = iw + p - kw;"),
     ("data backward: magnitude without abs",
      "a[ic] += fabs(t);", "a[ic] += t;"),
+    ("weight backward: padding sign flipped",
+     "int jh = oh * s - p + kh * d;", "int jh = oh * s + p + kh * d;"),
+    ("weight backward: stride dropped on columns",
+     "int jw = ow * s - p + kw * d;", "int jw = ow - p + kw * d;"),
+    ("weight backward: row dilation dropped",
+     "int jh = oh * s - p + kh * d;", "int jh = oh * s - p + kh;"),
+    ("weight backward: kernel flipped",
+     "const size_t wrow = (size_t)oc * KH * KW + (size_t)kh * KW + kw;",
+     "const size_t wrow = (size_t)oc * KH * KW + (size_t)(KH - 1 - kh) * KW + (KW - 1 - kw);"),
+    ("weight backward: input channels reversed",
+     "double t = gy * xr[ic];", "double t = gy * xr[IC - 1 - ic];"),
+    ("weight backward: magnitude without abs",
+     "m[ic] += fabs(t);", "m[ic] += t;"),
 ]
 
 
