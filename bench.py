@@ -7,6 +7,11 @@ fused bias, fp32 store) over the workload's batch, with every input already
 resident in device memory.  The default workload is the ResNet-style 3x3
 layer (N=16, 56x56, 64 -> 64 channels).  Prints ONE JSON line.
 
+--op wgrad times conv2d_bwd_weight (the gradient with respect to the
+weights): a step is the implicit-GEMM kernel plus, when the pixels are split
+into ranges, the ordered sum of the ranges; the roofline object prices the
+whole call.
+
 --op dgrad times conv2d_bwd_data instead (the gradient with respect to the
 input, stride-1 workloads only): a step is the weight flip-transpose plus
 the forward implicit GEMM it maps to; the roofline object then prices that
@@ -31,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "conv2d fwd TFLOP/s (2·M·N·K/s) + % of bf16 MFMA peak, 1×MI355X"
+METRIC_WGRAD = "conv2d bwd-weight TFLOP/s (2·N·OH·OW·OC·KH·KW·IC/s) + % of bf16 MFMA peak, 1×MI355X"
 METRIC_DGRAD = "conv2d bwd-data TFLOP/s (2·N·H·W·IC·OC·KH·KW/s) + % of bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_FP32_MFMA_TFLOPS = 157.3
@@ -60,6 +66,7 @@ TRAFFIC = {
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
 KIND_SOURCES = {
+    -2: ("igemm_wgrad.hpp",),                    # weight backward
     -1: ("igemm_regs.hpp",),                     # fp32 storage
     0: ("igemm_regs.hpp",),                      # CONVIMG_KIND_REGS
     1: ("igemm_pipe.hpp",),                      # CONVIMG_KIND_PIPE
@@ -88,7 +95,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="resnet3x3")
-    ap.add_argument("--op", choices=("fwd", "dgrad"), default="fwd")
+    ap.add_argument("--op", choices=("fwd", "dgrad", "wgrad"), default="fwd")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline sample (0 disables it)")
     ap.add_argument("--force", default=None,
@@ -119,6 +126,8 @@ def cpu_baseline(inp, wl, flops, seconds, op="fwd"):
     while True:
         if op == "fwd":
             o.conv2d_fwd(inp.x32, inp.w32, inp.bias, wl.stride, wl.pad, wl.dilation)
+        elif op == "wgrad":
+            o.conv2d_bwd_weight(inp.x32, inp.w32, wl.KH, wl.KW, wl.stride, wl.pad, wl.dilation)
         else:
             o.conv2d_bwd_data(inp.x32, inp.w32, wl.H, wl.W, wl.stride, wl.pad, wl.dilation)
         runs += 1
@@ -176,12 +185,13 @@ def main():
 
     from convolution_implicit_gemm_fwd_amd import abi
     from convolution_implicit_gemm_fwd_amd.workloads import (BF16, WORKLOADS, make_grad_inputs,
-                                                             make_inputs)
+                                                             make_inputs, make_wgrad_inputs)
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     lib = abi.load()                # fails loudly if the HIP library is not built
     wl = WORKLOADS[args.workload]
     dgrad = args.op == "dgrad"
+    wgrad = args.op == "wgrad"
     if dgrad and wl.stride != 1:
         print("--op dgrad needs a stride-1 workload (%s has stride %d)" % (wl.name, wl.stride),
               file=sys.stderr)
@@ -189,7 +199,8 @@ def main():
     OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
     OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
     M, K = wl.N * OH * OW, wl.IC * wl.KH * wl.KW
-    inp = make_grad_inputs(wl, OH, OW, seed=0) if dgrad else make_inputs(wl, seed=0)
+    inp = (make_grad_inputs(wl, OH, OW, seed=0) if dgrad
+           else make_wgrad_inputs(wl, OH, OW, seed=0) if wgrad else make_inputs(wl, seed=0))
 
     def up(a):
         t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
@@ -201,7 +212,19 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     esz = 2 if wl.dtype == BF16 else 4
-    if not dgrad:
+    if wgrad:
+        # x holds x, w holds dy [N,OH,OW,OC]
+        out = torch.empty((wl.OC, wl.KH, wl.KW, wl.IC), dtype=torch.float32, device="cuda")
+        rc, need = abi.conv2d_bwd_weight_workspace(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
+                                                   wl.stride, wl.pad, wl.dilation, wl.dtype)
+        assert rc == 0, abi.conv2d_strerror(rc)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        gemm = (wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride, wl.pad, wl.dilation)
+        call_args = ((x.data_ptr(), w.data_ptr()) + gemm
+                     + (wl.dtype, out.data_ptr(), ws.data_ptr(), need, sptr))
+        fn = lib.conv2d_bwd_weight
+        alg_bytes = (wl.N * wl.H * wl.W * wl.IC + M * wl.OC) * esz + wl.OC * K * 4
+    elif not dgrad:
         out = torch.empty((wl.N, OH, OW, wl.OC), dtype=torch.float32, device="cuda")
         gemm = (wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride, wl.pad, wl.dilation)
         call_args = ((x.data_ptr(), w.data_ptr(), b.data_ptr()) + gemm
@@ -221,6 +244,10 @@ def main():
         alg_bytes = (M * wl.OC + wl.OC * K) * esz + wl.N * wl.H * wl.W * wl.IC * 4
     rc, plan = abi.conv2d_fwd_plan(*gemm, wl.dtype, 0)
     assert rc == 0, abi.conv2d_strerror(rc)
+    if wgrad:
+        # the weight backward has its own kernel; report its workspace instead
+        plan = {"tile_id": -2, "BM": 64, "BN": 192, "BK": 64, "loader": -1, "splits": None,
+                "grid": None, "workspace_bytes": need}
 
     ms_step, wall_ms = timed(fn, call_args, args.steps, args.warmup, stream)
     assert abi.conv2d_fwd_status(sptr) == 0
@@ -244,14 +271,15 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / peak_flops, 4)}
-    kind = abi.conv2d_fwd_tile_kind(plan["tile_id"]) if plan["tile_id"] >= 0 else -1
+    kind = (abi.conv2d_fwd_tile_kind(plan["tile_id"]) if plan["tile_id"] >= 0
+            else -2 if wgrad else -1)
     ksrc = kernel_sources_hash(kind)
-    t = TRAFFIC.get(wl.name if not dgrad else "dgrad:" + wl.name)
+    t = TRAFFIC.get(wl.name if args.op == "fwd" else args.op + ":" + wl.name)
     roof["traffic"] = (t["bytes"] if t and t["tile"] == plan["tile_id"] and t["kernel"] == ksrc
                        else None)
 
     line = {
-        "metric": METRIC_DGRAD if dgrad else METRIC,
+        "metric": METRIC_DGRAD if dgrad else METRIC_WGRAD if wgrad else METRIC,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -262,15 +290,19 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == BF16 else "f32",
-        "data": "synthetic (seeded; %s %s, w %s%s; bf16-rounded)" % (
-            "dy" if dgrad else "x", dist_text(wl.x_dist), dist_text(wl.w_dist),
-            "" if dgrad else ", bias " + dist_text(wl.bias_dist)),
-        "config": {"workload": wl.name + (" data backward" if dgrad else ""), "N": wl.N,
+        "data": ("synthetic (seeded; x %s, dy N(0, sd 1); bf16-rounded)" % dist_text(wl.x_dist)
+                 if wgrad else
+                 "synthetic (seeded; %s %s, w %s%s; bf16-rounded)" % (
+                     "dy" if dgrad else "x", dist_text(wl.x_dist), dist_text(wl.w_dist),
+                     "" if dgrad else ", bias " + dist_text(wl.bias_dist))),
+        "config": {"workload": wl.name + (" data backward" if dgrad else " weight backward"
+                                          if wgrad else ""), "N": wl.N,
                    "H": wl.H, "W": wl.W, "IC": wl.IC,
                    "OC": wl.OC, "KH": wl.KH, "KW": wl.KW, "stride": wl.stride, "pad": wl.pad,
                    "dilation": wl.dilation, "M": M, "K": K,
                    "plan": {k: plan[k] for k in ("tile_id", "BM", "BN", "BK", "loader",
-                                                 "splits", "grid")}},
+                                                 "splits", "grid", "workspace_bytes")
+                            if k in plan}},
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "host_wall_ms_per_step": round(wall_ms, 6),

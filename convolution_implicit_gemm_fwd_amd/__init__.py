@@ -4,8 +4,9 @@ NHWC input, OHWI weight, fp32 bias and fp32 NHWC output; bf16 (or fp32)
 inputs; hand-written HIP kernels for gfx950 behind the C ABI of
 include/convimg.h.  ``abi`` is the ctypes binding of that ABI (same names);
 ``conv2d_nhwc`` below wraps it for torch tensors, using torch only for device
-memory and the current stream; ``conv2d_bwd_data_nhwc`` does the same for the
-gradient with respect to the input (stride 1).
+memory and the current stream; ``conv2d_bwd_data_nhwc`` and
+``conv2d_bwd_weight_nhwc`` do the same for the gradients with respect to the
+input (stride 1) and to the weights.
 
 Importing the package loads nothing; the HIP library is loaded on first use
 and its absence is an error (there is no fallback path).
@@ -14,11 +15,13 @@ from __future__ import annotations
 
 from . import abi
 from .abi import (CONVIMG_BF16, CONVIMG_FP32, LibraryMissing, conv2d_bwd_data,
-                  conv2d_bwd_data_weights, conv2d_fwd, conv2d_fwd_force, conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
+                  conv2d_bwd_data_weights, conv2d_bwd_weight, conv2d_bwd_weight_workspace,
+                  conv2d_fwd, conv2d_fwd_force, conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
                   conv2d_fwd_status, conv2d_release, conv2d_strerror)
 
-__all__ = ["abi", "conv2d_nhwc", "conv2d_bwd_data_nhwc", "conv2d_bwd_data",
-           "conv2d_bwd_data_weights", "conv2d_fwd",
+__all__ = ["abi", "conv2d_nhwc", "conv2d_bwd_data_nhwc", "conv2d_bwd_weight_nhwc",
+           "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
+           "conv2d_bwd_weight_workspace", "conv2d_fwd",
            "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror", "conv2d_fwd_force",
            "conv2d_fwd_num_tiles", "conv2d_fwd_status", "conv2d_release", "CONVIMG_BF16", "CONVIMG_FP32", "LibraryMissing"]
 
@@ -119,3 +122,53 @@ def conv2d_bwd_data_nhwc(dy, w, H, W, stride=1, pad=0, dilation=1, dx=None, wt=N
     if rc != 0:
         raise RuntimeError("conv2d_bwd_data failed: %s (status %d)" % (conv2d_strerror(rc), rc))
     return dx
+
+
+def conv2d_bwd_weight_nhwc(x, dy, KH, KW, stride=1, pad=0, dilation=1, dw=None, ws=None,
+                           stream=None):
+    """dw[OC,KH,KW,IC] (fp32): gradient of conv2d_nhwc's output with respect to w.
+
+    x: contiguous bfloat16 [N,H,W,IC] device tensor, dy: contiguous bfloat16
+    [N,OH,OW,OC] (the output gradient); KH, KW, stride, pad, dilation: the
+    forward problem.  ws: optional uint8 device workspace of at least
+    ``conv2d_bwd_weight_workspace`` bytes (allocated here when needed and not
+    given); dw: optional preallocated output.  Runs on ``stream`` (default:
+    torch's current stream) without waiting.
+    """
+    import torch
+
+    if x.dtype != torch.bfloat16 or dy.dtype != torch.bfloat16:
+        raise TypeError("the weight backward takes bfloat16 x and dy")
+    if not (x.is_cuda and dy.is_cuda):
+        raise ValueError("x and dy must be device tensors")
+    if x.dim() != 4 or dy.dim() != 4 or x.shape[0] != dy.shape[0]:
+        raise ValueError("x must be [N,H,W,IC] and dy [N,OH,OW,OC]")
+    if not (x.is_contiguous() and dy.is_contiguous()):
+        raise ValueError("x and dy must be contiguous (NHWC)")
+    N, H, W, IC = x.shape
+    _, OH, OW, OC = dy.shape
+    if (conv2d_fwd_out_dim(H, KH, stride, pad, dilation) != OH
+            or conv2d_fwd_out_dim(W, KW, stride, pad, dilation) != OW):
+        raise ValueError("dy's extent is not the forward output extent of H x W")
+    with torch.cuda.device(x.device):
+        rc, need = conv2d_bwd_weight_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation,
+                                               CONVIMG_BF16)
+        if rc != 0:
+            raise RuntimeError("conv2d_bwd_weight_workspace failed: %s (status %d)"
+                               % (conv2d_strerror(rc), rc))
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if dw is None:
+            dw = torch.empty((OC, KH, KW, IC), dtype=torch.float32, device=x.device)
+        elif (tuple(dw.shape) != (OC, KH, KW, IC) or dw.dtype != torch.float32
+              or not dw.is_contiguous() or not dw.is_cuda):
+            raise ValueError("dw must be a contiguous float32 [OC,KH,KW,IC] device tensor")
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        ws_ptr = ws.data_ptr() if ws is not None else None
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+        rc = conv2d_bwd_weight(x.data_ptr(), dy.data_ptr(), N, H, W, IC, OC, KH, KW, stride, pad,
+                               dilation, CONVIMG_BF16, dw.data_ptr(), ws_ptr, ws_bytes, stream)
+    if rc != 0:
+        raise RuntimeError("conv2d_bwd_weight failed: %s (status %d)" % (conv2d_strerror(rc), rc))
+    return dw

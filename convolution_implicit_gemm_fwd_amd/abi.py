@@ -25,6 +25,7 @@ CONVIMG_ERR_LAUNCH = 7
 CONVIMG_ERR_DEVICE = 8
 CONVIMG_ERR_TIMEOUT = 9
 CONVIMG_ERR_UNSUPPORTED = 10
+CONVIMG_ERR_WORKSPACE = 11
 
 CONVIMG_LOADER_TAP = 0
 CONVIMG_LOADER_VEC8 = 1
@@ -42,7 +43,8 @@ CONVIMG_KIND_IMAGE = 6
 # Every symbol include/convimg.h declares.
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror",
            "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_tile_kind", "conv2d_fwd_status",
-           "conv2d_release", "conv2d_bwd_data", "conv2d_bwd_data_weights")
+           "conv2d_release", "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
+           "conv2d_bwd_weight_workspace")
 
 
 class convimg_plan(ctypes.Structure):
@@ -97,6 +99,10 @@ def load(path: str = LIB_PATH):
     lib.conv2d_bwd_data.restype = i
     lib.conv2d_bwd_data_weights.argtypes = [vp] + [i] * 5 + [vp, vp]
     lib.conv2d_bwd_data_weights.restype = i
+    lib.conv2d_bwd_weight.argtypes = [vp, vp] + [i] * 11 + [vp, vp, ctypes.c_size_t, vp]
+    lib.conv2d_bwd_weight.restype = i
+    lib.conv2d_bwd_weight_workspace.argtypes = [i] * 11 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.conv2d_bwd_weight_workspace.restype = i
     _lib = lib
     return lib
 
@@ -116,6 +122,21 @@ def conv2d_bwd_data(dy, w, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype
 def conv2d_bwd_data_weights(w, OC, KH, KW, IC, dtype, wt, stream):
     """Raw C call of the data backward's weight transform, returns a status."""
     return load().conv2d_bwd_data_weights(w, OC, KH, KW, IC, dtype, wt, stream)
+
+
+def conv2d_bwd_weight(x, dy, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, dw, ws, ws_bytes,
+                      stream):
+    """Raw C call of the weight backward (device addresses as integers), returns a status."""
+    return load().conv2d_bwd_weight(x, dy, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, dw,
+                                    ws, ws_bytes, stream)
+
+
+def conv2d_bwd_weight_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype):
+    """Returns (status, workspace bytes the weight backward needs on the current device)."""
+    b = ctypes.c_size_t(0)
+    rc = load().conv2d_bwd_weight_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype,
+                                            ctypes.byref(b))
+    return rc, b.value
 
 
 def conv2d_fwd_out_dim(size, k, stride, pad, dilation):

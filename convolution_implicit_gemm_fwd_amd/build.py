@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libconvimg.so")
 SOURCES = [os.path.join(CSRC, "conv2d_fwd.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, h) for h in ("igemm_common.hpp", "igemm_regs.hpp", "igemm_pipe.hpp", "igemm_patch.hpp", "igemm_strip.hpp", "igemm_window.hpp", "igemm_resident.hpp", "igemm_image.hpp", "igemm_dgrad.hpp")] + [os.path.join(INCLUDE, "convimg.h")]
+DEPENDS = SOURCES + [os.path.join(CSRC, h) for h in ("igemm_common.hpp", "igemm_regs.hpp", "igemm_pipe.hpp", "igemm_patch.hpp", "igemm_strip.hpp", "igemm_window.hpp", "igemm_resident.hpp", "igemm_image.hpp", "igemm_dgrad.hpp", "igemm_wgrad.hpp")] + [os.path.join(INCLUDE, "convimg.h")]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

@@ -10,6 +10,7 @@
 #include "igemm_dgrad.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_window.hpp"
+#include "igemm_wgrad.hpp"
 
 #include <algorithm>
 #include <array>
@@ -244,6 +245,9 @@ int device_info(int dev, DeviceInfo **out)
         for (int mb = 1; mb <= kImgMaxMB; ++mb)
             (void)hipFuncSetAttribute((const void *)kImgKernels[mb],
                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        for (const void *f : {(const void *)igemm_wgrad_bf16<true, true>, (const void *)igemm_wgrad_bf16<true, false>,
+                              (const void *)igemm_wgrad_bf16<false, true>, (const void *)igemm_wgrad_bf16<false, false>})
+            (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kWgLdsBytes);
         for (int t = 0; t < kNumTiles; ++t)
             for (int l = 0; l < kNumLoaders; ++l) {
                 int nb = 1;
@@ -882,6 +886,63 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
     return e->rc;
 }
 
+FastDiv make_fast_div(int v)
+{
+    int l = 0;
+    while ((1LL << l) < v)
+        ++l;
+    const unsigned long long num = 1ULL << (31 + l);
+    FastDiv f;
+    f.mul = (unsigned)((num + (unsigned long long)v - 1) / (unsigned long long)v);
+    f.shift = 31 + l;
+    return f;
+}
+
+// Weight-backward plan: 64 x 192 output tiles; the pixels split into
+// contiguous ranges so that tiles x ranges covers the CUs, at least four
+// 64-pixel steps per range, partial sums (ranges x OC x KH*KW*IC fp32) kept
+// under 1 GiB.
+struct WgPlan {
+    int OH = 0, OW = 0, M = 0, KKIC = 0, tiles_m = 0, tiles_n = 0, splits = 1, chunk = 0;
+    size_t ws_bytes = 0;
+};
+
+int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d, int dtype,
+               int num_cus, WgPlan *wp)
+{
+    convimg_plan fwd;
+    int rc = make_plan(N, H, W, IC, OC, KH, KW, s, p, d, dtype, 1, true, nullptr, &fwd);
+    if (rc != CONVIMG_OK)
+        return rc;
+    if (dtype != CONVIMG_BF16)
+        return CONVIMG_ERR_UNSUPPORTED;
+    const long long lim = 0x7fffffffLL;
+    wp->OH = fwd.OH;
+    wp->OW = fwd.OW;
+    wp->M = (int)fwd.M;
+    wp->KKIC = fwd.K;
+    wp->tiles_m = ceil_div(OC, kWgBM);
+    wp->tiles_n = ceil_div(fwd.K, kWgBN);
+    const long long tiles = (long long)wp->tiles_m * wp->tiles_n;
+    const long long steps = (fwd.M + kWgBK - 1) / kWgBK;
+    long long S = tiles < num_cus ? (num_cus + tiles - 1) / tiles : 1;
+    if (S > steps / 4)
+        S = steps / 4;
+    const long long per = (long long)OC * fwd.K * 4;
+    if (S * per > (1LL << 30))
+        S = (1LL << 30) / per;
+    if (S < 1)
+        S = 1;
+    const long long chunk = (steps + S - 1) / S * kWgBK;
+    S = (fwd.M + chunk - 1) / chunk;
+    if (tiles * S >= lim)
+        return CONVIMG_ERR_RANGE;
+    wp->splits = (int)S;
+    wp->chunk = (int)chunk;
+    wp->ws_bytes = S > 1 ? (size_t)(S * per) : 0;
+    return CONVIMG_OK;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -1191,6 +1252,110 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
     return conv2d_fwd(dy, wt, nullptr, N, fwd.OH, fwd.OW, OC, IC, KH, KW, 1, pt, dilation, dtype, dx, stream);
 }
 
+int conv2d_bwd_weight_workspace(int N, int H, int W, int IC, int OC, int KH, int KW, int stride, int pad,
+                                int dilation, int dtype, size_t *bytes)
+{
+    if (!bytes)
+        return CONVIMG_ERR_NULL;
+    WgPlan wp;
+    int rc = plan_wgrad(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, &wp);
+    if (rc != CONVIMG_OK)
+        return rc;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return CONVIMG_ERR_DEVICE;
+    rc = device_info(dev, &info);
+    if (rc != CONVIMG_OK)
+        return rc;
+    rc = plan_wgrad(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, &wp);
+    if (rc != CONVIMG_OK)
+        return rc;
+    *bytes = wp.ws_bytes;
+    return CONVIMG_OK;
+}
+
+int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC, int OC, int KH, int KW,
+                      int stride, int pad, int dilation, int dtype, float *dw, void *ws, size_t ws_bytes,
+                      hipStream_t stream)
+{
+    if (!x || !dy || !dw)
+        return CONVIMG_ERR_NULL;
+    // argument errors first: they need no device
+    WgPlan wp;
+    int rc = plan_wgrad(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, &wp);
+    if (rc != CONVIMG_OK)
+        return rc;
+    const size_t nx = (size_t)N * H * W * IC * 2;
+    const size_t ny = (size_t)wp.M * OC * 2;
+    const size_t nw = (size_t)OC * wp.KKIC * 4;
+    if (overlaps(dw, nw, x, nx) || overlaps(dw, nw, dy, ny))
+        return CONVIMG_ERR_ALIAS;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return CONVIMG_ERR_DEVICE;
+    rc = device_info(dev, &info);
+    if (rc != CONVIMG_OK)
+        return rc;
+    rc = plan_wgrad(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, &wp);
+    if (rc != CONVIMG_OK)
+        return rc;
+    if (wp.ws_bytes > 0) {
+        if (!ws)
+            return CONVIMG_ERR_NULL;
+        if (ws_bytes < wp.ws_bytes)
+            return CONVIMG_ERR_WORKSPACE;
+        if (overlaps(ws, wp.ws_bytes, x, nx) || overlaps(ws, wp.ws_bytes, dy, ny)
+            || overlaps(ws, wp.ws_bytes, dw, nw))
+            return CONVIMG_ERR_ALIAS;
+    }
+    WgArgs a;
+    a.x = (const unsigned short *)x;
+    a.dy = (const unsigned short *)dy;
+    a.dst = wp.splits > 1 ? (float *)ws : dw;
+    a.N = N;
+    a.H = H;
+    a.W = W;
+    a.IC = IC;
+    a.OC = OC;
+    a.KH = KH;
+    a.KW = KW;
+    a.s = stride;
+    a.p = pad;
+    a.d = dilation;
+    a.OH = wp.OH;
+    a.OW = wp.OW;
+    a.M = wp.M;
+    a.KKIC = wp.KKIC;
+    a.tiles_m = wp.tiles_m;
+    a.tiles_n = wp.tiles_n;
+    a.splits = wp.splits;
+    a.chunk = wp.chunk;
+    a.div_ohw = make_fast_div(wp.OH * wp.OW);
+    a.div_ow = make_fast_div(wp.OW);
+    a.div_ic = make_fast_div(IC);
+    a.div_kw = make_fast_div(KW);
+    const bool vx = IC % 8 == 0 && ((uintptr_t)x & 15) == 0;
+    const bool vdy = OC % 8 == 0 && ((uintptr_t)dy & 15) == 0;
+    void (*k)(WgArgs) = vx ? (vdy ? igemm_wgrad_bf16<true, true> : igemm_wgrad_bf16<true, false>)
+                           : (vdy ? igemm_wgrad_bf16<false, true> : igemm_wgrad_bf16<false, false>);
+    const int grid = wp.tiles_m * wp.tiles_n * wp.splits;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kWgThreads), kWgLdsBytes, stream, a);
+    if (hipGetLastError() != hipSuccess)
+        return CONVIMG_ERR_LAUNCH;
+    if (wp.splits > 1) {
+        const int n = OC * wp.KKIC;
+        const int vec = (n % 4 == 0 && ((uintptr_t)ws & 15) == 0 && ((uintptr_t)dw & 15) == 0) ? 1 : 0;
+        const int blocks = ceil_div(ceil_div(n, 4), kWgReduceThreads);
+        hipLaunchKernelGGL(wgrad_reduce, dim3(blocks), dim3(kWgReduceThreads), 0, stream, (const float *)ws, dw,
+                           n, wp.splits, vec);
+        if (hipGetLastError() != hipSuccess)
+            return CONVIMG_ERR_LAUNCH;
+    }
+    return CONVIMG_OK;
+}
+
 const char *conv2d_strerror(int status)
 {
     switch (status) {
@@ -1204,7 +1369,10 @@ const char *conv2d_strerror(int status)
     case CONVIMG_ERR_LAUNCH: return "kernel launch failed";
     case CONVIMG_ERR_DEVICE: return "no usable HIP device";
     case CONVIMG_ERR_TIMEOUT: return "a split-K workgroup timed out waiting for its turn";
-    case CONVIMG_ERR_UNSUPPORTED: return "data backward needs stride 1, KH == KW and pad <= dilation*(KH-1)";
+    case CONVIMG_ERR_UNSUPPORTED:
+        return "unsupported by the backward passes (data: stride 1, KH == KW, pad <= dilation*(KH-1); "
+               "weights: bf16 storage)";
+    case CONVIMG_ERR_WORKSPACE: return "workspace smaller than conv2d_bwd_weight_workspace reports";
     default: return "unknown status";
     }
 }

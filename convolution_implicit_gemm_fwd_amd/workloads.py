@@ -167,3 +167,18 @@ def make_grad_inputs(wl: Workload, OH: int, OW: int, seed: int = 0,
     if dtype == BF16:
         return Inputs(wl, dy32, w32, b, dy, w, True)
     return Inputs(wl, dy32, w32, b, dy32, w32, True)
+
+
+def make_wgrad_inputs(wl: Workload, OH: int, OW: int, seed: int = 0) -> Inputs:
+    """Draw the weight-backward inputs of a workload: x [N,H,W,IC] from the
+    workload's x distribution, then dy [N,OH,OW,OC] from N(0, 1); both
+    bf16-rounded and stored as bf16.
+
+    OH, OW: the forward output extent, given by the caller.  The result's
+    x32/x_store hold x and its w32/w_store hold dy; bias is unused (zeros).
+    """
+    rng = np.random.default_rng(seed)
+    x = round_to_bf16_bits(_draw(rng, wl.x_dist, (wl.N, wl.H, wl.W, wl.IC)))
+    dy = round_to_bf16_bits(_draw(rng, ("normal", 0.0, 1.0), (wl.N, OH, OW, wl.OC)))
+    return Inputs(wl, bf16_bits_to_f32(x), bf16_bits_to_f32(dy), np.zeros(wl.OC, np.float32),
+                  x, dy, True)

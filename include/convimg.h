@@ -25,6 +25,7 @@
 #define CONVIMG_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -46,7 +47,9 @@ extern "C" {
 #define CONVIMG_ERR_LAUNCH  7  /* the HIP runtime refused the launch */
 #define CONVIMG_ERR_DEVICE  8  /* no usable HIP device, or a device query failed */
 #define CONVIMG_ERR_TIMEOUT 9  /* a split-K wait gave up (reported by conv2d_fwd_status) */
-#define CONVIMG_ERR_UNSUPPORTED 10 /* conv2d_bwd_data: stride != 1, KH != KW or pad > dilation*(KH-1) */
+#define CONVIMG_ERR_UNSUPPORTED 10 /* conv2d_bwd_data: stride != 1, KH != KW or pad > dilation*(KH-1);
+                                      conv2d_bwd_weight: fp32 storage */
+#define CONVIMG_ERR_WORKSPACE 11   /* conv2d_bwd_weight: ws_bytes below what it needs */
 
 /* Loader variants used by the plan. */
 #define CONVIMG_LOADER_TAP    0  /* IC % 64 == 0: one 64-channel slice of one tap per K tile, 16-byte loads */
@@ -209,6 +212,47 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
  * fails.  Asynchronous on `stream`. */
 int conv2d_bwd_data_weights(const void *w, int OC, int KH, int KW, int IC, int dtype, void *wt,
                             hipStream_t stream);
+
+/* Weight backward: the gradient of conv2d_fwd's output with respect to its
+ * weights w (burn-cubecl "kernel/conv/base.rs" listing, conv_weight_backward,
+ * whose implicit-GEMM route serves every groups = 1 problem):
+ *
+ *   dw[oc][kh][kw][ic] = sum_{n,oh,ow} dy[n][oh][ow][oc]
+ *                        * X(n, oh*stride - pad + kh*dilation, ow*stride - pad + kw*dilation, ic)
+ *
+ * with X = x inside the image and 0 in the padding; any stride, padding and
+ * dilation.  An implicit GEMM with M = OC, N = KH*KW*IC and the reduction
+ * over the N*OH*OW pixels, split into contiguous pixel ranges whose partial
+ * sums go to `ws` and are then added in a fixed order (the result is the
+ * same on every call).
+ *
+ *   x     device, N x H x W x IC (NHWC) bf16
+ *   dy    device, N x OH x OW x OC (NHWC) bf16, OH/OW the forward output
+ *         extents of H/W (the formula under conv2d_fwd)
+ *   dw    device, fp32 OC x KH x KW x IC (OHWI, the layout of w), fully
+ *         overwritten
+ *   ws    device workspace of ws_bytes bytes, caller-owned; at least what
+ *         conv2d_bwd_weight_workspace reports for the same problem on the
+ *         current device (NULL allowed when that is 0)
+ *   N, H, W, IC, OC, KH, KW, stride, pad, dilation: the forward problem
+ *   dtype must be CONVIMG_BF16
+ *
+ * Errors (returned before any work is queued): the argument errors of
+ * conv2d_fwd for the forward problem; CONVIMG_ERR_UNSUPPORTED for fp32
+ * storage; CONVIMG_ERR_NULL for a NULL x, dy or dw, or a NULL ws when one is
+ * needed; CONVIMG_ERR_WORKSPACE if ws_bytes is too small; CONVIMG_ERR_ALIAS
+ * if dw or the used part of ws overlaps another buffer.  CONVIMG_ERR_LAUNCH
+ * if a launch fails.  Asynchronous on `stream`; the workspace is in use
+ * until the stream has run the call. */
+int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC, int OC, int KH, int KW,
+                      int stride, int pad, int dilation, int dtype, float *dw, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Bytes of workspace conv2d_bwd_weight needs for this problem on the current
+ * device (0: none), in *bytes.  Errors: CONVIMG_ERR_NULL for a NULL bytes,
+ * the argument errors of conv2d_bwd_weight, CONVIMG_ERR_DEVICE. */
+int conv2d_bwd_weight_workspace(int N, int H, int W, int IC, int OC, int KH, int KW, int stride, int pad,
+                                int dilation, int dtype, size_t *bytes);
 
 /* Free every library-owned buffer (synchronising each device that has
  * one).  Later calls allocate again as needed. */

@@ -46,7 +46,7 @@ def test_out_dim_table(lib):
 
 
 def test_strerror(lib):
-    for code in range(11):
+    for code in range(12):
         msg = abi.conv2d_strerror(code)
         assert msg and msg != "unknown status"
     assert abi.conv2d_strerror(1234) == "unknown status"
@@ -333,3 +333,39 @@ def test_bwd_data_weights_errors_before_any_device_work(lib, kw, code):
     a.update(kw)
     assert abi.conv2d_bwd_data_weights(a["w"], a["OC"], a["KH"], a["KW"], a["IC"], a["dtype"],
                                        a["wt"], a["stream"]) == code
+
+
+
+def call_wgt(**kw):
+    a = dict(BASE, x=0x1000000, dy=0x2000000, dw=0x3000000, ws=0x5000000, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return abi.conv2d_bwd_weight(a["x"], a["dy"], a["N"], a["H"], a["W"], a["IC"], a["OC"], a["KH"],
+                                 a["KW"], a["stride"], a["pad"], a["dilation"], a["dtype"], a["dw"],
+                                 a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), abi.CONVIMG_ERR_NULL),
+    (dict(dy=None), abi.CONVIMG_ERR_NULL),
+    (dict(dw=None), abi.CONVIMG_ERR_NULL),
+    (dict(N=0), abi.CONVIMG_ERR_SHAPE),
+    (dict(H=2, pad=0), abi.CONVIMG_ERR_SHAPE),
+    (dict(stride=0), abi.CONVIMG_ERR_SHAPE),
+    (dict(dtype=2), abi.CONVIMG_ERR_DTYPE),
+    (dict(dtype=1), abi.CONVIMG_ERR_UNSUPPORTED),             # fp32 storage
+    (dict(N=1 << 12, H=1 << 10, W=1 << 10), abi.CONVIMG_ERR_RANGE),
+    (dict(dw=0x1000000 + 64), abi.CONVIMG_ERR_ALIAS),          # dw inside x
+    (dict(dw=0x2000000 - 16), abi.CONVIMG_ERR_ALIAS),          # dw runs into dy
+])
+def test_bwd_weight_errors_before_any_device_work(lib, kw, code):
+    assert call_wgt(**kw) == code
+
+
+def test_bwd_weight_workspace_argument_errors(lib):
+    assert lib.conv2d_bwd_weight_workspace(2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 0, None) \
+        == abi.CONVIMG_ERR_NULL
+    assert abi.conv2d_bwd_weight_workspace(2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 1)[0] \
+        == abi.CONVIMG_ERR_UNSUPPORTED
+    assert abi.conv2d_bwd_weight_workspace(2, 8, 8, 16, 16, 3, 3, 0, 1, 1, 0)[0] \
+        == abi.CONVIMG_ERR_SHAPE

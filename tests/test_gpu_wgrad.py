@@ -1,0 +1,149 @@
+"""GPU parity of the weight backward (conv2d_bwd_weight) against the fp64
+oracle's definition of the weight gradient, element by element with
+|err| <= 1e-3*S + 1e-5 (S: the oracle's sum of |dy*x| over each element's
+terms).
+
+The kernel sums each pixel range's products in its MFMA accumulators (one
+add per 32 pixels) and then the ranges in a fixed order, so the fp32
+rounding grows with (pixels per range)/32 + ranges + 32 additions, a few
+hundred at most here: far inside the bound.
+
+dw is pre-filled with NaN (an element never written fails) and followed by
+a sentinel guard; the workspace gets a guard after the bytes the library
+asks for.  Covered: the ResNet-style layer at full size (several pixel
+ranges), the 512-channel layer (one range per tile), the 7x7 stride-2 stem
+(IC = 3: element-wise gather), a dilated layer, channel tails, strides,
+dilations, non-square windows, OC off the vector width, misaligned x,
+fewer pixels than one step; repeatability; the workspace-size error; the
+torch wrapper.
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_implicit_gemm_fwd_amd as cig
+from convolution_implicit_gemm_fwd_amd import abi
+from convolution_implicit_gemm_fwd_amd.workloads import BF16, WORKLOADS, make_wgrad_inputs
+
+import oracle
+from gpu_harness import GUARD, SENTINEL, check, log, need_gpu, shape
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def upload(a, misalign=False):
+    t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).view(torch.bfloat16)
+    if not misalign:
+        return t.cuda()
+    flat = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+    flat[1:].copy_(t.reshape(-1))
+    return flat[1:].view(t.shape)
+
+
+def run_wgrad(wl, inp, misalign=False, ws_extra=0):
+    x, dy = upload(inp.x_store, misalign), upload(inp.w_store)
+    K = wl.KH * wl.KW * wl.IC
+    n_dw = wl.OC * K
+    dw = torch.full((n_dw + GUARD,), float("nan"), dtype=torch.float32, device="cuda")
+    dw[n_dw:] = SENTINEL
+    rc, need = abi.conv2d_bwd_weight_workspace(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
+                                               wl.stride, wl.pad, wl.dilation, BF16)
+    assert rc == 0, abi.conv2d_strerror(rc)
+    ws = torch.full((need + 4096 + ws_extra,), 0x5A, dtype=torch.uint8, device="cuda")
+    log("wgrad %s workspace %d bytes" % (wl, need))
+    rc = abi.conv2d_bwd_weight(x.data_ptr(), dy.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH,
+                               wl.KW, wl.stride, wl.pad, wl.dilation, BF16, dw.data_ptr(),
+                               ws.data_ptr() if need else None, need,
+                               torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, abi.conv2d_strerror(rc)
+    torch.cuda.synchronize()
+    host = dw.cpu().numpy()
+    assert (host[n_dw:] == SENTINEL).all(), "write past the end of dw"
+    assert (ws[need:].cpu().numpy() == 0x5A).all(), "write past the workspace it asked for"
+    return host[:n_dw].reshape(wl.OC, wl.KH, wl.KW, wl.IC), need
+
+
+def wgrad_parity(wl, seed=0, misalign=False):
+    OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
+    OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
+    inp = make_wgrad_inputs(wl, OH, OW, seed=seed)
+    y, need = run_wgrad(wl, inp, misalign)
+    yref, S = oracle.conv2d_bwd_weight(inp.x32, inp.w32, wl.KH, wl.KW, wl.stride, wl.pad,
+                                       wl.dilation)
+    ratio = check(y, yref, S, "wgrad %s" % (wl,))
+    log("wgrad %s worst err/tol %.3g (workspace %d)" % (wl.name, ratio, need))
+    return y, need
+
+
+FULL = [WORKLOADS["resnet3x3"], WORKLOADS["largek"].scaled(N=4, name="largek N=4"),
+        WORKLOADS["stem7x7"].scaled(N=2, name="stem7x7 N=2"),
+        WORKLOADS["dilated"].scaled(N=1, H=64, W=64, name="dilated 64x64")]
+
+SMALL = [
+    shape(2, 13, 11, 24, 40, 3, 3, 1, 1, 1, name="IC 24 OC 40 tails"),
+    shape(2, 15, 17, 16, 50, 3, 3, 2, 1, 1, name="stride 2, OC 50 (element-wise dy)"),
+    shape(1, 20, 20, 64, 64, 3, 3, 1, 2, 2, name="dilation 2"),
+    shape(3, 10, 10, 64, 96, 1, 1, 1, 0, 1, name="1x1"),
+    shape(2, 12, 14, 32, 48, 3, 5, 1, 2, 1, name="3x5 window"),
+    shape(2, 30, 30, 3, 64, 7, 7, 2, 3, 1, name="IC 3 7x7 stride 2"),
+    shape(1, 9, 9, 5, 7, 3, 3, 1, 1, 1, name="IC 5 OC 7"),
+    shape(1, 4, 5, 8, 8, 3, 3, 1, 1, 1, name="fewer pixels than a step"),
+    shape(1, 3, 3, 8, 8, 3, 3, 1, 0, 1, name="single output pixel"),
+    shape(4, 28, 28, 128, 128, 3, 3, 1, 1, 1, name="128 channels, several ranges"),
+]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
+def test_wgrad_full_size(wl):
+    wgrad_parity(wl)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_wgrad_shapes(wl):
+    wgrad_parity(wl)
+
+
+def test_wgrad_misaligned_x():
+    wgrad_parity(shape(2, 10, 10, 64, 64, 3, 3, 1, 1, 1, name="misaligned x"), misalign=True)
+
+
+def test_wgrad_repeatable():
+    wl = WORKLOADS["resnet3x3"].scaled(N=2)
+    OH, OW = wl.H, wl.W
+    inp = make_wgrad_inputs(wl, OH, OW, seed=5)
+    a, need = run_wgrad(wl, inp)
+    b, _ = run_wgrad(wl, inp)
+    assert need > 0, "this shape should use several pixel ranges"
+    assert np.array_equal(a, b), "two calls gave different bits"
+
+
+def test_wgrad_workspace_too_small():
+    wl = WORKLOADS["resnet3x3"].scaled(N=2)
+    rc, need = abi.conv2d_bwd_weight_workspace(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
+                                               wl.stride, wl.pad, wl.dilation, BF16)
+    assert rc == 0 and need > 0
+    x = torch.zeros((wl.N, wl.H, wl.W, wl.IC), dtype=torch.bfloat16, device="cuda")
+    dy = torch.zeros((wl.N, wl.H, wl.W, wl.OC), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((wl.OC, 3, 3, wl.IC), dtype=torch.float32, device="cuda")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), dy.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, 3, 3, 1, 1, 1, BF16,
+            dw.data_ptr())
+    assert abi.conv2d_bwd_weight(*args, ws.data_ptr(), need - 1, s) == abi.CONVIMG_ERR_WORKSPACE
+    assert abi.conv2d_bwd_weight(*args, None, need, s) == abi.CONVIMG_ERR_NULL
+    assert abi.conv2d_bwd_weight(*args, x.data_ptr(), need, s) == abi.CONVIMG_ERR_ALIAS
+
+
+def test_wgrad_torch_wrapper():
+    wl = shape(2, 14, 14, 48, 80, 3, 3, 1, 1, 1)
+    inp = make_wgrad_inputs(wl, 14, 14, seed=3)
+    x, dy = upload(inp.x_store), upload(inp.w_store)
+    dw = cig.conv2d_bwd_weight_nhwc(x, dy, 3, 3, stride=1, pad=1)
+    torch.cuda.synchronize()
+    yref, S = oracle.conv2d_bwd_weight(inp.x32, inp.w32, 3, 3, 1, 1, 1)
+    check(dw.cpu().numpy(), yref, S, "wrapper")
