@@ -245,9 +245,7 @@ int device_info(int dev, DeviceInfo **out)
         for (int mb = 1; mb <= kImgMaxMB; ++mb)
             (void)hipFuncSetAttribute((const void *)kImgKernels[mb],
                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        for (const void *f : {(const void *)igemm_wgrad_bf16<true, true>, (const void *)igemm_wgrad_bf16<true, false>,
-                              (const void *)igemm_wgrad_bf16<false, true>, (const void *)igemm_wgrad_bf16<false, false>})
-            (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kWgLdsBytes);
+        wgrad_set_attributes();
         for (int t = 0; t < kNumTiles; ++t)
             for (int l = 0; l < kNumLoaders; ++l) {
                 int nb = 1;
@@ -903,7 +901,7 @@ FastDiv make_fast_div(int v)
 // 64-pixel steps per range, partial sums (ranges x OC x KH*KW*IC fp32) kept
 // under 1 GiB.
 struct WgPlan {
-    int OH = 0, OW = 0, M = 0, KKIC = 0, tiles_m = 0, tiles_n = 0, splits = 1, chunk = 0;
+    int OH = 0, OW = 0, M = 0, KKIC = 0, bpr = 0, groups = 0, tiles_m = 0, tiles_n = 0, splits = 1, chunk = 0;
     size_t ws_bytes = 0;
 };
 
@@ -917,14 +915,22 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
     if (dtype != CONVIMG_BF16)
         return CONVIMG_ERR_UNSUPPORTED;
     const long long lim = 0x7fffffffLL;
+    // x and dy are read through buffer resources with 32-bit byte offsets
+    if ((long long)N * H * W * IC * 2 >= lim || fwd.M * OC * 2 >= lim)
+        return CONVIMG_ERR_RANGE;
     wp->OH = fwd.OH;
     wp->OW = fwd.OW;
     wp->M = (int)fwd.M;
     wp->KKIC = fwd.K;
+    wp->bpr = ceil_div(fwd.OW, 8);
+    const long long groups = (long long)N * fwd.OH * wp->bpr;
+    if (groups * 8 >= lim)
+        return CONVIMG_ERR_RANGE;
+    wp->groups = (int)groups;
     wp->tiles_m = ceil_div(OC, kWgBM);
     wp->tiles_n = ceil_div(fwd.K, kWgBN);
     const long long tiles = (long long)wp->tiles_m * wp->tiles_n;
-    const long long steps = (fwd.M + kWgBK - 1) / kWgBK;
+    const long long steps = (groups + 7) / 8;
     long long S = tiles < num_cus ? (num_cus + tiles - 1) / tiles : 1;
     if (S > steps / 4)
         S = steps / 4;
@@ -933,8 +939,8 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
         S = (1LL << 30) / per;
     if (S < 1)
         S = 1;
-    const long long chunk = (steps + S - 1) / S * kWgBK;
-    S = (fwd.M + chunk - 1) / chunk;
+    const long long chunk = (steps + S - 1) / S * 8;     // groups per range
+    S = (groups + chunk - 1) / chunk;
     if (tiles * S >= lim)
         return CONVIMG_ERR_RANGE;
     wp->splits = (int)S;
@@ -1332,25 +1338,25 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     a.tiles_n = wp.tiles_n;
     a.splits = wp.splits;
     a.chunk = wp.chunk;
-    a.div_ohw = make_fast_div(wp.OH * wp.OW);
-    a.div_ow = make_fast_div(wp.OW);
+    a.bpr = wp.bpr;
+    a.groups = wp.groups;
+    a.div_bpr = make_fast_div(wp.bpr);
+    a.div_oh = make_fast_div(wp.OH);
+    a.div_s = make_fast_div(stride);
     a.div_ic = make_fast_div(IC);
     a.div_kw = make_fast_div(KW);
+    a.x_bytes = (unsigned)nx;
+    a.dy_bytes = (unsigned)ny;
     const bool vx = IC % 8 == 0 && ((uintptr_t)x & 15) == 0;
     const bool vdy = OC % 8 == 0 && ((uintptr_t)dy & 15) == 0;
-    void (*k)(WgArgs) = vx ? (vdy ? igemm_wgrad_bf16<true, true> : igemm_wgrad_bf16<true, false>)
-                           : (vdy ? igemm_wgrad_bf16<false, true> : igemm_wgrad_bf16<false, false>);
     const int grid = wp.tiles_m * wp.tiles_n * wp.splits;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kWgThreads), kWgLdsBytes, stream, a);
-    if (hipGetLastError() != hipSuccess)
+    if (wgrad_launch(a, vx, vdy, grid, stream) != hipSuccess)
         return CONVIMG_ERR_LAUNCH;
     if (wp.splits > 1) {
         const int n = OC * wp.KKIC;
         const int vec = (n % 4 == 0 && ((uintptr_t)ws & 15) == 0 && ((uintptr_t)dw & 15) == 0) ? 1 : 0;
-        const int blocks = ceil_div(ceil_div(n, 4), kWgReduceThreads);
-        hipLaunchKernelGGL(wgrad_reduce, dim3(blocks), dim3(kWgReduceThreads), 0, stream, (const float *)ws, dw,
-                           n, wp.splits, vec);
-        if (hipGetLastError() != hipSuccess)
+        const int blocks = ceil_div(n, 4 * 64);
+        if (wgrad_reduce_launch((const float *)ws, dw, n, wp.splits, vec, blocks, stream) != hipSuccess)
             return CONVIMG_ERR_LAUNCH;
     }
     return CONVIMG_OK;

@@ -1,0 +1,41 @@
+// conv2d_wgrad.hip -- launchers of the weight-backward kernels
+// (igemm_wgrad.hpp).  A translation unit of its own so that it can be
+// compiled with the MFMA accumulators in VGPRs (-mllvm
+// -amdgpu-mfma-vgpr-form): in this kernel's loop the default form left
+// 76 register copies between AGPRs and VGPRs per step.
+#include "convimg.h"
+// igemm_common.hpp defines the split-K counter fill kernel, which the other
+// unit launches; this unit's copy takes another name so the two do not clash
+#define fill_zero_i32 fill_zero_i32_unused_in_wgrad_unit
+#include "igemm_pipe.hpp"
+#undef fill_zero_i32
+#define CONVIMG_WGRAD_KERNELS
+#include "igemm_wgrad.hpp"
+
+namespace convimg {
+
+void wgrad_set_attributes()
+{
+    for (const void *f : {(const void *)igemm_wgrad_bf16<true, true, kWgPF>,
+                          (const void *)igemm_wgrad_bf16<true, false, kWgPF>,
+                          (const void *)igemm_wgrad_bf16<false, true, kWgPF>,
+                          (const void *)igemm_wgrad_bf16<false, false, kWgPF>})
+        (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kWgLdsBytes);
+}
+
+hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_t stream)
+{
+    void (*k)(WgArgs) = vx ? (vdy ? igemm_wgrad_bf16<true, true, kWgPF> : igemm_wgrad_bf16<true, false, kWgPF>)
+                           : (vdy ? igemm_wgrad_bf16<false, true, kWgPF> : igemm_wgrad_bf16<false, false, kWgPF>);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kWgThreads), kWgLdsBytes, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
+                               hipStream_t stream)
+{
+    hipLaunchKernelGGL(wgrad_reduce, dim3(blocks), dim3(kWgReduceThreads), 0, stream, part, dw, n, splits, vec);
+    return hipGetLastError();
+}
+
+}  // namespace convimg

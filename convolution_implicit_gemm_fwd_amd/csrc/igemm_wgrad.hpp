@@ -14,13 +14,18 @@
 // with 16-byte loads, transposes it in registers and writes one 16-byte
 // LDS record per channel, so the LDS holds channel rows of 64 pixels.
 //
-// Workgroup: 256 threads, a 64 (oc) x 192 (j) tile, 64 pixels per step,
-// two LDS stages of 32 KB (the next step's loads are in flight while the
-// current one runs on the MFMAs), one barrier per step.  Wave w computes
-// all 64 rows x columns [48w, 48w+48) with 16x16x32 bf16 MFMAs.  The
-// pixels are split into `splits` contiguous ranges; each range's partial
-// tile goes to a workspace and a second kernel sums the ranges in order
-// (deterministic), or straight to dw when there is one range.
+// The pixels are walked in groups of 8 consecutive pixels of one output
+// row (a row of OW pixels is ceil(OW/8) groups, the last one masked), so a
+// group needs one row decode and its 8 gathers are one base offset plus a
+// constant stride.
+//
+// Workgroup: 256 threads, a 64 (oc) x 192 (j) tile, 8 groups (64 pixel
+// slots) per step, two LDS stages (the next step's loads are in flight
+// while the current one runs on the MFMAs), one barrier per step.  Wave w
+// computes all 64 rows x columns [48w, 48w+48) with 16x16x32 bf16 MFMAs.
+// The groups are split into `splits` contiguous ranges; each range's
+// partial tile goes to a workspace and a second kernel sums the ranges in
+// order (deterministic), or straight to dw when there is one range.
 #pragma once
 
 namespace convimg {
@@ -30,10 +35,18 @@ constexpr int kWgBN = 192;          // (tap, input channel) columns per tile
 constexpr int kWgBK = 64;           // pixels per step
 constexpr int kWgThreads = 256;
 constexpr int kWgRows = kWgBM + kWgBN;           // LDS rows per stage (A rows, then B rows)
-constexpr int kWgRowBytes = kWgBK * 2;           // one row: 64 pixels of one channel
+#ifndef CONVIMG_WG_PAD
+#define CONVIMG_WG_PAD 1
+#endif
+// one row: 64 pixels of one channel, padded by one 16-byte record (measured)
+constexpr int kWgRowBytes = kWgBK * 2 + (CONVIMG_WG_PAD ? 16 : 0);
 constexpr int kWgStageBytes = kWgRows * kWgRowBytes;
 constexpr int kWgLdsBytes = 2 * kWgStageBytes;
-constexpr int kWgReduceThreads = 256;
+constexpr int kWgReduceThreads = 512;
+#ifndef CONVIMG_WG_PF
+#define CONVIMG_WG_PF 1
+#endif
+constexpr int kWgPF = CONVIMG_WG_PF;    // steps of loads in flight (measured)
 
 // Division by a run-time constant with one 64-bit multiply (Granlund and
 // Montgomery, "Division by invariant integers using multiplication", 1994):
@@ -55,14 +68,25 @@ struct WgArgs {
     float *dst;                  // dw [OC][KKIC], or partial sums [splits][OC][KKIC]
     int N, H, W, IC, OC, KH, KW, s, p, d, OH, OW;
     int M, KKIC;                 // pixels N*OH*OW; columns KH*KW*IC
-    int tiles_m, tiles_n, splits, chunk;   // chunk: pixels per split, a multiple of kWgBK
-    FastDiv div_ohw, div_ow, div_ic, div_kw;
+    int bpr, groups;             // 8-pixel groups per output row; N*OH*bpr
+    int tiles_m, tiles_n, splits, chunk;   // chunk: groups per split, a multiple of 8
+    unsigned x_bytes, dy_bytes;            // both below 2^31
+    FastDiv div_bpr, div_oh, div_s, div_ic, div_kw;
 };
 
-// LDS byte offset of 16-byte record `chunk` (8 pixels) of row `row`; the
-// XOR keeps the 16 rows one MFMA operand read touches on distinct banks.
+// The kernels are compiled in conv2d_wgrad.hip only; other units see the
+// argument block and the launchers.
+#ifdef CONVIMG_WGRAD_KERNELS
+
+// LDS byte offset of 16-byte record `chunk` (8 pixels) of row `row`.  With
+// rows of 9 records, the 16 consecutive rows one MFMA operand read touches
+// and the 16 records one pass of the transposed writes stores (8 chunks x 2
+// rows 8 apart) fall on distinct bank groups.  Unpadded rows use an XOR of
+// the chunk instead, which serves the reads only.
 __device__ __forceinline__ int wg_rec(int row, int chunk)
 {
+    if (CONVIMG_WG_PAD)
+        return row * kWgRowBytes + (chunk << 4);
     return row * kWgRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
@@ -74,20 +98,25 @@ __device__ __forceinline__ void transpose8x8(const u32x4_t (&v)[8], u32x4_t (&ou
     for (int h = 0; h < 4; ++h) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            // byte selects over {hi, lo}: lo bytes are 0-3, hi bytes 4-7
             const unsigned lo = v[2 * q][h], hi = v[2 * q + 1][h];
-            out[2 * h][q] = (lo & 0xffffu) | (hi << 16);
-            out[2 * h + 1][q] = (lo >> 16) | (hi & 0xffff0000u);
+            out[2 * h][q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);       // low halves
+            out[2 * h + 1][q] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // high halves
         }
     }
 }
 
 // VX: IC % 8 == 0 and x 16-byte aligned (16-byte gathers of x), else
-// element-wise.  VDY: OC % 8 == 0 and dy 16-byte aligned, likewise.
-template <bool VX, bool VDY>
+// element-wise.  VDY: OC % 8 == 0 and dy 16-byte aligned, likewise.  PF:
+// steps whose loads are in flight while a step runs on the MFMAs (1 or 2).
+// Every load is a buffer load whose masked lanes take an offset past the
+// buffer's end and read zeros, so the loads issue back to back, unbranched.
+template <bool VX, bool VDY, int PF>
 __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
 {
     extern __shared__ __align__(16) unsigned char wg_lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // uniform: the roles below are per wave
     const int tiles = a.tiles_m * a.tiles_n;
     // ranges of one tile column share their dy rows and x windows: keep the
     // workgroups of one range together on one XCD
@@ -95,14 +124,17 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
     const int split = bid / tiles, tile = bid - split * tiles;
     const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
     const int oc0 = tm * kWgBM, j0 = tn * kWgBN;
-    const int m_begin = split * a.chunk;
-    const int m_end = min(a.M, m_begin + a.chunk);
-    const int steps = (m_end - m_begin + kWgBK - 1) / kWgBK;
+    const int g_begin = split * a.chunk;
+    const int g_end = min(a.groups, g_begin + a.chunk);
+    const int steps = (g_end - g_begin + 7) / 8;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc((void *)a.dy, 0, a.dy_bytes, kRsrcWord3);
 
-    // loader role: threads 0..191 gather 8 columns of x, 192..255 8 rows of dy
-    const bool is_b = tid < 3 * 64;
-    const int grp = is_b ? tid % 24 : (tid - 192) % 8;
-    const int pg = is_b ? tid / 24 : (tid - 192) / 8;      // 8-pixel group of the step
+    // loader role: waves 0..2 gather 8 columns of x per thread, wave 3 8 rows of dy
+    const bool is_b = wave < 3;
+    const int li = is_b ? tid : tid - 192;
+    const int grp = li >> 3;                                // 8-channel group of the tile
+    const int pg = li & 7;                                  // pixel group of the step
     const int row0 = is_b ? kWgBM + grp * 8 : grp * 8;    // first LDS row written
 
     // fixed per thread: the columns (tap, channel) or rows (oc) it loads
@@ -123,63 +155,83 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
             dwc[c] = (t - kh * a.KW) * a.d - a.p;
         }
     }
+    const unsigned sic = (unsigned)(a.s * a.IC);  // x elements between consecutive pixels of a row
 
-    u32x4_t v[8];
-    auto load = [&](int st) {
-        const int mb = m_begin + st * kWgBK + pg * 8;
-        int n = 0, oh = 0, ow = 0;
-        if (mb < m_end) {
-            n = fast_div(mb, a.div_ohw);
-            const int r = mb - n * a.OH * a.OW;
-            oh = fast_div(r, a.div_ow);
-            ow = r - oh * a.OW;
-        }
+    // bit e set: pixel e of the group reads input column iw0 + e*s inside
+    // [0, W) and is an output pixel (ow0 + e < OW)
+    auto col_mask = [&](int iw0, int valid_px) {
+        int lo = 0;
+        if (iw0 < 0)
+            lo = fast_div(-iw0 + a.s - 1, a.div_s);
+        int hi = a.W - iw0 > 0 ? fast_div(a.W - iw0 + a.s - 1, a.div_s) : 0;
+        hi = min(hi, valid_px);
+        return hi > lo ? (int)((0xffu >> (8 - hi)) & (0xffu << lo)) : 0;
+    };
+
+    auto load = [&](int st, u32x4_t (&v)[8]) {
+        const int g = g_begin + st * 8 + pg;
+        const bool gok = g < g_end;
+        const int gg = gok ? g : g_begin;
+        const int r = fast_div(gg, a.div_bpr);            // output row n*OH + oh
+        const int ow0 = (gg - r * a.bpr) * 8;
+        const int valid_px = gok ? min(8, a.OW - ow0) : 0;
+        if (is_b) {
+            const int n = fast_div(r, a.div_oh);
+            const int oh = r - n * a.OH;
+            if (VX) {
+                const int ih = oh * a.s + dh[0], iw0 = ow0 * a.s + dwc[0];
+                const bool rowok = colok[0] && ih >= 0 && ih < a.H;
+                const int mask = rowok ? col_mask(iw0, valid_px) : 0;
+                const unsigned base = 2u * ((unsigned)((n * a.H + ih) * a.W + iw0) * a.IC + icc[0]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bool pix = mb + e < m_end;
-            u32x4_t val = {0u, 0u, 0u, 0u};
-            if (is_b) {
-                if (VX) {
-                    const int ih = oh * a.s + dh[0], iw = ow * a.s + dwc[0];
-                    if (pix && colok[0] && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W)
-                        val = *(const u32x4_t *)(a.x + (size_t)((n * a.H + ih) * a.W + iw) * a.IC + icc[0]);
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const int ih = oh * a.s + dh[c], iw = ow * a.s + dwc[c];
-                        unsigned h = 0;
-                        if (pix && colok[c] && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W)
-                            h = a.x[(size_t)((n * a.H + ih) * a.W + iw) * a.IC + icc[c]];
-                        val[c >> 1] |= h << ((c & 1) * 16);
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    const unsigned off = ((mask >> e) & 1) ? base + 2u * sic * e : kOutOfRange;
+                    v[e] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
                 }
             } else {
-                const unsigned short *src = a.dy + (size_t)(mb + e) * a.OC + orow;
-                if (VDY) {
-                    if (pix && orow < a.OC)
-                        val = *(const u32x4_t *)src;
-                } else {
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        unsigned h = 0;
-                        if (pix && orow + c < a.OC)
-                            h = src[c];
-                        val[c >> 1] |= h << ((c & 1) * 16);
+                for (int e = 0; e < 8; ++e)
+                    v[e] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int ih = oh * a.s + dh[c], iw0 = ow0 * a.s + dwc[c];
+                    const bool rowok = colok[c] && ih >= 0 && ih < a.H;
+                    const int mask = rowok ? col_mask(iw0, valid_px) : 0;
+                    const unsigned base = 2u * ((unsigned)((n * a.H + ih) * a.W + iw0) * a.IC + icc[c]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const unsigned off = ((mask >> e) & 1) ? base + 2u * sic * e : kOutOfRange;
+                        const unsigned h = __builtin_amdgcn_raw_buffer_load_b16(rx, off, 0, 0);
+                        v[e][c >> 1] |= h << ((c & 1) * 16);
                     }
                 }
             }
-            v[e] = val;
-            // next pixel
-            if (++ow == a.OW) {
-                ow = 0;
-                if (++oh == a.OH) {
-                    oh = 0;
-                    ++n;
+        } else {
+            const unsigned base = (unsigned)(r * a.OW + ow0) * a.OC + orow;
+            const int mask = orow < a.OC ? (int)(0xffu >> (8 - valid_px)) : 0;
+            if (VDY) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const unsigned off = ((mask >> e) & 1) ? 2u * (base + (unsigned)a.OC * e) : kOutOfRange;
+                    v[e] = __builtin_amdgcn_raw_buffer_load_b128(rdy, off, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    u32x4_t val = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const bool ok = ((mask >> e) & 1) && orow + c < a.OC;
+                        const unsigned off = ok ? 2u * (base + (unsigned)a.OC * e + c) : kOutOfRange;
+                        const unsigned h = __builtin_amdgcn_raw_buffer_load_b16(rdy, off, 0, 0);
+                        val[c >> 1] |= h << ((c & 1) * 16);
+                    }
+                    v[e] = val;
                 }
             }
         }
     };
-    auto store = [&](int stage) {
+    auto store = [&](int stage, const u32x4_t (&v)[8]) {
         u32x4_t t[8];
         transpose8x8(v, t);
         unsigned char *base = wg_lds + stage * kWgStageBytes;
@@ -195,15 +247,9 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
         for (int j = 0; j < 3; ++j)
             acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    load(0);
-    store(0);
-    __syncthreads();
     const int lrow = lane & 15, lchk = lane >> 4;
-    for (int st = 0; st < steps; ++st) {
-        const bool more = st + 1 < steps;
-        if (more)
-            load(st + 1);
-        const unsigned char *base = wg_lds + (st & 1) * kWgStageBytes;
+    auto compute = [&](int stage) {
+        const unsigned char *base = wg_lds + stage * kWgStageBytes;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int ch = kb * 4 + lchk;
@@ -220,9 +266,35 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
                 for (int j = 0; j < 3; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        if (more)
-            store((st + 1) & 1);
-        __syncthreads();
+    };
+
+    // Register slot q holds the loads of the steps congruent to q mod PF:
+    // steps st+1 .. st+PF are in flight while step st runs on the MFMAs.
+    // The barriers wait for the LDS writes only (a workgroup fence would
+    // also wait for those loads).
+    u32x4_t v[PF][8];
+    load(0, v[0]);
+    store(0, v[0]);
+#pragma unroll
+    for (int q = 1; q <= PF; ++q)
+        if (q < steps)
+            load(q, v[q % PF]);
+    wait_lgkmcnt0();
+    lds_barrier();
+    for (int st0 = 0; st0 < steps; st0 += PF) {
+#pragma unroll
+        for (int q = 0; q < PF; ++q) {
+            const int st = st0 + q;
+            if (st >= steps)
+                break;
+            compute(st & 1);
+            if (st + 1 < steps)
+                store((st + 1) & 1, v[(q + 1) % PF]);
+            if (st + 1 + PF < steps)
+                load(st + 1 + PF, v[(q + 1) % PF]);
+            wait_lgkmcnt0();
+            lds_barrier();
+        }
     }
 
     // D[row = 4*(lane/16) + v][col = lane % 16] of each 16x16 block
@@ -242,35 +314,59 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
     }
 }
 
-// dw[i] = sum over s = 0..splits-1, in that order, of part[s][i]; four
-// consecutive elements per thread.  vec: n % 4 == 0 and both buffers
-// 16-byte aligned (16-byte accesses), else element by element.
+// dw = the sum of the pixel ranges' partial tiles, part[s][i] for s < splits.
+// One workgroup covers 256 consecutive elements (4 per lane); its 8 waves
+// each add an eighth of the ranges in order, then wave 0 adds the eight
+// partial sums in wave order: a fixed order, so every call gives the same
+// bits.  vec: n % 4 == 0 and both buffers 16-byte aligned (16-byte
+// accesses), else element by element.
 __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__restrict__ part,
                                                                  float *__restrict__ dw, int n, int splits,
                                                                  int vec)
 {
-    const int i = (blockIdx.x * kWgReduceThreads + threadIdx.x) * 4;
-    if (i >= n)
-        return;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    if (vec) {
-        for (int s = 0; s < splits; ++s) {
-            const floatx4_t v = *(const floatx4_t *)(part + (size_t)s * n + i);
-            s0 += v[0];
-            s1 += v[1];
-            s2 += v[2];
-            s3 += v[3];
+    constexpr int kWaves = kWgReduceThreads / 64;
+    __shared__ floatx4_t red[kWaves][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i = (blockIdx.x * 64 + lane) * 4;
+    const int s0 = (int)((long long)splits * w / kWaves), s1 = (int)((long long)splits * (w + 1) / kWaves);
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (i < n) {
+        if (vec) {
+#pragma unroll 4
+            for (int s = s0; s < s1; ++s)
+                acc += *(const floatx4_t *)(part + (size_t)s * n + i);
+        } else {
+            const int cnt = min(4, n - i);
+            for (int s = s0; s < s1; ++s)
+                for (int e = 0; e < cnt; ++e)
+                    acc[e] += part[(size_t)s * n + i + e];
         }
-        *(floatx4_t *)(dw + i) = floatx4_t{s0, s1, s2, s3};
-    } else {
-        const int cnt = min(4, n - i);
-        for (int e = 0; e < cnt; ++e) {
-            float acc = 0.f;
-            for (int s = 0; s < splits; ++s)
-                acc += part[(size_t)s * n + i + e];
-            dw[i + e] = acc;
+    }
+    red[w][lane] = acc;
+    __syncthreads();
+    if (w == 0 && i < n) {
+        floatx4_t t = red[0][lane];
+#pragma unroll
+        for (int q = 1; q < kWaves; ++q)
+            t += red[q][lane];
+        if (vec) {
+            *(floatx4_t *)(dw + i) = t;
+        } else {
+            const int cnt = min(4, n - i);
+            for (int e = 0; e < cnt; ++e)
+                dw[i + e] = t[e];
         }
     }
 }
+
+#endif  // CONVIMG_WGRAD_KERNELS
+
+// Launchers, defined in conv2d_wgrad.hip (its own translation unit: it is
+// compiled with the MFMA accumulators in VGPRs, which measured fewer
+// register copies for this kernel than the default AGPR form).
+void wgrad_set_attributes();
+hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_t stream);
+hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
+                               hipStream_t stream);
 
 }  // namespace convimg
