@@ -62,11 +62,15 @@ TRAFFIC = {
     "dgrad:resnet3x3": {"bytes": 19973550, "tile": 33, "kernel": "47a7c4e535ec5004"},
     # profiles/dgrad_image_largek.md
     "dgrad:largek": {"bytes": 32021082, "tile": 34, "kernel": "afb9c2480f4639b3"},
+    # weight backward: the whole call (igemm_wgrad_bf16 + wgrad_reduce), as
+    # the --op wgrad roofline times it; profiles/igemm_wgrad_*.md
+    "wgrad:resnet3x3": {"bytes": 36838091, "tile": -2, "kernel": "afde4a4a5552811f"},
+    "wgrad:largek": {"bytes": 72554492, "tile": -2, "kernel": "afde4a4a5552811f"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
 KIND_SOURCES = {
-    -2: ("igemm_wgrad.hpp",),                    # weight backward
+    -2: ("igemm_wgrad.hpp", "igemm_pipe.hpp", "conv2d_wgrad.hip"),   # weight backward
     -1: ("igemm_regs.hpp",),                     # fp32 storage
     0: ("igemm_regs.hpp",),                      # CONVIMG_KIND_REGS
     1: ("igemm_pipe.hpp",),                      # CONVIMG_KIND_PIPE

@@ -931,7 +931,8 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
     wp->tiles_n = ceil_div(fwd.K, kWgBN);
     const long long tiles = (long long)wp->tiles_m * wp->tiles_n;
     const long long steps = (groups + 7) / 8;
-    long long S = tiles < num_cus ? (num_cus + tiles - 1) / tiles : 1;
+    const long long slots = (long long)kWgOcc * num_cus;      // workgroups to aim for
+    long long S = tiles < slots ? (slots + tiles - 1) / tiles : 1;
     if (S > steps / 4)
         S = steps / 4;
     const long long per = (long long)OC * fwd.K * 4;

@@ -47,6 +47,10 @@ constexpr int kWgReduceThreads = 512;
 #define CONVIMG_WG_PF 1
 #endif
 constexpr int kWgPF = CONVIMG_WG_PF;    // steps of loads in flight (measured)
+#ifndef CONVIMG_WG_OCC
+#define CONVIMG_WG_OCC 1
+#endif
+constexpr int kWgOcc = CONVIMG_WG_OCC;  // workgroups per CU the pixel split aims for (measured)
 
 // Division by a run-time constant with one 64-bit multiply (Granlund and
 // Montgomery, "Division by invariant integers using multiplication", 1994):
@@ -175,7 +179,31 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
         const int r = fast_div(gg, a.div_bpr);            // output row n*OH + oh
         const int ow0 = (gg - r * a.bpr) * 8;
         const int valid_px = gok ? min(8, a.OW - ow0) : 0;
-        if (is_b) {
+        if (VX && VDY) {
+            // both roles: 8 16-byte loads at base + e*stride; the role only
+            // picks base, stride, mask and buffer (all wave-uniform choices
+            // but the values), so the loads sit in one straight line
+            unsigned base, stride;
+            int mask;
+            if (is_b) {
+                const int n = fast_div(r, a.div_oh);
+                const int oh = r - n * a.OH;
+                const int ih = oh * a.s + dh[0], iw0 = ow0 * a.s + dwc[0];
+                const bool rowok = colok[0] && ih >= 0 && ih < a.H;
+                mask = rowok ? col_mask(iw0, valid_px) : 0;
+                base = 2u * ((unsigned)((n * a.H + ih) * a.W + iw0) * a.IC + icc[0]);
+                stride = 2u * sic;
+            } else {
+                mask = orow < a.OC ? (int)(0xffu >> (8 - valid_px)) : 0;
+                base = 2u * ((unsigned)(r * a.OW + ow0) * a.OC + orow);
+                stride = 2u * (unsigned)a.OC;
+            }
+            const __amdgpu_buffer_rsrc_t rs = is_b ? rx : rdy;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((mask >> e) & 1) ? base + stride * e : kOutOfRange,
+                                                             0, 0);
+        } else if (is_b) {
             const int n = fast_div(r, a.div_oh);
             const int oh = r - n * a.OH;
             if (VX) {
@@ -277,8 +305,7 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
     store(0, v[0]);
 #pragma unroll
     for (int q = 1; q <= PF; ++q)
-        if (q < steps)
-            load(q, v[q % PF]);
+        load(q, v[q % PF]);
     wait_lgkmcnt0();
     lds_barrier();
     for (int st0 = 0; st0 < steps; st0 += PF) {
@@ -288,10 +315,12 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
             if (st >= steps)
                 break;
             compute(st & 1);
-            if (st + 1 < steps)
-                store((st + 1) & 1, v[(q + 1) % PF]);
-            if (st + 1 + PF < steps)
-                load(st + 1 + PF, v[(q + 1) % PF]);
+            // unconditional: past the last step the groups are out of range,
+            // every lane reads zeros and the stage written is not read again;
+            // straight-line code lets the compiler wait for the oldest loads
+            // only (vmcnt counts), not for all of them
+            store((st + 1) & 1, v[(q + 1) % PF]);
+            load(st + 1 + PF, v[(q + 1) % PF]);
             wait_lgkmcnt0();
             lds_barrier();
         }
