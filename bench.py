@@ -100,6 +100,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="resnet3x3")
     ap.add_argument("--op", choices=("fwd", "dgrad", "wgrad"), default="fwd")
+    ap.add_argument("--autotune", action="store_true",
+                    help="(--op fwd) let conv2d_fwd_autotune pick the plan on these inputs first")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline sample (0 disables it)")
     ap.add_argument("--force", default=None,
@@ -246,6 +248,12 @@ def main():
         gemm = (wl.N, OH, OW, wl.OC, wl.IC, wl.KH, wl.KW, 1,
                 wl.dilation * (wl.KH - 1) - wl.pad, wl.dilation)
         alg_bytes = (M * wl.OC + wl.OC * K) * esz + wl.N * wl.H * wl.W * wl.IC * 4
+    tuned = None
+    if args.autotune and args.op == "fwd":
+        rc, t_tile, t_splits, t_best, t_default = abi.conv2d_fwd_autotune(*call_args)
+        assert rc == 0, abi.conv2d_strerror(rc)
+        tuned = {"tile_id": t_tile, "splits": t_splits, "us_best": round(t_best, 3),
+                 "us_static": round(t_default, 3)}
     rc, plan = abi.conv2d_fwd_plan(*gemm, wl.dtype, 0)
     assert rc == 0, abi.conv2d_strerror(rc)
     if wgrad:
@@ -314,6 +322,8 @@ def main():
     }
     if dgrad:
         line["gemm_ms"] = round(ms_gemm, 6)
+    if tuned is not None:
+        line["autotune"] = tuned
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(inp, wl, flops, args.cpu_seconds, args.op)
     print(json.dumps(line), flush=True)

@@ -16,12 +16,13 @@ from __future__ import annotations
 from . import abi
 from .abi import (CONVIMG_BF16, CONVIMG_FP32, LibraryMissing, conv2d_bwd_data,
                   conv2d_bwd_data_weights, conv2d_bwd_weight, conv2d_bwd_weight_workspace,
-                  conv2d_fwd, conv2d_fwd_force, conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
+                  conv2d_fwd, conv2d_fwd_autotune, conv2d_fwd_autotune_clear, conv2d_fwd_force, conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
                   conv2d_fwd_status, conv2d_release, conv2d_strerror)
 
 __all__ = ["abi", "conv2d_nhwc", "conv2d_bwd_data_nhwc", "conv2d_bwd_weight_nhwc",
            "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
-           "conv2d_bwd_weight_workspace", "conv2d_fwd",
+           "conv2d_bwd_weight_workspace", "conv2d_fwd", "conv2d_fwd_autotune",
+           "conv2d_fwd_autotune_clear",
            "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror", "conv2d_fwd_force",
            "conv2d_fwd_num_tiles", "conv2d_fwd_status", "conv2d_release", "CONVIMG_BF16", "CONVIMG_FP32", "LibraryMissing"]
 

@@ -44,7 +44,7 @@ CONVIMG_KIND_IMAGE = 6
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror",
            "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_tile_kind", "conv2d_fwd_status",
            "conv2d_release", "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
-           "conv2d_bwd_weight_workspace")
+           "conv2d_bwd_weight_workspace", "conv2d_fwd_autotune", "conv2d_fwd_autotune_clear")
 
 
 class convimg_plan(ctypes.Structure):
@@ -103,6 +103,11 @@ def load(path: str = LIB_PATH):
     lib.conv2d_bwd_weight.restype = i
     lib.conv2d_bwd_weight_workspace.argtypes = [i] * 11 + [ctypes.POINTER(ctypes.c_size_t)]
     lib.conv2d_bwd_weight_workspace.restype = i
+    ip, fp = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)
+    lib.conv2d_fwd_autotune.argtypes = [vp, vp, vp] + [i] * 11 + [vp, vp, ip, ip, fp, fp]
+    lib.conv2d_fwd_autotune.restype = i
+    lib.conv2d_fwd_autotune_clear.argtypes = []
+    lib.conv2d_fwd_autotune_clear.restype = None
     _lib = lib
     return lib
 
@@ -137,6 +142,21 @@ def conv2d_bwd_weight_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation, 
     rc = load().conv2d_bwd_weight_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype,
                                             ctypes.byref(b))
     return rc, b.value
+
+
+def conv2d_fwd_autotune(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out,
+                        stream):
+    """Raw C call of the autotuner.  Returns (status, tile, splits, us_best, us_default)."""
+    t, sp = ctypes.c_int(-1), ctypes.c_int(-1)
+    ub, ud = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    rc = load().conv2d_fwd_autotune(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype,
+                                    out, stream, ctypes.byref(t), ctypes.byref(sp), ctypes.byref(ub),
+                                    ctypes.byref(ud))
+    return rc, t.value, sp.value, ub.value, ud.value
+
+
+def conv2d_fwd_autotune_clear():
+    load().conv2d_fwd_autotune_clear()
 
 
 def conv2d_fwd_out_dim(size, k, stride, pad, dilation):

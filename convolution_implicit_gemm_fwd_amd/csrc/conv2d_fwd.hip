@@ -13,6 +13,7 @@
 #include "igemm_wgrad.hpp"
 
 #include <algorithm>
+#include <vector>
 #include <array>
 #include <atomic>
 #include <cstdint>
@@ -583,7 +584,7 @@ bool fill_strip(StripPlan *sp, long long strip, long long chunk, int tiles_m, in
 int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d,
                        int dtype, int num_cus, bool aligned,
                        const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo,
-                       WinPlan *wpo, ResPlan *rpo, ImgPlan *ipo)
+                       WinPlan *wpo, ResPlan *rpo, ImgPlan *ipo, int ft, int fs, int fl)
 {
     if (N <= 0 || H <= 0 || W <= 0 || IC <= 0 || OC <= 0 || KH <= 0 || KW <= 0
         || s <= 0 || p < 0 || d <= 0)
@@ -630,7 +631,6 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
         loader = CONVIMG_LOADER_TAP;
     else if (aligned && IC % 8 == 0)
         loader = CONVIMG_LOADER_VEC8;
-    const int fl = g_force_loader.load();
     if (fl >= 0) {
         const bool allowed = fl == CONVIMG_LOADER_SCALAR
             || (fl == CONVIMG_LOADER_VEC8 && aligned && IC % 8 == 0)
@@ -684,7 +684,6 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
         tile = kResidentTile;   // weights and input rows fit in LDS: measured faster on every such shape
     if (window_ok && loader == CONVIMG_LOADER_SCALAR)
         tile = kWindowTile;     // few channels: the window kernel instead of the element-wise gather
-    const int ft = g_force_tile.load();
     if (ft >= 0 && ft < kNumTiles)
         tile = ft;
     if (kTiles[tile].kind == kWindow) {
@@ -794,7 +793,6 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
         if (splits < 1)
             splits = 1;
     }
-    const int fs = g_force_splits.load();
     if (fs >= 1)
         splits = fs;
     if (splits > ktiles)
@@ -825,6 +823,32 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
     return CONVIMG_OK;
 }
 
+// Choices made by conv2d_fwd_autotune, per problem (shape, dtype, CU count,
+// alignment): the tile and split-K factor that timed fastest.  Consulted by
+// the planner only while the table is not empty.
+typedef std::array<int, 13> TuneKey;
+std::mutex g_tune_mu;
+std::map<TuneKey, std::pair<int, int>> g_tuned;
+std::atomic<int> g_tuned_count{0};
+thread_local int t_try_tile = -1, t_try_splits = -1;   // set while a candidate is timed
+
+TuneKey tune_key(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d, int dtype,
+                 int num_cus, bool aligned)
+{
+    return TuneKey{N, H, W, IC, OC, KH, KW, s, p, d, dtype, num_cus, aligned ? 1 : 0};
+}
+
+void tuned_choice(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d, int dtype,
+                  int num_cus, bool aligned, int *ft, int *fs)
+{
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    auto it = g_tuned.find(tune_key(N, H, W, IC, OC, KH, KW, s, p, d, dtype, num_cus, aligned));
+    if (it != g_tuned.end()) {
+        *ft = it->second.first;
+        *fs = it->second.second;
+    }
+}
+
 // Plans of recent problems, per host thread (no lock): planning evaluates
 // every kernel family (several microseconds for some shapes), which would
 // otherwise be paid on each call of a layer that is run over and over.  The
@@ -849,8 +873,18 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
               const std::array<int, kNumLoaders> *occ, convimg_plan *pl, StripPlan *spo = nullptr,
               WinPlan *wpo = nullptr, ResPlan *rpo = nullptr, ImgPlan *ipo = nullptr)
 {
-    const int key[16] = {N, H, W, IC, OC, KH, KW, s, p, d, dtype, num_cus, aligned ? 1 : 0,
-                         g_force_tile.load(), g_force_splits.load(), g_force_loader.load()};
+    // the tile / split-K / loader to force: the test knob, else a plan the
+    // autotuner is timing (this thread), else a tuned choice for the problem
+    int ft = g_force_tile.load(), fs = g_force_splits.load(), fl = g_force_loader.load();
+    if (ft < 0 && fs < 0 && fl < 0) {
+        if (t_try_tile >= 0) {
+            ft = t_try_tile;
+            fs = t_try_splits;
+        } else if (g_tuned_count.load() > 0) {
+            tuned_choice(N, H, W, IC, OC, KH, KW, s, p, d, dtype, num_cus, aligned, &ft, &fs);
+        }
+    }
+    const int key[16] = {N, H, W, IC, OC, KH, KW, s, p, d, dtype, num_cus, aligned ? 1 : 0, ft, fs, fl};
     PlanCacheEntry *e = nullptr;
     for (PlanCacheEntry &c : t_plans)
         if (c.valid && c.occ == (const void *)occ && std::memcmp(c.key, key, sizeof(key)) == 0) {
@@ -865,7 +899,7 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
         e->rp = ResPlan();
         e->ip = ImgPlan();
         e->rc = make_plan_uncached(N, H, W, IC, OC, KH, KW, s, p, d, dtype, num_cus, aligned, occ,
-                                   &e->pl, &e->sp, &e->wp, &e->rp, &e->ip);
+                                   &e->pl, &e->sp, &e->wp, &e->rp, &e->ip, ft, fs, fl);
         std::memcpy(e->key, key, sizeof(key));
         e->occ = occ;
         e->valid = true;
@@ -1134,6 +1168,128 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     if (hipGetLastError() != hipSuccess)
         return CONVIMG_ERR_LAUNCH;
     return CONVIMG_OK;
+}
+
+int conv2d_fwd_autotune(const void *x, const void *w, const float *bias, int N, int H, int W, int IC, int OC,
+                        int KH, int KW, int stride, int pad, int dilation, int dtype, float *out,
+                        hipStream_t stream, int *tile_out, int *splits_out, float *us_best, float *us_default)
+{
+    if (!x || !w || !out)
+        return CONVIMG_ERR_NULL;
+    convimg_plan pl;
+    int rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, true, nullptr, &pl);
+    if (rc != CONVIMG_OK)
+        return rc;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return CONVIMG_ERR_DEVICE;
+    rc = device_info(dev, &info);
+    if (rc != CONVIMG_OK)
+        return rc;
+    const bool aligned = (((uintptr_t)x | (uintptr_t)w) & 15) == 0;
+    const TuneKey key = tune_key(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned);
+    {
+        // time the static choice, not an earlier tuned one
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        if (g_tuned.erase(key))
+            g_tuned_count.fetch_sub(1);
+    }
+    // candidates: what the planner makes of each forced tile (it falls back
+    // where a tile cannot serve the problem), with its split-K factor, half
+    // of it and none; the static choice first
+    std::vector<std::pair<int, int>> cand;
+    auto add = [&](int t, int sp) {
+        for (auto &c : cand)
+            if (c.first == t && c.second == sp)
+                return;
+        cand.emplace_back(t, sp);
+    };
+    rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned, info->occ, &pl);
+    if (rc != CONVIMG_OK)
+        return rc;
+    add(pl.tile_id, pl.splits);
+    if (dtype == CONVIMG_BF16) {
+        for (int t = 0; t < kNumTiles; ++t) {
+            convimg_plan c;
+            t_try_tile = t;
+            t_try_splits = -1;
+            rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned,
+                           info->occ, &c);
+            t_try_tile = -1;
+            if (rc != CONVIMG_OK)
+                continue;
+            add(c.tile_id, c.splits);
+            if (c.splits > 1) {
+                add(c.tile_id, c.splits / 2);
+                add(c.tile_id, 1);
+            }
+        }
+    }
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess)
+        return CONVIMG_ERR_DEVICE;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return CONVIMG_ERR_DEVICE;
+    }
+    constexpr int kWarm = 2, kReps = 5;
+    float best = 0.f, first = 0.f;
+    int best_i = -1;
+    rc = CONVIMG_OK;
+    for (size_t i = 0; i < cand.size() && rc == CONVIMG_OK; ++i) {
+        t_try_tile = cand[i].first;
+        t_try_splits = cand[i].second;
+        for (int r = 0; r < kWarm && rc == CONVIMG_OK; ++r)
+            rc = conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out, stream);
+        if (rc == CONVIMG_OK && hipEventRecord(e0, stream) != hipSuccess)
+            rc = CONVIMG_ERR_DEVICE;
+        for (int r = 0; r < kReps && rc == CONVIMG_OK; ++r)
+            rc = conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out, stream);
+        float ms = 0.f;
+        if (rc == CONVIMG_OK && (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess
+                                 || hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+            rc = CONVIMG_ERR_DEVICE;
+        t_try_tile = t_try_splits = -1;
+        if (rc != CONVIMG_OK)
+            break;
+        const float us = ms * 1000.f / kReps;
+        if (i == 0)
+            first = us;
+        if (best_i < 0 || us < best) {
+            best = us;
+            best_i = (int)i;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (rc != CONVIMG_OK)
+        return rc;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        if (g_tuned.emplace(key, cand[best_i]).second)
+            g_tuned_count.fetch_add(1);
+    }
+    // leave the tuned plan's result in out
+    rc = conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out, stream);
+    if (rc != CONVIMG_OK)
+        return rc;
+    if (tile_out)
+        *tile_out = cand[best_i].first;
+    if (splits_out)
+        *splits_out = cand[best_i].second;
+    if (us_best)
+        *us_best = best;
+    if (us_default)
+        *us_default = first;
+    return CONVIMG_OK;
+}
+
+void conv2d_fwd_autotune_clear(void)
+{
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tuned.clear();
+    g_tuned_count.store(0);
 }
 
 int conv2d_fwd_status(hipStream_t stream)

@@ -165,6 +165,30 @@ int conv2d_fwd_tile_kind(int tile_id);
  * function (the flag is then cleared).  Synchronises the stream. */
 int conv2d_fwd_status(hipStream_t stream);
 
+/* Run-time selection over the tile table (burn PR "Introduce autotuning to
+ * conv2d and conv_transpose2d with a new im2col/GEMM algorithm", Changes:
+ * the fastest of the candidate algorithms is picked by timing them on the
+ * problem and the choice is cached per problem).
+ *
+ * Times, on `stream` with the caller's buffers, the plan conv2d_fwd would
+ * use and the plans the planner makes of every other tile of the table
+ * (with its split-K factor, half of it and none), 2 warm-up and 5 timed
+ * launches each, and records the fastest for this problem: later
+ * conv2d_fwd and conv2d_fwd_plan calls (any thread) on the same shape,
+ * dtype, device CU count and 16-byte alignment of x and w use it.  `out`
+ * is overwritten many times and finally holds the chosen plan's result.
+ * Arguments as for conv2d_fwd; tile_out / splits_out receive the choice
+ * and us_best / us_default the mean microseconds per launch of it and of
+ * the static plan (each of the four may be NULL).  Synchronises `stream`.
+ * Errors: those of conv2d_fwd (nothing is recorded then). */
+int conv2d_fwd_autotune(const void *x, const void *w, const float *bias, int N, int H, int W, int IC, int OC,
+                        int KH, int KW, int stride, int pad, int dilation, int dtype, float *out,
+                        hipStream_t stream, int *tile_out, int *splits_out, float *us_best, float *us_default);
+
+/* Forget every choice conv2d_fwd_autotune recorded (the static plans apply
+ * again). */
+void conv2d_fwd_autotune_clear(void);
+
 /* Data backward: the gradient of conv2d_fwd's output with respect to its
  * input x (burn-cubecl "kernel/conv/base.rs" listing, conv_data_backward,
  * whose implicit-GEMM route serves groups = 1 and stride 1):

@@ -369,3 +369,18 @@ def test_bwd_weight_workspace_argument_errors(lib):
         == abi.CONVIMG_ERR_UNSUPPORTED
     assert abi.conv2d_bwd_weight_workspace(2, 8, 8, 16, 16, 3, 3, 0, 1, 1, 0)[0] \
         == abi.CONVIMG_ERR_SHAPE
+
+
+
+def test_autotune_argument_errors_before_any_device_work(lib):
+    a = dict(BASE, x=0x1000000, w=0x2000000, bias=None, out=0x3000000, stream=None)
+    args = lambda **kw: dict(a, **kw)
+    def call(d):
+        return abi.conv2d_fwd_autotune(d["x"], d["w"], d["bias"], d["N"], d["H"], d["W"], d["IC"],
+                                       d["OC"], d["KH"], d["KW"], d["stride"], d["pad"],
+                                       d["dilation"], d["dtype"], d["out"], d["stream"])[0]
+    assert call(args(x=None)) == abi.CONVIMG_ERR_NULL
+    assert call(args(out=None)) == abi.CONVIMG_ERR_NULL
+    assert call(args(N=0)) == abi.CONVIMG_ERR_SHAPE
+    assert call(args(dtype=7)) == abi.CONVIMG_ERR_DTYPE
+    abi.conv2d_fwd_autotune_clear()         # callable without a device
