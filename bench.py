@@ -100,6 +100,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="resnet3x3")
     ap.add_argument("--op", choices=("fwd", "dgrad", "wgrad"), default="fwd")
+    ap.add_argument("--nchw", choices=("f32", "bf16"), default=None,
+                    help="(--op fwd) time conv2d_fwd_nchw on NCHW/OIHW copies of the inputs, "
+                         "with an fp32 or bf16 NCHW output (permutes included)")
     ap.add_argument("--autotune", action="store_true",
                     help="(--op fwd) let conv2d_fwd_autotune pick the plan on these inputs first")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -248,6 +251,20 @@ def main():
         gemm = (wl.N, OH, OW, wl.OC, wl.IC, wl.KH, wl.KW, 1,
                 wl.dilation * (wl.KH - 1) - wl.pad, wl.dilation)
         alg_bytes = (M * wl.OC + wl.OC * K) * esz + wl.N * wl.H * wl.W * wl.IC * 4
+    if args.nchw and args.op == "fwd":
+        # NCHW / OIHW copies of the same values; the call permutes them in
+        # its workspace, runs the same implicit GEMM and permutes the result
+        xn = x.permute(0, 3, 1, 2).contiguous()
+        wn = w.permute(0, 3, 1, 2).contiguous()
+        rc, need = abi.conv2d_fwd_nchw_workspace(*gemm, wl.dtype)
+        assert rc == 0, abi.conv2d_strerror(rc)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        od = BF16 if args.nchw == "bf16" else 1
+        out = torch.empty(wl.N * wl.OC * OH * OW,
+                          dtype=torch.bfloat16 if od == BF16 else torch.float32, device="cuda")
+        call_args = ((xn.data_ptr(), wn.data_ptr(), b.data_ptr()) + gemm
+                     + (wl.dtype, od, out.data_ptr(), ws.data_ptr(), need, sptr))
+        fn = lib.conv2d_fwd_nchw
     tuned = None
     if args.autotune and args.op == "fwd":
         rc, t_tile, t_splits, t_best, t_default = abi.conv2d_fwd_autotune(*call_args)
@@ -286,7 +303,7 @@ def main():
     kind = (abi.conv2d_fwd_tile_kind(plan["tile_id"]) if plan["tile_id"] >= 0
             else -2 if wgrad else -1)
     ksrc = kernel_sources_hash(kind)
-    t = TRAFFIC.get(wl.name if args.op == "fwd" else args.op + ":" + wl.name)
+    t = None if args.nchw else TRAFFIC.get(wl.name if args.op == "fwd" else args.op + ":" + wl.name)
     roof["traffic"] = (t["bytes"] if t and t["tile"] == plan["tile_id"] and t["kernel"] == ksrc
                        else None)
 
@@ -308,7 +325,8 @@ def main():
                      "dy" if dgrad else "x", dist_text(wl.x_dist), dist_text(wl.w_dist),
                      "" if dgrad else ", bias " + dist_text(wl.bias_dist))),
         "config": {"workload": wl.name + (" data backward" if dgrad else " weight backward"
-                                          if wgrad else ""), "N": wl.N,
+                                          if wgrad else " NCHW, %s out" % args.nchw
+                                          if args.nchw else ""), "N": wl.N,
                    "H": wl.H, "W": wl.W, "IC": wl.IC,
                    "OC": wl.OC, "KH": wl.KH, "KW": wl.KW, "stride": wl.stride, "pad": wl.pad,
                    "dilation": wl.dilation, "M": M, "K": K,

@@ -6,7 +6,8 @@ include/convimg.h.  ``abi`` is the ctypes binding of that ABI (same names);
 ``conv2d_nhwc`` below wraps it for torch tensors, using torch only for device
 memory and the current stream; ``conv2d_bwd_data_nhwc`` and
 ``conv2d_bwd_weight_nhwc`` do the same for the gradients with respect to the
-input (stride 1) and to the weights.
+input (stride 1) and to the weights, and ``conv2d_nchw`` for NCHW / OIHW
+tensors with an fp32 or bf16 output.
 
 Importing the package loads nothing; the HIP library is loaded on first use
 and its absence is an error (there is no fallback path).
@@ -16,13 +17,14 @@ from __future__ import annotations
 from . import abi
 from .abi import (CONVIMG_BF16, CONVIMG_FP32, LibraryMissing, conv2d_bwd_data,
                   conv2d_bwd_data_weights, conv2d_bwd_weight, conv2d_bwd_weight_workspace,
-                  conv2d_fwd, conv2d_fwd_autotune, conv2d_fwd_autotune_clear, conv2d_fwd_force, conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
+                  conv2d_fwd, conv2d_fwd_autotune, conv2d_fwd_autotune_clear, conv2d_fwd_force,
+                  conv2d_fwd_nchw, conv2d_fwd_nchw_workspace, conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
                   conv2d_fwd_status, conv2d_release, conv2d_strerror)
 
 __all__ = ["abi", "conv2d_nhwc", "conv2d_bwd_data_nhwc", "conv2d_bwd_weight_nhwc",
            "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
            "conv2d_bwd_weight_workspace", "conv2d_fwd", "conv2d_fwd_autotune",
-           "conv2d_fwd_autotune_clear",
+           "conv2d_fwd_autotune_clear", "conv2d_fwd_nchw", "conv2d_fwd_nchw_workspace", "conv2d_nchw",
            "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror", "conv2d_fwd_force",
            "conv2d_fwd_num_tiles", "conv2d_fwd_status", "conv2d_release", "CONVIMG_BF16", "CONVIMG_FP32", "LibraryMissing"]
 
@@ -173,3 +175,57 @@ def conv2d_bwd_weight_nhwc(x, dy, KH, KW, stride=1, pad=0, dilation=1, dw=None, 
     if rc != 0:
         raise RuntimeError("conv2d_bwd_weight failed: %s (status %d)" % (conv2d_strerror(rc), rc))
     return dw
+
+
+def conv2d_nchw(x, w, bias=None, stride=1, pad=0, dilation=1, out_dtype=None, out=None, ws=None,
+                stream=None):
+    """out[N,OC,OH,OW] = conv2d(x[N,IC,H,W], w[OC,IC,KH,KW]) + bias[OC], NCHW.
+
+    x and w: contiguous device tensors, both bfloat16 or both float32.
+    out_dtype: torch.float32 (default) or torch.bfloat16 (the fp32 result
+    rounded to nearest even).  ws: optional uint8 workspace of at least
+    ``conv2d_fwd_nchw_workspace`` bytes (allocated here when not given).
+    Runs on ``stream`` (default: torch's current stream) without waiting.
+    """
+    import torch
+
+    dtype = _dtype_of(x, w, "x and w")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if not (x.is_cuda and w.is_cuda):
+        raise ValueError("x and w must be device tensors")
+    if x.dim() != 4 or w.dim() != 4 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [N,IC,H,W] and w [OC,IC,KH,KW]")
+    if not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous (NCHW / OIHW)")
+    N, IC, H, W = x.shape
+    OC, _, KH, KW = w.shape
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_cuda
+                             or bias.numel() != OC or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 device tensor of OC values")
+    OH = conv2d_fwd_out_dim(H, KH, stride, pad, dilation)
+    OW = conv2d_fwd_out_dim(W, KW, stride, pad, dilation)
+    if OH <= 0 or OW <= 0:
+        raise ValueError("no output pixel for this shape")
+    with torch.cuda.device(x.device):
+        rc, need = conv2d_fwd_nchw_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype)
+        if rc != 0:
+            raise RuntimeError("conv2d_fwd_nchw_workspace failed: %s (status %d)"
+                               % (conv2d_strerror(rc), rc))
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if out is None:
+            out = torch.empty((N, OC, OH, OW), dtype=out_dtype, device=x.device)
+        elif (tuple(out.shape) != (N, OC, OH, OW) or out.dtype != out_dtype
+              or not out.is_contiguous() or not out.is_cuda):
+            raise ValueError("out must be a contiguous [N,OC,OH,OW] device tensor of out_dtype")
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        od = CONVIMG_BF16 if out_dtype == torch.bfloat16 else CONVIMG_FP32
+        rc = conv2d_fwd_nchw(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                             N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, od, out.data_ptr(),
+                             ws.data_ptr(), ws.numel(), stream)
+    if rc != 0:
+        raise RuntimeError("conv2d_fwd_nchw failed: %s (status %d)" % (conv2d_strerror(rc), rc))
+    return out

@@ -44,7 +44,8 @@ CONVIMG_KIND_IMAGE = 6
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror",
            "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_tile_kind", "conv2d_fwd_status",
            "conv2d_release", "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
-           "conv2d_bwd_weight_workspace", "conv2d_fwd_autotune", "conv2d_fwd_autotune_clear")
+           "conv2d_bwd_weight_workspace", "conv2d_fwd_autotune", "conv2d_fwd_autotune_clear",
+           "conv2d_fwd_nchw", "conv2d_fwd_nchw_workspace")
 
 
 class convimg_plan(ctypes.Structure):
@@ -108,6 +109,10 @@ def load(path: str = LIB_PATH):
     lib.conv2d_fwd_autotune.restype = i
     lib.conv2d_fwd_autotune_clear.argtypes = []
     lib.conv2d_fwd_autotune_clear.restype = None
+    lib.conv2d_fwd_nchw.argtypes = [vp, vp, vp] + [i] * 12 + [vp, vp, ctypes.c_size_t, vp]
+    lib.conv2d_fwd_nchw.restype = i
+    lib.conv2d_fwd_nchw_workspace.argtypes = [i] * 11 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.conv2d_fwd_nchw_workspace.restype = i
     _lib = lib
     return lib
 
@@ -157,6 +162,21 @@ def conv2d_fwd_autotune(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilati
 
 def conv2d_fwd_autotune_clear():
     load().conv2d_fwd_autotune_clear()
+
+
+def conv2d_fwd_nchw(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out_dtype, out,
+                    ws, ws_bytes, stream):
+    """Raw C call of the NCHW entry point, returns a status."""
+    return load().conv2d_fwd_nchw(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype,
+                                  out_dtype, out, ws, ws_bytes, stream)
+
+
+def conv2d_fwd_nchw_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype):
+    """Returns (status, workspace bytes of conv2d_fwd_nchw)."""
+    b = ctypes.c_size_t(0)
+    rc = load().conv2d_fwd_nchw_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype,
+                                          ctypes.byref(b))
+    return rc, b.value
 
 
 def conv2d_fwd_out_dim(size, k, stride, pad, dilation):

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libconvimg.so")
 UNITS = [(os.path.join(CSRC, "conv2d_fwd.hip"), []),
          (os.path.join(CSRC, "conv2d_wgrad.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"])]
 SOURCES = [u[0] for u in UNITS]
-DEPENDS = SOURCES + [os.path.join(CSRC, h) for h in ("igemm_common.hpp", "igemm_regs.hpp", "igemm_pipe.hpp", "igemm_patch.hpp", "igemm_strip.hpp", "igemm_window.hpp", "igemm_resident.hpp", "igemm_image.hpp", "igemm_dgrad.hpp", "igemm_wgrad.hpp")] + [os.path.join(INCLUDE, "convimg.h")]
+DEPENDS = SOURCES + [os.path.join(CSRC, h) for h in ("igemm_common.hpp", "igemm_regs.hpp", "igemm_pipe.hpp", "igemm_patch.hpp", "igemm_strip.hpp", "igemm_window.hpp", "igemm_resident.hpp", "igemm_image.hpp", "igemm_dgrad.hpp", "igemm_wgrad.hpp", "igemm_layout.hpp")] + [os.path.join(INCLUDE, "convimg.h")]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

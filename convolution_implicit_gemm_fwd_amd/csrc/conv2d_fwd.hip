@@ -8,6 +8,7 @@
 #include "igemm_regs.hpp"
 #include "igemm_resident.hpp"
 #include "igemm_dgrad.hpp"
+#include "igemm_layout.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_window.hpp"
 #include "igemm_wgrad.hpp"
@@ -984,6 +985,23 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
     return CONVIMG_OK;
 }
 
+// Workspace of the NCHW entry point: NHWC copy of x, OHWI copy of w, fp32
+// NHWC result, each starting on a 256-byte boundary.
+struct NchwLayout {
+    size_t w_off = 0, y_off = 0, bytes = 0;
+};
+
+NchwLayout nchw_layout(const convimg_plan &pl, int N, int H, int W, int IC, int OC, int dtype)
+{
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
+    NchwLayout l;
+    l.w_off = up((size_t)N * H * W * IC * esz);
+    l.y_off = up(l.w_off + (size_t)OC * pl.K * esz);
+    l.bytes = up(l.y_off + (size_t)pl.M * OC * 4);
+    return l;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -1165,6 +1183,77 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     else
         hipLaunchKernelGGL(kKernels[pl.tile_id][pl.loader], dim3(pl.grid), dim3(pl.threads), 0,
                            stream, a);
+    if (hipGetLastError() != hipSuccess)
+        return CONVIMG_ERR_LAUNCH;
+    return CONVIMG_OK;
+}
+
+int conv2d_fwd_nchw_workspace(int N, int H, int W, int IC, int OC, int KH, int KW, int stride, int pad,
+                              int dilation, int dtype, size_t *bytes)
+{
+    if (!bytes)
+        return CONVIMG_ERR_NULL;
+    convimg_plan pl;
+    const int rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, true, nullptr, &pl);
+    if (rc != CONVIMG_OK)
+        return rc;
+    *bytes = nchw_layout(pl, N, H, W, IC, OC, dtype).bytes;
+    return CONVIMG_OK;
+}
+
+int conv2d_fwd_nchw(const void *x, const void *w, const float *bias, int N, int H, int W, int IC, int OC,
+                    int KH, int KW, int stride, int pad, int dilation, int dtype, int out_dtype, void *out,
+                    void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!x || !w || !out || !ws)
+        return CONVIMG_ERR_NULL;
+    convimg_plan pl;
+    int rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, true, nullptr, &pl);
+    if (rc != CONVIMG_OK)
+        return rc;
+    if (out_dtype != CONVIMG_BF16 && out_dtype != CONVIMG_FP32)
+        return CONVIMG_ERR_DTYPE;
+    const NchwLayout l = nchw_layout(pl, N, H, W, IC, OC, dtype);
+    if (ws_bytes < l.bytes)
+        return CONVIMG_ERR_WORKSPACE;
+    const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
+    const size_t nx = (size_t)N * H * W * IC * esz, nw = (size_t)OC * pl.K * esz;
+    const size_t no = (size_t)pl.M * OC * (out_dtype == CONVIMG_BF16 ? 2 : 4), nb = bias ? (size_t)OC * 4 : 0;
+    if (overlaps(out, no, x, nx) || overlaps(out, no, w, nw) || (bias && overlaps(out, no, bias, nb))
+        || overlaps(out, no, ws, l.bytes) || overlaps(ws, l.bytes, x, nx) || overlaps(ws, l.bytes, w, nw)
+        || (bias && overlaps(ws, l.bytes, bias, nb)))
+        return CONVIMG_ERR_ALIAS;
+    const int HW = H * W, OHW = pl.OH * pl.OW, KK = KH * KW;
+    auto tiles = [](int v) { return (unsigned)((v + kPermTile - 1) / kPermTile); };
+    if (N > 65535 || OC > 65535 || tiles(IC) > 65535u || tiles(OHW) > 65535u)
+        return CONVIMG_ERR_RANGE;
+    char *wsb = (char *)ws;
+    const dim3 blk(kPermThreads);
+    // x [N][IC][H*W] -> [N][H*W][IC]; w [OC][IC][KH*KW] -> [OC][KH*KW][IC]
+    if (dtype == CONVIMG_BF16) {
+        hipLaunchKernelGGL((transpose_batched<unsigned short, unsigned short>), dim3(tiles(HW), tiles(IC), N), blk, 0,
+                           stream, (const unsigned short *)x, (unsigned short *)wsb, IC, HW);
+        hipLaunchKernelGGL((transpose_batched<unsigned short, unsigned short>), dim3(tiles(KK), tiles(IC), OC), blk,
+                           0, stream, (const unsigned short *)w, (unsigned short *)(wsb + l.w_off), IC, KK);
+    } else {
+        hipLaunchKernelGGL((transpose_batched<float, float>), dim3(tiles(HW), tiles(IC), N), blk, 0, stream,
+                           (const float *)x, (float *)wsb, IC, HW);
+        hipLaunchKernelGGL((transpose_batched<float, float>), dim3(tiles(KK), tiles(IC), OC), blk, 0, stream,
+                           (const float *)w, (float *)(wsb + l.w_off), IC, KK);
+    }
+    if (hipGetLastError() != hipSuccess)
+        return CONVIMG_ERR_LAUNCH;
+    rc = conv2d_fwd(wsb, wsb + l.w_off, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype,
+                    (float *)(wsb + l.y_off), stream);
+    if (rc != CONVIMG_OK)
+        return rc;
+    // y [N][OH*OW][OC] -> out [N][OC][OH*OW], in out_dtype
+    if (out_dtype == CONVIMG_BF16)
+        hipLaunchKernelGGL((transpose_batched<float, unsigned short>), dim3(tiles(OC), tiles(OHW), N), blk, 0,
+                           stream, (const float *)(wsb + l.y_off), (unsigned short *)out, OHW, OC);
+    else
+        hipLaunchKernelGGL((transpose_batched<float, float>), dim3(tiles(OC), tiles(OHW), N), blk, 0, stream,
+                           (const float *)(wsb + l.y_off), (float *)out, OHW, OC);
     if (hipGetLastError() != hipSuccess)
         return CONVIMG_ERR_LAUNCH;
     return CONVIMG_OK;

@@ -1,0 +1,61 @@
+// igemm_layout.hpp -- layout conversions around the NHWC core, for callers
+// whose tensors are NCHW (input), OIHW (weights) and NCHW (output).
+//
+// burn-cubecl "kernel/conv/base.rs" listing: the NCHW entry points permute
+// the input to channels-last and the weight to [OC][KH][KW][IC] before the
+// NHWC convolution and permute the result back.  Here one batched-transpose
+// kernel does all three permutes (each is a transpose of the last two axes
+// of a [B][R][C] array), and the output permute can also round the fp32
+// result to bf16.  The implicit GEMM itself always writes fp32 (its split-K
+// reduction accumulates in the output buffer), into a workspace, so a bf16
+// output never aliases the accumulation buffer.
+#pragma once
+
+namespace convimg {
+
+constexpr int kPermTile = 64;
+constexpr int kPermThreads = 256;
+
+__device__ __forceinline__ float elem_to_float(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
+__device__ __forceinline__ float elem_to_float(float f) { return f; }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet).
+__device__ __forceinline__ unsigned short bf16_rne(float f)
+{
+    const unsigned u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (unsigned short)((u >> 16) | 0x40u);
+    return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T float_to_elem(float f);
+template <>
+__device__ __forceinline__ unsigned short float_to_elem<unsigned short>(float f) { return bf16_rne(f); }
+template <>
+__device__ __forceinline__ float float_to_elem<float>(float f) { return f; }
+
+// out[b][c][r] = in[b][r][c] for b < gridDim.z, r < R, c < C, converted from
+// Tin to Tout (exact between equal types and from bf16 to fp32; rounded to
+// nearest even from fp32 to bf16).  One workgroup moves a 64 x 64 tile
+// through LDS: reads along c, writes along r, both coalesced.
+// Grid: (ceil(C/64), ceil(R/64), B).
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(kPermThreads) void transpose_batched(const Tin *__restrict__ in,
+                                                                 Tout *__restrict__ out, int R, int C)
+{
+    __shared__ float tile[kPermTile][kPermTile + 1];
+    const size_t base = (size_t)blockIdx.z * R * C;
+    const int r0 = blockIdx.y * kPermTile, c0 = blockIdx.x * kPermTile;
+    const int tx = threadIdx.x % kPermTile, ty = threadIdx.x / kPermTile;
+    constexpr int kRows = kPermThreads / kPermTile;
+    for (int r = ty; r < kPermTile; r += kRows)
+        if (r0 + r < R && c0 + tx < C)
+            tile[r][tx] = elem_to_float(in[base + (size_t)(r0 + r) * C + c0 + tx]);
+    __syncthreads();
+    for (int c = ty; c < kPermTile; c += kRows)
+        if (c0 + c < C && r0 + tx < R)
+            out[base + (size_t)(c0 + c) * R + r0 + tx] = float_to_elem<Tout>(tile[tx][c]);
+}
+
+}  // namespace convimg

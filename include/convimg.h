@@ -165,6 +165,38 @@ int conv2d_fwd_tile_kind(int tile_id);
  * function (the flag is then cleared).  Synchronises the stream. */
 int conv2d_fwd_status(hipStream_t stream);
 
+/* NCHW tensors (burn-cubecl "kernel/conv/base.rs" listing: its NCHW entry
+ * points permute the input to channels-last and the weights to
+ * [OC][KH][KW][IC], run the NHWC convolution and permute the result back).
+ *
+ *   x     device, N x IC x H x W (NCHW) in `dtype`
+ *   w     device, OC x IC x KH x KW (OIHW) in `dtype`
+ *   bias  device, OC fp32 values, or NULL
+ *   out   device, N x OC x OH x OW (NCHW) in `out_dtype` (CONVIMG_FP32, or
+ *         CONVIMG_BF16: the fp32 result rounded to nearest even), fully
+ *         overwritten
+ *   ws    device workspace of ws_bytes >= conv2d_fwd_nchw_workspace bytes,
+ *         caller-owned: receives the NHWC copy of x, the OHWI copy of w and
+ *         the fp32 NHWC result, which conv2d_fwd computes (so a bf16 output
+ *         never serves as the split-K accumulation buffer)
+ *   other arguments and the output extent as for conv2d_fwd
+ *
+ * Errors (before any work is queued): those of conv2d_fwd;
+ * CONVIMG_ERR_NULL for a NULL ws; CONVIMG_ERR_DTYPE for another out_dtype;
+ * CONVIMG_ERR_WORKSPACE if ws_bytes is too small; CONVIMG_ERR_ALIAS if out
+ * or ws overlaps another buffer; CONVIMG_ERR_RANGE for N or OC above 65535
+ * or more than 65535 64-wide tiles of IC or OH*OW.  Asynchronous on
+ * `stream`; the workspace is in use until the stream has run the call. */
+int conv2d_fwd_nchw(const void *x, const void *w, const float *bias, int N, int H, int W, int IC, int OC,
+                    int KH, int KW, int stride, int pad, int dilation, int dtype, int out_dtype, void *out,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes conv2d_fwd_nchw needs for this problem, in *bytes.
+ * Errors: CONVIMG_ERR_NULL for a NULL bytes, the argument errors of
+ * conv2d_fwd. */
+int conv2d_fwd_nchw_workspace(int N, int H, int W, int IC, int OC, int KH, int KW, int stride, int pad,
+                              int dilation, int dtype, size_t *bytes);
+
 /* Run-time selection over the tile table (burn PR "Introduce autotuning to
  * conv2d and conv_transpose2d with a new im2col/GEMM algorithm", Changes:
  * the fastest of the candidate algorithms is picked by timing them on the

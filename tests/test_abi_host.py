@@ -384,3 +384,31 @@ def test_autotune_argument_errors_before_any_device_work(lib):
     assert call(args(N=0)) == abi.CONVIMG_ERR_SHAPE
     assert call(args(dtype=7)) == abi.CONVIMG_ERR_DTYPE
     abi.conv2d_fwd_autotune_clear()         # callable without a device
+
+
+
+def test_nchw_argument_errors_before_any_device_work(lib):
+    a = dict(BASE, x=0x1000000, w=0x2000000, bias=None, out=0x3000000, ws=0x6000000,
+             ws_bytes=1 << 30, out_dtype=1, stream=None)
+    def call(**kw):
+        d = dict(a, **kw)
+        return abi.conv2d_fwd_nchw(d["x"], d["w"], d["bias"], d["N"], d["H"], d["W"], d["IC"],
+                                   d["OC"], d["KH"], d["KW"], d["stride"], d["pad"], d["dilation"],
+                                   d["dtype"], d["out_dtype"], d["out"], d["ws"], d["ws_bytes"],
+                                   d["stream"])
+    assert call(x=None) == abi.CONVIMG_ERR_NULL
+    assert call(ws=None) == abi.CONVIMG_ERR_NULL
+    assert call(N=0) == abi.CONVIMG_ERR_SHAPE
+    assert call(dtype=9) == abi.CONVIMG_ERR_DTYPE
+    assert call(out_dtype=5) == abi.CONVIMG_ERR_DTYPE
+    rc, need = abi.conv2d_fwd_nchw_workspace(2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 0)
+    # x copy (4096 B), w copy (4608 B, ending on a 256-byte boundary), fp32 out (8192 B)
+    assert rc == 0 and need == 4096 + 4608 + 8192
+    rc, need3 = abi.conv2d_fwd_nchw_workspace(2, 8, 8, 16, 17, 3, 3, 1, 1, 1, 0)
+    # w copy of 17 rows (4896 B) rounds up to 5120 before the fp32 out (8704 B)
+    assert rc == 0 and need3 == 4096 + 5120 + 8704
+    assert call(ws_bytes=need - 1) == abi.CONVIMG_ERR_WORKSPACE
+    assert call(out=0x6000000 + 64) == abi.CONVIMG_ERR_ALIAS        # out inside ws
+    assert call(ws=0x1000000 + 64) == abi.CONVIMG_ERR_ALIAS         # ws overlaps x
+    assert lib.conv2d_fwd_nchw_workspace(2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 0, None) \
+        == abi.CONVIMG_ERR_NULL
