@@ -49,9 +49,20 @@ __global__ __launch_bounds__(kPermThreads) void transpose_batched(const Tin *__r
     const int r0 = blockIdx.y * kPermTile, c0 = blockIdx.x * kPermTile;
     const int tx = threadIdx.x % kPermTile, ty = threadIdx.x / kPermTile;
     constexpr int kRows = kPermThreads / kPermTile;
-    for (int r = ty; r < kPermTile; r += kRows)
-        if (r0 + r < R && c0 + tx < C)
-            tile[r][tx] = elem_to_float(in[base + (size_t)(r0 + r) * C + c0 + tx]);
+    // every lane loads (out-of-range lanes from the tile's first element,
+    // then discard it): no branch around the loads, so all 16 are in flight
+    // together instead of one round trip each
+    float v[kPermTile / kRows];
+#pragma unroll
+    for (int k = 0; k < kPermTile / kRows; ++k) {
+        const int r = ty + k * kRows;
+        const bool ok = r0 + r < R && c0 + tx < C;
+        v[k] = elem_to_float(in[base + (ok ? (size_t)(r0 + r) * C + c0 + tx : (size_t)r0 * C + c0)]);
+        v[k] = ok ? v[k] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kPermTile / kRows; ++k)
+        tile[ty + k * kRows][tx] = v[k];
     __syncthreads();
     for (int c = ty; c < kPermTile; c += kRows)
         if (c0 + c < C && r0 + tx < R)
