@@ -932,9 +932,9 @@ FastDiv make_fast_div(int v)
 }
 
 // Weight-backward plan: 64 x 192 output tiles; the pixels split into
-// contiguous ranges so that tiles x ranges covers the CUs, at least four
-// 64-pixel steps per range, partial sums (ranges x OC x KH*KW*IC fp32) kept
-// under 1 GiB.
+// contiguous ranges so that tiles x ranges fills the CUs evenly, at least
+// four steps of 8 pixel groups per range, partial sums (ranges x OC x
+// KH*KW*IC fp32) kept under 1 GiB.
 struct WgPlan {
     int OH = 0, OW = 0, M = 0, KKIC = 0, bpr = 0, groups = 0, tiles_m = 0, tiles_n = 0, splits = 1, chunk = 0;
     size_t ws_bytes = 0;
@@ -966,8 +966,14 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
     wp->tiles_n = ceil_div(fwd.K, kWgBN);
     const long long tiles = (long long)wp->tiles_m * wp->tiles_n;
     const long long steps = (groups + 7) / 8;
-    const long long slots = (long long)kWgOcc * num_cus;      // workgroups to aim for
-    long long S = tiles < slots ? (slots + tiles - 1) / tiles : 1;
+    // ranges per tile: as many as fit one workgroup per CU (rounded down, so
+    // no CU gets a second workgroup while others idle); where the tiles
+    // alone fill half the CUs, as many as fit two per CU (the LDS allows
+    // two).  Measured: a 12-tile layer ran 90 us with 22 ranges (264
+    // workgroups on 256 CUs), 66 us with 32 and 62 us with 21; a 192-tile
+    // layer 62 us with one range and 57 us with two.
+    const long long per_cu = 2 * tiles >= num_cus ? 2 : 1;
+    long long S = tiles < per_cu * num_cus ? per_cu * num_cus / tiles : 1;
     if (S > steps / 4)
         S = steps / 4;
     const long long per = (long long)OC * fwd.K * 4;

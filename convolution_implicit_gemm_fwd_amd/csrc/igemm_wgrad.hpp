@@ -47,10 +47,6 @@ constexpr int kWgReduceThreads = 512;
 #define CONVIMG_WG_PF 1
 #endif
 constexpr int kWgPF = CONVIMG_WG_PF;    // steps of loads in flight (measured)
-#ifndef CONVIMG_WG_OCC
-#define CONVIMG_WG_OCC 1
-#endif
-constexpr int kWgOcc = CONVIMG_WG_OCC;  // workgroups per CU the pixel split aims for (measured)
 
 // Division by a run-time constant with one 64-bit multiply (Granlund and
 // Montgomery, "Division by invariant integers using multiplication", 1994):
