@@ -412,3 +412,44 @@ def test_nchw_argument_errors_before_any_device_work(lib):
     assert call(ws=0x1000000 + 64) == abi.CONVIMG_ERR_ALIAS         # ws overlaps x
     assert lib.conv2d_fwd_nchw_workspace(2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 0, None) \
         == abi.CONVIMG_ERR_NULL
+
+
+def test_plan_cache_is_per_thread_and_consistent(lib):
+    """The planner keeps a small per-thread cache of recent plans: plans made
+    concurrently from many threads (ctypes releases the GIL) for an
+    interleaved mix of more shapes than the cache holds equal the plans made
+    one by one, and the forced-tile knob bypasses stale entries."""
+    import random
+    import threading
+    rng = random.Random(5)
+    shapes = []
+    while len(shapes) < 24:
+        s = (rng.randint(1, 16), rng.randint(5, 60), rng.randint(5, 60), rng.choice([3, 16, 64, 128, 256]),
+             rng.choice([32, 64, 96, 512]), 3, 3, rng.randint(1, 2), 1, rng.randint(1, 2), 0, 256)
+        if abi.conv2d_fwd_plan(*s)[0] == 0:
+            shapes.append(s)
+    want = {s: abi.conv2d_fwd_plan(*s)[1] for s in shapes}
+    bad = []
+
+    def worker(seed):
+        r = random.Random(seed)
+        for _ in range(300):
+            s = r.choice(shapes)
+            rc, p = abi.conv2d_fwd_plan(*s)
+            if rc != 0 or p != want[s]:
+                bad.append((s, p))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:2]
+    s = shapes[0]
+    try:
+        assert abi.conv2d_fwd_force(11, -1, -1) == 0
+        forced = abi.conv2d_fwd_plan(*s)[1]
+        assert forced["tile_id"] in (11, 0)          # 11, or the element-wise fallback
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+    assert abi.conv2d_fwd_plan(*s)[1] == want[s]
