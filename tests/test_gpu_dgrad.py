@@ -32,22 +32,32 @@ def _gpu():
     abi.conv2d_fwd_force(-1, -1, -1)
 
 
-def upload(a):
+def upload(a, misalign=False):
     if a.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).view(torch.bfloat16).cuda()
-    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    if not misalign:
+        return t.cuda()
+    flat = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+    flat[1:].copy_(t.reshape(-1))
+    return flat[1:].view(t.shape)          # one element past a 16-byte boundary
 
 
-def bwd_parity(wl, dtype=None, seed=0):
+def bwd_parity(wl, dtype=None, seed=0, misalign=False):
     dtype = wl.dtype if dtype is None else dtype
     OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, 1, wl.pad, wl.dilation)
     OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, 1, wl.pad, wl.dilation)
     assert OH > 0 and OW > 0
     inp = make_grad_inputs(wl, OH, OW, seed=seed, dtype=dtype)
-    dy, w = upload(inp.x_store), upload(inp.w_store)
-    wt = torch.empty_like(w.reshape(-1))
+    dy, w = upload(inp.x_store, misalign), upload(inp.w_store, misalign)
+    n_w = w.numel()
+    wt_buf = torch.empty(n_w + (1 if misalign else 0), dtype=w.dtype, device="cuda")
+    wt = wt_buf[1:] if misalign else wt_buf
     n_dx = wl.N * wl.H * wl.W * wl.IC
-    dx = torch.full((n_dx + GUARD,), float("nan"), dtype=torch.float32, device="cuda")
+    off = 1 if misalign else 0                 # dx 4-byte but not 16-byte aligned
+    dx_buf = torch.full((n_dx + GUARD + off,), float("nan"), dtype=torch.float32, device="cuda")
+    dx = dx_buf[off:]
     dx[n_dx:] = SENTINEL
     log("dgrad %s dtype=%d" % (wl, dtype))
     rc = abi.conv2d_bwd_data(dy.data_ptr(), w.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH,
@@ -146,3 +156,11 @@ def test_weight_transform_alone(OC, KH, KW, IC, dtype, misalign):
     assert (got[:off] == pad).all() and (got[off + n:] == pad).all(), "write outside wt"
     want = host.reshape(OC, KH, KW, IC)[:, ::-1, ::-1, :].transpose(3, 1, 2, 0)
     assert np.array_equal(got[off:off + n].reshape(IC, KH, KW, OC), want)
+
+
+def test_dgrad_misaligned_buffers():
+    """dy, w, the workspace and dx one element off their 16-byte boundaries:
+    the transform's element path and the forward's element-wise gather and
+    4-byte stores."""
+    bwd_parity(shape(2, 10, 10, 64, 64, 3, 3, 1, 1, 1, name="misaligned 64ch"), misalign=True)
+    bwd_parity(shape(1, 9, 12, 16, 40, 3, 3, 1, 2, 2, name="misaligned dilated"), misalign=True)

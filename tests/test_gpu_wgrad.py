@@ -45,8 +45,8 @@ def upload(a, misalign=False):
     return flat[1:].view(t.shape)
 
 
-def run_wgrad(wl, inp, misalign=False, ws_extra=0):
-    x, dy = upload(inp.x_store, misalign), upload(inp.w_store)
+def run_wgrad(wl, inp, misalign=False, ws_extra=0, misalign_dy=False):
+    x, dy = upload(inp.x_store, misalign), upload(inp.w_store, misalign_dy)
     K = wl.KH * wl.KW * wl.IC
     n_dw = wl.OC * K
     dw = torch.full((n_dw + GUARD,), float("nan"), dtype=torch.float32, device="cuda")
@@ -68,11 +68,11 @@ def run_wgrad(wl, inp, misalign=False, ws_extra=0):
     return host[:n_dw].reshape(wl.OC, wl.KH, wl.KW, wl.IC), need
 
 
-def wgrad_parity(wl, seed=0, misalign=False):
+def wgrad_parity(wl, seed=0, misalign=False, misalign_dy=False):
     OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
     OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
     inp = make_wgrad_inputs(wl, OH, OW, seed=seed)
-    y, need = run_wgrad(wl, inp, misalign)
+    y, need = run_wgrad(wl, inp, misalign, misalign_dy=misalign_dy)
     yref, S = oracle.conv2d_bwd_weight(inp.x32, inp.w32, wl.KH, wl.KW, wl.stride, wl.pad,
                                        wl.dilation)
     ratio = check(y, yref, S, "wgrad %s" % (wl,))
@@ -109,6 +109,14 @@ def test_wgrad_shapes(wl):
 
 def test_wgrad_misaligned_x():
     wgrad_parity(shape(2, 10, 10, 64, 64, 3, 3, 1, 1, 1, name="misaligned x"), misalign=True)
+
+
+def test_wgrad_misaligned_dy():
+    """dy one element off a 16-byte boundary: the element-wise dy gather with
+    the 16-byte x gather."""
+    wgrad_parity(shape(2, 11, 9, 32, 64, 3, 3, 1, 1, 1, name="misaligned dy"), misalign_dy=True)
+    wgrad_parity(shape(1, 12, 12, 24, 48, 3, 3, 2, 1, 1, name="misaligned x and dy"), misalign=True,
+                 misalign_dy=True)
 
 
 def test_wgrad_repeatable():
