@@ -64,8 +64,8 @@ TRAFFIC = {
     "dgrad:largek": {"bytes": 32021131, "tile": 34, "kernel": "afb9c2480f4639b3"},
     # weight backward: the whole call (igemm_wgrad_bf16 + wgrad_reduce), as
     # the --op wgrad roofline times it; profiles/igemm_wgrad_*.md
-    "wgrad:resnet3x3": {"bytes": 36838029, "tile": -2, "kernel": "d8c281f53bf10580"},
-    "wgrad:largek": {"bytes": 72554579, "tile": -2, "kernel": "d8c281f53bf10580"},
+    "wgrad:resnet3x3": {"bytes": 36843150, "tile": -2, "kernel": "b17c118594669fee"},
+    "wgrad:largek": {"bytes": 72559741, "tile": -2, "kernel": "b17c118594669fee"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
