@@ -201,6 +201,9 @@ def main():
     wl = WORKLOADS[args.workload]
     dgrad = args.op == "dgrad"
     wgrad = args.op == "wgrad"
+    if wgrad and wl.dtype != BF16:
+        print("--op wgrad takes bf16 storage (%s stores fp32)" % wl.name, file=sys.stderr)
+        sys.exit(2)
     if dgrad and wl.stride != 1:
         print("--op dgrad needs a stride-1 workload (%s has stride %d)" % (wl.name, wl.stride),
               file=sys.stderr)
