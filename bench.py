@@ -17,9 +17,15 @@ input, stride-1 workloads only): a step is the weight flip-transpose plus
 the forward implicit GEMM it maps to; the roofline object then prices that
 GEMM kernel alone (timed in its own loop on the same buffers).
 
-Timing: K back-to-back calls on one stream between two HIP events (recorded
-on that stream), synchronised on both sides.  TFLOP/s = 2*M*OC*K / time with
-the real K = IC*KH*KW.  The roofline object prices the kernel against HBM
+Timing: 11 windows (--windows) of K back-to-back calls on one stream, each
+between two HIP events recorded on that stream and synchronised on both
+sides; before each window's start event a sleep kernel holds the stream
+while the host queues the K calls, so the events time the GPU running the
+calls back to back (the host's own cost to queue a call is reported as
+host_ms_to_queue_a_step).  The value is the median window's time per call;
+min and max are reported too.  A cold-cache figure (single calls after
+writing a 1 GiB scrub buffer) is reported beside it.  TFLOP/s = 2*M*OC*K /
+time with the real K = IC*KH*KW.  The roofline object prices the kernel against HBM
 bandwidth or dense bf16 MFMA peak, whichever bounds it at the workload's
 arithmetic intensity.  The CPU baseline is the fp64 oracle timed on this
 host's cores on the same inputs.
@@ -105,6 +111,10 @@ def parse():
                          "with an fp32 or bf16 NCHW output (permutes included)")
     ap.add_argument("--autotune", action="store_true",
                     help="(--op fwd) let conv2d_fwd_autotune pick the plan on these inputs first")
+    ap.add_argument("--windows", type=int, default=11,
+                    help="timing windows of --steps calls each; the line reports their median")
+    ap.add_argument("--cold", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time single calls after scrubbing the caches (1 GiB write)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline sample (0 disables it)")
     ap.add_argument("--force", default=None,
@@ -158,25 +168,74 @@ def dist_text(dist):
     return dist[0]
 
 
-def timed(fn, call_args, steps, warmup, stream):
-    """ms per call of fn(*call_args): warmup calls, then `steps` calls
-    between two events recorded on `stream`, synchronised on both sides."""
+def sleep_cycles_per_us():
+    """Rate of the counter torch.cuda._sleep spins on, in cycles per us
+    (measured once with events around a sleep of known length)."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cycles = 2_000_000
+    torch.cuda._sleep(cycles // 10)          # first call: module load
+    e0.record()
+    torch.cuda._sleep(cycles)
+    e1.record()
+    torch.cuda.synchronize()
+    return cycles / max(e0.elapsed_time(e1) * 1e3, 1.0)
+
+
+def timed(fn, call_args, steps, warmup, stream, windows=11):
+    """Time `steps` back-to-back calls of fn(*call_args) in each of `windows`
+    windows.  A window: synchronise; hold the stream with a sleep kernel long
+    enough for the host to queue every call of the window; record a start
+    event on the stream; the `steps` calls; a stop event; synchronise.  The
+    events then bracket the GPU running exactly `steps` calls back to back,
+    whatever the host's own cost per call, which is reported separately.
+    Returns (median ms per call over the windows, min, max, host ms per
+    call to queue one call)."""
+    import statistics
     import torch
     rc = fn(*call_args)
     assert rc == 0, rc
     for _ in range(warmup):
         fn(*call_args)
     torch.cuda.synchronize()
+    rate = sleep_cycles_per_us()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
+    per, host = [], []
+    hold_us = 200.0 + 15.0 * steps
+    for _ in range(windows):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(hold_us * rate))      # on the current stream (= `stream`)
+        start.record(stream)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn(*call_args)
+        t1 = time.perf_counter()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        per.append(start.elapsed_time(stop) / steps)
+        host.append((t1 - t0) * 1e3 / steps)
+    return statistics.median(per), min(per), max(per), statistics.median(host)
+
+
+def timed_cold(fn, call_args, stream, launches=11, scrub_mib=1024):
+    """Single calls timed with events after writing a scrub buffer larger
+    than every cache (L2 and the 256 MB MALL): the inputs come from HBM.
+    Returns (median us, min us)."""
+    import statistics
+    import torch
+    scrub = torch.empty(scrub_mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    us = []
+    for i in range(launches):
+        scrub.fill_(float(i))
+        e0.record(stream)
         fn(*call_args)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(stop) / steps, wall * 1e3 / steps
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3)
+    del scrub
+    return statistics.median(us), min(us)
 
 
 def main():
@@ -281,15 +340,21 @@ def main():
         plan = {"tile_id": -2, "BM": 64, "BN": 192, "BK": 64, "loader": -1, "splits": None,
                 "grid": None, "workspace_bytes": need}
 
-    ms_step, wall_ms = timed(fn, call_args, args.steps, args.warmup, stream)
+    ms_step, ms_min, ms_max, host_ms = timed(fn, call_args, args.steps, args.warmup, stream,
+                                             args.windows)
     assert abi.conv2d_fwd_status(sptr) == 0
     if dgrad:
         # the implicit-GEMM kernel alone, on the weights the steps left in wt
         gemm_args = (x.data_ptr(), wt.data_ptr(), None) + gemm + (wl.dtype, out.data_ptr(), sptr)
-        ms_gemm, _ = timed(lib.conv2d_fwd, gemm_args, args.steps, args.warmup, stream)
+        ms_gemm = timed(lib.conv2d_fwd, gemm_args, args.steps, args.warmup, stream, args.windows)[0]
         assert abi.conv2d_fwd_status(sptr) == 0
     else:
         ms_gemm = ms_step
+    cold = None
+    if args.cold:
+        cold_med, cold_min = timed_cold(fn, call_args, stream)
+        cold = {"median_us": round(cold_med, 3), "min_us": round(cold_min, 3), "launches": 11,
+                "scrub_bytes": 1 << 30}
 
     flops = 2 * M * wl.OC * K          # = 2*N*H*W*IC*OC*KH*KW for the stride-1 data backward
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -338,11 +403,16 @@ def main():
                             if k in plan}},
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
-        "host_wall_ms_per_step": round(wall_ms, 6),
+        "windows": {"count": args.windows, "steps_each": args.steps,
+                    "median_ms_per_step": round(ms_step, 6), "min_ms_per_step": round(ms_min, 6),
+                    "max_ms_per_step": round(ms_max, 6)},
+        "host_ms_to_queue_a_step": round(host_ms, 6),
         "kernel_sources": ksrc,
     }
     if dgrad:
         line["gemm_ms"] = round(ms_gemm, 6)
+    if cold is not None:
+        line["cold_single_call"] = cold
     if tuned is not None:
         line["autotune"] = tuned
     if args.cpu_seconds > 0:

@@ -18,15 +18,38 @@ from . import abi
 from .abi import (CONVIMG_BF16, CONVIMG_FP32, LibraryMissing, conv2d_bwd_data,
                   conv2d_bwd_data_weights, conv2d_bwd_weight, conv2d_bwd_weight_workspace,
                   conv2d_fwd, conv2d_fwd_autotune, conv2d_fwd_autotune_clear, conv2d_fwd_force,
-                  conv2d_fwd_nchw, conv2d_fwd_nchw_workspace, conv2d_fwd_num_tiles, conv2d_fwd_out_dim, conv2d_fwd_plan,
-                  conv2d_fwd_status, conv2d_release, conv2d_strerror)
+                  conv2d_fwd_nchw, conv2d_fwd_nchw_workspace, conv2d_fwd_num_tiles, conv2d_fwd_out_dim,
+                  conv2d_fwd_plan, conv2d_fwd_status, conv2d_fwd_test_spin_limit, conv2d_release,
+                  conv2d_strerror)
 
 __all__ = ["abi", "conv2d_nhwc", "conv2d_bwd_data_nhwc", "conv2d_bwd_weight_nhwc",
            "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
            "conv2d_bwd_weight_workspace", "conv2d_fwd", "conv2d_fwd_autotune",
            "conv2d_fwd_autotune_clear", "conv2d_fwd_nchw", "conv2d_fwd_nchw_workspace", "conv2d_nchw",
            "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerror", "conv2d_fwd_force",
-           "conv2d_fwd_num_tiles", "conv2d_fwd_status", "conv2d_release", "CONVIMG_BF16", "CONVIMG_FP32", "LibraryMissing"]
+           "conv2d_fwd_num_tiles", "conv2d_fwd_status", "conv2d_fwd_test_spin_limit", "conv2d_release", "CONVIMG_BF16", "CONVIMG_FP32", "LibraryMissing"]
+
+
+def _stream_of(stream, device):
+    """(raw stream pointer, whether it is torch's current stream on device)."""
+    import torch
+
+    cur = torch.cuda.current_stream(device).cuda_stream
+    if stream is None:
+        return cur, True
+    return stream, stream == cur
+
+
+def _keep_for_stream(tensors, stream, device):
+    """Buffers allocated here on torch's current stream but used by work on
+    another stream: tell the caching allocator, so that it does not hand
+    their memory out again until that stream has run the work."""
+    import torch
+
+    ext = torch.cuda.ExternalStream(stream, device=device)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(ext)
 
 
 def _dtype_of(a, b, what):
@@ -66,19 +89,22 @@ def conv2d_nhwc(x, w, bias=None, stride=1, pad=0, dilation=1, out=None, stream=N
     OW = conv2d_fwd_out_dim(W, KW, stride, pad, dilation)
     if OH <= 0 or OW <= 0:
         raise ValueError("no output pixel for this shape")
+    fresh = []
     if out is None:
         out = torch.empty((N, OH, OW, OC), dtype=torch.float32, device=x.device)
+        fresh.append(out)
     elif (tuple(out.shape) != (N, OH, OW, OC) or out.dtype != torch.float32
           or not out.is_contiguous() or not out.is_cuda):
         raise ValueError("out must be a contiguous float32 [N,OH,OW,OC] device tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
+    stream, current = _stream_of(stream, x.device)
     with torch.cuda.device(x.device):
         rc = conv2d_fwd(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
                         N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out.data_ptr(),
                         stream)
     if rc != 0:
         raise RuntimeError("conv2d_fwd failed: %s (status %d)" % (conv2d_strerror(rc), rc))
+    if not current:
+        _keep_for_stream(fresh, stream, x.device)
     return out
 
 
@@ -107,23 +133,27 @@ def conv2d_bwd_data_nhwc(dy, w, H, W, stride=1, pad=0, dilation=1, dx=None, wt=N
     if (conv2d_fwd_out_dim(H, KH, stride, pad, dilation) != OH
             or conv2d_fwd_out_dim(W, KW, stride, pad, dilation) != OW):
         raise ValueError("dy's extent is not the forward output extent of H x W")
+    fresh = []
     if wt is None:
         wt = torch.empty(w.numel(), dtype=w.dtype, device=w.device)
+        fresh.append(wt)
     elif (wt.numel() != w.numel() or wt.dtype != w.dtype or not wt.is_contiguous()
           or not wt.is_cuda):
         raise ValueError("wt must be a contiguous device tensor of w's size and dtype")
     if dx is None:
         dx = torch.empty((N, H, W, IC), dtype=torch.float32, device=dy.device)
+        fresh.append(dx)
     elif (tuple(dx.shape) != (N, H, W, IC) or dx.dtype != torch.float32
           or not dx.is_contiguous() or not dx.is_cuda):
         raise ValueError("dx must be a contiguous float32 [N,H,W,IC] device tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(dy.device).cuda_stream
+    stream, current = _stream_of(stream, dy.device)
     with torch.cuda.device(dy.device):
         rc = conv2d_bwd_data(dy.data_ptr(), w.data_ptr(), N, H, W, IC, OC, KH, KW, stride, pad,
                              dilation, dtype, wt.data_ptr(), dx.data_ptr(), stream)
     if rc != 0:
         raise RuntimeError("conv2d_bwd_data failed: %s (status %d)" % (conv2d_strerror(rc), rc))
+    if not current:
+        _keep_for_stream(fresh, stream, dy.device)
     return dx
 
 
@@ -159,21 +189,25 @@ def conv2d_bwd_weight_nhwc(x, dy, KH, KW, stride=1, pad=0, dilation=1, dw=None, 
         if rc != 0:
             raise RuntimeError("conv2d_bwd_weight_workspace failed: %s (status %d)"
                                % (conv2d_strerror(rc), rc))
+        fresh = []
         if ws is None and need > 0:
             ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+            fresh.append(ws)
         if dw is None:
             dw = torch.empty((OC, KH, KW, IC), dtype=torch.float32, device=x.device)
+            fresh.append(dw)
         elif (tuple(dw.shape) != (OC, KH, KW, IC) or dw.dtype != torch.float32
               or not dw.is_contiguous() or not dw.is_cuda):
             raise ValueError("dw must be a contiguous float32 [OC,KH,KW,IC] device tensor")
-        if stream is None:
-            stream = torch.cuda.current_stream(x.device).cuda_stream
+        stream, current = _stream_of(stream, x.device)
         ws_ptr = ws.data_ptr() if ws is not None else None
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
         rc = conv2d_bwd_weight(x.data_ptr(), dy.data_ptr(), N, H, W, IC, OC, KH, KW, stride, pad,
                                dilation, CONVIMG_BF16, dw.data_ptr(), ws_ptr, ws_bytes, stream)
     if rc != 0:
         raise RuntimeError("conv2d_bwd_weight failed: %s (status %d)" % (conv2d_strerror(rc), rc))
+    if not current:
+        _keep_for_stream(fresh, stream, x.device)
     return dw
 
 
@@ -213,19 +247,23 @@ def conv2d_nchw(x, w, bias=None, stride=1, pad=0, dilation=1, out_dtype=None, ou
         if rc != 0:
             raise RuntimeError("conv2d_fwd_nchw_workspace failed: %s (status %d)"
                                % (conv2d_strerror(rc), rc))
+        fresh = []
         if ws is None:
             ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+            fresh.append(ws)
         if out is None:
             out = torch.empty((N, OC, OH, OW), dtype=out_dtype, device=x.device)
+            fresh.append(out)
         elif (tuple(out.shape) != (N, OC, OH, OW) or out.dtype != out_dtype
               or not out.is_contiguous() or not out.is_cuda):
             raise ValueError("out must be a contiguous [N,OC,OH,OW] device tensor of out_dtype")
-        if stream is None:
-            stream = torch.cuda.current_stream(x.device).cuda_stream
+        stream, current = _stream_of(stream, x.device)
         od = CONVIMG_BF16 if out_dtype == torch.bfloat16 else CONVIMG_FP32
         rc = conv2d_fwd_nchw(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
                              N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, od, out.data_ptr(),
                              ws.data_ptr(), ws.numel(), stream)
     if rc != 0:
         raise RuntimeError("conv2d_fwd_nchw failed: %s (status %d)" % (conv2d_strerror(rc), rc))
+    if not current:
+        _keep_for_stream(fresh, stream, x.device)
     return out

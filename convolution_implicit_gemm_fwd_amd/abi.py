@@ -45,7 +45,7 @@ EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerr
            "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_tile_kind", "conv2d_fwd_status",
            "conv2d_release", "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
            "conv2d_bwd_weight_workspace", "conv2d_fwd_autotune", "conv2d_fwd_autotune_clear",
-           "conv2d_fwd_nchw", "conv2d_fwd_nchw_workspace")
+           "conv2d_fwd_nchw", "conv2d_fwd_nchw_workspace", "conv2d_fwd_test_spin_limit")
 
 
 class convimg_plan(ctypes.Structure):
@@ -94,6 +94,8 @@ def load(path: str = LIB_PATH):
     lib.conv2d_fwd_tile_kind.restype = i
     lib.conv2d_fwd_status.argtypes = [vp]
     lib.conv2d_fwd_status.restype = i
+    lib.conv2d_fwd_test_spin_limit.argtypes = [i]
+    lib.conv2d_fwd_test_spin_limit.restype = i
     lib.conv2d_release.argtypes = []
     lib.conv2d_release.restype = None
     lib.conv2d_bwd_data.argtypes = [vp, vp] + [i] * 11 + [vp, vp, vp]
@@ -209,6 +211,12 @@ def conv2d_fwd_tile_kind(tile_id):
 
 def conv2d_fwd_status(stream):
     return load().conv2d_fwd_status(stream)
+
+
+def conv2d_fwd_test_spin_limit(iterations):
+    """Test knob: split-K wait bound in sleep iterations (< 1: default).
+    Returns the previous bound."""
+    return load().conv2d_fwd_test_spin_limit(iterations)
 
 
 def conv2d_release():

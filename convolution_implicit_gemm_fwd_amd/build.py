@@ -61,11 +61,27 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             print("\n".join(msgs))
 
     try:
+        # the translation units compile in parallel
+        procs = []
         for src, flags in UNITS:
             obj = os.path.join(PKG, os.path.basename(src) + ".%s.o" % tag)
             objs.append(obj)
             flags_c = [f for f in HIPCC_FLAGS if f != "-shared"]
-            run([hipcc(), *flags_c, *flags, *extra_flags, "-I", INCLUDE, "-c", src, "-o", obj])
+            cmd = [hipcc(), *flags_c, *flags, *extra_flags, "-I", INCLUDE, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                          text=True))
+        failed = []
+        for p in procs:
+            out, _ = p.communicate()
+            msgs = [ln for ln in out.splitlines() if noise not in ln]
+            if p.returncode != 0:
+                failed.append("\n".join(msgs))
+            elif verbose and msgs:
+                print("\n".join(msgs))
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
         tmp = LIB + ".tmp" + tag
         run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
         os.replace(tmp, LIB)

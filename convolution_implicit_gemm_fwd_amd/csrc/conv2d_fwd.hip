@@ -1,6 +1,6 @@
 // conv2d_fwd.hip -- the C ABI of libconvimg (declared in include/convimg.h):
 // argument checks, output extent, the tile plan, the split-K semaphore pool
-// and the kernel launch.  The kernels are in igemm_fwd.hpp.
+// and the kernel launches.  The kernels are in the igemm_*.hpp headers.
 #include "convimg.h"
 #include "igemm_image.hpp"
 #include "igemm_patch.hpp"
@@ -207,6 +207,7 @@ int lds_occupancy(int tile)
 }
 
 std::atomic<int> g_force_tile{-1}, g_force_splits{-1}, g_force_loader{-1};
+std::atomic<int> g_spin_limit{kSpinLimit};     // split-K wait bound (tests shorten it)
 
 bool log_enabled()
 {
@@ -262,6 +263,27 @@ int device_info(int dev, DeviceInfo **out)
     }
     *out = &it->second;
     return CONVIMG_OK;
+}
+
+// The current device and its facts.  The last device a host thread used is
+// remembered per thread, so the hot path takes no lock (entries of g_dev are
+// never removed, so the pointer stays valid).
+int current_device(int *dev, DeviceInfo **info)
+{
+    thread_local int t_dev = -1;
+    thread_local DeviceInfo *t_info = nullptr;
+    if (hipGetDevice(dev) != hipSuccess)
+        return CONVIMG_ERR_DEVICE;
+    if (*dev == t_dev && t_info != nullptr) {
+        *info = t_info;
+        return CONVIMG_OK;
+    }
+    const int rc = device_info(*dev, info);
+    if (rc == CONVIMG_OK) {
+        t_dev = *dev;
+        t_info = *info;
+    }
+    return rc;
 }
 
 // Split-K semaphores: one int per output tile plus a status word, per
@@ -1050,6 +1072,13 @@ int conv2d_fwd_force(int tile_id, int splits, int loader)
     return CONVIMG_OK;
 }
 
+int conv2d_fwd_test_spin_limit(int iterations)
+{
+    const int prev = g_spin_limit.load();
+    g_spin_limit.store(iterations < 1 ? kSpinLimit : iterations);
+    return prev;
+}
+
 int conv2d_fwd_plan(int N, int H, int W, int IC, int OC, int KH, int KW,
                     int stride, int pad, int dilation, int dtype, int num_cus,
                     convimg_plan *plan)
@@ -1079,9 +1108,22 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
 {
     if (!x || !w || !out)
         return CONVIMG_ERR_NULL;
-    // shape checks first: they need no device
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    const int rc_dev = current_device(&dev, &info);
     convimg_plan pl;
-    int rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, true, nullptr, &pl);
+    StripPlan sp;
+    WinPlan wnp;
+    ResPlan rsp;
+    ImgPlan imp;
+    // one plan per call: with the device's facts when there is a device,
+    // else host-only, so that argument errors still come before the device
+    // error
+    const bool aligned = (((uintptr_t)x | (uintptr_t)w) & 15) == 0;
+    int rc = rc_dev == CONVIMG_OK
+        ? make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned,
+                    info->occ, &pl, &sp, &wnp, &rsp, &imp)
+        : make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, true, nullptr, &pl);
     if (rc != CONVIMG_OK)
         return rc;
     const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
@@ -1091,23 +1133,8 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     if (overlaps(out, no, x, nx) || overlaps(out, no, w, nw)
         || (bias && overlaps(out, no, bias, (size_t)OC * 4)))
         return CONVIMG_ERR_ALIAS;
-
-    int dev = 0;
-    DeviceInfo *info = nullptr;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return CONVIMG_ERR_DEVICE;
-    rc = device_info(dev, &info);
-    if (rc != CONVIMG_OK)
-        return rc;
-    const bool aligned = (((uintptr_t)x | (uintptr_t)w) & 15) == 0;
-    StripPlan sp;
-    WinPlan wnp;
-    ResPlan rsp;
-    ImgPlan imp;
-    rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, info->num_cus, aligned,
-                   info->occ, &pl, &sp, &wnp, &rsp, &imp);
-    if (rc != CONVIMG_OK)
-        return rc;
+    if (rc_dev != CONVIMG_OK)
+        return rc_dev;
 
     ConvArgs a;
     a.x = x;
@@ -1115,9 +1142,12 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.bias = bias;
     a.out = out;
     a.sem = nullptr;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     a.x_bytes = (unsigned)(nx < 0xffffffffu ? nx : 0xffffffffu);
     a.w_bytes = (unsigned)(nw < 0xffffffffu ? nw : 0xffffffffu);
-    a.out_bytes = (unsigned)(no < 0xffffffffu ? no : 0xffffffffu);
+    // masked output lanes store to offset kOutOfRange: it must lie past the
+    // extent the buffer resource allows (larger outputs use 64-bit stores)
+    a.out_bytes = (unsigned)(no < (size_t)kOutOfRange ? no : (size_t)kOutOfRange);
     a.N = N;
     a.H = H;
     a.W = W;

@@ -40,7 +40,7 @@ enum : int { kLoaderTap = 0, kLoaderVec8 = 1, kLoaderScalar = 2 };
 
 constexpr int kBK = 64;              // K per tile (bf16 kernels)
 constexpr int kChunks = kBK / 8;     // 16-byte chunks per LDS row
-constexpr int kSpinLimit = 1 << 20;  // split-K wait bound (iterations of s_sleep)
+constexpr int kSpinLimit = 1 << 20;  // split-K wait bound (iterations of s_sleep), unless a test shortens it
 constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset past every buffer addressed so
 constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format
 constexpr int kCoherent = 16;                  // cache policy sc1: agent-coherent access
@@ -59,8 +59,9 @@ struct ConvArgs {
     const float *bias;
     float *out;
     int *sem;        // split-K: one int per output tile, then one status word
+    int spin_limit;  // split-K: iterations a workgroup waits for its turn before it gives up
     unsigned x_bytes, w_bytes;  // buffer extents for bounds-checked loads
-    unsigned out_bytes;         // extent of out (split-K only: below 2^31)
+    unsigned out_bytes;         // extent of out, at most kOutOfRange (buffer stores past it are dropped)
     int N, H, W, IC, OC, KH, KW, stride, pad, dil;
     int OH, OW, M, K;
     int tiles_m, tiles_n, ktiles, splits;
@@ -135,6 +136,14 @@ __device__ __forceinline__ TileCoord tile_coord(const ConvArgs &a)
     return t;
 }
 
+// Buffer stores to out are used only while out ends at or below
+// kOutOfRange: masked lanes store to that offset, which must then lie past
+// the buffer (the host clamps out_bytes to it as well).
+__device__ __forceinline__ bool out_fits_buffer(const ConvArgs &a)
+{
+    return (unsigned long long)a.M * (unsigned)a.OC * 4ull <= (unsigned long long)kOutOfRange;
+}
+
 // Row of value v of an S x S accumulator block, relative to the lane's row0.
 template <int S>
 __device__ __forceinline__ int acc_row(int v)
@@ -179,9 +188,10 @@ __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[
 {
     constexpr int NV = S * S / 64;      // results per lane per block
     if (a.splits == 1) {
-        // buffer stores (the output policy) while every byte offset fits 32
-        // bits, else plain 64-bit addressed stores
-        const bool small = (unsigned long long)a.M * (unsigned)a.OC * 4ull < 0xffffffffull;
+        // buffer stores (the output policy) while out ends at or below the
+        // out-of-range offset that masked lanes store to, else plain 64-bit
+        // addressed stores
+        const bool small = out_fits_buffer(a);
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -204,18 +214,39 @@ __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[
     }
 
     int *sem = a.sem + tile;
+    int late = 0;
     if (threadIdx.x == 0) {
         int spins = 0;
         while (__hip_atomic_load(sem, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != split) {
             __builtin_amdgcn_s_sleep(2);
-            if (++spins == kSpinLimit) {
+            if (++spins >= a.spin_limit) {
                 const int tiles = a.tiles_m * a.tiles_n;
                 __hip_atomic_store(a.sem + tiles, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                late = 1;
                 break;
             }
         }
     }
-    __syncthreads();
+    // A split whose wait gave up must not add its partial while the tile's
+    // turn holder may be writing it: it poisons the tile with NaN instead
+    // (so the failure shows in out without a status poll) and leaves the
+    // semaphore as it is; conv2d_fwd_status reports the timeout and resets
+    // the semaphores.
+    if (__syncthreads_or(late)) {
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
+        const unsigned nan = 0x7fc00000u;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int m = row0 + i * S + acc_row<S>(v), oc = col0 + j * S;
+                    const unsigned off = (m < a.M && oc < a.OC) ? 4u * (unsigned)(m * a.OC + oc) : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32(nan, ro, off, 0, kCoherent);
+                }
+        return;
+    }
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -276,7 +307,7 @@ __device__ __forceinline__ void store_tile_vec(const ConvArgs &a, const AccT (&a
     const int lane = threadIdx.x & 63;
     const int r0 = acc_row0<S>(lane), c0 = acc_col0<S>(lane);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
-    const bool small = (unsigned long long)a.M * (unsigned)a.OC * 4ull < 0xffffffffull;
+    const bool small = out_fits_buffer(a);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -291,7 +322,7 @@ __device__ __forceinline__ void store_tile_vec(const ConvArgs &a, const AccT (&a
             const floatx4_t val = *(const floatx4_t *)(scratch + row * STRIDE + c4);
             const int m = m_wave0 + i * S + row, oc = n_wave0 + c4;
             if (m < a.M && small) {
-                // (the output policy; byte offsets fit 32 bits)
+                // (the output policy; out ends at or below kOutOfRange)
                 const unsigned off = 4u * (unsigned)(m * a.OC + oc);
                 if (oc + 3 < a.OC) {
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), ro, off, 0, kOutAux);

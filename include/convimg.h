@@ -94,6 +94,14 @@ typedef struct convimg_plan {
  * untouched and queue nothing.  A fault inside the kernel surfaces at the
  * caller's next synchronisation, as for any HIP kernel.  Calls on different
  * streams may run concurrently; calls on one stream run in order.
+ *
+ * Split-K (plans with splits > 1): the splits of an output tile take turns
+ * on a semaphore, with a bounded wait.  The plan keeps every split of every
+ * tile resident at once, so the wait always ends in practice; if it ever
+ * gives up, that split writes NaN over its tile instead of adding its
+ * partial sums, so `out` is invalid and visibly so, and the stream's
+ * semaphores stay out of step until conv2d_fwd_status() is called, which
+ * reports CONVIMG_ERR_TIMEOUT and resets them.
  */
 int conv2d_fwd(const void *x, const void *w, const float *bias,
                int N, int H, int W, int IC, int OC, int KH, int KW,
@@ -101,17 +109,29 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
                float *out, hipStream_t stream);
 
 /* Output extent along one axis, or -1 when an argument is out of range or no
- * window fits.  Host only. */
+ * window fits.  Host only.  The pages give no formula for it: this is the
+ * floor formula quoted under conv2d_fwd (a trailing input row or column that
+ * does not complete a window is not used), the usual reading of the burn
+ * conv options' stride, padding and dilation (burn-cubecl
+ * "kernel/conv/base.rs" listing, ConvOptions). */
 int conv2d_fwd_out_dim(int in, int k, int stride, int pad, int dilation);
 
 /* The plan conv2d_fwd would use for this problem with 16-byte aligned
  * buffers, on a device with `num_cus` compute units (num_cus <= 0: query the
- * current device).  Host only when num_cus > 0.  Returns a status code. */
+ * current device).  Host only when num_cus > 0.  Returns a status code.
+ * The pages choose among their kernels by shape (burn PR "[Optimization]
+ * Implicit gemm rewrite", Changes: small and large K behave differently;
+ * burn PR "Introduce autotuning to conv2d and conv_transpose2d with a new
+ * im2col/GEMM algorithm", Changes: the implicit GEMM only where its
+ * divisibility conditions hold); this reports this library's own choice. */
 int conv2d_fwd_plan(int N, int H, int W, int IC, int OC, int KH, int KW,
                     int stride, int pad, int dilation, int dtype, int num_cus,
                     convimg_plan *plan);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL).  Library plumbing: the
+ * pages define no status codes (burn-cubecl "kernel/conv/base.rs" listing
+ * returns a ConvSetupError for setups it cannot run, the role these codes
+ * play here). */
 const char *conv2d_strerror(int status);
 
 /* Test knob: force the tile (-1 = automatic), the split-K factor (-1 =
@@ -122,7 +142,10 @@ const char *conv2d_strerror(int status);
  * CONVIMG_ERR_SHAPE for an unknown tile or loader. */
 int conv2d_fwd_force(int tile_id, int splits, int loader);
 
-/* Number of entries in the tile table (valid tile_id values are 0..n-1). */
+/* Number of entries in the tile table (valid tile_id values are 0..n-1).
+ * The table is this library's tile/occupancy table per shape class; the
+ * pages' kernels pick tile sizes per problem the same way (burn PR
+ * "[Optimization] Implicit gemm rewrite", Changes). */
 int conv2d_fwd_num_tiles(void);
 
 /* Kernel family of a tile table entry, or -1 for an unknown tile_id:
@@ -162,8 +185,18 @@ int conv2d_fwd_tile_kind(int tile_id);
 
 /* Split-K health on `stream`: CONVIMG_OK, or CONVIMG_ERR_TIMEOUT if a
  * workgroup gave up waiting for its turn since the last call of this
- * function (the flag is then cleared).  Synchronises the stream. */
+ * function (the flag and the stream's semaphores are then reset).
+ * Synchronises the stream.  The turn-taking is that of nvFuser issue
+ * "Split-K matmul is slow even for few partitions", section "Eliminating
+ * the workspace" (blocks serialised by a semaphore); the bounded wait and
+ * this report are this library's own. */
 int conv2d_fwd_status(hipStream_t stream);
+
+/* Test knob: the number of sleep iterations a split-K workgroup waits for
+ * its turn before it gives up (iterations < 1: the default, 2^20), for
+ * later calls in this process.  Lets tests force the timeout path from the
+ * host.  Returns the previous bound. */
+int conv2d_fwd_test_spin_limit(int iterations);
 
 /* NCHW tensors (burn-cubecl "kernel/conv/base.rs" listing: its NCHW entry
  * points permute the input to channels-last and the weights to
@@ -311,7 +344,9 @@ int conv2d_bwd_weight_workspace(int N, int H, int W, int IC, int OC, int KH, int
                                 int dilation, int dtype, size_t *bytes);
 
 /* Free every library-owned buffer (synchronising each device that has
- * one).  Later calls allocate again as needed. */
+ * one).  Later calls allocate again as needed.  Library plumbing with no
+ * counterpart on the pages: the only library-owned buffers are the split-K
+ * semaphores of conv2d_fwd. */
 void conv2d_release(void);
 
 #ifdef __cplusplus

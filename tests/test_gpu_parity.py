@@ -325,3 +325,77 @@ def test_largest_int32_output_sampled():
     check(rows, yref, S, "int32 edge")
     del out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("OC", [160, 158], ids=["OC160-16B-stores", "OC158-dword-stores"])
+@pytest.mark.parametrize("tile_kind", [abi.CONVIMG_KIND_REGS, abi.CONVIMG_KIND_PIPE])
+def test_output_between_2_and_4_gib_sampled(OC, tile_kind):
+    """An output of 2..4 GiB on the single-split kernels.  Masked lanes (the
+    last 64-channel tile is partly past OC) store to the out-of-range buffer
+    offset 2^31, which lies inside such an output: the library must take the
+    64-bit store path there.  Checked on sampled pixels, always including
+    those around flat element 2^29 (byte offset 2^31) and the last one."""
+    N, H, W, IC = 64, 256, 256, 8
+    wl = shape(N, H, W, IC, OC, 3, 3, 1, 1, 1, name="2-4 GiB out")
+    M = N * H * W
+    assert 2 ** 31 < M * OC * 4 < 2 ** 32
+    tile = [t for t in range(abi.conv2d_fwd_num_tiles())
+            if abi.conv2d_fwd_tile_kind(t) == tile_kind and t in (0, 4)][0]   # 128x64 tiles
+    inp = make_inputs(wl, seed=17)
+    x, w, b = to_device(inp)
+    out = torch.full((M * OC,), float("nan"), dtype=torch.float32, device="cuda")
+    abi.conv2d_fwd_force(tile, 1, abi.CONVIMG_LOADER_VEC8)
+    try:
+        rc, plan = abi.conv2d_fwd_plan(N, H, W, IC, OC, 3, 3, 1, 1, 1, BF16, 0)
+        assert plan["tile_id"] == tile and plan["splits"] == 1, plan
+        log("2-4 GiB OC=%d plan %s" % (OC, plan))
+        rc = abi.conv2d_fwd(x.data_ptr(), w.data_ptr(), b.data_ptr(), N, H, W, IC, OC, 3, 3,
+                            1, 1, 1, BF16, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, abi.conv2d_strerror(rc)
+        torch.cuda.synchronize()
+    finally:
+        abi.conv2d_fwd_force(-1, -1, -1)
+    hot = (2 ** 29) // OC
+    rng = np.random.default_rng(3)
+    pix = np.unique(np.concatenate([[0, hot - 1, hot, hot + 1, M - 1], rng.integers(0, M, 100)]))
+    rows = out.view(M, OC)[torch.from_numpy(pix).cuda()].cpu().numpy()
+    yref, S = oracle.conv2d_fwd_pixels(inp.x32, inp.w32, inp.bias, 1, 1, 1, pix)
+    check(rows, yref, S, "2-4 GiB output OC=%d" % OC)
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_splitk_timeout_poisons_and_resets():
+    """The split-K wait forced to give up from the host (a one-iteration
+    bound): a split that gives up writes NaN over its tile instead of adding
+    its partial, conv2d_fwd_status reports the timeout and resets the
+    semaphores, and the next call with the normal bound is correct.  (Whether
+    a split gives up depends on timing; either outcome is checked.)"""
+    wl = WORKLOADS["largek"]
+    inp = make_inputs(wl, seed=0)
+    x, w, b = to_device(inp)
+    sptr = torch.cuda.current_stream().cuda_stream
+    yref, S = oracle_full(inp, wl)
+    abi.conv2d_fwd_force(*SPLITK_FORCE)
+    prev = abi.conv2d_fwd_test_spin_limit(1)
+    try:
+        out, dims = run_hip(wl, x, w, b, wl.dtype)
+        torch.cuda.synchronize()
+        abi.conv2d_fwd_test_spin_limit(prev)
+        status = abi.conv2d_fwd_status(sptr)
+        OH, OW, n_out = dims
+        y = out[:n_out].cpu().numpy()
+        log("forced timeout: status %d, NaN outputs %d" % (status, int(np.isnan(y).sum())))
+        if status == abi.CONVIMG_OK:
+            check(y.reshape(wl.N, OH, OW, wl.OC), yref, S, "no split gave up")
+        else:
+            assert status == abi.CONVIMG_ERR_TIMEOUT
+            assert np.isnan(y).any(), "a split gave up but out shows no poisoned tile"
+        assert abi.conv2d_fwd_status(sptr) == abi.CONVIMG_OK
+        out, dims = run_hip(wl, x, w, b, wl.dtype)
+        y = fetch(out, dims, wl)
+    finally:
+        abi.conv2d_fwd_test_spin_limit(0)
+        abi.conv2d_fwd_force(-1, -1, -1)
+    assert abi.conv2d_fwd_status(sptr) == abi.CONVIMG_OK
+    check(y, yref, S, "after the reset")
