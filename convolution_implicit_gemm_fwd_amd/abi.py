@@ -26,6 +26,7 @@ CONVIMG_ERR_DEVICE = 8
 CONVIMG_ERR_TIMEOUT = 9
 CONVIMG_ERR_UNSUPPORTED = 10
 CONVIMG_ERR_WORKSPACE = 11
+CONVIMG_ERR_SCRATCH = 12
 
 CONVIMG_LOADER_TAP = 0
 CONVIMG_LOADER_VEC8 = 1
@@ -45,7 +46,8 @@ EXPORTS = ("conv2d_fwd", "conv2d_fwd_out_dim", "conv2d_fwd_plan", "conv2d_strerr
            "conv2d_fwd_force", "conv2d_fwd_num_tiles", "conv2d_fwd_tile_kind", "conv2d_fwd_status",
            "conv2d_release", "conv2d_bwd_data", "conv2d_bwd_data_weights", "conv2d_bwd_weight",
            "conv2d_bwd_weight_workspace", "conv2d_fwd_autotune", "conv2d_fwd_autotune_clear",
-           "conv2d_fwd_nchw", "conv2d_fwd_nchw_workspace", "conv2d_fwd_test_spin_limit")
+           "conv2d_fwd_nchw", "conv2d_fwd_nchw_workspace", "conv2d_fwd_test_spin_limit",
+           "conv2d_fwd_noalloc")
 
 
 class convimg_plan(ctypes.Structure):
@@ -80,6 +82,8 @@ def load(path: str = LIB_PATH):
     i, vp = ctypes.c_int, ctypes.c_void_p
     lib.conv2d_fwd.argtypes = [vp, vp, vp] + [i] * 11 + [vp, vp]
     lib.conv2d_fwd.restype = i
+    lib.conv2d_fwd_noalloc.argtypes = [vp, vp, vp] + [i] * 11 + [vp, vp]
+    lib.conv2d_fwd_noalloc.restype = i
     lib.conv2d_fwd_out_dim.argtypes = [i] * 5
     lib.conv2d_fwd_out_dim.restype = i
     lib.conv2d_fwd_plan.argtypes = [i] * 12 + [ctypes.POINTER(convimg_plan)]
@@ -123,6 +127,13 @@ def conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype
     """Raw C call: pointers are integers (device addresses), returns a status."""
     return load().conv2d_fwd(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation,
                              dtype, out, stream)
+
+
+def conv2d_fwd_noalloc(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out, stream):
+    """Raw C call of the entry point that allocates nothing (same arguments
+    as conv2d_fwd), returns a status."""
+    return load().conv2d_fwd_noalloc(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation,
+                                     dtype, out, stream)
 
 
 def conv2d_bwd_data(dy, w, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, wt, dx, stream):

@@ -1036,6 +1036,45 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Where the split-K semaphores of a call come from.
+enum SemSource { kSemPool, kSemScratch };
+
+int fwd_call(const void *x, const void *w, const float *bias,
+             int N, int H, int W, int IC, int OC, int KH, int KW,
+             int stride, int pad, int dilation, int dtype,
+             float *out, hipStream_t stream, SemSource sems);
+
+}  // namespace
+
+// Scratch of conv2d_fwd_noalloc: its split-K semaphores (one int per output
+// tile and a status word), a fixed array in each device's memory, so the
+// entry point never allocates.  The plan keeps tiles x splits within what is
+// resident at once (a few thousand workgroups on this chip), far below this.
+constexpr int kScratchInts = 4096;
+static __device__ __align__(256) int scratch[kScratchInts];
+
+namespace {
+
+// Device address of `scratch` on device `dev` (the current device), looked
+// up once per device with that device current and kept: in host code the
+// array's name is only a stand-in for the symbol, never a device address.
+std::mutex g_scratch_mu;
+std::map<int, int *> g_scratch;
+
+int scratch_of(int dev, int **out)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        int *ptr = nullptr;
+        if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return CONVIMG_ERR_DEVICE;
+        it = g_scratch.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return CONVIMG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1072,13 +1111,6 @@ int conv2d_fwd_force(int tile_id, int splits, int loader)
     return CONVIMG_OK;
 }
 
-int conv2d_fwd_test_spin_limit(int iterations)
-{
-    const int prev = g_spin_limit.load();
-    g_spin_limit.store(iterations < 1 ? kSpinLimit : iterations);
-    return prev;
-}
-
 int conv2d_fwd_plan(int N, int H, int W, int IC, int OC, int KH, int KW,
                     int stride, int pad, int dilation, int dtype, int num_cus,
                     convimg_plan *plan)
@@ -1105,6 +1137,39 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
                int N, int H, int W, int IC, int OC, int KH, int KW,
                int stride, int pad, int dilation, int dtype,
                float *out, hipStream_t stream)
+{
+    return fwd_call(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out, stream,
+                    kSemPool);
+}
+
+int conv2d_fwd_noalloc(const void *x, const void *w, const float *bias,
+                       int N, int H, int W, int IC, int OC, int KH, int KW,
+                       int stride, int pad, int dilation, int dtype,
+                       float *out, hipStream_t stream)
+{
+    return fwd_call(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, out, stream,
+                    kSemScratch);
+}
+
+int conv2d_fwd_test_spin_limit(int iterations)
+{
+    const int prev = g_spin_limit.load();
+    g_spin_limit.store(iterations < 1 ? kSpinLimit : iterations);
+    return prev;
+}
+
+}  // extern "C"
+
+namespace {
+
+// conv2d_fwd and conv2d_fwd_noalloc: checks, plan, launch.  `sems` says
+// where split-K semaphores come from: the library's per-stream pool (may
+// allocate on first use) or the device's static scratch array (never
+// allocates).
+int fwd_call(const void *x, const void *w, const float *bias,
+             int N, int H, int W, int IC, int OC, int KH, int KW,
+             int stride, int pad, int dilation, int dtype,
+             float *out, hipStream_t stream, SemSource sems)
 {
     if (!x || !w || !out)
         return CONVIMG_ERR_NULL;
@@ -1191,9 +1256,23 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
     a.lds_rows = pl.tile_id >= 0 && kTiles[pl.tile_id].kind == kResident ? rsp.lds_rows : wnp.lds_rows;
 
     if (pl.splits > 1) {
-        rc = get_semaphores(dev, stream, pl.tiles_m * pl.tiles_n + 1, &a.sem);
-        if (rc != CONVIMG_OK)
-            return rc;
+        const int need = pl.tiles_m * pl.tiles_n + 1;
+        if (sems == kSemScratch) {
+            // the device's static array: cleared here, since every call on
+            // this device shares it and a call that timed out leaves it dirty
+            if (need > kScratchInts)
+                return CONVIMG_ERR_SCRATCH;
+            rc = scratch_of(dev, &a.sem);
+            if (rc != CONVIMG_OK)
+                return rc;
+            hipLaunchKernelGGL(fill_zero_i32, dim3((need + 255) / 256), dim3(256), 0, stream, a.sem, need);
+            if (hipGetLastError() != hipSuccess)
+                return CONVIMG_ERR_LAUNCH;
+        } else {
+            rc = get_semaphores(dev, stream, need, &a.sem);
+            if (rc != CONVIMG_OK)
+                return rc;
+        }
     }
     if (log_enabled())
         std::fprintf(stderr,
@@ -1223,6 +1302,10 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
         return CONVIMG_ERR_LAUNCH;
     return CONVIMG_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int conv2d_fwd_nchw_workspace(int N, int H, int W, int IC, int OC, int KH, int KW, int stride, int pad,
                               int dilation, int dtype, size_t *bytes)
@@ -1661,6 +1744,8 @@ const char *conv2d_strerror(int status)
         return "unsupported by the backward passes (data: stride 1, KH == KW, pad <= dilation*(KH-1); "
                "weights: bf16 storage)";
     case CONVIMG_ERR_WORKSPACE: return "workspace smaller than conv2d_bwd_weight_workspace reports";
+    case CONVIMG_ERR_SCRATCH:
+        return "conv2d_fwd_noalloc: the plan needs more split-K semaphores than its fixed scratch holds";
     default: return "unknown status";
     }
 }

@@ -50,6 +50,7 @@ extern "C" {
 #define CONVIMG_ERR_UNSUPPORTED 10 /* conv2d_bwd_data: stride != 1, KH != KW or pad > dilation*(KH-1);
                                       conv2d_bwd_weight: fp32 storage */
 #define CONVIMG_ERR_WORKSPACE 11   /* conv2d_bwd_weight: ws_bytes below what it needs */
+#define CONVIMG_ERR_SCRATCH 12     /* conv2d_fwd_noalloc: the plan needs more semaphores than its scratch holds */
 
 /* Loader variants used by the plan. */
 #define CONVIMG_LOADER_TAP    0  /* IC % 64 == 0: one 64-channel slice of one tap per K tile, 16-byte loads */
@@ -107,6 +108,25 @@ int conv2d_fwd(const void *x, const void *w, const float *bias,
                int N, int H, int W, int IC, int OC, int KH, int KW,
                int stride, int pad, int dilation, int dtype,
                float *out, hipStream_t stream);
+
+/* conv2d_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, plan, kernels and result as conv2d_fwd; it calls no
+ * hipMalloc, hipFree or other allocating routine.  Its only scratch, the
+ * split-K semaphores, lives in a fixed array of 4096 int32 in each device's
+ * memory (held until the process ends), cleared by a small kernel on
+ * `stream` at the start of every split-K call.  Every call on one device
+ * shares that array: calls that overlap on one device (different streams
+ * running at once) race and must not be made.  A split-K wait that gives
+ * up shows only as NaN tiles in `out` (conv2d_fwd_status does not cover
+ * this entry point).  Errors: those of conv2d_fwd, and CONVIMG_ERR_SCRATCH
+ * (before any work is queued) if the plan would need more than 4095
+ * semaphores, which the plan's residency cap keeps from happening on
+ * MI355X. */
+int conv2d_fwd_noalloc(const void *x, const void *w, const float *bias,
+                       int N, int H, int W, int IC, int OC, int KH, int KW,
+                       int stride, int pad, int dilation, int dtype,
+                       float *out, hipStream_t stream);
 
 /* Output extent along one axis, or -1 when an argument is out of range or no
  * window fits.  Host only.  The pages give no formula for it: this is the
