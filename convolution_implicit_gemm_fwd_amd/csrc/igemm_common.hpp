@@ -9,8 +9,12 @@
 //
 // Common to every bf16 kernel:
 //   * LDS rows are 64 bf16 = 8 chunks of 16 bytes; logical chunk c of row r
-//     is stored at position c ^ (r & 7), so the eight lanes that read one
-//     chunk column of eight consecutive rows hit eight distinct 4-bank groups;
+//     is stored at position c ^ ((r >> 1) & 7).  A 128-bit LDS read serves
+//     16 lanes a clock, and the MFMA fragment reads give those 16 lanes one
+//     chunk column of 16 consecutive rows; a row covers half the banks (8
+//     of the 16 4-bank groups, by the row's parity), so among the 8 rows of
+//     each parity the positions must all differ, which (r >> 1) & 7 gives
+//     (r & 7 repeats every 8 rows: a 2-way conflict on every read);
 //   * MFMA, two shapes.  v_mfma_f32_16x16x32_bf16: lane l feeds row (l & 15)
 //     of a 16x16 block with the 8 consecutive k of chunk (l >> 4) of each
 //     32-wide k step; its 4 results are column (l & 15), rows 4*(l >> 4) + v.
@@ -100,7 +104,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg)
 
 __device__ __forceinline__ int swz(int row, int chunk)
 {
-    return row * kChunks + (chunk ^ (row & 7));
+    return row * kChunks + (chunk ^ ((row >> 1) & 7));
 }
 
 struct TileCoord {
@@ -134,6 +138,14 @@ __device__ __forceinline__ TileCoord tile_coord(const ConvArgs &a)
     t.kt_begin = (int)(((long long)t.split * a.ktiles) / a.splits);
     t.kt_end = (int)(((long long)(t.split + 1) * a.ktiles) / a.splits);
     return t;
+}
+
+// Bits of a float for a dword store.  Takes the value, not a vector
+// element: __builtin_bit_cast of an ext_vector element lvalue (v[e]) reads
+// element 0 with this compiler, whatever e is.
+__device__ __forceinline__ unsigned f32_bits(float f)
+{
+    return __builtin_bit_cast(unsigned, f);
 }
 
 // Buffer stores to out are used only while out ends at or below
@@ -213,9 +225,12 @@ __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[
         return;
     }
 
+    // Every wave waits for the turn itself (its first lane polls), so no
+    // workgroup-wide vote is needed (__syncthreads_or takes static LDS,
+    // which measured 4 % slower launches of the kernels that use this).
     int *sem = a.sem + tile;
     int late = 0;
-    if (threadIdx.x == 0) {
+    if ((threadIdx.x & 63) == 0) {
         int spins = 0;
         while (__hip_atomic_load(sem, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != split) {
             __builtin_amdgcn_s_sleep(2);
@@ -227,24 +242,24 @@ __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[
             }
         }
     }
-    // A split whose wait gave up must not add its partial while the tile's
-    // turn holder may be writing it: it poisons the tile with NaN instead
-    // (so the failure shows in out without a status poll) and leaves the
-    // semaphore as it is; conv2d_fwd_status reports the timeout and resets
-    // the semaphores.
-    if (__syncthreads_or(late)) {
+    late = __builtin_amdgcn_readfirstlane(late);
+    // A wave whose wait gave up must not add its partial while the tile's
+    // turn holder may be writing it: it poisons its part of the tile with
+    // NaN instead (so the failure shows in out without a status poll), and
+    // the semaphore is left as it is unless the first wave got the turn;
+    // conv2d_fwd_status reports the timeout and resets the semaphores.
+    if (late) {
+        // (a rolled loop: this path never runs in practice, and unrolled it
+        // would add a thousand instructions to every kernel that has it)
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
-        const unsigned nan = 0x7fc00000u;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const int m = row0 + i * S + acc_row<S>(v), oc = col0 + j * S;
-                    const unsigned off = (m < a.M && oc < a.OC) ? 4u * (unsigned)(m * a.OC + oc) : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32(nan, ro, off, 0, kCoherent);
-                }
+#pragma unroll 1
+        for (int q = 0; q < FM * FN * NV; ++q) {
+            const int i = q / (FN * NV), j = (q / NV) % FN, v = q % NV;
+            const int m = row0 + i * S + acc_row<S>(v), oc = col0 + j * S;
+            const unsigned off = (m < a.M && oc < a.OC) ? 4u * (unsigned)(m * a.OC + oc) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(0x7fc00000u, ro, off, 0, kCoherent);
+        }
+        __syncthreads();
         return;
     }
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
@@ -272,7 +287,7 @@ __device__ __forceinline__ void store_tile(const ConvArgs &a, const AccT (&acc)[
     }
     __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are acknowledged
     __syncthreads();
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0)            // (the first wave got the turn: it did not give up)
         __hip_atomic_store(sem, (split + 1 == a.splits) ? 0 : split + 1, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -329,7 +344,7 @@ __device__ __forceinline__ void store_tile_vec(const ConvArgs &a, const AccT (&a
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, val[e]), ro,
+                        __builtin_amdgcn_raw_buffer_store_b32(f32_bits(val[e]), ro,
                                                               oc + e < a.OC ? off + 4u * e : kOutOfRange, 0, kOutAux);
                 }
             } else if (m < a.M) {

@@ -100,9 +100,15 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_patch_bf16(ConvArgs a)
     const int lchk = lane >> 5;
 
     // ---- copies.  Lane l of a wave instruction fills slot (base + l): row
-    // (slot >> 3), physical chunk (l & 7), i.e. logical chunk (l & 7) ^ (row & 7).
+    // (slot >> 3), physical chunk (l & 7), i.e. logical chunk (l & 7) ^ f(row):
+    // f(row) = (row >> 1) & 7 for the weight rows (the swizzle of swz()),
+    // row & 7 for the patch pixels (their reads follow the im2col pattern).
     const int lr = lane >> 3;
-    const int cl_w = (lane & 7) ^ lr;                 // weight rows: row & 7 == lane >> 3
+    // weight rows j * RPP + wave * 8 + lr (RPP a multiple of 16): bits 1..3 of
+    // the row are those of wave * 8 + lr, so the logical chunk is (lane & 7)
+    // ^ ((row >> 1) & 7) for every pass
+    const int cl_w = (lane & 7) ^ ((4 * (wave & 1)) | (lr >> 1));
+    static_assert(RPP % 16 == 0, "weight rows of one pass keep bits 1..3 of the row");
     int woff[BP];
     bool wok[BP];
 #pragma unroll

@@ -8,9 +8,9 @@
 // buffer's extent writes zeros.  So the im2col gather costs no registers,
 // and the padding / tail masking is an out-of-range offset:
 //   * one wave instruction fills a contiguous 1 KB block = 8 LDS rows of 8
-//     chunks; lane l fills row (l >> 3), physical chunk (l & 7), so it loads
-//     logical chunk (l & 7) ^ (l >> 3) of that row (the XOR swizzle is applied
-//     on the global side);
+//     chunks; lane l fills row 8 b + (l >> 3) (b: the block's index), physical
+//     chunk (l & 7), so it loads logical chunk (l & 7) ^ ((row >> 1) & 7) of
+//     that row (the XOR swizzle is applied on the global side);
 //   * STAGES LDS buffers: K tiles t+1 .. t+STAGES-1 are in flight while the
 //     waves read K tile t from LDS and run MFMA on it (the rocMLIR PR "Double
 //     buffering improvements" splits LDS reads and matrix ops into
@@ -162,9 +162,12 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_pipe_bf16(ConvArgs a)
     const int lrow = lane % LGRP;               // row / column of an MFMA block this lane feeds
     const int lchk = lane / LGRP;               // k chunk within an MFMA k step
 
-    // ---- the rows this lane copies: row (pass * RPP + wave * 8 + lane / 8)
+    // ---- the rows this lane copies: row (pass * RPP + wave * 8 + lane / 8).
+    // RPP is a multiple of 16, so bits 1..3 of the row are those of
+    // wave * 8 + lane / 8: the logical chunk is the same for every pass.
     const int lr = lane >> 3;
-    const int cl = (lane & 7) ^ lr;             // logical chunk this lane loads
+    const int cl = (lane & 7) ^ ((4 * (wave & 1)) | (lr >> 1));   // logical chunk this lane loads
+    static_assert(RPP % 16 == 0, "rows of one pass keep bits 1..3 of the row");
     const int OHW = a.OH * a.OW;
     int xoff[AP], ih0[AP], iw0[AP];
     bool mok[AP];

@@ -99,7 +99,7 @@ typedef struct convimg_plan {
  * Split-K (plans with splits > 1): the splits of an output tile take turns
  * on a semaphore, with a bounded wait.  The plan keeps every split of every
  * tile resident at once, so the wait always ends in practice; if it ever
- * gives up, that split writes NaN over its tile instead of adding its
+ * gives up, that split writes NaN over (its part of) its tile instead of adding its
  * partial sums, so `out` is invalid and visibly so, and the stream's
  * semaphores stay out of step until conv2d_fwd_status() is called, which
  * reports CONVIMG_ERR_TIMEOUT and resets them.
