@@ -994,7 +994,10 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
     // two).  Measured: a 12-tile layer ran 90 us with 22 ranges (264
     // workgroups on 256 CUs), 66 us with 32 and 62 us with 21; a 192-tile
     // layer 62 us with one range and 57 us with two.
-    const long long per_cu = 2 * tiles >= num_cus ? 2 : 1;
+    // The transpose-read kernel (IC % 64 == 0, OC % 8 == 0) holds kWtStages
+    // stages of LDS: one workgroup per CU.
+    const bool tr = wgrad_tr_shape(IC, OC);
+    const long long per_cu = tr ? kWtOccupancy : (2 * tiles >= num_cus ? 2 : 1);
     long long S = tiles < per_cu * num_cus ? per_cu * num_cus / tiles : 1;
     if (S > steps / 4)
         S = steps / 4;
@@ -1715,7 +1718,11 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     const bool vx = IC % 8 == 0 && ((uintptr_t)x & 15) == 0;
     const bool vdy = OC % 8 == 0 && ((uintptr_t)dy & 15) == 0;
     const int grid = wp.tiles_m * wp.tiles_n * wp.splits;
-    if (wgrad_launch(a, vx, vdy, grid, stream) != hipSuccess)
+    // the transpose-read kernel where the shape and the alignment allow
+    // (same tiles and ranges as the other kernel, so the workspace fits)
+    const hipError_t le = (wgrad_tr_shape(IC, OC) && vx && vdy) ? wgrad_tr_launch(a, grid, stream)
+                                                                  : wgrad_launch(a, vx, vdy, grid, stream);
+    if (le != hipSuccess)
         return CONVIMG_ERR_LAUNCH;
     if (wp.splits > 1) {
         const int n = OC * wp.KKIC;

@@ -31,6 +31,12 @@ hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_
     return hipGetLastError();
 }
 
+hipError_t wgrad_tr_launch(const WgArgs &a, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL(igemm_wgrad_tr_bf16<kWtStages>, dim3(grid), dim3(kWgThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
                                hipStream_t stream)
 {

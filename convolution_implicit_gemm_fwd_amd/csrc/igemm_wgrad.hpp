@@ -71,6 +71,20 @@ struct WgArgs {
     FastDiv div_bpr, div_oh, div_s, div_ic, div_kw;
 };
 
+// The transpose-read kernel (below) serves IC % 64 == 0 and OC % 8 == 0
+// with 16-byte aligned x and dy; its LDS ring of kWtStages stages of 32 KB
+// leaves room for kWtOccupancy workgroups per CU.
+#ifndef CONVIMG_WT_STAGES
+#define CONVIMG_WT_STAGES 4
+#endif
+constexpr int kWtStages = CONVIMG_WT_STAGES;
+constexpr int kWtOccupancy = kWtStages <= 2 ? 2 : 1;
+
+inline bool wgrad_tr_shape(int IC, int OC)
+{
+    return IC % 64 == 0 && OC % 8 == 0;
+}
+
 // The kernels are compiled in conv2d_wgrad.hip only; other units see the
 // argument block and the launchers.
 #ifdef CONVIMG_WGRAD_KERNELS
@@ -338,6 +352,217 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Transpose-read weight backward (IC % 64 == 0, OC % 8 == 0, x and dy 16-byte
+// aligned).  Same GEMM, tile (64 oc x 192 columns) and pixel walk (row-aligned
+// groups of 8 output pixels, 64 pixels a step) as the kernel above, but no
+// register transposes: the loaders copy raw pixel rows straight into LDS
+// (16 bytes a lane, buffer loads to LDS), and the MFMA fragments are read
+// with the gfx950 LDS transpose read ds_read_b64_tr_b16.
+//
+// That read (measured with an in-bounds probe): within each group of 16
+// lanes, lane r fetches 4 consecutive 16-bit values at its own address; if
+// those are viewed as a 16 x 4 matrix F (rows = lanes), lane l receives
+// F[4e + (l >> 2)][l & 3] for e = 0..3.  So when lane r points at pixel row
+// kb + (r >> 2), column m0 + 4 (r & 3) of a pixel-major tile, lane l gets the
+// values of column m0 + l at pixels kb .. kb + 3: two such reads give the 8
+// consecutive reduction values a lane feeds to v_mfma_f32_16x16x32_bf16.
+//
+// LDS stage: four regions of 64 pixel rows x 64 bf16 (128 bytes a row): dy's
+// 64 output channels, then x's 192 columns as three regions of 64 (one tap's
+// 64-channel slice each, since IC % 64 == 0).  The 16-byte chunk c of row r
+// is stored at position c ^ s(r), s(r) = 2 (bit 1 of r) + 4 (bit 3 of r): the
+// 4 rows x 32 bytes a 16-lane transpose read touches, and those of the next
+// group 8 rows on, fall on distinct banks.  A copy instruction fills one
+// region's 8 rows of one pixel group (1 KB): lane l takes pixel l >> 3 and
+// physical chunk l & 7.
+//
+// STAGES stages in a ring: the copies of step st + STAGES - 1 are issued
+// after the barrier of step st, which certifies that every wave is done
+// with step st - 1's stage.  The step loop is unrolled by STAGES, so every
+// stage offset is a constant: the compiler can then tell the stage a copy
+// writes from the one the MFMA fragments are read from, and does not wait
+// for the copies in flight before those reads.
+constexpr int kWtRegion = kWgBK * 128;           // bytes: 64 pixel rows x 64 bf16
+constexpr int kWtStage = 4 * kWtRegion;          // dy, then three 64-column regions of x
+constexpr int kWtCopies = 8;                     // copy instructions per wave per step
+
+__device__ __forceinline__ int wt_swz(int row)
+{
+    return (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
+}
+
+template <int STAGES>
+__global__ __launch_bounds__(kWgThreads) void igemm_wgrad_tr_bf16(WgArgs a)
+{
+    static_assert(STAGES >= 2 && STAGES <= 5 && (STAGES - 1) * kWtCopies < 64, "vmcnt range");
+    // one LDS variable per stage: the compiler then knows that a copy into
+    // one stage and the fragment reads of another do not overlap (with one
+    // array it waited for every copy in flight before each step's reads)
+    __shared__ __align__(16) unsigned char lds0[kWtStage];
+    __shared__ __align__(16) unsigned char lds1[kWtStage];
+    __shared__ __align__(16) unsigned char lds2[STAGES > 2 ? kWtStage : 16];
+    __shared__ __align__(16) unsigned char lds3[STAGES > 3 ? kWtStage : 16];
+    __shared__ __align__(16) unsigned char lds4[STAGES > 4 ? kWtStage : 16];
+    auto stage_base = [&](int stage) -> unsigned char * {
+        return stage == 0 ? lds0 : stage == 1 ? lds1 : stage == 2 ? lds2 : stage == 3 ? lds3 : lds4;
+    };
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tiles = a.tiles_m * a.tiles_n;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int split = bid / tiles, tile = bid - split * tiles;
+    const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
+    const int oc0 = tm * kWgBM, j0 = tn * kWgBN;
+    const int g_begin = split * a.chunk;
+    const int g_end = min(a.groups, g_begin + a.chunk);
+    const int steps = (g_end - g_begin + 7) / 8;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc((void *)a.dy, 0, a.dy_bytes, kRsrcWord3);
+
+    // ---- copy roles.  Wave w copies pixel groups 2w and 2w + 1 of every
+    // step: per group one dy instruction and three x instructions.  Lane:
+    // pixel e = lane >> 3 of the group, physical chunk lane & 7, so logical
+    // chunk cq[q] = (lane & 7) ^ s(8 (2w + q) + e).
+    const int e = lane >> 3;
+    int cq[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        cq[q] = (lane & 7) ^ ((((e >> 1) & 1) << 1) | (q << 2));
+    // x regions: the columns j0 + 64 ci .. + 63 are input channels
+    // icb .. icb + 63 of one tap (kh, kw) (uniform values)
+    int rdh[3], rdw[3], ricb[3];
+    bool rok[3];
+#pragma unroll
+    for (int ci = 0; ci < 3; ++ci) {
+        const int j = j0 + 64 * ci;
+        rok[ci] = j < a.KKIC;
+        const int jj = rok[ci] ? j : 0;
+        const int t = fast_div(jj, a.div_ic);
+        const int kh = fast_div(t, a.div_kw);
+        ricb[ci] = jj - t * a.IC;
+        rdh[ci] = kh * a.d - a.p;
+        rdw[ci] = (t - kh * a.KW) * a.d - a.p;
+    }
+    const unsigned xpix = 2u * (unsigned)a.IC;          // bytes between neighbouring pixels of x
+    auto issue = [&](int st, int stage) {
+        unsigned char *const sbase = stage_base(stage);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int gi = 2 * wave + q;
+            const int g = g_begin + st * 8 + gi;
+            const bool gok = g < g_end;
+            const int gg = gok ? g : g_begin;
+            const int r = fast_div(gg, a.div_bpr);          // output row n*OH + oh
+            const int ow0 = (gg - r * a.bpr) * 8;
+            const int n = fast_div(r, a.div_oh);
+            const int oh = r - n * a.OH;
+            const bool pok = gok && ow0 + e < a.OW;
+            const int oc = oc0 + 8 * cq[q];
+            const unsigned aoff = (pok && oc < a.OC)
+                ? 2u * ((unsigned)(r * a.OW + ow0 + e) * (unsigned)a.OC + (unsigned)oc) : kOutOfRange;
+            dma16(rdy, (u32x4_t *)(sbase + gi * 1024), aoff);
+#pragma unroll
+            for (int ci = 0; ci < 3; ++ci) {
+                const int ih = oh * a.s + rdh[ci];
+                const int iw = (ow0 + e) * a.s + rdw[ci];
+                const bool ok = pok && rok[ci] && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+                const unsigned xoff = ok
+                    ? (unsigned)((n * a.H + ih) * a.W + iw) * xpix + 2u * (unsigned)(ricb[ci] + 8 * cq[q]) : kOutOfRange;
+                dma16(rx, (u32x4_t *)(sbase + (1 + ci) * kWtRegion + gi * 1024), xoff);
+            }
+        }
+    };
+
+    // ---- fragment addresses (bytes within a stage, before the k-step and
+    // half offsets).  Lane: group g16 = lane >> 4, r16 = lane & 15; it points
+    // at row 8 g16 + (r16 >> 2) (+ 32 ks + 4 h), column m0 + 4 (r16 & 3).
+    const int g16 = lane >> 4, r16 = lane & 15;
+    const int sl = (((r16 >> 3) & 1) << 1) | ((g16 & 1) << 2);     // s(row), the same for every ks and h
+    const int rowb = (8 * g16 + (r16 >> 2)) * 128 + 8 * (r16 & 1);
+    const int b1 = (r16 & 3) >> 1;
+    int abase[4], bbase[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        abase[i] = rowb + 16 * ((2 * i + b1) ^ sl);
+#pragma unroll
+    for (int jb = 0; jb < 3; ++jb) {
+        const int col = 48 * wave + 16 * jb;           // this wave's columns, within the tile
+        bbase[jb] = (1 + (col >> 6)) * kWtRegion + rowb + 16 * ((((col & 63) >> 3) + b1) ^ sl);
+    }
+
+    floatx4_t acc[4][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto tr = [&](const unsigned char *p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+    };
+    auto frag = [&](const unsigned char *p) {
+        const v4i16 lo = tr(p), hi = tr(p + 4 * 128);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto compute = [&](int stage) {
+        const unsigned char *const sbase = stage_base(stage);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8_t fa[4], fb[3];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fa[i] = frag(sbase + abase[i] + ks * 32 * 128);
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                fb[j] = frag(sbase + bbase[j] + ks * 32 * 128);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // ---- pipeline: steps past the last one are issued too (every lane of
+    // them is out of range: they write zeros into stages that are not read
+    // again), so every wave always has STAGES - 1 steps of copies in flight
+    // and the counted wait is a constant
+#pragma unroll
+    for (int q = 0; q < STAGES - 1; ++q)
+        issue(q, q);
+    for (int st0 = 0; st0 < steps; st0 += STAGES) {
+#pragma unroll
+        for (int q = 0; q < STAGES; ++q) {
+            const int st = st0 + q;
+            if (st < steps) {
+                wait_vmcnt<(STAGES - 2) * kWtCopies>();    // step st has landed (this wave's part)
+                lds_barrier();
+                issue(st + STAGES - 1, (q + STAGES - 1) % STAGES);
+                compute(q);
+            }
+        }
+    }
+    wait_vmcnt<0>();       // (the copies past the last step: done before the workgroup ends)
+
+    // D[row = 4*(lane/16) + v][col = lane % 16] of each 16x16 block
+    float *dst = a.dst + (size_t)split * a.OC * a.KKIC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int jj = j0 + 48 * wave + 16 * j + (lane & 15);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
+                if (oc < a.OC && jj < a.KKIC)
+                    dst[(size_t)oc * a.KKIC + jj] = acc[i][j][v];
+            }
+        }
+    }
+}
+
 // dw = the sum of the pixel ranges' partial tiles, part[s][i] for s < splits.
 // One workgroup covers 256 consecutive elements (4 per lane); its 8 waves
 // each add an eighth of the ranges in order, then wave 0 adds the eight
@@ -390,6 +615,7 @@ __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__
 // register copies for this kernel than the default AGPR form).
 void wgrad_set_attributes();
 hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_t stream);
+hipError_t wgrad_tr_launch(const WgArgs &a, int grid, hipStream_t stream);
 hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
                                hipStream_t stream);
 
