@@ -959,6 +959,7 @@ FastDiv make_fast_div(int v)
 // KH*KW*IC fp32) kept under 1 GiB.
 struct WgPlan {
     int OH = 0, OW = 0, M = 0, KKIC = 0, bpr = 0, groups = 0, tiles_m = 0, tiles_n = 0, splits = 1, chunk = 0;
+    int tr_stages = 4;            // LDS stages of the transpose-read kernel
     size_t ws_bytes = 0;
 };
 
@@ -994,18 +995,29 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
     // two).  Measured: a 12-tile layer ran 90 us with 22 ranges (264
     // workgroups on 256 CUs), 66 us with 32 and 62 us with 21; a 192-tile
     // layer 62 us with one range and 57 us with two.
-    // The transpose-read kernel (IC % 64 == 0, OC % 8 == 0) holds kWtStages
-    // stages of LDS: one workgroup per CU.
+    // The transpose-read kernel (IC % 64 == 0, OC % 8 == 0) runs with four
+    // LDS stages (one workgroup per CU) where the ranges are short, and with
+    // two stages (two workgroups per CU, each hiding the other's waits)
+    // where a range at one workgroup per CU would still be 16 steps or
+    // more.  Measured: the 512-channel 14x14 layer (56 steps a range) 45.5
+    // -> 43.0 us, a dilated 128-channel layer (49 steps) 45.0 -> 37.5 us,
+    // a 64-channel 56x56 layer (10 steps) 21.0 -> 22.0 us (kept at four).
     const bool tr = wgrad_tr_shape(IC, OC);
-    const long long per_cu = tr ? kWtOccupancy : (2 * tiles >= num_cus ? 2 : 1);
-    long long S = tiles < per_cu * num_cus ? per_cu * num_cus / tiles : 1;
-    if (S > steps / 4)
-        S = steps / 4;
     const long long per = (long long)OC * fwd.K * 4;
-    if (S * per > (1LL << 30))
-        S = (1LL << 30) / per;
-    if (S < 1)
-        S = 1;
+    auto ranges = [&](long long per_cu) {
+        long long S = tiles < per_cu * num_cus ? per_cu * num_cus / tiles : 1;
+        if (S > steps / 4)
+            S = steps / 4;
+        if (S * per > (1LL << 30))
+            S = (1LL << 30) / per;
+        return S < 1 ? 1LL : S;
+    };
+    long long S = ranges(tr ? 1 : (2 * tiles >= num_cus ? 2 : 1));
+    wp->tr_stages = kWtStagesDeep;
+    if (tr && steps / S >= 16) {
+        wp->tr_stages = kWtStagesPair;
+        S = ranges(2);
+    }
     const long long chunk = (steps + S - 1) / S * 8;     // groups per range
     S = (groups + chunk - 1) / chunk;
     if (tiles * S >= lim)
@@ -1720,7 +1732,7 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     const int grid = wp.tiles_m * wp.tiles_n * wp.splits;
     // the transpose-read kernel where the shape and the alignment allow
     // (same tiles and ranges as the other kernel, so the workspace fits)
-    const hipError_t le = (wgrad_tr_shape(IC, OC) && vx && vdy) ? wgrad_tr_launch(a, grid, stream)
+    const hipError_t le = (wgrad_tr_shape(IC, OC) && vx && vdy) ? wgrad_tr_launch(a, grid, wp.tr_stages, stream)
                                                                   : wgrad_launch(a, vx, vdy, grid, stream);
     if (le != hipSuccess)
         return CONVIMG_ERR_LAUNCH;

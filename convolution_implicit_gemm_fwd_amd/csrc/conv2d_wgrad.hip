@@ -31,9 +31,12 @@ hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_
     return hipGetLastError();
 }
 
-hipError_t wgrad_tr_launch(const WgArgs &a, int grid, hipStream_t stream)
+hipError_t wgrad_tr_launch(const WgArgs &a, int grid, int stages, hipStream_t stream)
 {
-    hipLaunchKernelGGL(igemm_wgrad_tr_bf16<kWtStages>, dim3(grid), dim3(kWgThreads), 0, stream, a);
+    if (stages == kWtStagesPair)
+        hipLaunchKernelGGL(igemm_wgrad_tr_bf16<kWtStagesPair>, dim3(grid), dim3(kWgThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(igemm_wgrad_tr_bf16<kWtStagesDeep>, dim3(grid), dim3(kWgThreads), 0, stream, a);
     return hipGetLastError();
 }
 

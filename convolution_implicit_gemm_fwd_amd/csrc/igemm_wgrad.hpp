@@ -72,13 +72,10 @@ struct WgArgs {
 };
 
 // The transpose-read kernel (below) serves IC % 64 == 0 and OC % 8 == 0
-// with 16-byte aligned x and dy; its LDS ring of kWtStages stages of 32 KB
-// leaves room for kWtOccupancy workgroups per CU.
-#ifndef CONVIMG_WT_STAGES
-#define CONVIMG_WT_STAGES 4
-#endif
-constexpr int kWtStages = CONVIMG_WT_STAGES;
-constexpr int kWtOccupancy = kWtStages <= 2 ? 2 : 1;
+// with 16-byte aligned x and dy.  Its LDS ring holds kWtStagesDeep stages
+// of 32 KB (one workgroup per CU) or kWtStagesPair (two per CU).
+constexpr int kWtStagesDeep = 4;
+constexpr int kWtStagesPair = 2;
 
 inline bool wgrad_tr_shape(int IC, int OC)
 {
@@ -615,7 +612,7 @@ __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__
 // register copies for this kernel than the default AGPR form).
 void wgrad_set_attributes();
 hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_t stream);
-hipError_t wgrad_tr_launch(const WgArgs &a, int grid, hipStream_t stream);
+hipError_t wgrad_tr_launch(const WgArgs &a, int grid, int stages, hipStream_t stream);
 hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
                                hipStream_t stream);
 
