@@ -127,6 +127,8 @@ def test_dgrad_torch_wrapper():
 
 @pytest.mark.parametrize("OC,KH,KW,IC,dtype,misalign", [
     (512, 3, 3, 512, BF16, False),      # 16-byte loads and stores
+    (8, 1, 1, 8, BF16, False),          # one partial tile
+    (64, 3, 3, 32, FP32, False),        # fp32, 16-byte loads and stores
     (40, 3, 5, 24, BF16, False),        # non-square window
     (70, 2, 3, 45, BF16, False),        # channel counts off the vector: element path
     (64, 3, 3, 64, BF16, True),         # misaligned w and wt: element path
