@@ -644,7 +644,7 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
         pl->tiles_n = ceil_div(OC, kF32BN);
         pl->ktiles = ceil_div(K, kF32BK);
         pl->grid = pl->tiles_m * pl->tiles_n;
-        pl->lds_bytes = (kF32BM + kF32BN) * (kF32BK + 1) * 4;
+        pl->lds_bytes = (kF32BM + kF32BN) * kF32Row * 4;
         return CONVIMG_OK;
     }
 

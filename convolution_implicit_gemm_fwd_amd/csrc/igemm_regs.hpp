@@ -272,15 +272,20 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_regs_bf16(ConvArgs a)
 
 // ---------------------------------------------------------------------------
 // fp32 storage: the same implicit GEMM with fp32 tiles and
-// v_mfma_f32_16x16x4_f32 (products and sums in fp32).  64x64 tile, K tile 16,
-// element-wise gather, single LDS buffer, no split.
+// v_mfma_f32_16x16x4_f32 (products and sums in fp32).  64x64 tile, no split.
+// K goes through LDS in chunks of kF32BK = 144 (a whole 3x3 x 16-channel K
+// in one): each chunk's element-wise gathers are all in flight together
+// before one barrier, so a small problem pays about one memory round trip
+// per chunk instead of one per 16-wide K step.
 // ---------------------------------------------------------------------------
-constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 144;
+constexpr int kF32Row = kF32BK + 1;             // LDS row stride (floats)
+constexpr int kF32Cols = kF32BK / 4;            // chunk columns per thread
 
 __global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
 {
-    __shared__ float sA[kF32BM][kF32BK + 1];
-    __shared__ float sB[kF32BN][kF32BK + 1];
+    __shared__ float sA[kF32BM][kF32Row];
+    __shared__ float sB[kF32BN][kF32Row];
     const float *__restrict__ x = (const float *)a.x;
     const float *__restrict__ w = (const float *)a.w;
 
@@ -293,27 +298,25 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
     const int m0 = tm * kF32BM, n0 = tn * kF32BN;
     const int OHW = a.OH * a.OW;
 
-    // each thread loads 4 elements of A and 4 of B per K tile: rows
-    // (tid >> 4) + 16*q, column k = tid & 15
-    const int lk = tid & 15;
-    int xoff[4], ih0[4], iw0[4], woff[4];
-    bool mok[4], wok[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int m = m0 + (tid >> 4) + 16 * q;
-        mok[q] = m < a.M;
-        const int mm = mok[q] ? m : 0;
+    // each thread loads row tid / 4 of the A and B tiles, chunk columns
+    // (tid & 3) + 4 j
+    const int row = tid >> 2, c0 = tid & 3;
+    const int m = m0 + row;
+    const bool mok = m < a.M;
+    int xoff, ih0, iw0;
+    {
+        const int mm = mok ? m : 0;
         const int n = mm / OHW;
         const int r = mm - n * OHW;
         const int oh = r / a.OW;
         const int ow = r - oh * a.OW;
-        xoff[q] = n * a.H * a.W * a.IC;
-        ih0[q] = oh * a.stride - a.pad;
-        iw0[q] = ow * a.stride - a.pad;
-        const int oc = n0 + (tid >> 4) + 16 * q;
-        wok[q] = oc < a.OC;
-        woff[q] = wok[q] ? oc * a.K : 0;
+        xoff = n * a.H * a.W * a.IC;
+        ih0 = oh * a.stride - a.pad;
+        iw0 = ow * a.stride - a.pad;
     }
+    const int oc_row = n0 + row;
+    const bool wok = oc_row < a.OC;
+    const int woff = wok ? oc_row * a.K : 0;
 
     floatx4_t acc[2][2];
 #pragma unroll
@@ -323,23 +326,30 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
             acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     const int lrow = lane & 15, lchk = lane >> 4;
-    for (int kt = 0; kt < a.ktiles; ++kt) {
-        const int k = kt * kF32BK + lk;
-        const bool okk = k < a.K;
-        const int tap = k / a.IC;
-        const int ic = k - tap * a.IC;
-        const int kh = tap / a.KW;
-        const int kw = tap - kh * a.KW;
-        const int dh = kh * a.dil, dw = kw * a.dil;
+    for (int k0 = 0; k0 < a.K; k0 += kF32BK) {
+        // the whole chunk's loads first (k past K reads as zero)
+        float va[kF32Cols], vb[kF32Cols];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int ih = ih0[q] + dh, iw = iw0[q] + dw;
-            const bool ok = okk && mok[q] && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
-            sA[(tid >> 4) + 16 * q][lk] = ok ? x[xoff[q] + (ih * a.W + iw) * a.IC + ic] : 0.f;
-            sB[(tid >> 4) + 16 * q][lk] = (okk && wok[q]) ? w[woff[q] + k] : 0.f;
+        for (int j = 0; j < kF32Cols; ++j) {
+            const int k = k0 + c0 + 4 * j;
+            const bool okk = k < a.K;
+            const int kk = okk ? k : 0;
+            const int tap = kk / a.IC;
+            const int ic = kk - tap * a.IC;
+            const int kh = tap / a.KW;
+            const int kw = tap - kh * a.KW;
+            const int ih = ih0 + kh * a.dil, iw = iw0 + kw * a.dil;
+            const bool ok = okk && mok && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+            va[j] = ok ? x[xoff + (ih * a.W + iw) * a.IC + ic] : 0.f;
+            vb[j] = (okk && wok) ? w[woff + k] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kF32Cols; ++j) {
+            sA[row][c0 + 4 * j] = va[j];
+            sB[row][c0 + 4 * j] = vb[j];
         }
         __syncthreads();
-#pragma unroll
+#pragma unroll 4
         for (int ks = 0; ks < kF32BK / 4; ++ks) {
             float af[2], bfg[2];
 #pragma unroll
@@ -365,9 +375,9 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int m = m0 + wm * 32 + i * 16 + lchk * 4 + v;
-                if (m < a.M && oc < a.OC)
-                    a.out[m * a.OC + oc] = acc[i][j][v] + bv;
+                const int mo = m0 + wm * 32 + i * 16 + lchk * 4 + v;
+                if (mo < a.M && oc < a.OC)
+                    a.out[mo * a.OC + oc] = acc[i][j][v] + bv;
             }
     }
 }
