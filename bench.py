@@ -56,22 +56,23 @@ MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per by
 # the sources are unchanged; otherwise traffic is null.
 TRAFFIC = {
     # profiles/igemm_resident_resnet3x3.md: 7.147 MB read + 12.845 MB written
-    "resnet3x3": {"bytes": 19992019, "tile": 33, "kernel": "47a7c4e535ec5004"},
+    "resnet3x3": {"bytes": 19992005, "tile": 33, "kernel": "3e790e5d21f9351e"},
     # profiles/igemm_image_largek.md: 25.607 MB read + 6.423 MB written
-    "largek": {"bytes": 32029414, "tile": 34, "kernel": "afb9c2480f4639b3"},
+    "largek": {"bytes": 32029430, "tile": 34, "kernel": "24670c0da0ea97b5"},
     # profiles/igemm_window_stem7x7.md: 5.301 MB read + 51.380 MB written
-    "stem7x7": {"bytes": 56681384, "tile": 32, "kernel": "38c0bae53d9aeee5"},
-    # profiles/igemm_pipe_dilated.md: 19.923 MB read + 33.554 MB written
-    "dilated": {"bytes": 53477287, "tile": 15, "kernel": "967f9af2851f572e"},
+    "stem7x7": {"bytes": 56681436, "tile": 32, "kernel": "903ad63fa784d891"},
+    # profiles/igemm_pipe_dilated.md: 19.925 MB read + 33.554 MB written
+    "dilated": {"bytes": 53479330, "tile": 15, "kernel": "7811d2fa92cc429b"},
     # data backward, the GEMM on the mapped problem (--op dgrad)
     # profiles/dgrad_resident_resnet3x3.md
-    "dgrad:resnet3x3": {"bytes": 19989925, "tile": 33, "kernel": "47a7c4e535ec5004"},
+    "dgrad:resnet3x3": {"bytes": 19989947, "tile": 33, "kernel": "3e790e5d21f9351e"},
     # profiles/dgrad_image_largek.md
-    "dgrad:largek": {"bytes": 32021131, "tile": 34, "kernel": "afb9c2480f4639b3"},
-    # weight backward: the whole call (igemm_wgrad_bf16 + wgrad_reduce), as
+    "dgrad:largek": {"bytes": 32021140, "tile": 34, "kernel": "24670c0da0ea97b5"},
+    # weight backward: the whole call (igemm_wgrad_tr_bf16 + wgrad_reduce), as
     # the --op wgrad roofline times it; profiles/igemm_wgrad_*.md
-    "wgrad:resnet3x3": {"bytes": 36843150, "tile": -2, "kernel": "b17c118594669fee"},
-    "wgrad:largek": {"bytes": 72559741, "tile": -2, "kernel": "b17c118594669fee"},
+    "wgrad:resnet3x3": {"bytes": 36924190, "tile": -2, "kernel": "b62eabdd88ec07f6"},
+    "wgrad:largek": {"bytes": 72569043, "tile": -2, "kernel": "b62eabdd88ec07f6"},
+    "wgrad:dilated": {"bytes": 88837936, "tile": -2, "kernel": "b62eabdd88ec07f6"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
