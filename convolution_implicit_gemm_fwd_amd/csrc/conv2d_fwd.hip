@@ -960,6 +960,7 @@ FastDiv make_fast_div(int v)
 struct WgPlan {
     int OH = 0, OW = 0, M = 0, KKIC = 0, bpr = 0, groups = 0, tiles_m = 0, tiles_n = 0, splits = 1, chunk = 0;
     int tr_stages = 4;            // LDS stages of the transpose-read kernel
+    int inplace = 0;              // 1: the ranges add into dw in turn (no workspace)
     size_t ws_bytes = 0;
 };
 
@@ -1024,7 +1025,11 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
         return CONVIMG_ERR_RANGE;
     wp->splits = (int)S;
     wp->chunk = (int)chunk;
-    wp->ws_bytes = S > 1 ? (size_t)(S * per) : 0;
+    // a few ranges add into dw in turn; the plan keeps every workgroup
+    // resident at once (tiles x ranges within the occupancy used above), so
+    // a range's predecessor is always running
+    wp->inplace = (S > 1 && S <= kWgInplaceMax && per < (long long)kOutOfRange) ? 1 : 0;
+    wp->ws_bytes = (S > 1 && !wp->inplace) ? (size_t)(S * per) : 0;
     return CONVIMG_OK;
 }
 
@@ -1699,7 +1704,15 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     WgArgs a;
     a.x = (const unsigned short *)x;
     a.dy = (const unsigned short *)dy;
-    a.dst = wp.splits > 1 ? (float *)ws : dw;
+    a.dst = (wp.splits > 1 && !wp.inplace) ? (float *)ws : dw;
+    a.inplace = wp.inplace;
+    a.sem = nullptr;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    if (wp.inplace) {
+        rc = get_semaphores(dev, stream, wp.tiles_m * wp.tiles_n + 1, &a.sem);
+        if (rc != CONVIMG_OK)
+            return rc;
+    }
     a.N = N;
     a.H = H;
     a.W = W;
@@ -1736,7 +1749,7 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
                                                                   : wgrad_launch(a, vx, vdy, grid, stream);
     if (le != hipSuccess)
         return CONVIMG_ERR_LAUNCH;
-    if (wp.splits > 1) {
+    if (wp.splits > 1 && !wp.inplace) {
         const int n = OC * wp.KKIC;
         const int vec = (n % 4 == 0 && ((uintptr_t)ws & 15) == 0 && ((uintptr_t)dw & 15) == 0) ? 1 : 0;
         const int blocks = ceil_div(n, 4 * 64);

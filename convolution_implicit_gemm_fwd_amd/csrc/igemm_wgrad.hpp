@@ -23,9 +23,12 @@
 // slots) per step, two LDS stages (the next step's loads are in flight
 // while the current one runs on the MFMAs), one barrier per step.  Wave w
 // computes all 64 rows x columns [48w, 48w+48) with 16x16x32 bf16 MFMAs.
-// The groups are split into `splits` contiguous ranges; each range's
-// partial tile goes to a workspace and a second kernel sums the ranges in
-// order (deterministic), or straight to dw when there is one range.
+// The groups are split into `splits` contiguous ranges.  With one range
+// the tile goes straight to dw; with at most kWgInplaceMax ranges they take
+// turns on a per-tile semaphore and add into dw in range order (the
+// forward's serial split-K, so the sum has a fixed order); with more, each
+// range's partial tile goes to a workspace and a second kernel sums the
+// ranges in order.  Either way every call gives the same bits.
 #pragma once
 
 namespace convimg {
@@ -63,6 +66,9 @@ struct WgArgs {
     const unsigned short *x;     // [N][H][W][IC] bf16
     const unsigned short *dy;    // [N][OH][OW][OC] bf16
     float *dst;                  // dw [OC][KKIC], or partial sums [splits][OC][KKIC]
+    int *sem;                    // in place: one int per tile, then a status word
+    int spin_limit;              // in place: polls before a range gives up its turn
+    int inplace;                 // 1: the ranges add into dw in turn (dst = dw)
     int N, H, W, IC, OC, KH, KW, s, p, d, OH, OW;
     int M, KKIC;                 // pixels N*OH*OW; columns KH*KW*IC
     int bpr, groups;             // 8-pixel groups per output row; N*OH*bpr
@@ -81,6 +87,10 @@ inline bool wgrad_tr_shape(int IC, int OC)
 {
     return IC % 64 == 0 && OC % 8 == 0;
 }
+
+// Most pixel ranges that add into dw in turn (more go through a workspace:
+// each turn waits for the previous range's stores).
+constexpr int kWgInplaceMax = 4;
 
 // The kernels are compiled in conv2d_wgrad.hip only; other units see the
 // argument block and the launchers.
@@ -110,6 +120,90 @@ __device__ __forceinline__ void transpose8x8(const u32x4_t (&v)[8], u32x4_t (&ou
             out[2 * h + 1][q] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // high halves
         }
     }
+}
+
+// A wave's results: acc[i][j] is the 16x16 block at rows oc0 + 16 i,
+// columns jbase + 16 j of dw; lane l holds rows 4 (l >> 4) .. +3 of column
+// l & 15.  Without `inplace`, range `split` writes its partial tile
+// (dst + split * OC * KKIC).  In place, the range waits until the tile's
+// semaphore equals `split` (every wave's first lane polls, with a bound: a
+// wave that gives up sets the status word after the semaphores and writes
+// NaN over its part), then range 0 stores and later ranges add to what is
+// there, with agent-coherent (sc1) loads and stores, which reach the other
+// XCDs' workgroups; after its stores are acknowledged and the workgroup has
+// met, thread 0 passes the turn on (the last range resets it to 0).
+__device__ __forceinline__ void wg_store(const WgArgs &a, const floatx4_t (&acc)[4][3], int oc0, int jbase,
+                                         int split, int tile)
+{
+    const int lane = threadIdx.x & 63;
+    if (!a.inplace) {
+        float *dst = a.dst + (size_t)split * a.OC * a.KKIC;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int jj = jbase + 16 * j + (lane & 15);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
+                    if (oc < a.OC && jj < a.KKIC)
+                        dst[(size_t)oc * a.KKIC + jj] = acc[i][j][v];
+                }
+            }
+        }
+        return;
+    }
+    int *sem = a.sem + tile;
+    int late = 0;
+    if (lane == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(sem, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != split) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins >= a.spin_limit) {
+                __hip_atomic_store(a.sem + a.tiles_m * a.tiles_n, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                late = 1;
+                break;
+            }
+        }
+    }
+    late = __builtin_amdgcn_readfirstlane(late);
+    // dw is below 2 GiB (the plan checks), so every offset and the
+    // out-of-range offset of masked lanes fit the buffer resource
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        a.dst, 0, (unsigned)((size_t)a.OC * a.KKIC * 4), kRsrcWord3);
+    auto offset = [&](int i, int j, int v) {
+        const int jj = jbase + 16 * j + (lane & 15), oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
+        return (oc < a.OC && jj < a.KKIC) ? 4u * (unsigned)(oc * a.KKIC + jj) : kOutOfRange;
+    };
+    if (late) {
+#pragma unroll 1
+        for (int q = 0; q < 48; ++q)
+            __builtin_amdgcn_raw_buffer_store_b32(0x7fc00000u, rd, offset(q / 12, (q / 4) % 3, q % 4), 0, kCoherent);
+        __syncthreads();
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // one block row at a time: its loads go out as one batch
+        float prev[3][4];
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                prev[j][v] = split == 0 ? 0.f
+                    : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, offset(i, j, v), 0, kCoherent));
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                __builtin_amdgcn_raw_buffer_store_b32(f32_bits(prev[j][v] + acc[i][j][v]), rd, offset(i, j, v), 0,
+                                                      kCoherent);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(sem, (split + 1 == a.splits) ? 0 : split + 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // VX: IC % 8 == 0 and x 16-byte aligned (16-byte gathers of x), else
@@ -332,21 +426,7 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
         }
     }
 
-    // D[row = 4*(lane/16) + v][col = lane % 16] of each 16x16 block
-    float *dst = a.dst + (size_t)split * a.OC * a.KKIC;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int jj = j0 + wave * 48 + j * 16 + lrow;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int oc = oc0 + i * 16 + 4 * lchk + e;
-                if (oc < a.OC && jj < a.KKIC)
-                    dst[(size_t)oc * a.KKIC + jj] = acc[i][j][e];
-            }
-        }
-    }
+    wg_store(a, acc, oc0, j0 + wave * 48, split, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -543,21 +623,7 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_tr_bf16(WgArgs a)
     }
     wait_vmcnt<0>();       // (the copies past the last step: done before the workgroup ends)
 
-    // D[row = 4*(lane/16) + v][col = lane % 16] of each 16x16 block
-    float *dst = a.dst + (size_t)split * a.OC * a.KKIC;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int jj = j0 + 48 * wave + 16 * j + (lane & 15);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
-                if (oc < a.OC && jj < a.KKIC)
-                    dst[(size_t)oc * a.KKIC + jj] = acc[i][j][v];
-            }
-        }
-    }
+    wg_store(a, acc, oc0, j0 + 48 * wave, split, tile);
 }
 
 // dw = the sum of the pixel ranges' partial tiles, part[s][i] for s < splits.

@@ -203,7 +203,8 @@ int conv2d_fwd_num_tiles(void);
 #define CONVIMG_KIND_IMAGE 6
 int conv2d_fwd_tile_kind(int tile_id);
 
-/* Split-K health on `stream`: CONVIMG_OK, or CONVIMG_ERR_TIMEOUT if a
+/* Split-K health on `stream` (conv2d_fwd's splits and conv2d_bwd_weight's
+ * in-place pixel ranges): CONVIMG_OK, or CONVIMG_ERR_TIMEOUT if a
  * workgroup gave up waiting for its turn since the last call of this
  * function (the flag and the stream's semaphores are then reset).
  * Synchronises the stream.  The turn-taking is that of nvFuser issue
@@ -212,8 +213,9 @@ int conv2d_fwd_tile_kind(int tile_id);
  * this report are this library's own. */
 int conv2d_fwd_status(hipStream_t stream);
 
-/* Test knob: the number of sleep iterations a split-K workgroup waits for
- * its turn before it gives up (iterations < 1: the default, 2^20), for
+/* Test knob: the number of sleep iterations a split-K workgroup (of
+ * conv2d_fwd, or a pixel range of conv2d_bwd_weight adding into dw) waits
+ * for its turn before it gives up (iterations < 1: the default, 2^20), for
  * later calls in this process.  Lets tests force the timeout path from the
  * host.  Returns the previous bound. */
 int conv2d_fwd_test_spin_limit(int iterations);
@@ -331,9 +333,13 @@ int conv2d_bwd_data_weights(const void *w, int OC, int KH, int KW, int IC, int d
  *
  * with X = x inside the image and 0 in the padding; any stride, padding and
  * dilation.  An implicit GEMM with M = OC, N = KH*KW*IC and the reduction
- * over the N*OH*OW pixels, split into contiguous pixel ranges whose partial
- * sums go to `ws` and are then added in a fixed order (the result is the
- * same on every call).
+ * over the N*OH*OW pixels, split into contiguous pixel ranges.  Up to four
+ * ranges add into dw in range order, taking turns on the library's split-K
+ * semaphores (the forward's serial split-K; no workspace); more ranges
+ * write partial sums to `ws`, which a second kernel adds in a fixed order.
+ * Either way the result is the same on every call.  A range whose wait for
+ * its turn gives up (a bound of many milliseconds) writes NaN over its part
+ * of dw and sets the status that conv2d_fwd_status reports.
  *
  *   x     device, N x H x W x IC (NHWC) bf16
  *   dy    device, N x OH x OW x OC (NHWC) bf16, OH/OW the forward output
@@ -366,7 +372,7 @@ int conv2d_bwd_weight_workspace(int N, int H, int W, int IC, int OC, int KH, int
 /* Free every library-owned buffer (synchronising each device that has
  * one).  Later calls allocate again as needed.  Library plumbing with no
  * counterpart on the pages: the only library-owned buffers are the split-K
- * semaphores of conv2d_fwd. */
+ * semaphores of conv2d_fwd and conv2d_bwd_weight. */
 void conv2d_release(void);
 
 #ifdef __cplusplus

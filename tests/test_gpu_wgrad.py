@@ -14,8 +14,10 @@ asks for.  Covered: the ResNet-style layer at full size (several pixel
 ranges), the 512-channel layer (one range per tile), the 7x7 stride-2 stem
 (IC = 3: element-wise gather), a dilated layer, channel tails, strides,
 dilations, non-square windows, OC off the vector width, misaligned x,
-fewer pixels than one step; repeatability; the workspace-size error; the
-torch wrapper.  The named layers run at full size.
+fewer pixels than one step; repeatability through the workspace and in
+place (ranges adding into dw in turn), the in-place wait forced to time
+out; the workspace-size error; the torch wrapper.  The named layers run at
+full size.
 """
 import numpy as np
 import pytest
@@ -127,6 +129,48 @@ def test_wgrad_repeatable():
     b, _ = run_wgrad(wl, inp)
     assert need > 0, "this shape should use several pixel ranges"
     assert np.array_equal(a, b), "two calls gave different bits"
+
+
+def test_wgrad_in_place_ranges_repeatable():
+    """The 512-channel layer's two pixel ranges add into dw in turn (no
+    workspace): the same bits on every call, and the status stays clean."""
+    wl = WORKLOADS["largek"]
+    inp = make_wgrad_inputs(wl, wl.H, wl.W, seed=4)
+    a, need = run_wgrad(wl, inp)
+    b, _ = run_wgrad(wl, inp)
+    assert need == 0, "two ranges should add in place"
+    assert np.array_equal(a, b), "two calls gave different bits"
+    assert abi.conv2d_fwd_status(torch.cuda.current_stream().cuda_stream) == abi.CONVIMG_OK
+
+
+def test_wgrad_in_place_timeout_poisons_and_resets():
+    """The in-place turn wait forced to give up from the host (a
+    one-iteration bound): a range that gives up writes NaN over its part of
+    dw, conv2d_fwd_status reports the timeout and resets the semaphores, and
+    the next call with the normal bound is correct.  (Whether a range gives up
+    depends on timing; either outcome is checked.)"""
+    wl = WORKLOADS["largek"]
+    inp = make_wgrad_inputs(wl, wl.H, wl.W, seed=0)
+    yref, S = oracle.conv2d_bwd_weight(inp.x32, inp.w32, wl.KH, wl.KW, wl.stride, wl.pad,
+                                       wl.dilation)
+    sptr = torch.cuda.current_stream().cuda_stream
+    prev = abi.conv2d_fwd_test_spin_limit(1)
+    try:
+        y, _ = run_wgrad(wl, inp)
+        abi.conv2d_fwd_test_spin_limit(prev)
+        status = abi.conv2d_fwd_status(sptr)
+        log("forced wgrad timeout: status %d, NaN values %d" % (status, int(np.isnan(y).sum())))
+        if status == abi.CONVIMG_OK:
+            check(y, yref, S, "no range gave up")
+        else:
+            assert status == abi.CONVIMG_ERR_TIMEOUT
+            assert np.isnan(y).any(), "a range gave up but dw shows no poisoned part"
+        assert abi.conv2d_fwd_status(sptr) == abi.CONVIMG_OK
+        y, _ = run_wgrad(wl, inp)
+    finally:
+        abi.conv2d_fwd_test_spin_limit(0)
+    assert abi.conv2d_fwd_status(sptr) == abi.CONVIMG_OK
+    check(y, yref, S, "after the reset")
 
 
 def test_wgrad_workspace_too_small():
