@@ -143,6 +143,15 @@ def test_wgrad_in_place_ranges_repeatable():
     assert abi.conv2d_fwd_status(torch.cuda.current_stream().cuda_stream) == abi.CONVIMG_OK
 
 
+@pytest.mark.parametrize("misalign", [False, True], ids=["transpose-read kernel", "misaligned x: general kernel"])
+def test_wgrad_four_ranges_in_place(misalign):
+    """A shape planned with four pixel ranges per tile, the most that add in
+    place: no workspace, parity with the oracle, through either kernel."""
+    wl = shape(2, 24, 24, 64, 64, 3, 3, 1, 1, 1, name="four ranges in place")
+    y, need = wgrad_parity(wl, seed=2, misalign=misalign)
+    assert need == 0, "four ranges should add in place"
+
+
 def test_wgrad_in_place_timeout_poisons_and_resets():
     """The in-place turn wait forced to give up from the host (a
     one-iteration bound): a range that gives up writes NaN over its part of
