@@ -636,15 +636,15 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
     if (dtype == CONVIMG_FP32) {
         pl->tile_id = -1;
         pl->BM = kF32BM;
-        pl->BN = kF32BN;
+        pl->BN = OC <= kF32BNSmall ? kF32BNSmall : kF32BN;
         pl->BK = kF32BK;
         pl->loader = CONVIMG_LOADER_FP32;
         pl->splits = 1;
         pl->tiles_m = ceil_div(M, kF32BM);
-        pl->tiles_n = ceil_div(OC, kF32BN);
+        pl->tiles_n = ceil_div(OC, pl->BN);
         pl->ktiles = ceil_div(K, kF32BK);
         pl->grid = pl->tiles_m * pl->tiles_n;
-        pl->lds_bytes = (kF32BM + kF32BN) * kF32Row * 4;
+        pl->lds_bytes = (kF32BM + pl->BN) * kF32Row * 4;
         return CONVIMG_OK;
     }
 
@@ -1302,7 +1302,8 @@ int fwd_call(const void *x, const void *w, const float *bias,
                      pl.BK, pl.loader, pl.splits, pl.grid, pl.lds_bytes);
 
     if (dtype == CONVIMG_FP32)
-        hipLaunchKernelGGL(igemm_fwd_f32, dim3(pl.grid), dim3(kRegsThreads), 0, stream, a);
+        hipLaunchKernelGGL(pl.BN == kF32BNSmall ? igemm_fwd_f32<kF32BNSmall> : igemm_fwd_f32<kF32BN>,
+                           dim3(pl.grid), dim3(kRegsThreads), 0, stream, a);
     else if (kTiles[pl.tile_id].kind == kWindow)
         hipLaunchKernelGGL(kWinKernels[KH], dim3(pl.grid), dim3(pl.threads), (unsigned)pl.lds_bytes,
                            stream, a);

@@ -272,30 +272,36 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_regs_bf16(ConvArgs a)
 
 // ---------------------------------------------------------------------------
 // fp32 storage: the same implicit GEMM with fp32 tiles and
-// v_mfma_f32_16x16x4_f32 (products and sums in fp32).  64x64 tile, no split.
+// v_mfma_f32_16x16x4_f32 (products and sums in fp32).  64 x BN tiles (BN =
+// 64, or 16 where OC <= 16: four waves of 16 rows then do no dead work on
+// channels past OC), no split.
 // K goes through LDS in chunks of kF32BK = 144 (a whole 3x3 x 16-channel K
 // in one): each chunk's element-wise gathers are all in flight together
 // before one barrier, so a small problem pays about one memory round trip
 // per chunk instead of one per 16-wide K step.
 // ---------------------------------------------------------------------------
-constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 144;
+constexpr int kF32BM = 64, kF32BN = 64, kF32BNSmall = 16, kF32BK = 144;
 constexpr int kF32Row = kF32BK + 1;             // LDS row stride (floats)
 constexpr int kF32Cols = kF32BK / 4;            // chunk columns per thread
 
+template <int BN>
 __global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
 {
+    // waves WMW x WNW, each FM x FN blocks of 16 x 16
+    constexpr int WNW = BN == 64 ? 2 : 1, WMW = 4 / WNW;
+    constexpr int FM = kF32BM / (16 * WMW), FN = BN / (16 * WNW);
     __shared__ float sA[kF32BM][kF32Row];
-    __shared__ float sB[kF32BN][kF32Row];
+    __shared__ float sB[BN][kF32Row];
     const float *__restrict__ x = (const float *)a.x;
     const float *__restrict__ w = (const float *)a.w;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;   // 2 x 2 waves, 32 x 32 each
+    const int wm = wave % WMW, wn = wave / WMW;
     const int tm = blockIdx.x % a.tiles_m;
     const int tn = blockIdx.x / a.tiles_m;
-    const int m0 = tm * kF32BM, n0 = tn * kF32BN;
+    const int m0 = tm * kF32BM, n0 = tn * BN;
     const int OHW = a.OH * a.OW;
 
     // each thread loads row tid / 4 of the A and B tiles, chunk columns
@@ -315,67 +321,82 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
         iw0 = ow * a.stride - a.pad;
     }
     const int oc_row = n0 + row;
-    const bool wok = oc_row < a.OC;
+    const bool wok = row < BN && oc_row < a.OC;
     const int woff = wok ? oc_row * a.K : 0;
 
-    floatx4_t acc[2][2];
+    floatx4_t acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
             acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     const int lrow = lane & 15, lchk = lane >> 4;
     for (int k0 = 0; k0 < a.K; k0 += kF32BK) {
-        // the whole chunk's loads first (k past K reads as zero)
+        // the whole chunk's loads first (k past K reads as zero).  This
+        // thread's k values step by 4: (kh, kw, ic) is decoded once per
+        // chunk and then advanced (integer division by a run-time value
+        // costs tens of instructions, and there are 36 columns)
         float va[kF32Cols], vb[kF32Cols];
+        int ic, kh, kw;
+        {
+            const int kk = k0 + c0;
+            const int tap = kk / a.IC;
+            ic = kk - tap * a.IC;
+            kh = tap / a.KW;
+            kw = tap - kh * a.KW;
+        }
 #pragma unroll
         for (int j = 0; j < kF32Cols; ++j) {
             const int k = k0 + c0 + 4 * j;
             const bool okk = k < a.K;
-            const int kk = okk ? k : 0;
-            const int tap = kk / a.IC;
-            const int ic = kk - tap * a.IC;
-            const int kh = tap / a.KW;
-            const int kw = tap - kh * a.KW;
             const int ih = ih0 + kh * a.dil, iw = iw0 + kw * a.dil;
             const bool ok = okk && mok && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
             va[j] = ok ? x[xoff + (ih * a.W + iw) * a.IC + ic] : 0.f;
             vb[j] = (okk && wok) ? w[woff + k] : 0.f;
+            ic += 4;
+            while (ic >= a.IC) {
+                ic -= a.IC;
+                if (++kw == a.KW) {
+                    kw = 0;
+                    ++kh;
+                }
+            }
         }
 #pragma unroll
         for (int j = 0; j < kF32Cols; ++j) {
             sA[row][c0 + 4 * j] = va[j];
-            sB[row][c0 + 4 * j] = vb[j];
+            if (row < BN)
+                sB[row][c0 + 4 * j] = vb[j];
         }
         __syncthreads();
 #pragma unroll 4
         for (int ks = 0; ks < kF32BK / 4; ++ks) {
-            float af[2], bfg[2];
+            float af[FM], bfg[FN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = sA[wm * 32 + i * 16 + lrow][ks * 4 + lchk];
+            for (int i = 0; i < FM; ++i)
+                af[i] = sA[wm * 16 * FM + i * 16 + lrow][ks * 4 + lchk];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bfg[j] = sB[wn * 32 + j * 16 + lrow][ks * 4 + lchk];
+            for (int j = 0; j < FN; ++j)
+                bfg[j] = sB[wn * 16 * FN + j * 16 + lrow][ks * 4 + lchk];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bfg[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
     }
 
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int oc = n0 + wn * 32 + j * 16 + lrow;
+    for (int j = 0; j < FN; ++j) {
+        const int oc = n0 + wn * 16 * FN + j * 16 + lrow;
         const float bv = (a.bias != nullptr && oc < a.OC) ? a.bias[oc] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int mo = m0 + wm * 32 + i * 16 + lchk * 4 + v;
+                const int mo = m0 + wm * 16 * FM + i * 16 + lchk * 4 + v;
                 if (mo < a.M && oc < a.OC)
                     a.out[mo * a.OC + oc] = acc[i][j][v] + bv;
             }
