@@ -332,6 +332,11 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
             acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     const int lrow = lane & 15, lchk = lane >> 4;
+    // x and w below 2 GiB: buffer loads (masked lanes read zero from past
+    // the end); else plain loads guarded per element
+    const bool small = a.x_bytes < kOutOfRange && a.w_bytes < kOutOfRange;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)a.w, 0, a.w_bytes, kRsrcWord3);
     for (int k0 = 0; k0 < a.K; k0 += kF32BK) {
         // the whole chunk's loads first (k past K reads as zero).  This
         // thread's k values step by 4: (kh, kw, ic) is decoded once per
@@ -346,20 +351,45 @@ __global__ __launch_bounds__(kRegsThreads) void igemm_fwd_f32(ConvArgs a)
             kh = tap / a.KW;
             kw = tap - kh * a.KW;
         }
+        if (small) {
+            // buffer loads: a masked lane's offset lies past the buffer and
+            // reads zero, so no branch surrounds a load and all 72 go out
+            // back to back
 #pragma unroll
-        for (int j = 0; j < kF32Cols; ++j) {
-            const int k = k0 + c0 + 4 * j;
-            const bool okk = k < a.K;
-            const int ih = ih0 + kh * a.dil, iw = iw0 + kw * a.dil;
-            const bool ok = okk && mok && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
-            va[j] = ok ? x[xoff + (ih * a.W + iw) * a.IC + ic] : 0.f;
-            vb[j] = (okk && wok) ? w[woff + k] : 0.f;
-            ic += 4;
-            while (ic >= a.IC) {
-                ic -= a.IC;
-                if (++kw == a.KW) {
-                    kw = 0;
-                    ++kh;
+            for (int j = 0; j < kF32Cols; ++j) {
+                const int k = k0 + c0 + 4 * j;
+                const bool okk = k < a.K;
+                const int ih = ih0 + kh * a.dil, iw = iw0 + kw * a.dil;
+                const bool ok = okk && mok && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+                va[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    rx, ok ? 4u * (unsigned)(xoff + (ih * a.W + iw) * a.IC + ic) : kOutOfRange, 0, 0));
+                vb[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    rw, (okk && wok) ? 4u * (unsigned)(woff + k) : kOutOfRange, 0, 0));
+                ic += 4;
+                while (ic >= a.IC) {
+                    ic -= a.IC;
+                    if (++kw == a.KW) {
+                        kw = 0;
+                        ++kh;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kF32Cols; ++j) {
+                const int k = k0 + c0 + 4 * j;
+                const bool okk = k < a.K;
+                const int ih = ih0 + kh * a.dil, iw = iw0 + kw * a.dil;
+                const bool ok = okk && mok && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+                va[j] = ok ? x[xoff + (ih * a.W + iw) * a.IC + ic] : 0.f;
+                vb[j] = (okk && wok) ? w[woff + k] : 0.f;
+                ic += 4;
+                while (ic >= a.IC) {
+                    ic -= a.IC;
+                    if (++kw == a.KW) {
+                        kw = 0;
+                        ++kh;
+                    }
                 }
             }
         }
