@@ -68,9 +68,9 @@ TRAFFIC = {
     "dgrad:resnet3x3": {"bytes": 19989947, "tile": 33, "kernel": "3e790e5d21f9351e"},
     # profiles/dgrad_image_largek.md
     "dgrad:largek": {"bytes": 32021140, "tile": 34, "kernel": "24670c0da0ea97b5"},
-    # weight backward: the whole call (igemm_wgrad_tr_bf16, + wgrad_reduce where
-    # the ranges go through the workspace), as the --op wgrad roofline times
-    # it; profiles/igemm_wgrad_*.md
+    # weight backward: the whole call (igemm_wgrad_row_bf16, + wgrad_reduce
+    # where the ranges go through the workspace), as the --op wgrad roofline
+    # times it; profiles/igemm_wgrad_*.md
     "wgrad:resnet3x3": {"bytes": 36945819, "tile": -2, "kernel": "b7870400b6426b2a"},
     "wgrad:largek": {"bytes": 53749736, "tile": -2, "kernel": "b7870400b6426b2a"},
     "wgrad:dilated": {"bytes": 88694654, "tile": -2, "kernel": "b7870400b6426b2a"},

@@ -961,7 +961,11 @@ struct WgPlan {
     int OH = 0, OW = 0, M = 0, KKIC = 0, bpr = 0, groups = 0, tiles_m = 0, tiles_n = 0, splits = 1, chunk = 0;
     int tr_stages = 4;            // LDS stages of the transpose-read kernel
     int inplace = 0;              // 1: the ranges add into dw in turn (no workspace)
-    size_t ws_bytes = 0;
+    // the row-window kernel's own tiles and ranges (row = 1 where the shape
+    // allows it; it runs where x and dy are also 16-byte aligned)
+    int row = 0, row_xi = 16, row_stages = 3, row_rl = 0, row_rsp = 0, row_rr = 0, row_nseg = 1, row_steps = 0;
+    int row_tiles_n = 0, row_splits = 1, row_chunk = 0, row_inplace = 0;
+    size_t ws_bytes = 0;          // enough for whichever kernel the call's alignment selects
 };
 
 int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p, int d, int dtype,
@@ -1030,6 +1034,62 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
     // a range's predecessor is always running
     wp->inplace = (S > 1 && S <= kWgInplaceMax && per < (long long)kOutOfRange) ? 1 : 0;
     wp->ws_bytes = (S > 1 && !wp->inplace) ? (size_t)(S * per) : 0;
+
+    // Row-window kernel: units of rl output pixels (a whole row where OW <=
+    // 64, else rnseg equal segments; unequal ones are left to the kernels
+    // above), rr units in a step's 128 slots; 128 x rows a stage where that
+    // holds as many units as 192 rows would (three or four stages, whichever
+    // gives the shorter longest range), else 192 (three stages).  Ranges:
+    // one workgroup per CU (8 waves, 96-128 KB of LDS), in whole rounds of
+    // the stages.
+    if (wgrad_row_shape(IC, OC, KW, s)) {
+        const int OW = fwd.OW;
+        const int nseg = ceil_div(OW, 64);
+        const int rl = OW / nseg, rsp = rl + 2 * d;
+        // (rows - 1: the last x row stays zero; empty slots read it)
+        auto fit = [&](int rows) { return std::min(kWrSlots / rl, (rows - 1) / rsp); };
+        const int r16 = fit(128), r24 = fit(192);
+        const int xi = (r16 >= 1 && r16 == r24) ? 16 : (r24 >= 1 ? 24 : 0);
+        const long long units = (long long)N * fwd.OH * nseg;
+        // (units below 2^21: the kernel divides with float reciprocals)
+        if (OW % nseg == 0 && xi && units < (1LL << 21)) {
+            const int rr = xi == 16 ? r16 : r24;
+            const long long rsteps = (units + rr - 1) / rr;
+            const long long rtiles = (long long)wp->tiles_m * KH * (IC / 64);
+            auto ranges_for = [&](int stages, long long *chunk) {
+                long long R = rtiles < num_cus ? num_cus / rtiles : 1;
+                if (R > rsteps / stages)
+                    R = rsteps / stages;
+                if (R * per > (1LL << 30))
+                    R = (1LL << 30) / per;
+                if (R < 1)
+                    R = 1;
+                *chunk = ((rsteps + R - 1) / R + stages - 1) / stages * stages;
+                return (rsteps + *chunk - 1) / *chunk;
+            };
+            long long c3 = 0, c4 = 0;
+            const long long R3 = ranges_for(3, &c3), R4 = xi == 16 ? ranges_for(4, &c4) : 0;
+            const int stages = (xi == 16 && c4 <= c3) ? 4 : 3;
+            const long long R = stages == 4 ? R4 : R3, rchunk = stages == 4 ? c4 : c3;
+            if (rtiles * R < lim) {
+                wp->row = 1;
+                wp->row_xi = xi;
+                wp->row_stages = stages;
+                wp->row_rl = rl;
+                wp->row_rsp = rsp;
+                wp->row_rr = rr;
+                wp->row_nseg = nseg;
+                wp->row_steps = (int)rsteps;
+                wp->row_tiles_n = KH * (IC / 64);
+                wp->row_splits = (int)R;
+                wp->row_chunk = (int)rchunk;
+                wp->row_inplace = (R > 1 && R <= kWgInplaceMax && per < (long long)kOutOfRange) ? 1 : 0;
+                const size_t ws_row = (R > 1 && !wp->row_inplace) ? (size_t)(R * per) : 0;
+                if (ws_row > wp->ws_bytes)
+                    wp->ws_bytes = ws_row;
+            }
+        }
+    }
     return CONVIMG_OK;
 }
 
@@ -1702,15 +1762,23 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
             || overlaps(ws, wp.ws_bytes, dw, nw))
             return CONVIMG_ERR_ALIAS;
     }
+    const bool vx = IC % 8 == 0 && ((uintptr_t)x & 15) == 0;
+    const bool vdy = OC % 8 == 0 && ((uintptr_t)dy & 15) == 0;
+    // the row-window kernel, else the transpose-read kernel, where the shape
+    // and the alignment allow (the workspace fits either plan)
+    const bool row = wp.row && vx && vdy;
+    const int tiles_n = row ? wp.row_tiles_n : wp.tiles_n;
+    const int splits = row ? wp.row_splits : wp.splits;
+    const int inplace = row ? wp.row_inplace : wp.inplace;
     WgArgs a;
     a.x = (const unsigned short *)x;
     a.dy = (const unsigned short *)dy;
-    a.dst = (wp.splits > 1 && !wp.inplace) ? (float *)ws : dw;
-    a.inplace = wp.inplace;
+    a.dst = (splits > 1 && !inplace) ? (float *)ws : dw;
+    a.inplace = inplace;
     a.sem = nullptr;
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-    if (wp.inplace) {
-        rc = get_semaphores(dev, stream, wp.tiles_m * wp.tiles_n + 1, &a.sem);
+    if (inplace) {
+        rc = get_semaphores(dev, stream, wp.tiles_m * tiles_n + 1, &a.sem);
         if (rc != CONVIMG_OK)
             return rc;
     }
@@ -1729,9 +1797,9 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     a.M = wp.M;
     a.KKIC = wp.KKIC;
     a.tiles_m = wp.tiles_m;
-    a.tiles_n = wp.tiles_n;
-    a.splits = wp.splits;
-    a.chunk = wp.chunk;
+    a.tiles_n = tiles_n;
+    a.splits = splits;
+    a.chunk = row ? wp.row_chunk : wp.chunk;
     a.bpr = wp.bpr;
     a.groups = wp.groups;
     a.div_bpr = make_fast_div(wp.bpr);
@@ -1741,20 +1809,25 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     a.div_kw = make_fast_div(KW);
     a.x_bytes = (unsigned)nx;
     a.dy_bytes = (unsigned)ny;
-    const bool vx = IC % 8 == 0 && ((uintptr_t)x & 15) == 0;
-    const bool vdy = OC % 8 == 0 && ((uintptr_t)dy & 15) == 0;
-    const int grid = wp.tiles_m * wp.tiles_n * wp.splits;
-    // the transpose-read kernel where the shape and the alignment allow
-    // (same tiles and ranges as the other kernel, so the workspace fits)
-    const hipError_t le = (wgrad_tr_shape(IC, OC) && vx && vdy) ? wgrad_tr_launch(a, grid, wp.tr_stages, stream)
-                                                                  : wgrad_launch(a, vx, vdy, grid, stream);
+    a.rl = wp.row_rl;
+    a.rsp = wp.row_rsp;
+    a.rr = wp.row_rr;
+    a.rnseg = wp.row_nseg;
+    a.rsteps = wp.row_steps;
+    a.nicb = IC / 64;
+    a.NR = N * wp.OH;
+    a.div_rnseg = make_fast_div(wp.row_nseg);
+    const int grid = wp.tiles_m * tiles_n * splits;
+    const hipError_t le = row ? wgrad_row_launch(a, grid, wp.row_xi, wp.row_stages, stream)
+                        : (wgrad_tr_shape(IC, OC) && vx && vdy) ? wgrad_tr_launch(a, grid, wp.tr_stages, stream)
+                                                                : wgrad_launch(a, vx, vdy, grid, stream);
     if (le != hipSuccess)
         return CONVIMG_ERR_LAUNCH;
-    if (wp.splits > 1 && !wp.inplace) {
+    if (splits > 1 && !inplace) {
         const int n = OC * wp.KKIC;
         const int vec = (n % 4 == 0 && ((uintptr_t)ws & 15) == 0 && ((uintptr_t)dw & 15) == 0) ? 1 : 0;
         const int blocks = ceil_div(n, 4 * 64);
-        if (wgrad_reduce_launch((const float *)ws, dw, n, wp.splits, vec, blocks, stream) != hipSuccess)
+        if (wgrad_reduce_launch((const float *)ws, dw, n, splits, vec, blocks, stream) != hipSuccess)
             return CONVIMG_ERR_LAUNCH;
     }
     return CONVIMG_OK;

@@ -40,6 +40,17 @@ hipError_t wgrad_tr_launch(const WgArgs &a, int grid, int stages, hipStream_t st
     return hipGetLastError();
 }
 
+hipError_t wgrad_row_launch(const WgArgs &a, int grid, int xi, int stages, hipStream_t stream)
+{
+    // SEG: units are segments of rows wider than 64 (else whole rows)
+    const bool seg = a.rnseg > 1;
+    void (*k)(WgArgs) = xi == 24 ? (seg ? igemm_wgrad_row_bf16<24, 3, true> : igemm_wgrad_row_bf16<24, 3, false>)
+                      : stages == 3 ? (seg ? igemm_wgrad_row_bf16<16, 3, true> : igemm_wgrad_row_bf16<16, 3, false>)
+                                    : (seg ? igemm_wgrad_row_bf16<16, 4, true> : igemm_wgrad_row_bf16<16, 4, false>);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kWrThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
                                hipStream_t stream)
 {

@@ -31,6 +31,8 @@
 // ranges in order.  Either way every call gives the same bits.
 #pragma once
 
+#include <type_traits>
+
 namespace convimg {
 
 constexpr int kWgBM = 64;           // output channels per tile
@@ -75,6 +77,12 @@ struct WgArgs {
     int tiles_m, tiles_n, splits, chunk;   // chunk: groups per split, a multiple of 8
     unsigned x_bytes, dy_bytes;            // both below 2^31
     FastDiv div_bpr, div_oh, div_s, div_ic, div_kw;
+    // row-window kernel only: a step is rr units of rl output pixels (whole
+    // rows when rnseg == 1, else one of a row's rnseg equal segments), a
+    // unit's x span rsp = rl + 2d input pixels; rsteps steps in all (chunk
+    // is then steps per range); nicb = IC / 64; NR = N * OH output rows
+    int rl, rsp, rr, rnseg, rsteps, nicb, NR;
+    FastDiv div_rnseg;
 };
 
 // The transpose-read kernel (below) serves IC % 64 == 0 and OC % 8 == 0
@@ -86,6 +94,17 @@ constexpr int kWtStagesPair = 2;
 inline bool wgrad_tr_shape(int IC, int OC)
 {
     return IC % 64 == 0 && OC % 8 == 0;
+}
+
+// The row-window kernel (below): stride 1, KW == 3, IC % 64 == 0,
+// OC % 8 == 0, 16-byte aligned x and dy.  Eight waves; a stage holds 128 dy
+// slots and 8 XI x rows (XI = 16 or 24), in three or four stages.
+constexpr int kWrThreads = 512;
+constexpr int kWrSlots = 128;
+
+inline bool wgrad_row_shape(int IC, int OC, int KW, int s)
+{
+    return IC % 64 == 0 && OC % 8 == 0 && KW == 3 && s == 1;
 }
 
 // Most pixel ranges that add into dw in turn (more go through a workspace:
@@ -122,27 +141,29 @@ __device__ __forceinline__ void transpose8x8(const u32x4_t (&v)[8], u32x4_t (&ou
     }
 }
 
-// A wave's results: acc[i][j] is the 16x16 block at rows oc0 + 16 i,
-// columns jbase + 16 j of dw; lane l holds rows 4 (l >> 4) .. +3 of column
-// l & 15.  Without `inplace`, range `split` writes its partial tile
-// (dst + split * OC * KKIC).  In place, the range waits until the tile's
-// semaphore equals `split` (every wave's first lane polls, with a bound: a
-// wave that gives up sets the status word after the semaphores and writes
-// NaN over its part), then range 0 stores and later ranges add to what is
-// there, with agent-coherent (sc1) loads and stores, which reach the other
-// XCDs' workgroups; after its stores are acknowledged and the workgroup has
-// met, thread 0 passes the turn on (the last range resets it to 0).
-__device__ __forceinline__ void wg_store(const WgArgs &a, const floatx4_t (&acc)[4][3], int oc0, int jbase,
-                                         int split, int tile)
+// A wave's results: acc[i][j] (i < NI, j < NJ) is the 16x16 block at rows
+// oc0 + 16 i, columns jc[j] .. jc[j] + 15 of dw; lane l holds rows 4 (l >> 4) .. +3 of
+// column jc[j] + (l & 15).  Without `inplace`, range `split` writes its
+// partial tile (dst + split * OC * KKIC).  In place, the range waits until
+// the tile's semaphore equals `split` (every wave's first lane polls, with a
+// bound: a wave that gives up sets the status word after the semaphores and
+// writes NaN over its part), then range 0 stores and later ranges add to
+// what is there, with agent-coherent (sc1) loads and stores, which reach the
+// other XCDs' workgroups; after its stores are acknowledged and the
+// workgroup has met, thread 0 passes the turn on (the last range resets it
+// to 0).  Every thread of the workgroup calls this (it holds barriers).
+template <int NI, int NJ>
+__device__ __forceinline__ void wg_store(const WgArgs &a, const floatx4_t (&acc)[NI][NJ], int oc0,
+                                         const int (&jc)[NJ], int split, int tile)
 {
     const int lane = threadIdx.x & 63;
     if (!a.inplace) {
         float *dst = a.dst + (size_t)split * a.OC * a.KKIC;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NI; ++i) {
 #pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const int jj = jbase + 16 * j + (lane & 15);
+            for (int j = 0; j < NJ; ++j) {
+                const int jj = jc[j] + (lane & 15);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
@@ -172,28 +193,29 @@ __device__ __forceinline__ void wg_store(const WgArgs &a, const floatx4_t (&acc)
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
         a.dst, 0, (unsigned)((size_t)a.OC * a.KKIC * 4), kRsrcWord3);
     auto offset = [&](int i, int j, int v) {
-        const int jj = jbase + 16 * j + (lane & 15), oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
+        const int jj = jc[j] + (lane & 15), oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
         return (oc < a.OC && jj < a.KKIC) ? 4u * (unsigned)(oc * a.KKIC + jj) : kOutOfRange;
     };
     if (late) {
 #pragma unroll 1
-        for (int q = 0; q < 48; ++q)
-            __builtin_amdgcn_raw_buffer_store_b32(0x7fc00000u, rd, offset(q / 12, (q / 4) % 3, q % 4), 0, kCoherent);
+        for (int q = 0; q < NI * NJ * 4; ++q)
+            __builtin_amdgcn_raw_buffer_store_b32(0x7fc00000u, rd, offset(q / (4 * NJ), (q / 4) % NJ, q % 4), 0,
+                                                  kCoherent);
         __syncthreads();
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NI; ++i) {
         // one block row at a time: its loads go out as one batch
-        float prev[3][4];
+        float prev[NJ][4];
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 prev[j][v] = split == 0 ? 0.f
                     : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, offset(i, j, v), 0, kCoherent));
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 __builtin_amdgcn_raw_buffer_store_b32(f32_bits(prev[j][v] + acc[i][j][v]), rd, offset(i, j, v), 0,
@@ -426,7 +448,8 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_bf16(WgArgs a)
         }
     }
 
-    wg_store(a, acc, oc0, j0 + wave * 48, split, tile);
+    const int jc[3] = {j0 + 48 * wave, j0 + 48 * wave + 16, j0 + 48 * wave + 32};
+    wg_store<4, 3>(a, acc, oc0, jc, split, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -623,7 +646,262 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_tr_bf16(WgArgs a)
     }
     wait_vmcnt<0>();       // (the copies past the last step: done before the workgroup ends)
 
-    wg_store(a, acc, oc0, j0 + 48 * wave, split, tile);
+    const int jc[3] = {j0 + 48 * wave, j0 + 48 * wave + 16, j0 + 48 * wave + 32};
+    wg_store<4, 3>(a, acc, oc0, jc, split, tile);
+}
+
+// Row-window kernel.  A tile is 64 output channels x the three taps of one
+// kernel row kh at one block of 64 input channels: columns (kh, kw, 64 icb
+// + c) for kw = 0..2, c < 64.  At stride 1 those three taps read one input
+// row, shifted by d pixels from tap to tap, so a step copies, beside dy,
+// each unit's input row segment once (rsp = rl + 2d pixels for rl output
+// pixels) instead of three gathered slices (half the bytes of the
+// transpose-read kernel above).  The MFMA fragments are read with
+// ds_read_b64_tr_b16 as there; a lane's x row is its pixel slot's, shifted
+// by kw d.
+//
+// A step is 128 pixel slots holding rr units; a unit is rl consecutive
+// output pixels of one output row (the whole row where OW <= 64, else one of
+// rnseg equal segments), units numbered row by row.  Slot p = i rl + c (unit
+// i, column c); slots from rr rl on are empty (dy zero, x read from a zero
+// row, so a non-finite x value never meets them).
+//
+// LDS stage: 128 dy rows (slot p: 64 output channels, 128 bytes), then 8 XI
+// x rows (unit i's span at rows i rsp .. i rsp + rsp - 1: 64 input
+// channels), the 16-byte chunks of every row swizzled by wt_swz.  A copy
+// instruction fills 8 rows (1 KB): wave w issues dy copies w, w + 8 and x
+// copies w, w + 8, ...; rows past the step's data are copied as zeros, so
+// every wave issues the same number each step and the counted wait is a
+// constant.
+//
+// Waves: 8, two a SIMD.  Wave w computes the 64 x 96 block of columns
+// 96 (w & 1) .. + 95 over slots 32 (w >> 1) .. + 31 of every step (one k
+// step of v_mfma_f32_16x16x32_bf16: 4 A and 6 B fragments for 24 MFMAs,
+// against 7 for 12 with 64 x 48 blocks).  After the last step the four
+// waves of a column half add their blocks through LDS in wave order, each
+// keeping 16 rows, and store them.
+template <int XI, int STAGES, bool SEG>
+__global__ __launch_bounds__(kWrThreads) void igemm_wgrad_row_bf16(WgArgs a)
+{
+    constexpr int kXRows = 8 * XI;
+    constexpr int kXBase = kWrSlots * 128;           // x rows follow the dy slots
+    constexpr int kStage = kXBase + kXRows * 128;
+    constexpr int kDyCopies = kWrSlots / 64;         // dy copy instructions a wave issues per step
+    constexpr int kCpw = kDyCopies + XI / 8;         // copy instructions a wave issues per step
+    constexpr int kSlot = 9 * 64 * 16;               // exchange bytes a wave writes per column triple
+    static_assert((XI == 16 || XI == 24) && STAGES >= 3 && STAGES <= 4 && (STAGES - 1) * kCpw < 64, "shape");
+    static_assert(((8 + STAGES - 1) / STAGES) * kSlot <= kStage, "exchange slots fit the stages");
+    __shared__ __align__(16) unsigned char lds0[kStage];
+    __shared__ __align__(16) unsigned char lds1[kStage];
+    __shared__ __align__(16) unsigned char lds2[kStage];
+    __shared__ __align__(16) unsigned char lds3[STAGES > 3 ? kStage : 16];
+    auto stage_base = [&](int stage) -> unsigned char * {
+        return stage == 0 ? lds0 : stage == 1 ? lds1 : stage == 2 ? lds2 : lds3;
+    };
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cw = wave & 1, ksw = wave >> 1;
+    const int tiles = a.tiles_m * a.tiles_n;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int split = bid / tiles, tile = bid - split * tiles;
+    // (run-time divisions as float-reciprocal ones: every quotient in this
+    // kernel is below 2^21, and an integer division costs dozens of VALU
+    // instructions a lane)
+    const float inv_rl = __builtin_amdgcn_rcpf((float)a.rl), inv_rsp = __builtin_amdgcn_rcpf((float)a.rsp);
+    const int tn = tile / a.tiles_m, tm = tile - tn * a.tiles_m;
+    const int kh = tn / a.nicb, icb = tn - kh * a.nicb;
+    const int oc0 = tm * kWgBM;
+    const int s_begin = split * a.chunk;
+    const int s_end = min(a.rsteps, s_begin + a.chunk);
+    const int steps = s_end - s_begin;
+    const int ih_off = kh * a.d - a.p;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc((void *)a.dy, 0, a.dy_bytes, kRsrcWord3);
+
+    // ---- copy roles.  Lane: row e8 = lane >> 3 of the instruction's 8,
+    // physical chunk lane & 7.  Units are rl pixels wide and numbered row by
+    // row, so slot p of the step whose first unit is u0 holds output pixel
+    // u0 rl + p: a dy offset is a per-step scalar plus a per-lane constant.
+    // Divisions by run-time values use float reciprocals (small_div: every
+    // quotient here is below 2^21) and the products 24-bit multiplies (x
+    // holds fewer than 2^24 pixels since IC >= 64 and it is below 2 GiB),
+    // both full-rate, where 64-bit and 32-bit integer multiplies are not.
+    const int e8 = lane >> 3;
+    const int units = a.NR * a.rnseg;
+    unsigned doff[kDyCopies];
+    int dlim[kDyCopies];
+#pragma unroll
+    for (int k = 0; k < kDyCopies; ++k) {
+        const int pd = 8 * (wave + 8 * k) + e8;      // dy slot
+        const int du = small_div(pd, inv_rl);
+        const int doc = oc0 + 8 * ((lane & 7) ^ wt_swz(pd));
+        doff[k] = 2u * ((unsigned)pd * (unsigned)a.OC + (unsigned)doc);
+        dlim[k] = (du < a.rr && doc < a.OC) ? du : units;   // valid while u0 + dlim < units
+    }
+    int xu[XI / 8], xpos[XI / 8];
+    unsigned xch[XI / 8];
+#pragma unroll
+    for (int k = 0; k < XI / 8; ++k) {
+        const int q = 8 * (wave + 8 * k) + e8;       // x row
+        const int u = small_div(q, inv_rsp);
+        xpos[k] = q - u * a.rsp - a.p;
+        // rows past the units never valid; whole-row units: the column is
+        // the same every step, so its bounds test is made here
+        xu[k] = (u < a.rr && (SEG || (unsigned)xpos[k] < (unsigned)a.W)) ? u : units;
+        xch[k] = 2u * (unsigned)(icb * 64 + 8 * ((lane & 7) ^ wt_swz(q)));
+    }
+    const float inv_nseg = __builtin_amdgcn_rcpf((float)a.rnseg), inv_oh = __builtin_amdgcn_rcpf((float)a.OH);
+    const unsigned xpix = 2u * (unsigned)a.IC;
+    const unsigned dy_unit = 2u * (unsigned)a.rl * (unsigned)a.OC;  // dy bytes a unit
+    auto issue = [&](int st, int stage) {
+        unsigned char *const sb = stage_base(stage);
+        const int gs = s_begin + st;
+        const int u0 = gs < s_end ? gs * a.rr : units;           // past the range: nothing valid
+#pragma unroll
+        for (int k = 0; k < kDyCopies; ++k) {
+            const unsigned off = u0 + dlim[k] < units ? (unsigned)u0 * dy_unit + doff[k] : kOutOfRange;
+            dma16(rdy, (u32x4_t *)(sb + (wave + 8 * k) * 1024), off);
+        }
+#pragma unroll
+        for (int k = 0; k < XI / 8; ++k) {
+            const int u = u0 + xu[k];
+            const int r = SEG ? small_div(u, inv_nseg) : u;        // output row n OH + oh
+            const int n = small_div(r, inv_oh);
+            const int ih = r - (int)__umul24(n, a.OH) + ih_off;
+            const int iw = SEG ? (int)__umul24(u - (int)__umul24(r, a.rnseg), a.rl) + xpos[k] : xpos[k];
+            const bool ok = u < units && (unsigned)ih < (unsigned)a.H && (!SEG || (unsigned)iw < (unsigned)a.W);
+            const unsigned pix = __umul24(__umul24(n, a.H) + ih, a.W) + iw;
+            const unsigned off = ok ? __umul24(pix, xpix) + xch[k] : kOutOfRange;
+            dma16(rx, (u32x4_t *)(sb + kXBase + (wave + 8 * k) * 1024), off);
+        }
+    };
+
+    // ---- fragment addresses.  Lane: group g16 = lane >> 4, r16 = lane & 15
+    // fetches slot prow (+ 4 for the second half), columns 4 (r16 & 3) ..
+    // of its 16-column block; it receives slots kb .. kb + 3 of column l.
+    // A slot past the step's pixels fetches x from the last x row, which no
+    // unit reaches (the plan leaves it), so it holds zeros: dy is zero there
+    // too, and a non-finite x value never meets an empty slot.
+    const int g16 = lane >> 4, r16 = lane & 15;
+    const int b1 = (r16 & 3) >> 1;
+    const int prow = 32 * ksw + 8 * g16 + (r16 >> 2);
+    int abase[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        abase[i] = prow * 128 + 16 * ((2 * i + b1) ^ wt_swz(prow)) + 8 * (r16 & 1);
+    int xb[2][6];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int p = prow + 4 * h;
+        const int i = small_div(p, inv_rl), c = p - i * a.rl;
+#pragma unroll
+        for (int jb = 0; jb < 6; ++jb) {
+            const int col = 96 * cw + 16 * jb;
+            const int xr = i < a.rr ? i * a.rsp + c + (col >> 6) * a.d : kXRows - 1;
+            xb[h][jb] = kXBase + xr * 128 + 16 * ((((col & 63) >> 3) + b1) ^ wt_swz(xr)) + 8 * (r16 & 1);
+        }
+    }
+
+    floatx4_t acc[4][6];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 6; ++j)
+            acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto tr = [&](const unsigned char *p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+    };
+    auto compute = [&](int stage) {
+        const unsigned char *const sb = stage_base(stage);
+        bf16x8_t fa[4], fb[6];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v4i16 lo = tr(sb + abase[i]), hi = tr(sb + abase[i] + 4 * 128);
+            fa[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+            const v4i16 lo = tr(sb + xb[0][j]), hi = tr(sb + xb[1][j]);
+            fb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 6; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+
+    // ---- pipeline in whole rounds of STAGES steps: steps past the range's
+    // last copy zeros and add nothing (the plan sizes the ranges in whole
+    // rounds where it can).  A branch around a step made the compiler wait
+    // for nearly every copy in flight before the next step's fragment reads.
+#pragma unroll
+    for (int q = 0; q < STAGES - 1; ++q)
+        issue(q, q);
+    for (int st0 = 0; st0 < steps; st0 += STAGES) {
+#pragma unroll
+        for (int q = 0; q < STAGES; ++q) {
+            wait_vmcnt<(STAGES - 2) * kCpw>();        // step st0 + q has landed (this wave's part)
+            lds_barrier();
+            issue(st0 + q + STAGES - 1, (q + STAGES - 1) % STAGES);
+            compute(q);
+        }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();          // every copy has landed and every fragment read is done
+
+    // ---- the four waves of a column half: in two passes of three column
+    // blocks, every wave writes the three row blocks the others keep to its
+    // own slot, then wave w adds row block w >> 1 of the four waves in wave
+    // order (its own from registers).  One copy of this code per row block
+    // kept (ksw is the same for the whole wave): with ksw a run-time index
+    // into the accumulators the compiler branched around every access.
+    floatx4_t keep[1][6];
+    auto exchange = [&](auto kept) {
+        constexpr int KS = decltype(kept)::value;
+        unsigned char *const mine = stage_base(wave % STAGES) + (wave / STAGES) * kSlot;
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i == KS)
+                    continue;
+                const int idx = i - (i > KS ? 1 : 0);
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    ((floatx4_t *)mine)[(3 * idx + j) * 64 + lane] = acc[i][3 * jp + j];
+            }
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int jj = 3 * jp + j;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int src = 2 * k + cw;
+                    const floatx4_t *const theirs =
+                        (const floatx4_t *)(stage_base(src % STAGES) + (src / STAGES) * kSlot);
+                    const floatx4_t v = k == KS ? acc[KS][jj] : theirs[(3 * (KS - (KS > k ? 1 : 0)) + j) * 64 + lane];
+                    keep[0][jj] = k == 0 ? v : keep[0][jj] + v;
+                }
+            }
+            lds_barrier();
+        }
+    };
+    switch (ksw) {
+    case 0: exchange(std::integral_constant<int, 0>{}); break;
+    case 1: exchange(std::integral_constant<int, 1>{}); break;
+    case 2: exchange(std::integral_constant<int, 2>{}); break;
+    default: exchange(std::integral_constant<int, 3>{}); break;
+    }
+    int jc[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+        const int col = 96 * cw + 16 * j;
+        jc[j] = (kh * 3 + (col >> 6)) * a.IC + 64 * icb + (col & 63);
+    }
+    wg_store<1, 6>(a, keep, oc0 + 16 * ksw, jc, split, tile);
 }
 
 // dw = the sum of the pixel ranges' partial tiles, part[s][i] for s < splits.
@@ -679,6 +957,7 @@ __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__
 void wgrad_set_attributes();
 hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_t stream);
 hipError_t wgrad_tr_launch(const WgArgs &a, int grid, int stages, hipStream_t stream);
+hipError_t wgrad_row_launch(const WgArgs &a, int grid, int xi, int stages, hipStream_t stream);
 hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
                                hipStream_t stream);
 

@@ -3,10 +3,11 @@ oracle's definition of the weight gradient, element by element with
 |err| <= 1e-3*S + 1e-5 (S: the oracle's sum of |dy*x| over each element's
 terms).
 
-The kernel sums each pixel range's products in its MFMA accumulators (one
-add per 32 pixels) and then the ranges in a fixed order, so the fp32
-rounding grows with (pixels per range)/32 + ranges + 32 additions, a few
-hundred at most here: far inside the bound.
+The kernels sum each pixel range's products in MFMA accumulators (one add
+per 32 pixels; the row-window kernel then adds its four pixel quarters),
+then the ranges in a fixed order, so the fp32 rounding grows with (pixels
+per range)/32 + ranges + 32 additions, a few hundred at most here: far
+inside the bound.
 
 dw is pre-filled with NaN (an element never written fails) and followed by
 a sentinel guard; the workspace gets a guard after the bytes the library
@@ -14,7 +15,9 @@ asks for.  Covered: the ResNet-style layer at full size (several pixel
 ranges), the 512-channel layer (one range per tile), the 7x7 stride-2 stem
 (IC = 3: element-wise gather), a dilated layer, channel tails, strides,
 dilations, non-square windows, OC off the vector width, misaligned x,
-fewer pixels than one step; repeatability through the workspace and in
+fewer pixels than one step, the row-window kernel's unit layouts (short
+rows, rows cut into segments, unequal segments left to the transpose-read
+kernel); repeatability through the workspace and in
 place (ranges adding into dw in turn), the in-place wait forced to time
 out; the workspace-size error; the torch wrapper.  The named layers run at
 full size.
@@ -96,7 +99,18 @@ SMALL = [
     shape(1, 4, 5, 8, 8, 3, 3, 1, 1, 1, name="fewer pixels than a step"),
     shape(1, 3, 3, 8, 8, 3, 3, 1, 0, 1, name="single output pixel"),
     shape(4, 28, 28, 128, 128, 3, 3, 1, 1, 1, name="128 channels, several ranges"),
+    # the row-window kernel's unit layouts: several short rows a step, rows
+    # cut into equal segments (one and two a step, a step's segments from two
+    # rows, OC off the tile), unequal segments (the transpose-read kernel)
+    shape(3, 9, 7, 64, 64, 3, 3, 1, 1, 1, name="rows of 7: eighteen a step"),
+    shape(1, 6, 100, 64, 64, 3, 3, 1, 1, 1, name="rows of 100: two segments of 50"),
+    shape(2, 7, 80, 64, 72, 3, 3, 1, 1, 1, name="rows of 80: segments across rows, OC 72"),
+    shape(1, 5, 127, 64, 64, 3, 3, 1, 1, 1, name="rows of 127: unequal segments"),
 ]
+# planned with four pixel ranges per tile by both kernels (the most that add
+# into dw in turn): the row-window kernel with 16-byte aligned x, the
+# general kernel with x one element off
+IN_PLACE = shape(1, 24, 48, 64, 128, 3, 3, 1, 1, 1, name="four ranges in place")
 
 
 @pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
@@ -132,23 +146,22 @@ def test_wgrad_repeatable():
 
 
 def test_wgrad_in_place_ranges_repeatable():
-    """The 512-channel layer's two pixel ranges add into dw in turn (no
-    workspace): the same bits on every call, and the status stays clean."""
-    wl = WORKLOADS["largek"]
-    inp = make_wgrad_inputs(wl, wl.H, wl.W, seed=4)
+    """Four pixel ranges a tile add into dw in turn (no workspace): the same
+    bits on every call, and the status stays clean."""
+    wl = IN_PLACE
+    inp = make_wgrad_inputs(wl, 24, 48, seed=4)
     a, need = run_wgrad(wl, inp)
     b, _ = run_wgrad(wl, inp)
-    assert need == 0, "two ranges should add in place"
+    assert need == 0, "four ranges should add in place"
     assert np.array_equal(a, b), "two calls gave different bits"
     assert abi.conv2d_fwd_status(torch.cuda.current_stream().cuda_stream) == abi.CONVIMG_OK
 
 
-@pytest.mark.parametrize("misalign", [False, True], ids=["transpose-read kernel", "misaligned x: general kernel"])
+@pytest.mark.parametrize("misalign", [False, True], ids=["row-window kernel", "misaligned x: general kernel"])
 def test_wgrad_four_ranges_in_place(misalign):
-    """A shape planned with four pixel ranges per tile, the most that add in
-    place: no workspace, parity with the oracle, through either kernel."""
-    wl = shape(2, 24, 24, 64, 64, 3, 3, 1, 1, 1, name="four ranges in place")
-    y, need = wgrad_parity(wl, seed=2, misalign=misalign)
+    """Four pixel ranges per tile, the most that add in place: no
+    workspace, parity with the oracle, through either kernel."""
+    y, need = wgrad_parity(IN_PLACE, seed=2, misalign=misalign)
     assert need == 0, "four ranges should add in place"
 
 
@@ -158,8 +171,8 @@ def test_wgrad_in_place_timeout_poisons_and_resets():
     dw, conv2d_fwd_status reports the timeout and resets the semaphores, and
     the next call with the normal bound is correct.  (Whether a range gives up
     depends on timing; either outcome is checked.)"""
-    wl = WORKLOADS["largek"]
-    inp = make_wgrad_inputs(wl, wl.H, wl.W, seed=0)
+    wl = IN_PLACE
+    inp = make_wgrad_inputs(wl, 24, 48, seed=0)
     yref, S = oracle.conv2d_bwd_weight(inp.x32, inp.w32, wl.KH, wl.KW, wl.stride, wl.pad,
                                        wl.dilation)
     sptr = torch.cuda.current_stream().cuda_stream
