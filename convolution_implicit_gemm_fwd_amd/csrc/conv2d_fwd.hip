@@ -402,8 +402,9 @@ bool plan_window(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int
     if (gm < 1)
         gm = 1;
     const long long units = (long long)N * OH * segs;
-    // the kernel's 32-bit row offsets and float-reciprocal unit divisions
-    if (xbytes >= (1LL << 30) || units >= (1LL << 21))
+    // the kernel's 32-bit row offsets, float-reciprocal unit divisions and
+    // 32-bit unit-range products (units times the group count)
+    if (xbytes >= (1LL << 30) || units >= (1LL << 21) || units * (units < gm ? units : gm) >= (1LL << 31))
         return false;
     wp->seg = seg;
     wp->segs = segs;
@@ -943,6 +944,8 @@ int make_plan(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p,
 
 FastDiv make_fast_div(int v)
 {
+    if (v < 1)
+        v = 1;   // (callers pass divisors >= 1; a 0 from an unused plan field stays harmless)
     int l = 0;
     while ((1LL << l) < v)
         ++l;
@@ -1324,6 +1327,9 @@ int fwd_call(const void *x, const void *w, const float *bias,
     a.win_seg = wnp.seg;
     a.win_segs = wnp.segs;
     a.win_sets = wnp.sets;
+    a.win_div_g = make_fast_div(std::max(wnp.tiles_m, 1));      // (0 when the plan is not a window one)
+    a.win_div_q = make_fast_div(std::max(wnp.tiles_m >> 3, 1));
+    a.win_div_q1 = make_fast_div((wnp.tiles_m >> 3) + 1);
     a.win_sh = wnp.sh;
     a.win_wp = wnp.wp;
     a.win_rb = wnp.rb;
@@ -1826,7 +1832,7 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     if (splits > 1 && !inplace) {
         const int n = OC * wp.KKIC;
         const int vec = (n % 4 == 0 && ((uintptr_t)ws & 15) == 0 && ((uintptr_t)dw & 15) == 0) ? 1 : 0;
-        const int blocks = ceil_div(n, 4 * 64);
+        const int blocks = ceil_div(n, 4 * kWgRedCols);
         if (wgrad_reduce_launch((const float *)ws, dw, n, splits, vec, blocks, stream) != hipSuccess)
             return CONVIMG_ERR_LAUNCH;
     }

@@ -57,6 +57,20 @@ constexpr int kCoherent = 16;                  // cache policy sc1: agent-cohere
 #endif
 constexpr int kOutAux = CONVIMG_OUT_AUX;
 
+// Division by a run-time constant with one 64-bit multiply (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// for 0 <= n < 2^31 and divisor v >= 1, with l = ceil(log2 v),
+// mul = ceil(2^(31+l) / v) < 2^32 gives n / v = (n * mul) >> (31 + l).
+struct FastDiv {
+    unsigned mul;
+    int shift;
+};
+
+__device__ __forceinline__ int fast_div(int n, FastDiv f)
+{
+    return (int)(((unsigned long long)(unsigned)n * f.mul) >> f.shift);
+}
+
 struct ConvArgs {
     const void *x;
     const void *w;
@@ -83,6 +97,8 @@ struct ConvArgs {
     int win_wp, win_rb;      // LDS bytes per weight row, per input-row buffer
     int lds_rows;            // LDS offset of the input-row buffers
     int win_sets;            // input-row buffer sets (units in flight + 1)
+    FastDiv win_div_g;       // division by tiles_m (the unit groups)
+    FastDiv win_div_q, win_div_q1;  // by tiles_m / 8 and tiles_m / 8 + 1 (an XCD's groups)
     // resident kernel only (also lds_rows: LDS offset of the input rows)
     int res_zero;            // LDS offset of the zero pixel record
     int res_scr;             // LDS offset of the per-wave store scratch, or -1 (dword stores)

@@ -44,25 +44,14 @@ constexpr int kWgRows = kWgBM + kWgBN;           // LDS rows per stage (A rows, 
 constexpr int kWgRowBytes = kWgBK * 2 + 16;
 constexpr int kWgStageBytes = kWgRows * kWgRowBytes;
 constexpr int kWgLdsBytes = 2 * kWgStageBytes;
-constexpr int kWgReduceThreads = 512;
+constexpr int kWgReduceThreads = 256;
+constexpr int kWgRedCols = 16;                          // 4-element columns a reduce workgroup covers
+constexpr int kWgRedGroups = kWgReduceThreads / kWgRedCols;   // range groups per column
+constexpr int kWgRedBatch = 8;                          // loads a thread issues before adding
 #ifndef CONVIMG_WG_PF
 #define CONVIMG_WG_PF 1
 #endif
 constexpr int kWgPF = CONVIMG_WG_PF;    // steps of loads in flight (measured)
-
-// Division by a run-time constant with one 64-bit multiply (Granlund and
-// Montgomery, "Division by invariant integers using multiplication", 1994):
-// for 0 <= n < 2^31 and divisor v >= 1, with l = ceil(log2 v),
-// mul = ceil(2^(31+l) / v) < 2^32 gives n / v = (n * mul) >> (31 + l).
-struct FastDiv {
-    unsigned mul;
-    int shift;
-};
-
-__device__ __forceinline__ int fast_div(int n, FastDiv f)
-{
-    return (int)(((unsigned long long)(unsigned)n * f.mul) >> f.shift);
-}
 
 struct WgArgs {
     const unsigned short *x;     // [N][H][W][IC] bf16
@@ -905,26 +894,42 @@ __global__ __launch_bounds__(kWrThreads) void igemm_wgrad_row_bf16(WgArgs a)
 }
 
 // dw = the sum of the pixel ranges' partial tiles, part[s][i] for s < splits.
-// One workgroup covers 256 consecutive elements (4 per lane); its 8 waves
-// each add an eighth of the ranges in order, then wave 0 adds the eight
-// partial sums in wave order: a fixed order, so every call gives the same
-// bits.  vec: n % 4 == 0 and both buffers 16-byte aligned (16-byte
+// A workgroup covers kWgRedCols consecutive 4-element columns; thread t takes
+// column t % kWgRedCols and range group t / kWgRedCols (ranges split evenly
+// and in order over kWgRedGroups groups), loads all of its group's ranges
+// before adding them in order, and the groups' sums are then added in group
+// order through LDS: a fixed order, so every call gives the same bits, with
+// every load of the call in flight at once instead of a few rounds of them
+// per wave.  vec: n % 4 == 0 and both buffers 16-byte aligned (16-byte
 // accesses), else element by element.
 __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__restrict__ part,
                                                                  float *__restrict__ dw, int n, int splits,
                                                                  int vec)
 {
-    constexpr int kWaves = kWgReduceThreads / 64;
-    __shared__ floatx4_t red[kWaves][64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int i = (blockIdx.x * 64 + lane) * 4;
-    const int s0 = (int)((long long)splits * w / kWaves), s1 = (int)((long long)splits * (w + 1) / kWaves);
+    __shared__ floatx4_t red[kWgRedGroups][kWgRedCols];
+    const int t = threadIdx.x;
+    const int col = t % kWgRedCols, g = t / kWgRedCols;
+    const int i = (blockIdx.x * kWgRedCols + col) * 4;
+    const int s0 = (int)((long long)splits * g / kWgRedGroups), s1 = (int)((long long)splits * (g + 1) / kWgRedGroups);
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (i < n) {
         if (vec) {
-#pragma unroll 4
-            for (int s = s0; s < s1; ++s)
-                acc += *(const floatx4_t *)(part + (size_t)s * n + i);
+            // buffer loads, ranges past the group's reading zeros through an
+            // offset past the workspace (below 1 GiB, so every offset fits):
+            // no branch around a load, which made the compiler wait for each
+            const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)part, 0, (unsigned)((size_t)splits * n * 4), kRsrcWord3);
+            floatx4_t v[kWgRedBatch];
+            for (int sb = s0; sb < s1; sb += kWgRedBatch) {
+#pragma unroll
+                for (int q = 0; q < kWgRedBatch; ++q) {
+                    const unsigned off = sb + q < s1 ? 4u * ((unsigned)(sb + q) * (unsigned)n + (unsigned)i) : kOutOfRange;
+                    v[q] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
+                }
+#pragma unroll
+                for (int q = 0; q < kWgRedBatch; ++q)
+                    acc += v[q];
+            }
         } else {
             const int cnt = min(4, n - i);
             for (int s = s0; s < s1; ++s)
@@ -932,19 +937,19 @@ __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__
                     acc[e] += part[(size_t)s * n + i + e];
         }
     }
-    red[w][lane] = acc;
+    red[g][col] = acc;
     __syncthreads();
-    if (w == 0 && i < n) {
-        floatx4_t t = red[0][lane];
+    if (g == 0 && i < n) {
+        floatx4_t sum = red[0][col];
 #pragma unroll
-        for (int q = 1; q < kWaves; ++q)
-            t += red[q][lane];
+        for (int q = 1; q < kWgRedGroups; ++q)
+            sum += red[q][col];
         if (vec) {
-            *(floatx4_t *)(dw + i) = t;
+            *(floatx4_t *)(dw + i) = sum;
         } else {
             const int cnt = min(4, n - i);
             for (int e = 0; e < cnt; ++e)
-                dw[i + e] = t[e];
+                dw[i + e] = sum[e];
         }
     }
 }

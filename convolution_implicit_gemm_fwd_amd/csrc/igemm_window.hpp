@@ -74,21 +74,26 @@ __global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvAr
                  "s"(a.lds_rows), "s"(a.K));
     const int units = a.N * a.OH * a.win_segs;
     int gn, u_begin, u_end;
+    // (divisions by the host's multiply-shift constants: the plan keeps
+    // units * tiles_m below 2^31; an integer division by a run-time value
+    // is a long chain of quarter-rate VALU multiplies, all of it before the
+    // first row copy goes out)
     if (a.tiles_n == 1) {
         const int G = a.tiles_m, q = G >> 3, r = G & 7;      // (the grid: tiles_m groups of units)
         const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
         const int cnt = q + (x < r ? 1 : 0);                      // workgroups of XCD x
         const int base = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
-        const int ux0 = (int)((long long)units * base / G);
-        const int ux1 = (int)((long long)units * (base + cnt) / G);
-        const int per = (ux1 - ux0) / cnt, extra = (ux1 - ux0) - per * cnt;
+        const int ux0 = fast_div(units * base, a.win_div_g);
+        const int ux1 = fast_div(units * (base + cnt), a.win_div_g);
+        const int per = fast_div(ux1 - ux0, x < r ? a.win_div_q1 : a.win_div_q);
+        const int extra = (ux1 - ux0) - per * cnt;
         gn = 0;
         u_begin = ux0 + j * per + min(j, extra);
         u_end = u_begin + per + (j < extra ? 1 : 0);
     } else {
-        gn = blockIdx.x / a.tiles_m;
+        gn = fast_div(blockIdx.x, a.win_div_g);
         const int gm = blockIdx.x - gn * a.tiles_m;
-        const int per = units / a.tiles_m, extra = units - per * a.tiles_m;
+        const int per = fast_div(units, a.win_div_g), extra = units - per * a.tiles_m;
         u_begin = gm * per + min(gm, extra);
         u_end = u_begin + per + (gm < extra ? 1 : 0);
     }
@@ -187,9 +192,9 @@ __global__ __launch_bounds__(kWinThreads, kWinOcc) void igemm_window_bf16(ConvAr
     __syncthreads();
     if (tid < a.K) {
         const int kwic = KW * IC;
-        const int kh = tid / kwic;
+        const int kh = small_div(tid, __builtin_amdgcn_rcpf((float)kwic));
         const int rem = tid - kh * kwic;
-        const int kw = rem / IC;
+        const int kw = small_div(rem, __builtin_amdgcn_rcpf((float)IC));
         const int c = rem - kw * IC;
         char *const col = lds + 2 * (kh * 32 + sh + kw * a.dil * IC + c);
 #pragma unroll
