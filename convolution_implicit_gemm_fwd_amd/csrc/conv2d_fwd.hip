@@ -1316,6 +1316,8 @@ int fwd_call(const void *x, const void *w, const float *bias,
     a.splits = pl.splits;
     a.tiles_pad = pl.grid / pl.splits;
     a.vec_out = (((uintptr_t)out & 15) == 0 && OC % 4 == 0) ? 1 : 0;
+    a.div_ohw = make_fast_div(pl.OH * pl.OW);
+    a.div_ow = make_fast_div(pl.OW);
     a.remap = pl.splits == 1 ? 1 : 0;
     a.nfast = (pl.splits > 1 && nw > nx) ? 1 : 0;
     a.strip_px = sp.strip_px;

@@ -87,6 +87,7 @@ struct ConvArgs {
     int remap;       // 1: XCD-aware order of tiles (single split only)
     int nfast;       // 1: tiles numbered N-fastest (split-K with weights larger than x)
     int vec_out;     // 1: out is 16-byte aligned and OC % 4 == 0 (16-byte stores allowed)
+    FastDiv div_ohw, div_ow;    // division by OH * OW and by OW
     // strip kernel only
     int strip_px;    // output pixels per workgroup
     int chunk_px;    // output pixels per patch load

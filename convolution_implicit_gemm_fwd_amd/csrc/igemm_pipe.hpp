@@ -145,7 +145,9 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_pipe_bf16(ConvArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // (uniform: the copies' LDS addresses are then scalar, with no
+    // readfirstlane per copy instruction)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
 
@@ -169,20 +171,28 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_pipe_bf16(ConvArgs a)
     const int cl = (lane & 7) ^ ((4 * (wave & 1)) | (lr >> 1));   // logical chunk this lane loads
     static_assert(RPP % 16 == 0, "rows of one pass keep bits 1..3 of the row");
     const int OHW = a.OH * a.OW;
-    int xoff[AP], ih0[AP], iw0[AP];
+    // xbase[j]: byte offset of this lane's chunk of row j at tap (0, 0),
+    // channel 0 (negative where the tap falls in the top or left padding);
+    // the tap-aligned loader adds one per-tile scalar to it, with no
+    // multiply per copy
+    // (the row decode divides by the host's multiply-shift constants: an
+    // integer division by a run-time value is a chain of quarter-rate
+    // multiplies, and all of it comes before the first copy)
+    int xoff[AP], ih0[AP], iw0[AP], xbase[AP];
     bool mok[AP];
 #pragma unroll
     for (int j = 0; j < AP; ++j) {
         const int m = m0 + j * RPP + wave * 8 + lr;
         mok[j] = m < a.M;
         const int mm = mok[j] ? m : 0;
-        const int n = mm / OHW;
+        const int n = fast_div(mm, a.div_ohw);
         const int r = mm - n * OHW;
-        const int oh = r / a.OW;
+        const int oh = fast_div(r, a.div_ow);
         const int ow = r - oh * a.OW;
         xoff[j] = n * a.H * a.W * a.IC;
         ih0[j] = oh * a.stride - a.pad;
         iw0[j] = ow * a.stride - a.pad;
+        xbase[j] = 2 * (xoff[j] + (ih0[j] * a.W + iw0[j]) * a.IC + cl * 8);
     }
     int woff[BP];
     bool wok[BP];
@@ -232,11 +242,16 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_pipe_bf16(ConvArgs a)
             dh = kh * a.dil;
             dw = (tap - kh * a.KW) * a.dil;
         }
+        // tap-aligned: the tap's row and column shift and the channel block
+        // are the same for every lane (one scalar); else per lane
+        const int sdelta = LOADER == kLoaderTap ? 2 * ((dh * a.W + dw) * a.IC + cofs - cl * 8) : 0;
 #pragma unroll
         for (int j = 0; j < AP; ++j) {
             const int ih = ih0[j] + dh, iw = iw0[j] + dw;
             const bool ok = okk && mok[j] && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
-            const unsigned off = ok ? 2u * (unsigned)(xoff[j] + (ih * a.W + iw) * a.IC + cofs) : kOutOfRange;
+            const unsigned off = !ok ? kOutOfRange
+                : LOADER == kLoaderTap ? (unsigned)(xbase[j] + sdelta)
+                                       : 2u * (unsigned)(xoff[j] + (ih * a.W + iw) * a.IC + cofs);
             dma16(rx, sa + j * RPP * kChunks, off);
         }
 #pragma unroll
