@@ -150,14 +150,17 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
         else if (j < cins)
             dma16(rw, (u32x4_t *)(lds + wofs) + first(j - pins, kImgWChunks), off);
     }
-    // copy k of chunk c into set b
-    auto issue_one = [&](int k, int c, int b) {
+    // copy k of chunk c into set b.  lp, lc, lpc: pins, cins and PC as the
+    // chunk's own copies (see run), so that the few scalar operations that
+    // place each copy are redone per chunk instead of being kept, for all
+    // eleven copies and both sets, in registers the loop then spilled
+    auto issue_one = [&](int k, int c, int b, int lp, int lc, int lpc) {
         const int j = wave + kImgWaves * k;
         char *const base = lds + b * set_bytes;
-        if (j < pins)
-            dma16(rx, (u32x4_t *)base + first(j, PC), soff[k] + 128u * c);
-        else if (j < cins)
-            dma16(rw, (u32x4_t *)(base + wofs) + first(j - pins, kImgWChunks), soff[k] + 128u * c);
+        if (j < lp)
+            dma16(rx, (u32x4_t *)base + first(j, lpc), soff[k] + 128u * c);
+        else if (j < lc)
+            dma16(rw, (u32x4_t *)(base + wofs) + first(j - lp, kImgWChunks), soff[k] + 128u * c);
     };
 
     auto tap_off = [&](int t) { return ((t / 3) * a.dil * RU + (t % 3) * a.dil * 9) * 16; };
@@ -200,6 +203,10 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
             constexpr int M = kImgNT * NB;                              // MFMAs of the chunk
             constexpr int S = M < kImgCopySpread ? M : kImgCopySpread;  // MFMA slots the copies use
             const bool more = cn < nchunks;
+            // (opaque copies: the compiler cannot hoist what depends on them
+            // out of the chunk loop)
+            int lp = pins, lc = cins, lpc = PC;
+            asm volatile("" : "+s"(lp), "+s"(lc), "+s"(lpc));
             // copies k with slot(k) == m follow MFMA m (slot(k) = k S / K)
             auto copies_after = [&](int m) {
                 if (!more)
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
 #pragma unroll
                 for (int k = 0; k < kImgMaxCopies; ++k)
                     if ((k * S) / kImgMaxCopies == m)
-                        issue_one(k, cn, B ^ 1);
+                        issue_one(k, cn, B ^ 1, lp, lc, lpc);
             };
             const char *const sb = lds + B * set_bytes;
             auto af = [&](int i, int t) {
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
                 if (more) {
 #pragma unroll
                     for (int k = 0; k < kImgMaxCopies; ++k)
-                        issue_one(k, cn, B ^ 1);
+                        issue_one(k, cn, B ^ 1, lp, lc, lpc);
                 }
                 return;
             }
