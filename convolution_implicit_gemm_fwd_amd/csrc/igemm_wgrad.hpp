@@ -147,20 +147,35 @@ __device__ __forceinline__ void wg_store(const WgArgs &a, const floatx4_t (&acc)
 {
     const int lane = threadIdx.x & 63;
     if (!a.inplace) {
-        float *dst = a.dst + (size_t)split * a.OC * a.KKIC;
+        // One range: dw itself, with streaming stores (the forward's output
+        // policy; with the default one the tile stays dirty in the XCD's L2
+        // until the kernel ends and is written back then: 512-channel layer
+        // -2 %).  Partial tiles keep the default policy, which the reduce
+        // that reads them measured slightly faster with.  dw is below 2 GiB
+        // (the plan checks).
+        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+            a.dst + (size_t)split * a.OC * a.KKIC, 0, (unsigned)((size_t)a.OC * a.KKIC * 4), kRsrcWord3);
+        auto store = [&](auto aux) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
+            for (int i = 0; i < NI; ++i) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int jj = jc[j] + (lane & 15);
+                for (int j = 0; j < NJ; ++j) {
+                    const int jj = jc[j] + (lane & 15);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
-                    if (oc < a.OC && jj < a.KKIC)
-                        dst[(size_t)oc * a.KKIC + jj] = acc[i][j][v];
+                    for (int v = 0; v < 4; ++v) {
+                        const int oc = oc0 + 16 * i + 4 * (lane >> 4) + v;
+                        const unsigned off = (oc < a.OC && jj < a.KKIC) ? 4u * (unsigned)(oc * a.KKIC + jj)
+                                                                        : kOutOfRange;
+                        __builtin_amdgcn_raw_buffer_store_b32(f32_bits(acc[i][j][v]), rd, off, 0,
+                                                              decltype(aux)::value);
+                    }
                 }
             }
-        }
+        };
+        if (a.splits == 1)
+            store(std::integral_constant<int, kOutAux>{});
+        else
+            store(std::integral_constant<int, 0>{});
         return;
     }
     int *sem = a.sem + tile;
