@@ -1437,18 +1437,19 @@ int conv2d_fwd_nchw(const void *x, const void *w, const float *bias, int N, int 
         return CONVIMG_ERR_RANGE;
     char *wsb = (char *)ws;
     const dim3 blk(kPermThreads);
-    // x [N][IC][H*W] -> [N][H*W][IC]; w [OC][IC][KH*KW] -> [OC][KH*KW][IC]
-    if (dtype == CONVIMG_BF16) {
-        hipLaunchKernelGGL((transpose_batched<unsigned short, unsigned short>), dim3(tiles(HW), tiles(IC), N), blk, 0,
-                           stream, (const unsigned short *)x, (unsigned short *)wsb, IC, HW);
-        hipLaunchKernelGGL((transpose_batched<unsigned short, unsigned short>), dim3(tiles(KK), tiles(IC), OC), blk,
-                           0, stream, (const unsigned short *)w, (unsigned short *)(wsb + l.w_off), IC, KK);
-    } else {
-        hipLaunchKernelGGL((transpose_batched<float, float>), dim3(tiles(HW), tiles(IC), N), blk, 0, stream,
-                           (const float *)x, (float *)wsb, IC, HW);
-        hipLaunchKernelGGL((transpose_batched<float, float>), dim3(tiles(KK), tiles(IC), OC), blk, 0, stream,
-                           (const float *)w, (float *)(wsb + l.w_off), IC, KK);
-    }
+    // x [N][IC][H*W] -> [N][H*W][IC] and w [OC][IC][KH*KW] -> [OC][KH*KW][IC],
+    // one launch
+    const TransposeJob jx{IC, HW, (int)tiles(HW), (int)tiles(IC)}, jw{IC, KK, (int)tiles(KK), (int)tiles(IC)};
+    const long long t1 = (long long)jx.cx * jx.ry * N, t2 = (long long)jw.cx * jw.ry * OC;
+    if (t1 + t2 >= 0x7fffffffLL)
+        return CONVIMG_ERR_RANGE;
+    if (dtype == CONVIMG_BF16)
+        hipLaunchKernelGGL(transpose_batched2<unsigned short>, dim3((unsigned)(t1 + t2)), blk, 0, stream,
+                           (const unsigned short *)x, (unsigned short *)wsb, jx, (int)t1, (const unsigned short *)w,
+                           (unsigned short *)(wsb + l.w_off), jw);
+    else
+        hipLaunchKernelGGL(transpose_batched2<float>, dim3((unsigned)(t1 + t2)), blk, 0, stream, (const float *)x,
+                           (float *)wsb, jx, (int)t1, (const float *)w, (float *)(wsb + l.w_off), jw);
     if (hipGetLastError() != hipSuccess)
         return CONVIMG_ERR_LAUNCH;
     rc = conv2d_fwd(wsb, wsb + l.w_off, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype,

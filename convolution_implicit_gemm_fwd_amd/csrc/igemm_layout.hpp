@@ -35,18 +35,17 @@ __device__ __forceinline__ unsigned short float_to_elem<unsigned short>(float f)
 template <>
 __device__ __forceinline__ float float_to_elem<float>(float f) { return f; }
 
-// out[b][c][r] = in[b][r][c] for b < gridDim.z, r < R, c < C, converted from
-// Tin to Tout (exact between equal types and from bf16 to fp32; rounded to
-// nearest even from fp32 to bf16).  One workgroup moves a 64 x 64 tile
-// through LDS: reads along c, writes along r, both coalesced.
-// Grid: (ceil(C/64), ceil(R/64), B).
+// out[b][c][r] = in[b][r][c] for r < R, c < C, converted from Tin to Tout
+// (exact between equal types and from bf16 to fp32; rounded to nearest even
+// from fp32 to bf16), for the 64 x 64 tile (c0, r0) of batch b.  One
+// workgroup moves the tile through LDS: reads along c, writes along r, both
+// coalesced.
 template <typename Tin, typename Tout>
-__global__ __launch_bounds__(kPermThreads) void transpose_batched(const Tin *__restrict__ in,
-                                                                 Tout *__restrict__ out, int R, int C)
+__device__ __forceinline__ void transpose_tile(const Tin *__restrict__ in, Tout *__restrict__ out, int R, int C,
+                                               int b, int r0, int c0)
 {
     __shared__ float tile[kPermTile][kPermTile + 1];
-    const size_t base = (size_t)blockIdx.z * R * C;
-    const int r0 = blockIdx.y * kPermTile, c0 = blockIdx.x * kPermTile;
+    const size_t base = (size_t)b * R * C;
     const int tx = threadIdx.x % kPermTile, ty = threadIdx.x / kPermTile;
     constexpr int kRows = kPermThreads / kPermTile;
     // every lane loads (out-of-range lanes from the tile's first element,
@@ -67,6 +66,41 @@ __global__ __launch_bounds__(kPermThreads) void transpose_batched(const Tin *__r
     for (int c = ty; c < kPermTile; c += kRows)
         if (c0 + c < C && r0 + tx < R)
             out[base + (size_t)(c0 + c) * R + r0 + tx] = float_to_elem<Tout>(tile[tx][c]);
+}
+
+// One batched transpose (above) per launch.  Grid: (ceil(C/64), ceil(R/64), B).
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(kPermThreads) void transpose_batched(const Tin *__restrict__ in,
+                                                                 Tout *__restrict__ out, int R, int C)
+{
+    transpose_tile(in, out, R, C, blockIdx.z, blockIdx.y * kPermTile, blockIdx.x * kPermTile);
+}
+
+// Two batched transposes in one launch (x and w of the NCHW entry point):
+// workgroup g < t1 takes tile g of the first (tiles numbered c fastest, then
+// r, then batch: cx1 x ry1 per batch), the rest the second.  One launch
+// instead of two: each costs a dependent launch on the stream, more than
+// the small weight transpose's own work.  Grid: t1 + t2 workgroups.
+struct TransposeJob {
+    int R, C, cx, ry;        // extents; tiles along c and r
+};
+
+template <typename T>
+__global__ __launch_bounds__(kPermThreads) void transpose_batched2(const T *__restrict__ in1, T *__restrict__ out1,
+                                                                  TransposeJob j1, int t1,
+                                                                  const T *__restrict__ in2, T *__restrict__ out2,
+                                                                  TransposeJob j2)
+{
+    const bool first = (int)blockIdx.x < t1;
+    const TransposeJob j = first ? j1 : j2;
+    const int g = first ? (int)blockIdx.x : (int)blockIdx.x - t1;
+    const int per = j.cx * j.ry;
+    const int b = g / per, rem = g - b * per;
+    const int ry = rem / j.cx, cx = rem - ry * j.cx;
+    if (first)
+        transpose_tile(in1, out1, j.R, j.C, b, ry * kPermTile, cx * kPermTile);
+    else
+        transpose_tile(in2, out2, j.R, j.C, b, ry * kPermTile, cx * kPermTile);
 }
 
 }  // namespace convimg
