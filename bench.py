@@ -55,25 +55,25 @@ MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per by
 # hash of that kernel family's sources.  Reported only while the plan and
 # the sources are unchanged; otherwise traffic is null.
 TRAFFIC = {
-    # profiles/igemm_resident_resnet3x3.md: 7.147 MB read + 12.845 MB written
-    "resnet3x3": {"bytes": 19992005, "tile": 33, "kernel": "3e790e5d21f9351e"},
-    # profiles/igemm_image_largek.md: 25.607 MB read + 6.423 MB written
-    "largek": {"bytes": 32029430, "tile": 34, "kernel": "24670c0da0ea97b5"},
-    # profiles/igemm_window_stem7x7.md: 5.301 MB read + 51.380 MB written
-    "stem7x7": {"bytes": 56681436, "tile": 32, "kernel": "903ad63fa784d891"},
-    # profiles/igemm_pipe_dilated.md: 19.925 MB read + 33.554 MB written
-    "dilated": {"bytes": 53479330, "tile": 15, "kernel": "7811d2fa92cc429b"},
+    # profiles/igemm_resident_resnet3x3.md: 7.134 MB read + 12.845 MB written
+    "resnet3x3": {"bytes": 19978712, "tile": 33, "kernel": "d0577a4ca5fffa80"},
+    # profiles/igemm_image_largek.md: 25.598 MB read + 6.423 MB written
+    "largek": {"bytes": 32020104, "tile": 34, "kernel": "2dfdbad2f8f6097c"},
+    # profiles/igemm_window_stem7x7.md: 5.287 MB read + 51.380 MB written
+    "stem7x7": {"bytes": 56667036, "tile": 32, "kernel": "a434d75e49f3ce1e"},
+    # profiles/igemm_pipe_dilated.md: 19.912 MB read + 33.554 MB written
+    "dilated": {"bytes": 53466020, "tile": 15, "kernel": "799da7af733cc74c"},
     # data backward, the GEMM on the mapped problem (--op dgrad)
     # profiles/dgrad_resident_resnet3x3.md
-    "dgrad:resnet3x3": {"bytes": 19989947, "tile": 33, "kernel": "3e790e5d21f9351e"},
+    "dgrad:resnet3x3": {"bytes": 19976604, "tile": 33, "kernel": "d0577a4ca5fffa80"},
     # profiles/dgrad_image_largek.md
-    "dgrad:largek": {"bytes": 32021140, "tile": 34, "kernel": "24670c0da0ea97b5"},
+    "dgrad:largek": {"bytes": 32011860, "tile": 34, "kernel": "2dfdbad2f8f6097c"},
     # weight backward: the whole call (igemm_wgrad_row_bf16, + wgrad_reduce
     # where the ranges go through the workspace), as the --op wgrad roofline
     # times it; profiles/igemm_wgrad_*.md
-    "wgrad:resnet3x3": {"bytes": 36945819, "tile": -2, "kernel": "b7870400b6426b2a"},
-    "wgrad:largek": {"bytes": 53749736, "tile": -2, "kernel": "b7870400b6426b2a"},
-    "wgrad:dilated": {"bytes": 88694654, "tile": -2, "kernel": "b7870400b6426b2a"},
+    "wgrad:resnet3x3": {"bytes": 36184133, "tile": -2, "kernel": "0c7e15dc67145a3f"},
+    "wgrad:largek": {"bytes": 44504399, "tile": -2, "kernel": "0c7e15dc67145a3f"},
+    "wgrad:dilated": {"bytes": 68871200, "tile": -2, "kernel": "0c7e15dc67145a3f"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).

@@ -3,10 +3,10 @@
 //
 // burn-cubecl "kernel/conv/base.rs" listing: the NCHW entry points permute
 // the input to channels-last and the weight to [OC][KH][KW][IC] before the
-// NHWC convolution and permute the result back.  Here one batched-transpose
-// kernel does all three permutes (each is a transpose of the last two axes
-// of a [B][R][C] array), and the output permute can also round the fp32
-// result to bf16.  The implicit GEMM itself always writes fp32 (its split-K
+// NHWC convolution and permute the result back.  Here each permute is a
+// transpose of the last two axes of a [B][R][C] array, 64 x 64 tiles through
+// LDS: the input and weight permutes share one launch, and the output
+// permute can also round the fp32 result to bf16.  The implicit GEMM itself always writes fp32 (its split-K
 // reduction accumulates in the output buffer), into a workspace, so a bf16
 // output never aliases the accumulation buffer.
 #pragma once
