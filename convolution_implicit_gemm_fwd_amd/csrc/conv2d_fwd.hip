@@ -1125,7 +1125,7 @@ enum SemSource { kSemPool, kSemScratch };
 int fwd_call(const void *x, const void *w, const float *bias,
              int N, int H, int W, int IC, int OC, int KH, int KW,
              int stride, int pad, int dilation, int dtype,
-             float *out, hipStream_t stream, SemSource sems);
+             float *out, hipStream_t stream, SemSource sems, int flipw = 0);
 
 }  // namespace
 
@@ -1252,7 +1252,7 @@ namespace {
 int fwd_call(const void *x, const void *w, const float *bias,
              int N, int H, int W, int IC, int OC, int KH, int KW,
              int stride, int pad, int dilation, int dtype,
-             float *out, hipStream_t stream, SemSource sems)
+             float *out, hipStream_t stream, SemSource sems, int flipw)
 {
     if (!x || !w || !out)
         return CONVIMG_ERR_NULL;
@@ -1337,6 +1337,16 @@ int fwd_call(const void *x, const void *w, const float *bias,
     a.win_rb = wnp.rb;
     a.res_zero = rsp.zero;
     a.res_scr = a.vec_out ? rsp.scr : -1;
+    a.res_flipw = 0;
+    if (flipw) {
+        // only the resident kernel flips its weights in LDS, and only the
+        // 64 x 64 slice of a square kernel (the caller then runs the
+        // separate transform instead)
+        if (pl.tile_id < 0 || kTiles[pl.tile_id].kind != kResident || IC != 64 || OC != 64 || KH != KW
+            || dtype != CONVIMG_BF16)
+            return CONVIMG_ERR_UNSUPPORTED;
+        a.res_flipw = 1;
+    }
     a.img_set = imp.set;
     a.img_wofs = imp.wofs;
     a.img_ti = imp.ti;
@@ -1707,6 +1717,15 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
     if (overlaps(wt, nw, dy, ny) || overlaps(dx, nx, w, nw) || overlaps(dx, nx, dy, ny)
         || overlaps(dx, nx, wt, nw))
         return CONVIMG_ERR_ALIAS;
+    // 64 -> 64 channels on the resident kernel: it flips and transposes the
+    // forward weights in LDS (one launch, wt untouched); else the transform
+    // into wt, then the forward on the mapped problem
+    if (IC == 64 && OC == 64 && dtype == CONVIMG_BF16) {
+        rc = fwd_call(dy, w, nullptr, N, fwd.OH, fwd.OW, OC, IC, KH, KW, 1, pt, dilation, dtype, dx, stream,
+                      kSemPool, 1);
+        if (rc != CONVIMG_ERR_UNSUPPORTED)
+            return rc;
+    }
     rc = conv2d_bwd_data_weights(w, OC, KH, KW, IC, dtype, wt, stream);
     if (rc != CONVIMG_OK)
         return rc;

@@ -103,6 +103,9 @@ struct ConvArgs {
     // resident kernel only (also lds_rows: LDS offset of the input rows)
     int res_zero;            // LDS offset of the zero pixel record
     int res_scr;             // LDS offset of the per-wave store scratch, or -1 (dword stores)
+    int res_flipw;           // 1: w holds the forward weights of a data backward's mapped
+                             // problem (64 x 64 channels, square kernel), flipped and
+                             // transposed in LDS by the prologue
     // image kernel only
     int img_set, img_wofs;   // LDS bytes per buffer set; weights' offset within a set
     int img_ti, img_ts;      // workgroup blocks: images x channel slices (dividing N and tiles_n)

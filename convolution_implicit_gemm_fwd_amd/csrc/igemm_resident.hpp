@@ -129,6 +129,38 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
     }
     wait_vmcnt<0>();
     __syncthreads();
+    if (a.res_flipw) {
+        // The data backward's mapped problem, its weights copied as the
+        // forward's are (64 x 64 channels): record oc holds w[oc][t][ic].
+        // Flip and transpose them in place, so that record ic holds, at tap
+        // NT - 1 - t, w[oc][t][ic] for oc = 0 .. 63: the mapped problem's
+        // weights (the transform a separate launch would otherwise write).
+        // The 64 x 64 x NT elements are 64 NT tiles of 4 (oc) x 16 (ic),
+        // one per 16-lane group and read: ds_read_b64_tr_b16 gives lane l
+        // the 4 rows oc .. oc + 3 of column ic0 + l, which are 8 contiguous
+        // bytes of record ic0 + l.  Every read completes before any write.
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        constexpr int NQ = 2 * NT;                  // reads a wave (64 NT tiles over 8 waves x 4 groups)
+        const int G = lane >> 4, r = lane & 15;
+        v4i16 v[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int T = (wave * NQ + q) * 4 + G;
+            const int t = T >> 6, ocq = (T >> 2) & 15, icb = T & 3;
+            v[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(
+                lds + (4 * ocq + (r >> 2)) * wrec + 2 * (64 * t + 16 * icb + 4 * (r & 3))));
+        }
+        wait_lgkmcnt0();
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int T = (wave * NQ + q) * 4 + G;
+            const int t = T >> 6, ocq = (T >> 2) & 15, icb = T & 3;
+            *(v4i16 *)(lds + (16 * icb + r) * wrec + 2 * (64 * (NT - 1 - t) + 4 * ocq)) = v[q];
+        }
+        wait_lgkmcnt0();
+        __syncthreads();
+    }
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
     const int nunits = (m_b - m_a + 31) / 32;
     const float inv_ohw = __builtin_amdgcn_rcpf((float)ohw), inv_ow = __builtin_amdgcn_rcpf((float)a.OW);

@@ -290,14 +290,18 @@ void conv2d_fwd_autotune_clear(void);
  * writes those weights to `wt` (conv2d_bwd_data_weights), then runs
  * conv2d_fwd(dy, wt, NULL, N, OH, OW, OC, IC, KH, KW, 1,
  * dilation*(KH-1) - pad, dilation, dtype, dx, stream) -- same plans, same
- * kernels, no bias.  A caller whose weights do not change between calls
- * may transform them once and make that conv2d_fwd call itself.
+ * kernels, no bias.  Where that forward runs on the resident kernel with
+ * 64 -> 64 channels (bf16), the kernel instead copies w itself and flips
+ * and transposes it in LDS: one launch, and `wt` is left as it was.  A
+ * caller whose weights do not change between calls may transform them once
+ * and make that conv2d_fwd call itself.
  *
  *   dy    device, N x OH x OW x OC (NHWC) in `dtype`, OH/OW the forward
  *         output extents of H/W (the formula under conv2d_fwd)
  *   w     device, OC x KH x KW x IC (OHWI) in `dtype`: the forward weights
  *   wt    device, OC*KH*KW*IC elements of `dtype`, caller-owned workspace;
- *         receives IC x KH x KW x OC, the flipped and transposed weights
+ *         receives IC x KH x KW x OC, the flipped and transposed weights,
+ *         except on the in-LDS path above (then untouched)
  *   dx    device, fp32 N x H x W x IC (NHWC), fully overwritten
  *   N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype: the forward
  *         problem's arguments

@@ -54,6 +54,9 @@ def bwd_parity(wl, dtype=None, seed=0, misalign=False):
     n_w = w.numel()
     wt_buf = torch.empty(n_w + (1 if misalign else 0), dtype=w.dtype, device="cuda")
     wt = wt_buf[1:] if misalign else wt_buf
+    # a pattern no transform writes everywhere: wt must come back either
+    # untouched (the GEMM flipped the weights in LDS itself) or transformed
+    wt.view(torch.int16).fill_(0x7F81)
     n_dx = wl.N * wl.H * wl.W * wl.IC
     off = 1 if misalign else 0                 # dx 4-byte but not 16-byte aligned
     dx_buf = torch.full((n_dx + GUARD + off,), float("nan"), dtype=torch.float32, device="cuda")
@@ -68,15 +71,20 @@ def bwd_parity(wl, dtype=None, seed=0, misalign=False):
     host = dx.cpu().numpy()
     assert (host[n_dx:] == SENTINEL).all(), "write past the end of dx"
     y = host[:n_dx].reshape(wl.N, wl.H, wl.W, wl.IC)
-    # the workspace: w[oc][kh][kw][ic] -> wt[ic][KH-1-kh][KW-1-kw][oc], bit for bit
+    # the workspace: untouched where the GEMM flips the weights in LDS (the
+    # resident kernel at 64 -> 64 channels), else w[oc][kh][kw][ic] ->
+    # wt[ic][KH-1-kh][KW-1-kw][oc], bit for bit
     want = np.ascontiguousarray(inp.w_store[:, ::-1, ::-1, :].transpose(3, 1, 2, 0))
-    got = wt.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == BF16 \
-        else wt.cpu().numpy()
-    assert np.array_equal(got.reshape(want.shape), want), "flipped weights differ"
+    raw = wt.view(torch.int16).cpu().numpy()
+    untouched = bool((raw == 0x7F81).all())
+    if not untouched:
+        got = raw.view(np.uint16) if dtype == BF16 else wt.cpu().numpy()
+        assert np.array_equal(got.reshape(want.shape), want), "flipped weights differ"
+    log("dgrad %s: %s" % (wl.name, "weights flipped in LDS" if untouched else "weights transformed into wt"))
     yref, S = oracle.conv2d_bwd_data(inp.x32, inp.w32, wl.H, wl.W, 1, wl.pad, wl.dilation)
     ratio = check(y, yref, S, "dgrad %s" % (wl,))
     log("dgrad %s worst err/tol %.3g" % (wl.name, ratio))
-    return y, yref
+    return y, yref, untouched
 
 
 # the stride-1 named layers at full size, planned as bench.py --op dgrad runs them
@@ -95,6 +103,15 @@ SMALL = [
     shape(1, 8, 8, 1, 1, 3, 3, 1, 1, 1, name="IC 1 OC 1"),
     shape(1, 3, 3, 8, 8, 3, 3, 1, 0, 1, name="single output pixel"),
 ]
+
+
+def test_dgrad_weights_flipped_in_lds():
+    """64 -> 64 channels, 3x3, on the resident kernel: the GEMM flips and
+    transposes the forward weights in LDS itself (one launch, wt left as
+    it was), at full size and on a small image with several rows a CU."""
+    for wl in (WORKLOADS["resnet3x3"], shape(2, 16, 16, 64, 64, 3, 3, 1, 1, 1, name="64 -> 64 small")):
+        _, _, untouched = bwd_parity(wl, seed=3)
+        assert untouched, "%s: expected the in-LDS flip, got the transform into wt" % wl.name
 
 
 @pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
