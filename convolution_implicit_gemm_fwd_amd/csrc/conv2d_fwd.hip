@@ -1338,14 +1338,20 @@ int fwd_call(const void *x, const void *w, const float *bias,
     a.res_zero = rsp.zero;
     a.res_scr = a.vec_out ? rsp.scr : -1;
     a.res_flipw = 0;
+    a.img_flipw = 0;
     if (flipw) {
-        // only the resident kernel flips its weights in LDS, and only the
-        // 64 x 64 slice of a square kernel (the caller then runs the
-        // separate transform instead)
-        if (pl.tile_id < 0 || kTiles[pl.tile_id].kind != kResident || IC != 64 || OC != 64 || KH != KW
-            || dtype != CONVIMG_BF16)
+        // the resident kernel (the 64 x 64 slice) and the image kernel flip
+        // the weights of a square kernel in LDS themselves; elsewhere the
+        // caller runs the separate transform instead
+        const int kind = pl.tile_id >= 0 ? kTiles[pl.tile_id].kind : -1;
+        if (KH != KW || dtype != CONVIMG_BF16)
             return CONVIMG_ERR_UNSUPPORTED;
-        a.res_flipw = 1;
+        if (kind == kResident && IC == 64 && OC == 64)
+            a.res_flipw = 1;
+        else if (kind == kImage)
+            a.img_flipw = 1;
+        else
+            return CONVIMG_ERR_UNSUPPORTED;
     }
     a.img_set = imp.set;
     a.img_wofs = imp.wofs;
@@ -1717,10 +1723,11 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
     if (overlaps(wt, nw, dy, ny) || overlaps(dx, nx, w, nw) || overlaps(dx, nx, dy, ny)
         || overlaps(dx, nx, wt, nw))
         return CONVIMG_ERR_ALIAS;
-    // 64 -> 64 channels on the resident kernel: it flips and transposes the
+    // where the mapped problem runs on the resident kernel (64 -> 64
+    // channels) or the image kernel, the kernel flips and transposes the
     // forward weights in LDS (one launch, wt untouched); else the transform
     // into wt, then the forward on the mapped problem
-    if (IC == 64 && OC == 64 && dtype == CONVIMG_BF16) {
+    if (dtype == CONVIMG_BF16) {
         rc = fwd_call(dy, w, nullptr, N, fwd.OH, fwd.OW, OC, IC, KH, KW, 1, pt, dilation, dtype, dx, stream,
                       kSemPool, 1);
         if (rc != CONVIMG_ERR_UNSUPPORTED)

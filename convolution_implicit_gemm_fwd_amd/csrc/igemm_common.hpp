@@ -109,6 +109,8 @@ struct ConvArgs {
     // image kernel only
     int img_set, img_wofs;   // LDS bytes per buffer set; weights' offset within a set
     int img_ti, img_ts;      // workgroup blocks: images x channel slices (dividing N and tiles_n)
+    int img_flipw;           // 1: w holds the forward weights of a data backward's mapped problem,
+                             // copied as they are and flipped and transposed in LDS per chunk
 };
 
 // Workgroup IDs are dealt round-robin to the 8 XCDs (id % 8).  Renumber them

@@ -43,6 +43,9 @@ constexpr int kImgRec = 144;                   // LDS record: 64 bf16 + a spare 
 constexpr int kImgBN = 32;                     // output channels per workgroup
 constexpr int kImgMaxCopies = 11;              // copies per wave per chunk at most (the plan checks)
 constexpr int kImgWChunks = kImgNT * kImgBN * 9;  // 16-byte chunks of a chunk's weights
+constexpr int kImgFlipChunks = kImgNT * 64 * 4;   // the same, copied as forward-weight rows (flipw)
+constexpr int kImgFlipReads = kImgNT * 16 * 2 / (kImgWaves * 4);   // transposed reads a wave per chunk (flipw)
+static_assert(kImgFlipChunks * 16 <= kImgWChunks * 16, "the rows fit the records' area");
 constexpr int kImgRedRow = 40;                     // floats per pixel of the partial sums in LDS
 #ifndef CONVIMG_IMG_SPREAD
 #define CONVIMG_IMG_SPREAD 22
@@ -109,8 +112,16 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
     // past its region.  Each lane's source offsets are worked out once:
     // chunk c only adds c * 128 bytes (64 channels) to every one, and an
     // out-of-range offset stays out of range.
+    // flipw: w holds the forward weights of a data backward's mapped problem
+    // (rows = the mapped input channels); a chunk's weights are then copied
+    // as they are, 64-byte pieces w[oc][t][n0 .. n0 + 31], into rows (t, oc)
+    // of the set's weight area, and flipped and transposed into the records
+    // after the chunk's barrier (flip_weights below)
+    const bool flipw = a.img_flipw != 0;
+    const int wch = flipw ? kImgFlipChunks : kImgWChunks;     // 16-byte chunks of a chunk's weights
+    const unsigned cstride = flipw ? 64u * (unsigned)kImgNT * 2u * (unsigned)a.OC : 128u;  // bytes a chunk moves them
     const int pins = (PC + 63) / 64;
-    const int wins = (kImgWChunks + 63) / 64;
+    const int wins = (wch + 63) / 64;
     const int cins = pins + wins;
     auto first = [&](int j, int n) { return min(64 * j, max(n - 64, 0)); };
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
@@ -137,30 +148,64 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
             const int ih = pr - p, iw = pc - p;
             if (sub < 8 && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W)
                 off = xbase + __umul24(__umul24(ih, W) + iw, IC2) + 16u * sub;
-        } else if (j < cins) {
+        } else if (j < cins && !flipw) {
             const int q = first(j - pins, kImgWChunks) + lane;
             const int rec = div9(q), sub = q - 9 * rec;             // rec = tap * 32 + r
             const int t = rec >> 5, r = rec & 31;
             if (sub < 8)
                 off = wbase + __umul24(r, K2) + __umul24(t, IC2) + 16u * sub;
+        } else if (j < cins) {
+            // row (t, oc) of 64 bytes: w[oc][t][n0 .. n0 + 31] (past the end
+            // of w: zeros; past OC in a row: channels never stored)
+            const int q = first(j - pins, kImgFlipChunks) + lane;
+            const int row = q >> 2, t = row >> 6, oc = row & 63;
+            off = __umul24(oc * kImgNT + t, 2u * (unsigned)a.OC) + 2u * (unsigned)n0 + 16u * (q & 3);
         }
         soff[k] = off;
         if (j < pins)
             dma16(rx, dsm + first(j, PC), off);
         else if (j < cins)
-            dma16(rw, (u32x4_t *)(lds + wofs) + first(j - pins, kImgWChunks), off);
+            dma16(rw, (u32x4_t *)(lds + wofs) + first(j - pins, wch), off);
     }
     // copy k of chunk c into set b.  lp, lc, lpc: pins, cins and PC as the
     // chunk's own copies (see run), so that the few scalar operations that
     // place each copy are redone per chunk instead of being kept, for all
     // eleven copies and both sets, in registers the loop then spilled
-    auto issue_one = [&](int k, int c, int b, int lp, int lc, int lpc) {
+    auto issue_one = [&](int k, int c, int b, int lp, int lc, int lpc, int lwch) {
         const int j = wave + kImgWaves * k;
         char *const base = lds + b * set_bytes;
         if (j < lp)
             dma16(rx, (u32x4_t *)base + first(j, lpc), soff[k] + 128u * c);
         else if (j < lc)
-            dma16(rw, (u32x4_t *)(base + wofs) + first(j - lp, kImgWChunks), soff[k] + 128u * c);
+            dma16(rw, (u32x4_t *)(base + wofs) + first(j - lp, lwch), soff[k] + cstride * c);
+    };
+    // flipw: rows (t, oc) of set b's weight area -> records (NT - 1 - t) * 32
+    // + ic, bytes 2 oc.  288 tiles of 4 (oc) x 16 (ic), one per 16-lane group
+    // and read (9 reads a wave): ds_read_b64_tr_b16 gives lane l the 4 rows
+    // oc .. oc + 3 of column ic0 + l, 8 contiguous bytes of record ic0 + l.
+    // Every read completes before any write (the two layouts overlap).
+    auto flip_weights = [&](int b) {
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        char *const wb = lds + b * set_bytes + wofs;
+        const int G = lane >> 4, r = lane & 15;
+        v4i16 v[kImgFlipReads];
+#pragma unroll
+        for (int q = 0; q < kImgFlipReads; ++q) {
+            const int T = (wave * kImgFlipReads + q) * 4 + G;
+            const int t = T >> 5, ocq = (T >> 1) & 15, icb = T & 1;
+            v[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(
+                wb + (t * 64 + 4 * ocq + (r >> 2)) * 64 + 2 * (16 * icb + 4 * (r & 3))));
+        }
+        wait_lgkmcnt0();
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < kImgFlipReads; ++q) {
+            const int T = (wave * kImgFlipReads + q) * 4 + G;
+            const int t = T >> 5, ocq = (T >> 1) & 15, icb = T & 1;
+            *(v4i16 *)(wb + ((kImgNT - 1 - t) * 32 + 16 * icb + r) * kImgRec + 8 * ocq) = v[q];
+        }
+        wait_lgkmcnt0();
+        lds_barrier();
     };
 
     auto tap_off = [&](int t) { return ((t / 3) * a.dil * RU + (t % 3) * a.dil * 9) * 16; };
@@ -205,8 +250,8 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
             const bool more = cn < nchunks;
             // (opaque copies: the compiler cannot hoist what depends on them
             // out of the chunk loop)
-            int lp = pins, lc = cins, lpc = PC;
-            asm volatile("" : "+s"(lp), "+s"(lc), "+s"(lpc));
+            int lp = pins, lc = cins, lpc = PC, lwch = wch;
+            asm volatile("" : "+s"(lp), "+s"(lc), "+s"(lpc), "+s"(lwch));
             // copies k with slot(k) == m follow MFMA m (slot(k) = k S / K)
             auto copies_after = [&](int m) {
                 if (!more)
@@ -214,7 +259,7 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
 #pragma unroll
                 for (int k = 0; k < kImgMaxCopies; ++k)
                     if ((k * S) / kImgMaxCopies == m)
-                        issue_one(k, cn, B ^ 1, lp, lc, lpc);
+                        issue_one(k, cn, B ^ 1, lp, lc, lpc, lwch);
             };
             const char *const sb = lds + B * set_bytes;
             auto af = [&](int i, int t) {
@@ -227,7 +272,7 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
                 if (more) {
 #pragma unroll
                     for (int k = 0; k < kImgMaxCopies; ++k)
-                        issue_one(k, cn, B ^ 1, lp, lc, lpc);
+                        issue_one(k, cn, B ^ 1, lp, lc, lpc, lwch);
                 }
                 return;
             }
@@ -260,6 +305,8 @@ __global__ __launch_bounds__(kImgThreads, 1) void igemm_image_bf16(ConvArgs a)
             // then refills
             wait_vmcnt<0>();
             lds_barrier();
+            if (flipw)
+                flip_weights(decltype(b_tag)::value);
             run(b_tag, c + 1);
         };
         for (int c = 0; c < nchunks; c += 2) {

@@ -290,9 +290,10 @@ void conv2d_fwd_autotune_clear(void);
  * writes those weights to `wt` (conv2d_bwd_data_weights), then runs
  * conv2d_fwd(dy, wt, NULL, N, OH, OW, OC, IC, KH, KW, 1,
  * dilation*(KH-1) - pad, dilation, dtype, dx, stream) -- same plans, same
- * kernels, no bias.  Where that forward runs on the resident kernel with
- * 64 -> 64 channels (bf16), the kernel instead copies w itself and flips
- * and transposes it in LDS: one launch, and `wt` is left as it was.  A
+ * kernels, no bias.  Where that forward runs (bf16) on the resident kernel
+ * with 64 -> 64 channels or on the image kernel, the kernel instead copies
+ * w itself and flips and transposes it in LDS: one launch, and `wt` is
+ * left as it was.  A
  * caller whose weights do not change between calls may transform them once
  * and make that conv2d_fwd call itself.
  *

@@ -106,10 +106,13 @@ SMALL = [
 
 
 def test_dgrad_weights_flipped_in_lds():
-    """64 -> 64 channels, 3x3, on the resident kernel: the GEMM flips and
-    transposes the forward weights in LDS itself (one launch, wt left as
-    it was), at full size and on a small image with several rows a CU."""
-    for wl in (WORKLOADS["resnet3x3"], shape(2, 16, 16, 64, 64, 3, 3, 1, 1, 1, name="64 -> 64 small")):
+    """The GEMM flips and transposes the forward weights in LDS itself (one
+    launch, wt left as it was): the resident kernel at 64 -> 64 channels
+    (full size, and a small image), the image kernel per 64-channel chunk
+    (the 512-channel layer, 128 -> 192 channels, 64 -> 256 on 7x7 maps)."""
+    for wl in (WORKLOADS["resnet3x3"], shape(2, 16, 16, 64, 64, 3, 3, 1, 1, 1, name="64 -> 64 small"),
+               WORKLOADS["largek"], shape(4, 14, 14, 128, 192, 3, 3, 1, 1, 1, name="image 128 -> 192"),
+               shape(2, 7, 7, 64, 256, 3, 3, 1, 1, 1, name="image 64 -> 256 7x7")):
         _, _, untouched = bwd_parity(wl, seed=3)
         assert untouched, "%s: expected the in-LDS flip, got the transform into wt" % wl.name
 
