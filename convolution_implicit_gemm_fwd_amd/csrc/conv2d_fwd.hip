@@ -1119,6 +1119,28 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// The argument errors of the weight transform (returned before any work is
+// queued); *grid: its launch grid.
+int flip_args(const void *w, int OC, int KH, int KW, int IC, int dtype, const void *wt, dim3 *grid)
+{
+    if (!w || !wt)
+        return CONVIMG_ERR_NULL;
+    if (OC <= 0 || KH <= 0 || KW <= 0 || IC <= 0)
+        return CONVIMG_ERR_SHAPE;
+    if (dtype != CONVIMG_BF16 && dtype != CONVIMG_FP32)
+        return CONVIMG_ERR_DTYPE;
+    if ((long long)OC * KH * KW * IC >= 0x7fffffffLL)
+        return CONVIMG_ERR_RANGE;
+    const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
+    const size_t nw = (size_t)OC * KH * KW * IC * esz;
+    if (overlaps(wt, nw, w, nw))
+        return CONVIMG_ERR_ALIAS;
+    *grid = dim3((IC + kFlipTile - 1) / kFlipTile, (OC + kFlipTile - 1) / kFlipTile, KH * KW);
+    if (grid->y > 65535u || grid->z > 65535u)
+        return CONVIMG_ERR_RANGE;
+    return CONVIMG_OK;
+}
+
 // Where the split-K semaphores of a call come from.
 enum SemSource { kSemPool, kSemScratch };
 
@@ -1666,21 +1688,11 @@ void conv2d_release(void)
 int conv2d_bwd_data_weights(const void *w, int OC, int KH, int KW, int IC, int dtype, void *wt,
                             hipStream_t stream)
 {
-    if (!w || !wt)
-        return CONVIMG_ERR_NULL;
-    if (OC <= 0 || KH <= 0 || KW <= 0 || IC <= 0)
-        return CONVIMG_ERR_SHAPE;
-    if (dtype != CONVIMG_BF16 && dtype != CONVIMG_FP32)
-        return CONVIMG_ERR_DTYPE;
-    if ((long long)OC * KH * KW * IC >= 0x7fffffffLL)
-        return CONVIMG_ERR_RANGE;
+    dim3 grid;
+    const int rc = flip_args(w, OC, KH, KW, IC, dtype, wt, &grid);
+    if (rc != CONVIMG_OK)
+        return rc;
     const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
-    const size_t nw = (size_t)OC * KH * KW * IC * esz;
-    if (overlaps(wt, nw, w, nw))
-        return CONVIMG_ERR_ALIAS;
-    const dim3 grid((IC + kFlipTile - 1) / kFlipTile, (OC + kFlipTile - 1) / kFlipTile, KH * KW);
-    if (grid.y > 65535u || grid.z > 65535u)
-        return CONVIMG_ERR_RANGE;
     const int vlen = (int)(16 / esz);
     const int vec_in = (IC % vlen == 0 && ((uintptr_t)w & 15) == 0) ? 1 : 0;
     const int vec_out = (OC % vlen == 0 && ((uintptr_t)wt & 15) == 0) ? 1 : 0;
@@ -1723,6 +1735,14 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
     if (overlaps(wt, nw, dy, ny) || overlaps(dx, nx, w, nw) || overlaps(dx, nx, dy, ny)
         || overlaps(dx, nx, wt, nw))
         return CONVIMG_ERR_ALIAS;
+    // the transform's own argument errors first (before any device work,
+    // whichever path runs)
+    {
+        dim3 grid;
+        rc = flip_args(w, OC, KH, KW, IC, dtype, wt, &grid);
+        if (rc != CONVIMG_OK)
+            return rc;
+    }
     // where the mapped problem runs on the resident kernel (64 -> 64
     // channels) or the image kernel, the kernel flips and transposes the
     // forward weights in LDS (one launch, wt untouched); else the transform
