@@ -147,6 +147,13 @@ const KernelFn kResKernels[4] = {
     &igemm_resident_bf16<9, 1>, &igemm_resident_bf16<9, 2>, &igemm_resident_bf16<9, 4>,
     &igemm_resident_bf16<9, 8>,
 };
+// The same with x and out in NCHW order: [fp32 out, bf16 out][IC / 16 = 1, 2, 4, 8].
+const KernelFn kResNchwKernels[2][4] = {
+    {&igemm_resident_bf16<9, 1, kResNchwF32>, &igemm_resident_bf16<9, 2, kResNchwF32>,
+     &igemm_resident_bf16<9, 4, kResNchwF32>, &igemm_resident_bf16<9, 8, kResNchwF32>},
+    {&igemm_resident_bf16<9, 1, kResNchwBf16>, &igemm_resident_bf16<9, 2, kResNchwBf16>,
+     &igemm_resident_bf16<9, 4, kResNchwBf16>, &igemm_resident_bf16<9, 8, kResNchwBf16>},
+};
 // Image kernels by blocks of 32 output pixels per image (1 .. kImgMaxMB).
 const KernelFn kImgKernels[kImgMaxMB + 1] = {
     nullptr, &igemm_image_bf16<1>, &igemm_image_bf16<2>, &igemm_image_bf16<3>, &igemm_image_bf16<4>,
@@ -245,6 +252,9 @@ int device_info(int dev, DeviceInfo **out)
                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         for (KernelFn f : kResKernels)
             (void)hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        for (const auto &row : kResNchwKernels)
+            for (KernelFn f : row)
+                (void)hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         for (int mb = 1; mb <= kImgMaxMB; ++mb)
             (void)hipFuncSetAttribute((const void *)kImgKernels[mb],
                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
@@ -1147,7 +1157,7 @@ enum SemSource { kSemPool, kSemScratch };
 int fwd_call(const void *x, const void *w, const float *bias,
              int N, int H, int W, int IC, int OC, int KH, int KW,
              int stride, int pad, int dilation, int dtype,
-             float *out, hipStream_t stream, SemSource sems, int flipw = 0);
+             float *out, hipStream_t stream, SemSource sems, int flipw = 0, int nchw = 0);
 
 }  // namespace
 
@@ -1270,11 +1280,15 @@ namespace {
 // conv2d_fwd and conv2d_fwd_noalloc: checks, plan, launch.  `sems` says
 // where split-K semaphores come from: the library's per-stream pool (may
 // allocate on first use) or the device's static scratch array (never
-// allocates).
+// allocates).  flipw: the data backward's in-LDS weight flip (see below).
+// nchw (1: fp32 out, 2: bf16 out): x, w and out in NCHW, OIHW and NCHW
+// order, computed by the resident kernel's NCHW variant;
+// CONVIMG_ERR_UNSUPPORTED before any launch where that kernel does not
+// serve the problem.
 int fwd_call(const void *x, const void *w, const float *bias,
              int N, int H, int W, int IC, int OC, int KH, int KW,
              int stride, int pad, int dilation, int dtype,
-             float *out, hipStream_t stream, SemSource sems, int flipw)
+             float *out, hipStream_t stream, SemSource sems, int flipw, int nchw)
 {
     if (!x || !w || !out)
         return CONVIMG_ERR_NULL;
@@ -1299,12 +1313,20 @@ int fwd_call(const void *x, const void *w, const float *bias,
     const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
     const size_t nx = (size_t)N * H * W * IC * esz;
     const size_t nw = (size_t)OC * pl.K * esz;
-    const size_t no = (size_t)pl.M * OC * 4;
+    const size_t no = (size_t)pl.M * OC * (nchw == 2 ? 2 : 4);
     if (overlaps(out, no, x, nx) || overlaps(out, no, w, nw)
         || (bias && overlaps(out, no, bias, (size_t)OC * 4)))
         return CONVIMG_ERR_ALIAS;
     if (rc_dev != CONVIMG_OK)
         return rc_dev;
+    if (nchw) {
+        // the NCHW variant: resident plans, 8-pixel runs of whole rows, out
+        // 16-byte aligned, the range's 8 x 8 blocks within its loader's rounds
+        const int kind = pl.tile_id >= 0 ? kTiles[pl.tile_id].kind : -1;
+        if (kind != kResident || dtype != CONVIMG_BF16 || W % 8 != 0 || (((uintptr_t)x | (uintptr_t)out) & 15) != 0
+            || (long long)rsp.rows * (W / 8) * (IC / 8) > (long long)kResThreads * kResNchwRounds)
+            return CONVIMG_ERR_UNSUPPORTED;
+    }
 
     ConvArgs a;
     a.x = x;
@@ -1358,7 +1380,7 @@ int fwd_call(const void *x, const void *w, const float *bias,
     a.win_wp = wnp.wp;
     a.win_rb = wnp.rb;
     a.res_zero = rsp.zero;
-    a.res_scr = a.vec_out ? rsp.scr : -1;
+    a.res_scr = (a.vec_out || nchw) ? rsp.scr : -1;   // (the NCHW variant needs only out 16-byte aligned, checked above)
     a.res_flipw = 0;
     a.img_flipw = 0;
     if (flipw) {
@@ -1413,6 +1435,9 @@ int fwd_call(const void *x, const void *w, const float *bias,
     else if (kTiles[pl.tile_id].kind == kWindow)
         hipLaunchKernelGGL(kWinKernels[KH], dim3(pl.grid), dim3(pl.threads), (unsigned)pl.lds_bytes,
                            stream, a);
+    else if (kTiles[pl.tile_id].kind == kResident && nchw)
+        hipLaunchKernelGGL(kResNchwKernels[nchw - 1][res_index(IC)], dim3(pl.grid), dim3(pl.threads),
+                           (unsigned)pl.lds_bytes, stream, a);
     else if (kTiles[pl.tile_id].kind == kResident)
         hipLaunchKernelGGL(kResKernels[res_index(IC)], dim3(pl.grid), dim3(pl.threads),
                            (unsigned)pl.lds_bytes, stream, a);
@@ -1474,6 +1499,12 @@ int conv2d_fwd_nchw(const void *x, const void *w, const float *bias, int N, int 
     if (N > 65535 || OC > 65535 || tiles(IC) > 65535u || tiles(OHW) > 65535u)
         return CONVIMG_ERR_RANGE;
     char *wsb = (char *)ws;
+    // the resident kernel's NCHW variant where it serves the problem: one
+    // launch, no permute (the workspace is not used)
+    rc = fwd_call(x, w, bias, N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, (float *)out, stream,
+                  kSemPool, 0, out_dtype == CONVIMG_BF16 ? 2 : 1);
+    if (rc != CONVIMG_ERR_UNSUPPORTED)
+        return rc;
     const dim3 blk(kPermThreads);
     // x [N][IC][H*W] -> [N][H*W][IC] and w [OC][IC][KH*KW] -> [OC][KH*KW][IC],
     // one launch

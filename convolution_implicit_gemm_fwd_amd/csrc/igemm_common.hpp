@@ -71,6 +71,34 @@ __device__ __forceinline__ int fast_div(int n, FastDiv f)
     return (int)(((unsigned long long)(unsigned)n * f.mul) >> f.shift);
 }
 
+// An 8 x 8 transpose of 16-bit elements held as eight 16-byte rows: v[e]
+// holds elements (e, 0 .. 7) (element 2h in the low half of dword h);
+// out[c] receives elements (0 .. 7, c) (element 2q in the low half of dword
+// q).  In the kernels a row is 8 channels of one pixel and a column 8
+// pixels of one channel, or the other way round.
+__device__ __forceinline__ void transpose8x8(const u32x4_t (&v)[8], u32x4_t (&out)[8])
+{
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // byte selects over {hi, lo}: lo bytes are 0-3, hi bytes 4-7
+            const unsigned lo = v[2 * q][h], hi = v[2 * q + 1][h];
+            out[2 * h][q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);       // low halves
+            out[2 * h + 1][q] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // high halves
+        }
+    }
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet).
+__device__ __forceinline__ unsigned short bf16_rne(float f)
+{
+    const unsigned u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (unsigned short)((u >> 16) | 0x40u);
+    return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
 struct ConvArgs {
     const void *x;
     const void *w;

@@ -1,5 +1,7 @@
 // igemm_layout.hpp -- layout conversions around the NHWC core, for callers
-// whose tensors are NCHW (input), OIHW (weights) and NCHW (output).
+// whose tensors are NCHW (input), OIHW (weights) and NCHW (output) and
+// whose problem the resident kernel's NCHW variant (which needs none of
+// them) does not serve.
 //
 // burn-cubecl "kernel/conv/base.rs" listing: the NCHW entry points permute
 // the input to channels-last and the weight to [OC][KH][KW][IC] before the
@@ -18,15 +20,6 @@ constexpr int kPermThreads = 256;
 
 __device__ __forceinline__ float elem_to_float(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
 __device__ __forceinline__ float elem_to_float(float f) { return f; }
-
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet).
-__device__ __forceinline__ unsigned short bf16_rne(float f)
-{
-    const unsigned u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (unsigned short)((u >> 16) | 0x40u);
-    return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
 
 template <typename T>
 __device__ __forceinline__ T float_to_elem(float f);

@@ -22,6 +22,16 @@
 // lane where the output does not allow them); no copy or barrier follows
 // the prologue, so one wave's stores overlap the other waves' MFMAs.
 //
+// With LAYOUT kResNchwF32 or kResNchwBf16 the same kernel reads x in NCHW
+// order and writes out in NCHW order (fp32, or bf16 rounded to nearest
+// even): the input rows arrive as 16-byte runs of 8 pixels of one channel,
+// eight channels a lane, which the lane transposes in registers into the
+// 16-byte chunks of 8 pixel records; and each lane's accumulators already
+// hold, for one output channel, four runs of 4 consecutive pixels, stored
+// as they are.  The NCHW entry point then needs no input or output permute
+// around the GEMM; the weights then come in OIHW order too, and each
+// weight record is reordered in LDS after the copies.
+//
 // Measured on MI355X (ResNet 3x3 layer above), this order beat the
 // alternatives tried: copying the rows before the weights, tap-major weight
 // records with a barrier per tap or per kernel row (MFMAs starting before
@@ -42,9 +52,14 @@ constexpr int kResScrBytes = kResWaves * 32 * kResScrRow * 4;  // one 32-pixel x
 #define CONVIMG_RES_PF 1
 #endif
 constexpr int kResPF = CONVIMG_RES_PF;     // k steps whose fragments are in flight ahead of the MFMAs
+constexpr int kResNchwRounds = 2;          // NCHW x: 8 x 8 blocks a thread (the plan checks the rows fit)
+
+// Layouts of x and out: NHWC with fp32 out (the forward's), or NCHW with
+// fp32 or bf16 out.
+constexpr int kResNhwc = 0, kResNchwF32 = 1, kResNchwBf16 = 2;
 
 // NT: taps (KH * KW); CPS: 16-wide k steps per tap (IC / 16).
-template <int NT, int CPS>
+template <int NT, int CPS, int LAYOUT = kResNhwc>
 __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a)
 {
     extern __shared__ u32x4_t dsm[];
@@ -105,7 +120,38 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
         const unsigned wbase = (unsigned)n0 * (unsigned)K * 2u;
         const unsigned xbase = (unsigned)g_lo * (unsigned)W * (unsigned)IC * 2u;
         const int npx = nrows * W;
-        for (int i = wave; i < wins + rins; i += kResWaves) {
+        // NCHW x: a lane takes 8 channels (block cb) of 8 pixels (group pg,
+        // within one row: W % 8 == 0) of the range's rows, eight 16-byte
+        // loads from the channel planes; blocks numbered cb fastest, so 16
+        // consecutive lanes write 16 distinct bank groups.  All loads are
+        // issued before the weight copies; the transposed writes follow
+        // them (the plan's LDS rows hold at most kResThreads * kResNchwRounds
+        // blocks).
+        constexpr int CB = 2 * CPS;
+        u32x4_t xv[LAYOUT != kResNhwc ? kResNchwRounds : 1][8];
+        int xrec[LAYOUT != kResNhwc ? kResNchwRounds : 1];
+        if constexpr (LAYOUT != kResNhwc) {
+            const int nblk = (npx >> 3) * CB;
+            const unsigned plane = (unsigned)(H * W) * 2u;
+            const float inv_w = __builtin_amdgcn_rcpf((float)W), inv_h = __builtin_amdgcn_rcpf((float)H);
+            const int n_lo = g_lo / H, ih_lo = g_lo - n_lo * H;
+#pragma unroll
+            for (int r = 0; r < kResNchwRounds; ++r) {
+                const int q = r * kResThreads + tid;
+                const int cb = q & (CB - 1), px0 = 8 * (q / CB);
+                const int gr = small_div(px0, inv_w), iw0 = px0 - gr * W;
+                const int t = small_div(ih_lo + gr, inv_h);
+                const int n = n_lo + t, ih = ih_lo + gr - t * H;
+                const bool ok = q < nblk;
+                xrec[r] = ok ? a.lds_rows + px0 * prec + 16 * cb : -1;
+                const unsigned off = 2u * ((unsigned)((n * IC + 8 * cb) * H + ih) * (unsigned)W + (unsigned)iw0);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    xv[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off + (unsigned)j * plane : kOutOfRange,
+                                                                     0, 0);
+            }
+        }
+        for (int i = wave; i < (LAYOUT == kResNhwc ? wins + rins : wins); i += kResWaves) {
             if (i < wins) {
                 const int q = i * 64 + lane;
                 const int r = small_div(q, inv_wch), c = q - (int)__umul24(r, wchunks);
@@ -120,6 +166,19 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
         }
         if (tid < pchunks)
             ((u32x4_t *)zero)[tid] = u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (LAYOUT != kResNhwc) {
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int r = 0; r < kResNchwRounds; ++r) {
+                if (xrec[r] < 0)
+                    continue;
+                u32x4_t t[8];
+                transpose8x8(xv[r], t);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *(u32x4_t *)(lds + xrec[r] + e * prec) = t[e];
+            }
+        }
     }
     float bv[2];
 #pragma unroll
@@ -129,6 +188,39 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
     }
     wait_vmcnt<0>();
     __syncthreads();
+    if constexpr (LAYOUT != kResNhwc) {
+        // The weights came in OIHW order: record oc holds w[oc][ic][t] at
+        // element 9 ic + t.  Reorder each record in place to element
+        // t IC + ic (the OHWI record the k steps read).  A task is the
+        // channel pair 2p, 2p + 1 of one record: its 18 elements are the 9
+        // dwords at byte 36 p, and output dword t pairs (2p, t) with
+        // (2p + 1, t), at byte 2 (t IC + 2p).  Every read completes before
+        // any write.
+        static_assert(NT == 9, "the NCHW variant serves 3x3 kernels");
+        constexpr int ICN = 16 * CPS, PAIRS = ICN / 2, NTASK = 64 * PAIRS / kResThreads;
+        unsigned d[NTASK][NT];
+#pragma unroll
+        for (int k = 0; k < NTASK; ++k) {
+            const int T = k * kResThreads + tid;
+            const char *const src = lds + (T / PAIRS) * wrec + 36 * (T % PAIRS);
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                d[k][j] = *(const unsigned *)(src + 4 * j);
+        }
+        wait_lgkmcnt0();
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NTASK; ++k) {
+            const int T = k * kResThreads + tid;
+            char *const dst = lds + (T / PAIRS) * wrec + 4 * (T % PAIRS);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *(unsigned *)(dst + 2 * ICN * t) =
+                    __builtin_amdgcn_perm(d[k][(NT + t) >> 1], d[k][t >> 1], (t & 1) ? 0x05040302u : 0x07060100u);
+        }
+        wait_lgkmcnt0();
+        __syncthreads();
+    }
     if (a.res_flipw) {
         // The data backward's mapped problem, its weights copied as the
         // forward's are (64 x 64 channels): record oc holds w[oc][t][ic].
@@ -162,7 +254,13 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
         __syncthreads();
     }
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.out_bytes, kRsrcWord3);
-    const int nunits = (m_b - m_a + 31) / 32;
+    // units of 32 pixels from the range's start; in NCHW order from the
+    // 32-pixel boundary at or before it, so that where OH * OW % 32 == 0 a
+    // whole unit's run of each channel is one aligned 128-byte line (fp32)
+    // or half of one (bf16).  Pixels of a unit outside the range are
+    // computed from an in-range pixel and never stored.
+    const int ubase = LAYOUT == kResNhwc ? m_a : (m_a & ~31);
+    const int nunits = (m_b - ubase + 31) / 32;
     const float inv_ohw = __builtin_amdgcn_rcpf((float)ohw), inv_ow = __builtin_amdgcn_rcpf((float)a.OW);
     // this lane's part of each output offset: row 4 lk of a unit, channel lr
     const unsigned lane_out = 4u * (__umul24(4 * lk, a.OC) + (unsigned)lr);
@@ -170,9 +268,9 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
     const char *const b0 = lds + lr * wrec + 16 * lk;
     const char *const b1 = b0 + 32 * wrec;
     for (int u = wave; u < nunits; u += kResWaves) {
-        const int m0 = m_a + 32 * u;
+        const int m0 = ubase + 32 * u;
         // this lane's output pixel (past the range: any pixel, never stored)
-        const int m = min(m0 + lr, m_b - 1);
+        const int m = min(max(m0 + lr, m_a), m_b - 1);
         const int n = small_div(m, inv_ohw);
         const int rem = m - (int)__umul24(n, ohw);
         const int oh = small_div(rem, inv_ow);
@@ -227,6 +325,135 @@ __global__ __launch_bounds__(kResThreads, 1) void igemm_resident_bf16(ConvArgs a
         }
         acc0 += acc2;
         acc1 += acc3;
+        if constexpr (LAYOUT != kResNhwc) {
+            // NCHW: value v of block j is channel oc = n0 + 32 j + lr at pixel
+            // m0 + 8 (v >> 2) + 4 lk + (v & 3).
+            constexpr int ES = LAYOUT == kResNchwBf16 ? 2 : 4;
+            if (a.res_scr >= 0) {
+                // Through this wave's scratch, channel-major (36 floats a
+                // channel: the 16 lanes of a 128-bit write pass fall on 16
+                // distinct bank groups), read back as 16 bytes a lane: 4
+                // (fp32) or 8 (bf16) consecutive pixels of one channel.  A
+                // unit wholly inside the range, in one image, on a 32-pixel
+                // boundary of it (OH * OW % 32 == 0) stores 16 bytes a lane:
+                // whole lines (fp32, streaming stores) or half lines (bf16,
+                // the default policy: streaming stores of partial lines cost
+                // more than the kernel's MFMAs here); other units store
+                // element by element, their lines shared with the
+                // neighbouring range's first or last unit.
+                float *const scr = (float *)(lds + a.res_scr) + wave * (32 * kResScrRow);
+                const bool full = m0 >= m_a && m0 + 32 <= m_b && ohw % 32 == 0;
+                const int nu = small_div(max(m0, m_a), inv_ohw);
+                const int p0 = m0 - (int)__umul24(nu, ohw);
+                constexpr int LPC = ES == 4 ? 8 : 4;          // lanes a channel run
+                constexpr int PPL = 32 / LPC;                 // pixels a lane
+                const int cl = lane / LPC, q = lane % LPC;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const floatx16_t &acc = j == 0 ? acc0 : acc1;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *(floatx4_t *)(scr + lr * kResScrRow + 8 * i + 4 * lk) =
+                            floatx4_t{acc[4 * i] + bv[j], acc[4 * i + 1] + bv[j], acc[4 * i + 2] + bv[j],
+                                      acc[4 * i + 3] + bv[j]};
+#pragma unroll
+                    for (int i = 0; i < 32 / (64 / LPC); ++i) {
+                        const int c = i * (64 / LPC) + cl;
+                        const int oc = n0 + 32 * j + c;
+                        float v[PPL];
+#pragma unroll
+                        for (int h4 = 0; h4 < PPL / 4; ++h4) {
+                            const floatx4_t t = *(const floatx4_t *)(scr + c * kResScrRow + PPL * q + 4 * h4);
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                v[4 * h4 + b] = t[b];
+                        }
+                        if (full) {
+                            const unsigned off = oc < a.OC
+                                ? ES * ((unsigned)(nu * a.OC + oc) * (unsigned)ohw + (unsigned)(p0 + PPL * q))
+                                : kOutOfRange;
+                            u32x4_t val;
+                            if constexpr (ES == 2) {
+#pragma unroll
+                                for (int b = 0; b < 4; ++b)
+                                    val[b] = (unsigned)bf16_rne(v[2 * b]) | ((unsigned)bf16_rne(v[2 * b + 1]) << 16);
+                            } else {
+#pragma unroll
+                                for (int b = 0; b < 4; ++b)
+                                    val[b] = __float_as_uint(v[b]);
+                            }
+                            // streaming where the unit's run is a whole line
+                            if constexpr (ES == 4)
+                                __builtin_amdgcn_raw_buffer_store_b128(val, ro, off, 0, kOutAux);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b128(val, ro, off, 0, 0);
+                        } else {
+#pragma unroll
+                            for (int b = 0; b < PPL; ++b) {
+                                const int mm = m0 + PPL * q + b;
+                                const int nb = small_div(min(max(mm, m_a), m_b - 1), inv_ohw);
+                                const int pb = mm - (int)__umul24(nb, ohw);
+                                const unsigned off = (mm >= m_a && mm < m_b && oc < a.OC)
+                                    ? ES * ((unsigned)(nb * a.OC + oc) * (unsigned)ohw + (unsigned)pb) : kOutOfRange;
+                                if constexpr (ES == 2)
+                                    __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(v[b]), ro, off, 0, 0);
+                                else
+                                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[b]), ro, off, 0, 0);
+                            }
+                        }
+                    }
+                }
+                continue;
+            }
+            // else from the accumulators: values 4 i .. 4 i + 3 are 4
+            // consecutive pixels; one 16-byte (fp32) or 8-byte (bf16) store
+            // where they lie inside the range, in one image, on a 4-pixel
+            // boundary of it (out is 16-byte aligned), else one element at
+            // a time; default policy (the pieces of a line meet in L2).
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int mq = m0 + 8 * i + 4 * lk;
+                const int nq = small_div(min(max(mq, m_a), m_b - 1), inv_ohw);
+                const int pq = mq - (int)__umul24(nq, ohw);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int oc = n0 + 32 * j + lr;
+                    const floatx16_t &acc = j == 0 ? acc0 : acc1;
+                    float v[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        v[b] = acc[4 * i + b] + bv[j];
+                    if (mq >= m_a && mq + 3 < m_b && oc < a.OC && (pq & 3) == 0 && pq + 3 < ohw) {
+                        const unsigned off = ES * ((unsigned)(nq * a.OC + oc) * (unsigned)ohw + (unsigned)pq);
+                        if constexpr (ES == 2) {
+                            const unsigned lo = (unsigned)bf16_rne(v[0]) | ((unsigned)bf16_rne(v[1]) << 16);
+                            const unsigned hi = (unsigned)bf16_rne(v[2]) | ((unsigned)bf16_rne(v[3]) << 16);
+                            typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+                            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, ro, off, 0, 0);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                        __float_as_uint(v[3])},
+                                ro, off, 0, 0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const int mm = mq + b;
+                            const int nb = small_div(min(max(mm, m_a), m_b - 1), inv_ohw);
+                            const int pb = mm - (int)__umul24(nb, ohw);
+                            const unsigned off = (mm >= m_a && mm < m_b && oc < a.OC)
+                                ? ES * ((unsigned)(nb * a.OC + oc) * (unsigned)ohw + (unsigned)pb) : kOutOfRange;
+                            if constexpr (ES == 2)
+                                __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(v[b]), ro, off, 0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[b]), ro, off, 0, 0);
+                        }
+                    }
+                }
+            }
+            continue;
+        }
         // value v of block j: pixel m0 + 8*(v >> 2) + 4*lk + (v & 3), channel
         // n0 + j*32 + lr
         if (a.res_scr >= 0) {

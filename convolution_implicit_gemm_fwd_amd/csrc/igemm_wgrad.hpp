@@ -114,22 +114,6 @@ __device__ __forceinline__ int wg_rec(int row, int chunk)
     return row * kWgRowBytes + ((chunk ^ ((row >> 3) & 7)) << 4);
 }
 
-// v[e] holds 8 channels of pixel e (channel 2h in the low half of dword h);
-// out[c] receives 8 pixels of channel c (pixel 2q in the low half of dword q).
-__device__ __forceinline__ void transpose8x8(const u32x4_t (&v)[8], u32x4_t (&out)[8])
-{
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            // byte selects over {hi, lo}: lo bytes are 0-3, hi bytes 4-7
-            const unsigned lo = v[2 * q][h], hi = v[2 * q + 1][h];
-            out[2 * h][q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);       // low halves
-            out[2 * h + 1][q] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // high halves
-        }
-    }
-}
-
 // A wave's results: acc[i][j] (i < NI, j < NJ) is the 16x16 block at rows
 // oc0 + 16 i, columns jc[j] .. jc[j] + 15 of dw; lane l holds rows 4 (l >> 4) .. +3 of
 // column jc[j] + (l & 15).  Without `inplace`, range `split` writes its

@@ -223,6 +223,11 @@ int conv2d_fwd_test_spin_limit(int iterations);
 /* NCHW tensors (burn-cubecl "kernel/conv/base.rs" listing: its NCHW entry
  * points permute the input to channels-last and the weights to
  * [OC][KH][KW][IC], run the NHWC convolution and permute the result back).
+ * Here bf16 problems that conv2d_fwd runs on its resident kernel (3x3),
+ * with W % 8 == 0 and x and out 16-byte aligned, take one launch of that
+ * kernel's NCHW variant instead, which reads x and w and writes out in
+ * these layouts itself (the workspace is then not used); every other
+ * problem takes the permutes around conv2d_fwd.
  *
  *   x     device, N x IC x H x W (NCHW) in `dtype`
  *   w     device, OC x IC x KH x KW (OIHW) in `dtype`
@@ -231,9 +236,10 @@ int conv2d_fwd_test_spin_limit(int iterations);
  *         CONVIMG_BF16: the fp32 result rounded to nearest even), fully
  *         overwritten
  *   ws    device workspace of ws_bytes >= conv2d_fwd_nchw_workspace bytes,
- *         caller-owned: receives the NHWC copy of x, the OHWI copy of w and
- *         the fp32 NHWC result, which conv2d_fwd computes (so a bf16 output
- *         never serves as the split-K accumulation buffer)
+ *         caller-owned: on the permute route receives the NHWC copy of x,
+ *         the OHWI copy of w and the fp32 NHWC result, which conv2d_fwd
+ *         computes (so a bf16 output never serves as the split-K
+ *         accumulation buffer); required on both routes
  *   other arguments and the output extent as for conv2d_fwd
  *
  * Errors (before any work is queued): those of conv2d_fwd;

@@ -1,6 +1,12 @@
 """GPU parity of the NCHW entry point (conv2d_fwd_nchw) against the fp64
 oracle, whose NHWC result is permuted to NCHW here.
 
+Two routes: the resident kernel's NCHW variant (bf16 input, 3x3 resident
+plans, W % 8 == 0: reads NCHW x and writes NCHW out itself, so the
+workspace's x and result regions stay untouched), and the permutes around
+conv2d_fwd (every other problem).  The workspace is pre-filled with a byte
+pattern to tell them apart.
+
 fp32 output: |err| <= 1e-3*S + 1e-5, as for conv2d_fwd.  bf16 output: the
 fp32 result rounded to nearest even adds at most 2^-8 of its magnitude, so
 |err| <= (1e-3*S + 1e-5)*(1 + 2^-8) + 2^-8*|y_oracle|.  The output is
@@ -34,7 +40,8 @@ def dev(a, is_bf16):
     return torch.from_numpy(a).cuda()
 
 
-def nchw_parity(wl, out_bf16=False, dtype=None, use_bias=True):
+def nchw_parity(wl, out_bf16=False, dtype=None, use_bias=True, fused=None):
+    """fused: None (either route), True / False (the route that must run)."""
     dtype = wl.dtype if dtype is None else dtype
     inp = make_inputs(wl, seed=6, dtype=dtype)
     is_bf16 = dtype == BF16
@@ -47,7 +54,7 @@ def nchw_parity(wl, out_bf16=False, dtype=None, use_bias=True):
     rc, need = abi.conv2d_fwd_nchw_workspace(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
                                              wl.stride, wl.pad, wl.dilation, dtype)
     assert rc == 0
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
     odt = torch.bfloat16 if out_bf16 else torch.float32
     out = torch.full((n_out + GUARD,), float("nan"), dtype=odt, device="cuda")
     out[n_out:] = 7.0
@@ -58,6 +65,10 @@ def nchw_parity(wl, out_bf16=False, dtype=None, use_bias=True):
                              ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
     assert rc == 0, abi.conv2d_strerror(rc)
     torch.cuda.synchronize()
+    nx = wl.N * wl.IC * wl.H * wl.W * (2 if is_bf16 else 4)
+    if fused is not None:
+        untouched = bool((ws[:nx] == 0xA5).all().item())
+        assert untouched == fused, "expected the %s route" % ("fused" if fused else "permute")
     host = out.float().cpu().numpy()
     assert (host[n_out:] == 7.0).all(), "write past the end of out"
     y = host[:n_out].reshape(wl.N, wl.OC, OH, OW)
@@ -87,6 +98,33 @@ def test_nchw_fp32_out(wl):
 @pytest.mark.parametrize("wl", CASES[:3] + CASES[4:5], ids=lambda w: w.name)
 def test_nchw_bf16_out(wl):
     nchw_parity(wl, out_bf16=True)
+
+
+FUSED = [WORKLOADS["resnet3x3"].scaled(N=2, name="resnet3x3 N=2"),
+         shape(6, 28, 40, 64, 64, 3, 3, 1, 1, 1, name="ranges of 26-27 px across images"),
+         shape(20, 32, 32, 32, 64, 3, 3, 1, 1, 1, name="IC 32, ranges of 80 px across images"),
+         shape(3, 7, 8, 64, 64, 3, 3, 1, 0, 1, name="OH*OW 30, one pixel a range"),
+         shape(4, 20, 24, 16, 40, 3, 3, 1, 1, 1, name="IC 16 OC 40"),
+         shape(2, 9, 24, 32, 72, 3, 3, 2, 1, 1, name="IC 32 stride 2, OC 72"),
+         shape(1, 6, 8, 128, 64, 3, 3, 1, 1, 2, name="IC 128 dilation 2")]
+
+
+@pytest.mark.parametrize("out_bf16", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("wl", FUSED, ids=lambda w: w.name)
+def test_nchw_fused_route(wl, out_bf16):
+    """The resident kernel's NCHW variant: parity, and the workspace's x
+    region untouched (no input permute ran)."""
+    nchw_parity(wl, out_bf16=out_bf16, fused=True)
+
+
+def test_nchw_route_choice():
+    """Problems the NCHW variant does not serve take the permutes: W % 8 != 0
+    on a resident plan, a non-resident plan, fp32 storage."""
+    nchw_parity(shape(2, 14, 14, 64, 64, 3, 3, 1, 1, 1, name="W 14"), fused=False)
+    nchw_parity(WORKLOADS["largek"].scaled(N=1, name="largek N=1"), fused=False)
+    nchw_parity(WORKLOADS["tiny"], dtype=FP32, fused=False)
+    nchw_parity(WORKLOADS["resnet3x3"], fused=True)
+    nchw_parity(shape(3, 12, 16, 64, 64, 3, 3, 1, 1, 1, name="null bias"), use_bias=False, fused=True)
 
 
 def test_nchw_fp32_storage_and_null_bias():
