@@ -13,9 +13,14 @@ into ranges, the ordered sum of the ranges; the roofline object prices the
 whole call.
 
 --op dgrad times conv2d_bwd_data instead (the gradient with respect to the
-input, stride-1 workloads only): a step is the weight flip-transpose plus
-the forward implicit GEMM it maps to; the roofline object then prices that
-GEMM kernel alone (timed in its own loop on the same buffers).
+input, stride-1 workloads only): a step is the forward implicit GEMM it maps
+to, whose kernel flips and transposes the weights in LDS where it can (one
+launch), else the separate weight transform plus that GEMM; in the latter
+case the roofline object prices the GEMM kernel alone (timed in its own
+loop on the same buffers).
+
+--nchw f32|bf16 times conv2d_fwd_nchw on NCHW / OIHW copies of the same
+inputs (fp32 or bf16 NCHW output).
 
 Timing: 11 windows (--windows) of K back-to-back calls on one stream, each
 between two HIP events recorded on that stream and synchronised on both
@@ -55,25 +60,27 @@ MACHINE_BALANCE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per by
 # hash of that kernel family's sources.  Reported only while the plan and
 # the sources are unchanged; otherwise traffic is null.
 TRAFFIC = {
-    # profiles/igemm_resident_resnet3x3.md: 7.134 MB read + 12.845 MB written
-    "resnet3x3": {"bytes": 19978712, "tile": 33, "kernel": "d0577a4ca5fffa80"},
-    # profiles/igemm_image_largek.md: 25.598 MB read + 6.423 MB written
-    "largek": {"bytes": 32020104, "tile": 34, "kernel": "2dfdbad2f8f6097c"},
-    # profiles/igemm_window_stem7x7.md: 5.287 MB read + 51.380 MB written
-    "stem7x7": {"bytes": 56667036, "tile": 32, "kernel": "a434d75e49f3ce1e"},
-    # profiles/igemm_pipe_dilated.md: 19.912 MB read + 33.554 MB written
-    "dilated": {"bytes": 53466020, "tile": 15, "kernel": "799da7af733cc74c"},
-    # data backward, the GEMM on the mapped problem (--op dgrad)
-    # profiles/dgrad_resident_resnet3x3.md
-    "dgrad:resnet3x3": {"bytes": 19976604, "tile": 33, "kernel": "d0577a4ca5fffa80"},
-    # profiles/dgrad_image_largek.md
-    "dgrad:largek": {"bytes": 32011860, "tile": 34, "kernel": "2dfdbad2f8f6097c"},
+    # profiles/igemm_resident_resnet3x3.md: 7.162 MB read + 12.845 MB written
+    "resnet3x3": {"bytes": 20007329, "tile": 33, "kernel": "4cb778c4babd73af"},
+    # profiles/igemm_image_largek.md: 25.638 MB read + 6.423 MB written
+    "largek": {"bytes": 32060100, "tile": 34, "kernel": "b5fa9f7b6da1e3fe"},
+    # profiles/igemm_window_stem7x7.md: 5.283 MB read + 51.380 MB written
+    "stem7x7": {"bytes": 56662923, "tile": 32, "kernel": "cc44bd8bb5fdb554"},
+    # profiles/igemm_pipe_dilated.md: 19.915 MB read + 33.554 MB written
+    "dilated": {"bytes": 53469028, "tile": 15, "kernel": "97d2b4355ecb97cc"},
+    # data backward: one launch, the GEMM kernel flipping the weights in LDS
+    # (--op dgrad); profiles/dgrad_resident_resnet3x3.md, dgrad_image_largek.md
+    "dgrad:resnet3x3": {"bytes": 20009376, "tile": 33, "kernel": "4cb778c4babd73af"},
+    "dgrad:largek": {"bytes": 32051800, "tile": 34, "kernel": "b5fa9f7b6da1e3fe"},
+    # NCHW entry point with bf16 out: one launch of the resident kernel's
+    # NCHW variant (--nchw bf16); profiles/nchw_resident_resnet3x3.md
+    "nchw_bf16:resnet3x3": {"bytes": 13725142, "tile": 33, "kernel": "4cb778c4babd73af"},
     # weight backward: the whole call (igemm_wgrad_row_bf16, + wgrad_reduce
     # where the ranges go through the workspace), as the --op wgrad roofline
     # times it; profiles/igemm_wgrad_*.md
-    "wgrad:resnet3x3": {"bytes": 36184133, "tile": -2, "kernel": "0c7e15dc67145a3f"},
-    "wgrad:largek": {"bytes": 44504399, "tile": -2, "kernel": "0c7e15dc67145a3f"},
-    "wgrad:dilated": {"bytes": 68871200, "tile": -2, "kernel": "0c7e15dc67145a3f"},
+    "wgrad:resnet3x3": {"bytes": 36184191, "tile": -2, "kernel": "a59ae32436ecbf96"},
+    "wgrad:largek": {"bytes": 44504409, "tile": -2, "kernel": "a59ae32436ecbf96"},
+    "wgrad:dilated": {"bytes": 68872306, "tile": -2, "kernel": "a59ae32436ecbf96"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
@@ -308,7 +315,9 @@ def main():
         # x holds dy [N,OH,OW,OC]; the data backward maps to a forward
         # convolution of dy with the flipped, transposed weights
         out = torch.empty((wl.N, wl.H, wl.W, wl.IC), dtype=torch.float32, device="cuda")
-        wt = torch.empty_like(w)
+        # a byte pattern that no transform leaves: tells the one-launch path
+        # (wt untouched) from the transform + GEMM path
+        wt = torch.full(w.shape, 0x7F81, dtype=torch.int16, device="cuda").view(w.dtype)
         call_args = (x.data_ptr(), w.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
                      1, wl.pad, wl.dilation, wl.dtype, wt.data_ptr(), out.data_ptr(), sptr)
         fn = lib.conv2d_bwd_data
@@ -329,6 +338,8 @@ def main():
         call_args = ((xn.data_ptr(), wn.data_ptr(), b.data_ptr()) + gemm
                      + (wl.dtype, od, out.data_ptr(), ws.data_ptr(), need, sptr))
         fn = lib.conv2d_fwd_nchw
+        if od == BF16:
+            alg_bytes -= M * wl.OC * 2
     tuned = None
     if args.autotune and args.op == "fwd":
         rc, t_tile, t_splits, t_best, t_default = abi.conv2d_fwd_autotune(*call_args)
@@ -345,7 +356,8 @@ def main():
     ms_step, ms_min, ms_max, host_ms = timed(fn, call_args, args.steps, args.warmup, stream,
                                              args.windows)
     assert abi.conv2d_fwd_status(sptr) == 0
-    if dgrad:
+    one_launch = dgrad and bool((wt.view(torch.int16) == 0x7F81).all().item())
+    if dgrad and not one_launch:
         # the implicit-GEMM kernel alone, on the weights the steps left in wt
         gemm_args = (x.data_ptr(), wt.data_ptr(), None) + gemm + (wl.dtype, out.data_ptr(), sptr)
         ms_gemm = timed(lib.conv2d_fwd, gemm_args, args.steps, args.warmup, stream, args.windows)[0]
@@ -373,7 +385,8 @@ def main():
     kind = (abi.conv2d_fwd_tile_kind(plan["tile_id"]) if plan["tile_id"] >= 0
             else -2 if wgrad else -1)
     ksrc = kernel_sources_hash(kind)
-    t = None if args.nchw else TRAFFIC.get(wl.name if args.op == "fwd" else args.op + ":" + wl.name)
+    t = TRAFFIC.get("nchw_%s:%s" % (args.nchw, wl.name) if args.nchw
+                    else wl.name if args.op == "fwd" else args.op + ":" + wl.name)
     roof["traffic"] = (t["bytes"] if t and t["tile"] == plan["tile_id"] and t["kernel"] == ksrc
                        else None)
 
@@ -413,6 +426,7 @@ def main():
     }
     if dgrad:
         line["gemm_ms"] = round(ms_gemm, 6)
+        line["dgrad_launches"] = 1 if one_launch else 2
     if cold is not None:
         line["cold_single_call"] = cold
     if tuned is not None:
