@@ -22,6 +22,11 @@ loop on the same buffers).
 --nchw f32|bf16 times conv2d_fwd_nchw on NCHW / OIHW copies of the same
 inputs (fp32 or bf16 NCHW output).
 
+The default run (the ResNet-style forward) also times the other named
+forward configurations -- the large-K layer, the RGB stem and the dilated
+layer -- after its own measurement, 3 windows each, and reports them under
+other_configs (--no-others skips them); `value` is the main workload's.
+
 Timing: 11 windows (--windows) of K back-to-back calls on one stream, each
 between two HIP events recorded on that stream and synchronised on both
 sides; before each window's start event a sleep kernel holds the stream
@@ -128,6 +133,9 @@ def parse():
                     help="bound on the CPU-baseline sample (0 disables it)")
     ap.add_argument("--force", default=None,
                     help="tile,splits,loader to force instead of the automatic plan (-1 = auto)")
+    ap.add_argument("--others", action=argparse.BooleanOptionalAction, default=True,
+                    help="(default forward run) also time the other named forward configurations "
+                         "after the main measurement and report them under other_configs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -245,6 +253,55 @@ def timed_cold(fn, call_args, stream, launches=11, scrub_mib=1024):
         us.append(e0.elapsed_time(e1) * 1e3)
     del scrub
     return statistics.median(us), min(us)
+
+
+def time_other_forward(names, steps, warmup, windows, stream):
+    """The other named forward configurations, each on its own seeded
+    inputs with its automatic plan, timed like the main line (fewer
+    windows): {name: {us_per_call, tflops, mfma_peak_frac, roofline}}.
+    Reported beside the main line, outside its timed region."""
+    import numpy as np
+    import torch
+    from convolution_implicit_gemm_fwd_amd import abi
+    from convolution_implicit_gemm_fwd_amd.workloads import BF16, WORKLOADS, make_inputs
+    lib = abi.load()
+    sptr = stream.cuda_stream
+    res = {}
+    for name in names:
+        wl = WORKLOADS[name]
+        OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
+        OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
+        M, K = wl.N * OH * OW, wl.IC * wl.KH * wl.KW
+        inp = make_inputs(wl, seed=0)
+
+        def up(a):
+            t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
+            return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).cuda()
+
+        x, w, b = up(inp.x_store), up(inp.w_store), torch.from_numpy(inp.bias).cuda()
+        out = torch.empty((wl.N, OH, OW, wl.OC), dtype=torch.float32, device="cuda")
+        args = ((x.data_ptr(), w.data_ptr(), b.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
+                 wl.stride, wl.pad, wl.dilation, wl.dtype, out.data_ptr(), sptr))
+        ms = timed(lib.conv2d_fwd, args, steps, warmup, stream, windows)[0]
+        esz = 2 if wl.dtype == BF16 else 4
+        flops = 2 * M * wl.OC * K
+        alg = (wl.N * wl.H * wl.W * wl.IC + wl.OC * K) * esz + wl.OC * 4 + M * wl.OC * 4
+        tfl = flops / (ms * 1e-3) / 1e12
+        if flops / alg < MACHINE_BALANCE:
+            gbs = alg / (ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        else:
+            roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tfl / PEAK_BF16_TFLOPS, 4)}
+        rc, plan = abi.conv2d_fwd_plan(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW, wl.stride, wl.pad,
+                                       wl.dilation, wl.dtype, 0)
+        res[name] = {"us_per_call": round(ms * 1e3, 3), "tflops": round(tfl, 2),
+                     "mfma_peak_frac": round(tfl / PEAK_BF16_TFLOPS, 4), "roofline": roof,
+                     "tile_id": plan["tile_id"] if rc == 0 else None,
+                     "steps": steps, "windows": windows}
+        del x, w, b, out
+    return res
 
 
 def main():
@@ -431,6 +488,10 @@ def main():
         line["cold_single_call"] = cold
     if tuned is not None:
         line["autotune"] = tuned
+    if args.others and args.op == "fwd" and not args.nchw and not args.force and not args.autotune \
+            and args.workload == "resnet3x3":
+        line["other_configs"] = time_other_forward(("largek", "stem7x7", "dilated"), min(args.steps, 500),
+                                                   min(args.warmup, 50), 3, stream)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(inp, wl, flops, args.cpu_seconds, args.op)
     print(json.dumps(line), flush=True)
