@@ -133,6 +133,9 @@ def parse():
                     help="bound on the CPU-baseline sample (0 disables it)")
     ap.add_argument("--force", default=None,
                     help="tile,splits,loader to force instead of the automatic plan (-1 = auto)")
+    ap.add_argument("--storage", choices=("bf16", "fp32"), default=None,
+                    help="store x and w (dy) in this type instead of the workload's own "
+                         "(fp32: the fp32 kernels, products and sums in fp32)")
     ap.add_argument("--others", action=argparse.BooleanOptionalAction, default=True,
                     help="(default forward run) also time the other named forward configurations "
                          "after the main measurement and report them under other_configs")
@@ -324,11 +327,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     lib = abi.load()                # fails loudly if the HIP library is not built
     wl = WORKLOADS[args.workload]
+    if args.storage and (BF16 if args.storage == "bf16" else 1) != wl.dtype:
+        wl = wl.scaled(dtype=BF16 if args.storage == "bf16" else 1,
+                       name="%s, %s storage" % (wl.name, args.storage))
     dgrad = args.op == "dgrad"
     wgrad = args.op == "wgrad"
-    if wgrad and wl.dtype != BF16:
-        print("--op wgrad takes bf16 storage (%s stores fp32)" % wl.name, file=sys.stderr)
-        sys.exit(2)
     if dgrad and wl.stride != 1:
         print("--op dgrad needs a stride-1 workload (%s has stride %d)" % (wl.name, wl.stride),
               file=sys.stderr)
@@ -336,8 +339,9 @@ def main():
     OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
     OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
     M, K = wl.N * OH * OW, wl.IC * wl.KH * wl.KW
-    inp = (make_grad_inputs(wl, OH, OW, seed=0) if dgrad
-           else make_wgrad_inputs(wl, OH, OW, seed=0) if wgrad else make_inputs(wl, seed=0))
+    inp = (make_grad_inputs(wl, OH, OW, seed=0, dtype=wl.dtype) if dgrad
+           else make_wgrad_inputs(wl, OH, OW, seed=0, dtype=wl.dtype) if wgrad
+           else make_inputs(wl, seed=0))
 
     def up(a):
         t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
@@ -407,7 +411,7 @@ def main():
     assert rc == 0, abi.conv2d_strerror(rc)
     if wgrad:
         # the weight backward has its own kernel; report its workspace instead
-        plan = {"tile_id": -2, "BM": 64, "BN": 192, "BK": 64, "loader": -1, "splits": None,
+        plan = {"tile_id": -2, "BM": 64, "BN": 192 if wl.dtype == BF16 else 64, "BK": 64, "loader": -1, "splits": None,
                 "grid": None, "workspace_bytes": need}
 
     ms_step, ms_min, ms_max, host_ms = timed(fn, call_args, args.steps, args.warmup, stream,
@@ -459,7 +463,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == BF16 else "f32",
-        "data": ("synthetic (seeded; x %s, dy N(0, sd 1); bf16-rounded)" % dist_text(wl.x_dist)
+        "data": ("synthetic (seeded; x %s, dy N(0, sd 1); %s)" % (
+                     dist_text(wl.x_dist), "bf16-rounded" if wl.dtype == BF16 else "fp32 as drawn")
                  if wgrad else
                  "synthetic (seeded; %s %s, w %s%s; bf16-rounded)" % (
                      "dy" if dgrad else "x", dist_text(wl.x_dist), dist_text(wl.w_dist),
@@ -489,7 +494,7 @@ def main():
     if tuned is not None:
         line["autotune"] = tuned
     if args.others and args.op == "fwd" and not args.nchw and not args.force and not args.autotune \
-            and args.workload == "resnet3x3":
+            and not args.storage and args.workload == "resnet3x3":
         line["other_configs"] = time_other_forward(("largek", "stem7x7", "dilated"), min(args.steps, 500),
                                                    min(args.warmup, 50), 3, stream)
     if args.cpu_seconds > 0:

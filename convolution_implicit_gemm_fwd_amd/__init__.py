@@ -161,8 +161,9 @@ def conv2d_bwd_weight_nhwc(x, dy, KH, KW, stride=1, pad=0, dilation=1, dw=None, 
                            stream=None):
     """dw[OC,KH,KW,IC] (fp32): gradient of conv2d_nhwc's output with respect to w.
 
-    x: contiguous bfloat16 [N,H,W,IC] device tensor, dy: contiguous bfloat16
-    [N,OH,OW,OC] (the output gradient); KH, KW, stride, pad, dilation: the
+    x: contiguous [N,H,W,IC] device tensor, dy: contiguous [N,OH,OW,OC] (the
+    output gradient), both bfloat16 or both float32 (fp32 storage: the fp32
+    kernel); KH, KW, stride, pad, dilation: the
     forward problem.  ws: optional uint8 device workspace of at least
     ``conv2d_bwd_weight_workspace`` bytes (allocated here when needed and not
     given); dw: optional preallocated output.  Runs on ``stream`` (default:
@@ -170,8 +171,9 @@ def conv2d_bwd_weight_nhwc(x, dy, KH, KW, stride=1, pad=0, dilation=1, dw=None, 
     """
     import torch
 
-    if x.dtype != torch.bfloat16 or dy.dtype != torch.bfloat16:
-        raise TypeError("the weight backward takes bfloat16 x and dy")
+    if x.dtype != dy.dtype or x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("the weight backward takes x and dy both bfloat16 or both float32")
+    dtype = CONVIMG_BF16 if x.dtype == torch.bfloat16 else CONVIMG_FP32
     if not (x.is_cuda and dy.is_cuda):
         raise ValueError("x and dy must be device tensors")
     if x.dim() != 4 or dy.dim() != 4 or x.shape[0] != dy.shape[0]:
@@ -185,7 +187,7 @@ def conv2d_bwd_weight_nhwc(x, dy, KH, KW, stride=1, pad=0, dilation=1, dw=None, 
         raise ValueError("dy's extent is not the forward output extent of H x W")
     with torch.cuda.device(x.device):
         rc, need = conv2d_bwd_weight_workspace(N, H, W, IC, OC, KH, KW, stride, pad, dilation,
-                                               CONVIMG_BF16)
+                                               dtype)
         if rc != 0:
             raise RuntimeError("conv2d_bwd_weight_workspace failed: %s (status %d)"
                                % (conv2d_strerror(rc), rc))
@@ -203,7 +205,7 @@ def conv2d_bwd_weight_nhwc(x, dy, KH, KW, stride=1, pad=0, dilation=1, dw=None, 
         ws_ptr = ws.data_ptr() if ws is not None else None
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
         rc = conv2d_bwd_weight(x.data_ptr(), dy.data_ptr(), N, H, W, IC, OC, KH, KW, stride, pad,
-                               dilation, CONVIMG_BF16, dw.data_ptr(), ws_ptr, ws_bytes, stream)
+                               dilation, dtype, dw.data_ptr(), ws_ptr, ws_bytes, stream)
     if rc != 0:
         raise RuntimeError("conv2d_bwd_weight failed: %s (status %d)" % (conv2d_strerror(rc), rc))
     if not current:

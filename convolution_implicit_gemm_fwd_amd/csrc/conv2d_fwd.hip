@@ -988,11 +988,10 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
     int rc = make_plan(N, H, W, IC, OC, KH, KW, s, p, d, dtype, 1, true, nullptr, &fwd);
     if (rc != CONVIMG_OK)
         return rc;
-    if (dtype != CONVIMG_BF16)
-        return CONVIMG_ERR_UNSUPPORTED;
     const long long lim = 0x7fffffffLL;
+    const int esz = dtype == CONVIMG_FP32 ? 4 : 2;
     // x and dy are read through buffer resources with 32-bit byte offsets
-    if ((long long)N * H * W * IC * 2 >= lim || fwd.M * OC * 2 >= lim)
+    if ((long long)N * H * W * IC * esz >= lim || fwd.M * OC * esz >= lim)
         return CONVIMG_ERR_RANGE;
     wp->OH = fwd.OH;
     wp->OW = fwd.OW;
@@ -1004,6 +1003,33 @@ int plan_wgrad(int N, int H, int W, int IC, int OC, int KH, int KW, int s, int p
         return CONVIMG_ERR_RANGE;
     wp->groups = (int)groups;
     wp->tiles_m = ceil_div(OC, kWgBM);
+    if (dtype == CONVIMG_FP32) {
+        // fp32 storage: the fp32 kernel's 64 x 64 tiles; ranges for two
+        // workgroups per CU, and at most kWgF32MaxSteps steps (8192 pixel
+        // slots) each, so that a range's fp32 sum adds at most 8192
+        // products per output before the ranges are added in order
+        wp->tiles_n = ceil_div(fwd.K, kWgF32BN);
+        const long long tiles = (long long)wp->tiles_m * wp->tiles_n;
+        const long long steps = (groups + 7) / 8;
+        const long long per = (long long)OC * fwd.K * 4;
+        long long S = tiles < 2LL * num_cus ? 2LL * num_cus / tiles : 1;
+        if (S > steps)
+            S = steps;
+        if (S < (steps + kWgF32MaxSteps - 1) / kWgF32MaxSteps)
+            S = (steps + kWgF32MaxSteps - 1) / kWgF32MaxSteps;
+        if (S < 1)
+            S = 1;
+        const long long chunk = (steps + S - 1) / S * 8;
+        S = (groups + chunk - 1) / chunk;
+        if (tiles * S >= lim || S * per > (1LL << 30))      // (the workspace stays within 1 GiB)
+            return CONVIMG_ERR_RANGE;
+        wp->splits = (int)S;
+        wp->chunk = (int)chunk;
+        wp->inplace = 0;
+        wp->row = 0;
+        wp->ws_bytes = S > 1 ? (size_t)(S * per) : 0;
+        return CONVIMG_OK;
+    }
     wp->tiles_n = ceil_div(fwd.K, kWgBN);
     const long long tiles = (long long)wp->tiles_m * wp->tiles_n;
     const long long steps = (groups + 7) / 8;
@@ -1824,8 +1850,9 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     int rc = plan_wgrad(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, &wp);
     if (rc != CONVIMG_OK)
         return rc;
-    const size_t nx = (size_t)N * H * W * IC * 2;
-    const size_t ny = (size_t)wp.M * OC * 2;
+    const size_t esz = dtype == CONVIMG_FP32 ? 4 : 2;
+    const size_t nx = (size_t)N * H * W * IC * esz;
+    const size_t ny = (size_t)wp.M * OC * esz;
     const size_t nw = (size_t)OC * wp.KKIC * 4;
     if (overlaps(dw, nw, x, nx) || overlaps(dw, nw, dy, ny))
         return CONVIMG_ERR_ALIAS;
@@ -1904,7 +1931,8 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     a.NR = N * wp.OH;
     a.div_rnseg = make_fast_div(wp.row_nseg);
     const int grid = wp.tiles_m * tiles_n * splits;
-    const hipError_t le = row ? wgrad_row_launch(a, grid, wp.row_xi, wp.row_stages, stream)
+    const hipError_t le = dtype == CONVIMG_FP32 ? wgrad_f32_launch(a, grid, stream)
+                        : row ? wgrad_row_launch(a, grid, wp.row_xi, wp.row_stages, stream)
                         : (wgrad_tr_shape(IC, OC) && vx && vdy) ? wgrad_tr_launch(a, grid, wp.tr_stages, stream)
                                                                 : wgrad_launch(a, vx, vdy, grid, stream);
     if (le != hipSuccess)

@@ -51,6 +51,12 @@ hipError_t wgrad_row_launch(const WgArgs &a, int grid, int xi, int stages, hipSt
     return hipGetLastError();
 }
 
+hipError_t wgrad_f32_launch(const WgArgs &a, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL(igemm_wgrad_f32, dim3(grid), dim3(kWgThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
                                hipStream_t stream)
 {

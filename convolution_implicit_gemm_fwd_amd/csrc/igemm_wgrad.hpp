@@ -54,8 +54,8 @@ constexpr int kWgRedBatch = 8;                          // loads a thread issues
 constexpr int kWgPF = CONVIMG_WG_PF;    // steps of loads in flight (measured)
 
 struct WgArgs {
-    const unsigned short *x;     // [N][H][W][IC] bf16
-    const unsigned short *dy;    // [N][OH][OW][OC] bf16
+    const unsigned short *x;     // [N][H][W][IC] bf16 (fp32 for the fp32-storage kernel)
+    const unsigned short *dy;    // [N][OH][OW][OC] bf16 (likewise)
     float *dst;                  // dw [OC][KKIC], or partial sums [splits][OC][KKIC]
     int *sem;                    // in place: one int per tile, then a status word
     int spin_limit;              // in place: polls before a range gives up its turn
@@ -99,6 +99,14 @@ inline bool wgrad_row_shape(int IC, int OC, int KW, int s)
 // Most pixel ranges that add into dw in turn (more go through a workspace:
 // each turn waits for the previous range's stores).
 constexpr int kWgInplaceMax = 4;
+
+// The fp32-storage kernel (below): 64 x 64 tiles, LDS rows of 80 floats
+// (a pixel slot's 64 values and 16 floats of padding: the four slots an
+// MFMA operand read spans fall on four disjoint bank quarters), at most
+// kWgF32MaxSteps steps (64 pixel slots each) a range.
+constexpr int kWgF32BN = 64;
+constexpr int kWgF32Row = 80;
+constexpr int kWgF32MaxSteps = 128;
 
 // The kernels are compiled in conv2d_wgrad.hip only; other units see the
 // argument block and the launchers.
@@ -953,6 +961,126 @@ __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__
     }
 }
 
+// fp32 storage (CONVIMG_FP32): 64 (oc) x 64 (j) tiles of dw over the same
+// pixel ranges as the general kernel (groups of 8 pixels of one output row,
+// 64 pixel slots a step), the products and sums in fp32 with
+// v_mfma_f32_16x16x4_f32, four waves of 32 x 32.  A step stages dy and the
+// im2col gather of x in LDS, pixel-major (slot rows of 64 values), one
+// element a lane: a thread keeps one column (tap, channel) and one output
+// channel for the whole range and takes 16 slots a step, whose pixel
+// decodes the step's first 64 threads write to LDS beforehand.  Buffer loads
+// whose masked lanes read zero past the end of the buffer; the loads of
+// step st + 1 are in flight during step st's MFMAs.
+__global__ __launch_bounds__(kWgThreads) void igemm_wgrad_f32(WgArgs a)
+{
+    __shared__ float sA[64 * kWgF32Row];      // [slot][oc - oc0]
+    __shared__ float sB[64 * kWgF32Row];      // [slot][j - j0]
+    __shared__ int4 pinf[2][64];              // per slot: pixel m (-1: none), n H, oh s, ow s
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tiles = a.tiles_m * a.tiles_n;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int split = bid / tiles, tile = bid - split * tiles;
+    const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
+    const int oc0 = tm * kWgBM, j0 = tn * kWgF32BN;
+    const int g_begin = split * a.chunk;
+    const int g_end = min(a.groups, g_begin + a.chunk);
+    const int steps = (g_end - g_begin + 7) / 8;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)a.x, 0, a.x_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc((void *)a.dy, 0, a.dy_bytes, kRsrcWord3);
+
+    // this thread's column c (j = j0 + c) and output channel oc0 + c; its
+    // slots (tid >> 6) + 4 k
+    const int c = tid & 63;
+    const int j = j0 + c;
+    const bool cok = j < a.KKIC, ook = oc0 + c < a.OC;
+    int dh = 0, dwc = 0, ic = 0;
+    if (cok) {
+        const int t = fast_div(j, a.div_ic);
+        const int kh = fast_div(t, a.div_kw);
+        ic = j - t * a.IC;
+        dh = kh * a.d - a.p;
+        dwc = (t - kh * a.KW) * a.d - a.p;
+    }
+    // threads 0..63: slot `tid` of step st
+    auto decode = [&](int st, int buf) {
+        const int g = g_begin + st * 8 + (tid >> 3);
+        int4 pi = make_int4(-1, 0, 0, 0);
+        if (g < g_end) {
+            const int r = fast_div(g, a.div_bpr);            // output row n OH + oh
+            const int ow = (g - r * a.bpr) * 8 + (tid & 7);
+            if (ow < a.OW) {
+                const int n = fast_div(r, a.div_oh), oh = r - n * a.OH;
+                pi = make_int4(r * a.OW + ow, n * a.H, oh * a.s, ow * a.s);
+            }
+        }
+        pinf[buf][tid] = pi;
+    };
+    float va[16], vb[16];
+    auto load = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int4 pi = pinf[buf][(tid >> 6) + 4 * k];
+            const bool mok = pi.x >= 0;
+            const int ih = pi.z + dh, iw = pi.w + dwc;
+            const bool xok = mok && cok && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+            const unsigned oa = (mok && ook) ? 4u * (unsigned)(pi.x * a.OC + oc0 + c) : kOutOfRange;
+            const unsigned ob = xok ? 4u * (unsigned)(((pi.y + ih) * a.W + iw) * a.IC + ic) : kOutOfRange;
+            va[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, oa, 0, 0));
+            vb[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, ob, 0, 0));
+        }
+    };
+
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lrow = lane & 15, lk = lane >> 4;
+    floatx4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+            acc[i][jb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    if (steps > 0) {
+        if (tid < 64)
+            decode(0, 0);
+        __syncthreads();
+        load(0);
+    }
+    for (int st = 0; st < steps; ++st) {
+        const int buf = st & 1;
+        __syncthreads();            // the previous step's operand reads are done
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int ps = (tid >> 6) + 4 * k;
+            sA[ps * kWgF32Row + c] = va[k];
+            sB[ps * kWgF32Row + c] = vb[k];
+        }
+        if (tid < 64 && st + 1 < steps)
+            decode(st + 1, buf ^ 1);
+        __syncthreads();
+        if (st + 1 < steps)
+            load(buf ^ 1);
+#pragma unroll 4
+        for (int kk = 0; kk < 16; ++kk) {
+            const int row = (4 * kk + lk) * kWgF32Row;
+            float af[2], bfv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = sA[row + 32 * wm + 16 * i + lrow];
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+                bfv[jb] = sB[row + 32 * wn + 16 * jb + lrow];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+                    acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bfv[jb], acc[i][jb], 0, 0, 0);
+        }
+    }
+    const int jc[2] = {j0 + 32 * wn, j0 + 32 * wn + 16};
+    wg_store<2, 2>(a, acc, oc0 + 32 * wm, jc, split, tile);
+}
+
 #endif  // CONVIMG_WGRAD_KERNELS
 
 // Launchers, defined in conv2d_wgrad.hip (its own translation unit: it is
@@ -962,6 +1090,7 @@ void wgrad_set_attributes();
 hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_t stream);
 hipError_t wgrad_tr_launch(const WgArgs &a, int grid, int stages, hipStream_t stream);
 hipError_t wgrad_row_launch(const WgArgs &a, int grid, int xi, int stages, hipStream_t stream);
+hipError_t wgrad_f32_launch(const WgArgs &a, int grid, hipStream_t stream);
 hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
                                hipStream_t stream);
 

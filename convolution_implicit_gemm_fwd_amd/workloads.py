@@ -169,16 +169,23 @@ def make_grad_inputs(wl: Workload, OH: int, OW: int, seed: int = 0,
     return Inputs(wl, dy32, w32, b, dy32, w32, True)
 
 
-def make_wgrad_inputs(wl: Workload, OH: int, OW: int, seed: int = 0) -> Inputs:
+def make_wgrad_inputs(wl: Workload, OH: int, OW: int, seed: int = 0,
+                      dtype: int | None = None) -> Inputs:
     """Draw the weight-backward inputs of a workload: x [N,H,W,IC] from the
-    workload's x distribution, then dy [N,OH,OW,OC] from N(0, 1); both
-    bf16-rounded and stored as bf16.
+    workload's x distribution, then dy [N,OH,OW,OC] from N(0, 1); for bf16
+    storage (the default) both bf16-rounded and stored as bf16, for fp32
+    storage (``dtype`` FP32) both kept and stored as drawn in float32.
 
     OH, OW: the forward output extent, given by the caller.  The result's
     x32/x_store hold x and its w32/w_store hold dy; bias is unused (zeros).
     """
+    dtype = BF16 if dtype is None else dtype
     rng = np.random.default_rng(seed)
-    x = round_to_bf16_bits(_draw(rng, wl.x_dist, (wl.N, wl.H, wl.W, wl.IC)))
-    dy = round_to_bf16_bits(_draw(rng, ("normal", 0.0, 1.0), (wl.N, OH, OW, wl.OC)))
+    x = _draw(rng, wl.x_dist, (wl.N, wl.H, wl.W, wl.IC))
+    dy = _draw(rng, ("normal", 0.0, 1.0), (wl.N, OH, OW, wl.OC))
+    if dtype == FP32:
+        x, dy = x.astype(np.float32), dy.astype(np.float32)
+        return Inputs(wl, x, dy, np.zeros(wl.OC, np.float32), x, dy, False)
+    x, dy = round_to_bf16_bits(x), round_to_bf16_bits(dy)
     return Inputs(wl, bf16_bits_to_f32(x), bf16_bits_to_f32(dy), np.zeros(wl.OC, np.float32),
                   x, dy, True)

@@ -47,8 +47,7 @@ extern "C" {
 #define CONVIMG_ERR_LAUNCH  7  /* the HIP runtime refused the launch */
 #define CONVIMG_ERR_DEVICE  8  /* no usable HIP device, or a device query failed */
 #define CONVIMG_ERR_TIMEOUT 9  /* a split-K wait gave up (reported by conv2d_fwd_status) */
-#define CONVIMG_ERR_UNSUPPORTED 10 /* conv2d_bwd_data: stride != 1, KH != KW or pad > dilation*(KH-1);
-                                      conv2d_bwd_weight: fp32 storage */
+#define CONVIMG_ERR_UNSUPPORTED 10 /* conv2d_bwd_data: stride != 1, KH != KW or pad > dilation*(KH-1) */
 #define CONVIMG_ERR_WORKSPACE 11   /* conv2d_bwd_weight: ws_bytes below what it needs */
 #define CONVIMG_ERR_SCRATCH 12     /* conv2d_fwd_noalloc: the plan needs more semaphores than its scratch holds */
 
@@ -350,22 +349,26 @@ int conv2d_bwd_data_weights(const void *w, int OC, int KH, int KW, int IC, int d
  * write partial sums to `ws`, which a second kernel adds in a fixed order.
  * Either way the result is the same on every call.  A range whose wait for
  * its turn gives up (a bound of many milliseconds) writes NaN over its part
- * of dw and sets the status that conv2d_fwd_status reports.
+ * of dw and sets the status that conv2d_fwd_status reports.  fp32 storage
+ * runs a kernel of its own with fp32 products and sums (v_mfma_f32_16x16x4
+ * _f32), its ranges at most 8192 pixels each and always through `ws` when
+ * there are several.
  *
- *   x     device, N x H x W x IC (NHWC) bf16
- *   dy    device, N x OH x OW x OC (NHWC) bf16, OH/OW the forward output
- *         extents of H/W (the formula under conv2d_fwd)
+ *   x     device, N x H x W x IC (NHWC) in `dtype`
+ *   dy    device, N x OH x OW x OC (NHWC) in `dtype`, OH/OW the forward
+ *         output extents of H/W (the formula under conv2d_fwd)
  *   dw    device, fp32 OC x KH x KW x IC (OHWI, the layout of w), fully
  *         overwritten
  *   ws    device workspace of ws_bytes bytes, caller-owned; at least what
  *         conv2d_bwd_weight_workspace reports for the same problem on the
  *         current device (NULL allowed when that is 0)
  *   N, H, W, IC, OC, KH, KW, stride, pad, dilation: the forward problem
- *   dtype must be CONVIMG_BF16
+ *   dtype CONVIMG_BF16 or CONVIMG_FP32
  *
  * Errors (returned before any work is queued): the argument errors of
- * conv2d_fwd for the forward problem; CONVIMG_ERR_UNSUPPORTED for fp32
- * storage; CONVIMG_ERR_NULL for a NULL x, dy or dw, or a NULL ws when one is
+ * conv2d_fwd for the forward problem; CONVIMG_ERR_RANGE (fp32) when the
+ * ranges' partial sums would need more than 1 GiB of workspace;
+ * CONVIMG_ERR_NULL for a NULL x, dy or dw, or a NULL ws when one is
  * needed; CONVIMG_ERR_WORKSPACE if ws_bytes is too small; CONVIMG_ERR_ALIAS
  * if dw or the used part of ws overlaps another buffer.  CONVIMG_ERR_LAUNCH
  * if a launch fails.  Asynchronous on `stream`; the workspace is in use

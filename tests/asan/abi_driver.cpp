@@ -79,8 +79,8 @@ int main()
     bad += conv2d_bwd_data(a, b, 2, 8, 8, 16, 16, 3, 3, 2, 1, 1, 0, o, (float *)((char *)o + (1 << 20)), 0)
            != CONVIMG_ERR_UNSUPPORTED;
     bad += conv2d_bwd_data_weights(a, 16, 3, 3, 16, 0, a, 0) != CONVIMG_ERR_ALIAS;
-    bad += conv2d_bwd_weight(a, b, 2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 1, (float *)o, nullptr, 0, 0)
-           != CONVIMG_ERR_UNSUPPORTED;
+    bad += conv2d_bwd_weight(a, b, 2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 2, (float *)o, nullptr, 0, 0)
+           != CONVIMG_ERR_DTYPE;
     bad += conv2d_fwd_nchw(a, b, nullptr, 2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 0, 1, o, (void *)0x6000000, 16, 0)
            != CONVIMG_ERR_WORKSPACE;
     bad += conv2d_fwd_autotune(a, b, nullptr, 2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 7, (float *)o, 0, nullptr, nullptr,

@@ -353,7 +353,6 @@ def call_wgt(**kw):
     (dict(H=2, pad=0), abi.CONVIMG_ERR_SHAPE),
     (dict(stride=0), abi.CONVIMG_ERR_SHAPE),
     (dict(dtype=2), abi.CONVIMG_ERR_DTYPE),
-    (dict(dtype=1), abi.CONVIMG_ERR_UNSUPPORTED),             # fp32 storage
     (dict(N=1 << 12, H=1 << 10, W=1 << 10), abi.CONVIMG_ERR_RANGE),
     (dict(dw=0x1000000 + 64), abi.CONVIMG_ERR_ALIAS),          # dw inside x
     (dict(dw=0x2000000 - 16), abi.CONVIMG_ERR_ALIAS),          # dw runs into dy
@@ -365,8 +364,10 @@ def test_bwd_weight_errors_before_any_device_work(lib, kw, code):
 def test_bwd_weight_workspace_argument_errors(lib):
     assert lib.conv2d_bwd_weight_workspace(2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 0, None) \
         == abi.CONVIMG_ERR_NULL
+    # fp32 storage passes the argument checks (its plan then needs the
+    # device's CU count: OK on a GPU host, the device error here)
     assert abi.conv2d_bwd_weight_workspace(2, 8, 8, 16, 16, 3, 3, 1, 1, 1, 1)[0] \
-        == abi.CONVIMG_ERR_UNSUPPORTED
+        in (abi.CONVIMG_OK, abi.CONVIMG_ERR_DEVICE)
     assert abi.conv2d_bwd_weight_workspace(2, 8, 8, 16, 16, 3, 3, 0, 1, 1, 0)[0] \
         == abi.CONVIMG_ERR_SHAPE
 

@@ -28,7 +28,7 @@ import torch
 
 import convolution_implicit_gemm_fwd_amd as cig
 from convolution_implicit_gemm_fwd_amd import abi
-from convolution_implicit_gemm_fwd_amd.workloads import BF16, WORKLOADS, make_wgrad_inputs
+from convolution_implicit_gemm_fwd_amd.workloads import BF16, FP32, WORKLOADS, make_wgrad_inputs
 
 import oracle
 from gpu_harness import GUARD, SENTINEL, check, log, need_gpu, shape
@@ -42,7 +42,10 @@ def _gpu():
 
 
 def upload(a, misalign=False):
-    t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).view(torch.bfloat16)
+    if a.dtype == np.float32:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).view(torch.bfloat16)
     if not misalign:
         return t.cuda()
     flat = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
@@ -50,19 +53,19 @@ def upload(a, misalign=False):
     return flat[1:].view(t.shape)
 
 
-def run_wgrad(wl, inp, misalign=False, ws_extra=0, misalign_dy=False):
+def run_wgrad(wl, inp, misalign=False, ws_extra=0, misalign_dy=False, dtype=BF16):
     x, dy = upload(inp.x_store, misalign), upload(inp.w_store, misalign_dy)
     K = wl.KH * wl.KW * wl.IC
     n_dw = wl.OC * K
     dw = torch.full((n_dw + GUARD,), float("nan"), dtype=torch.float32, device="cuda")
     dw[n_dw:] = SENTINEL
     rc, need = abi.conv2d_bwd_weight_workspace(wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
-                                               wl.stride, wl.pad, wl.dilation, BF16)
+                                               wl.stride, wl.pad, wl.dilation, dtype)
     assert rc == 0, abi.conv2d_strerror(rc)
     ws = torch.full((need + 4096 + ws_extra,), 0x5A, dtype=torch.uint8, device="cuda")
-    log("wgrad %s workspace %d bytes" % (wl, need))
+    log("wgrad %s dtype %d workspace %d bytes" % (wl, dtype, need))
     rc = abi.conv2d_bwd_weight(x.data_ptr(), dy.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH,
-                               wl.KW, wl.stride, wl.pad, wl.dilation, BF16, dw.data_ptr(),
+                               wl.KW, wl.stride, wl.pad, wl.dilation, dtype, dw.data_ptr(),
                                ws.data_ptr() if need else None, need,
                                torch.cuda.current_stream().cuda_stream)
     assert rc == 0, abi.conv2d_strerror(rc)
@@ -73,11 +76,11 @@ def run_wgrad(wl, inp, misalign=False, ws_extra=0, misalign_dy=False):
     return host[:n_dw].reshape(wl.OC, wl.KH, wl.KW, wl.IC), need
 
 
-def wgrad_parity(wl, seed=0, misalign=False, misalign_dy=False):
+def wgrad_parity(wl, seed=0, misalign=False, misalign_dy=False, dtype=BF16):
     OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
     OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
-    inp = make_wgrad_inputs(wl, OH, OW, seed=seed)
-    y, need = run_wgrad(wl, inp, misalign, misalign_dy=misalign_dy)
+    inp = make_wgrad_inputs(wl, OH, OW, seed=seed, dtype=dtype)
+    y, need = run_wgrad(wl, inp, misalign, misalign_dy=misalign_dy, dtype=dtype)
     yref, S = oracle.conv2d_bwd_weight(inp.x32, inp.w32, wl.KH, wl.KW, wl.stride, wl.pad,
                                        wl.dilation)
     ratio = check(y, yref, S, "wgrad %s" % (wl,))
@@ -116,6 +119,43 @@ IN_PLACE = shape(1, 24, 48, 64, 128, 3, 3, 1, 1, 1, name="four ranges in place")
 @pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
 def test_wgrad_full_size(wl):
     wgrad_parity(wl)
+
+
+# fp32 storage: the fp32 kernel (64 x 64 tiles, fp32 products and sums),
+# values as drawn (not bf16-rounded); one pixel range a tile (dw written
+# directly) and several (the workspace and the ordered sum), channel tails,
+# strides, dilations, windows, and layers of the named shapes at N = 2
+F32 = [
+    shape(1, 8, 8, 16, 16, 3, 3, 1, 1, 1, dtype=FP32, name="fp32 tiny"),
+    shape(1, 9, 9, 5, 7, 3, 3, 1, 1, 1, dtype=FP32, name="fp32 IC 5 OC 7"),
+    shape(2, 13, 11, 24, 40, 3, 3, 1, 1, 1, dtype=FP32, name="fp32 IC 24 OC 40"),
+    shape(2, 15, 17, 16, 50, 3, 3, 2, 1, 1, dtype=FP32, name="fp32 stride 2, OC 50"),
+    shape(1, 20, 20, 64, 64, 3, 3, 1, 2, 2, dtype=FP32, name="fp32 dilation 2"),
+    shape(3, 10, 10, 64, 96, 1, 1, 1, 0, 1, dtype=FP32, name="fp32 1x1"),
+    shape(2, 12, 14, 32, 48, 3, 5, 1, 2, 1, dtype=FP32, name="fp32 3x5 window"),
+    shape(2, 30, 30, 3, 64, 7, 7, 2, 3, 1, dtype=FP32, name="fp32 IC 3 7x7 stride 2"),
+    shape(1, 3, 3, 8, 8, 3, 3, 1, 0, 1, dtype=FP32, name="fp32 single output pixel"),
+    WORKLOADS["resnet3x3"].scaled(N=2, dtype=FP32, name="fp32 resnet3x3 N=2"),
+    WORKLOADS["largek"].scaled(N=2, dtype=FP32, name="fp32 largek N=2"),
+]
+
+
+@pytest.mark.parametrize("wl", F32, ids=lambda w: w.name)
+def test_wgrad_fp32_storage(wl):
+    wgrad_parity(wl, dtype=FP32)
+
+
+def test_wgrad_fp32_repeatable():
+    """The fp32 path's ranges through the workspace are added in a fixed
+    order: two calls give the same bits."""
+    wl = F32[-2]
+    OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
+    OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
+    inp = make_wgrad_inputs(wl, OH, OW, seed=3, dtype=FP32)
+    y1, need = run_wgrad(wl, inp, dtype=FP32)
+    y2, _ = run_wgrad(wl, inp, dtype=FP32)
+    assert need > 0, "expected several ranges through the workspace"
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
