@@ -83,9 +83,9 @@ TRAFFIC = {
     # weight backward: the whole call (igemm_wgrad_row_bf16, + wgrad_reduce
     # where the ranges go through the workspace), as the --op wgrad roofline
     # times it; profiles/igemm_wgrad_*.md
-    "wgrad:resnet3x3": {"bytes": 36184191, "tile": -2, "kernel": "a59ae32436ecbf96"},
-    "wgrad:largek": {"bytes": 44504409, "tile": -2, "kernel": "a59ae32436ecbf96"},
-    "wgrad:dilated": {"bytes": 68872306, "tile": -2, "kernel": "a59ae32436ecbf96"},
+    "wgrad:resnet3x3": {"bytes": 36180125, "tile": -2, "kernel": "4bb0b58facb58f2e"},
+    "wgrad:largek": {"bytes": 44511574, "tile": -2, "kernel": "4bb0b58facb58f2e"},
+    "wgrad:dilated": {"bytes": 68869858, "tile": -2, "kernel": "4bb0b58facb58f2e"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
