@@ -13,11 +13,11 @@ into ranges, the ordered sum of the ranges; the roofline object prices the
 whole call.
 
 --op dgrad times conv2d_bwd_data instead (the gradient with respect to the
-input, stride-1 workloads only): a step is the forward implicit GEMM it maps
-to, whose kernel flips and transposes the weights in LDS where it can (one
-launch), else the separate weight transform plus that GEMM; in the latter
-case the roofline object prices the GEMM kernel alone (timed in its own
-loop on the same buffers).
+input): at stride 1 a step is the forward implicit GEMM it maps to, whose
+kernel flips and transposes the weights in LDS where it can (one launch),
+else the separate weight transform plus that GEMM (the roofline object then
+prices the GEMM kernel alone, timed in its own loop on the same buffers);
+other problems (the stem's stride 2) run the general kernel, one launch.
 
 --nchw f32|bf16 times conv2d_fwd_nchw on NCHW / OIHW copies of the same
 inputs (fp32 or bf16 NCHW output).
@@ -91,6 +91,7 @@ TRAFFIC = {
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
 KIND_SOURCES = {
     -2: ("igemm_wgrad.hpp", "igemm_pipe.hpp", "conv2d_wgrad.hip"),   # weight backward
+    -3: ("igemm_dgrad.hpp",),                    # data backward, general kernel
     -1: ("igemm_regs.hpp",),                     # fp32 storage
     0: ("igemm_regs.hpp",),                      # CONVIMG_KIND_REGS
     1: ("igemm_pipe.hpp",),                      # CONVIMG_KIND_PIPE
@@ -332,10 +333,6 @@ def main():
                        name="%s, %s storage" % (wl.name, args.storage))
     dgrad = args.op == "dgrad"
     wgrad = args.op == "wgrad"
-    if dgrad and wl.stride != 1:
-        print("--op dgrad needs a stride-1 workload (%s has stride %d)" % (wl.name, wl.stride),
-              file=sys.stderr)
-        sys.exit(2)
     OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
     OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
     M, K = wl.N * OH * OW, wl.IC * wl.KH * wl.KW
@@ -380,7 +377,7 @@ def main():
         # (wt untouched) from the transform + GEMM path
         wt = torch.full(w.shape, 0x7F81, dtype=torch.int16, device="cuda").view(w.dtype)
         call_args = (x.data_ptr(), w.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH, wl.KW,
-                     1, wl.pad, wl.dilation, wl.dtype, wt.data_ptr(), out.data_ptr(), sptr)
+                     wl.stride, wl.pad, wl.dilation, wl.dtype, wt.data_ptr(), out.data_ptr(), sptr)
         fn = lib.conv2d_bwd_data
         gemm = (wl.N, OH, OW, wl.OC, wl.IC, wl.KH, wl.KW, 1,
                 wl.dilation * (wl.KH - 1) - wl.pad, wl.dilation)
@@ -407,8 +404,14 @@ def main():
         assert rc == 0, abi.conv2d_strerror(rc)
         tuned = {"tile_id": t_tile, "splits": t_splits, "us_best": round(t_best, 3),
                  "us_static": round(t_default, 3)}
-    rc, plan = abi.conv2d_fwd_plan(*gemm, wl.dtype, 0)
-    assert rc == 0, abi.conv2d_strerror(rc)
+    # the data backward's general kernel (stride > 1, KH != KW, pad beyond
+    # dilation*(KH-1)) maps to no forward problem
+    general = dgrad and (wl.stride != 1 or wl.KH != wl.KW or wl.pad > wl.dilation * (wl.KH - 1))
+    if general:
+        plan = {"tile_id": -3, "BM": 64, "BN": 64, "BK": 64, "loader": -1, "splits": None, "grid": None}
+    else:
+        rc, plan = abi.conv2d_fwd_plan(*gemm, wl.dtype, 0)
+        assert rc == 0, abi.conv2d_strerror(rc)
     if wgrad:
         # the weight backward has its own kernel; report its workspace instead
         plan = {"tile_id": -2, "BM": 64, "BN": 192 if wl.dtype == BF16 else 64, "BK": 64, "loader": -1, "splits": None,
@@ -444,7 +447,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / peak_flops, 4)}
     kind = (abi.conv2d_fwd_tile_kind(plan["tile_id"]) if plan["tile_id"] >= 0
-            else -2 if wgrad else -1)
+            else -2 if wgrad else -3 if general else -1)
     ksrc = kernel_sources_hash(kind)
     t = TRAFFIC.get("nchw_%s:%s" % (args.nchw, wl.name) if args.nchw
                     else wl.name if args.op == "fwd" else args.op + ":" + wl.name)

@@ -114,7 +114,7 @@ def conv2d_bwd_data_nhwc(dy, w, H, W, stride=1, pad=0, dilation=1, dx=None, wt=N
 
     dy: contiguous [N,OH,OW,OC] device tensor (the output gradient), w: the
     forward weights [OC,KH,KW,IC]; both bfloat16 or both float32.  H, W,
-    stride, pad, dilation: the forward problem (stride must be 1 and KH == KW).
+    stride, pad, dilation: the forward problem (any stride, window and padding).
     wt: optional workspace of w's numel and dtype that receives the flipped,
     transposed weights [IC,KH,KW,OC]; dx: optional preallocated output.  Runs
     on ``stream`` (default: torch's current stream) without waiting.

@@ -1776,8 +1776,57 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
     int rc = make_plan(N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype, 1, true, nullptr, &fwd);
     if (rc != CONVIMG_OK)
         return rc;
-    if (stride != 1 || KH != KW || pad > dilation * (KH - 1))
-        return CONVIMG_ERR_UNSUPPORTED;
+    if (stride != 1 || KH != KW || pad > dilation * (KH - 1)) {
+        // the general kernel: the gradient from its definition, any stride,
+        // kernel shape and padding (wt unused)
+        const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
+        const size_t nw = (size_t)OC * KH * KW * IC * esz;
+        const size_t ny = (size_t)fwd.M * OC * esz;
+        const size_t nx = (size_t)N * H * W * IC * 4;
+        if (overlaps(dx, nx, w, nw) || overlaps(dx, nx, dy, ny))
+            return CONVIMG_ERR_ALIAS;
+        const size_t lim = 0x7fffffff;
+        const long long M = (long long)N * H * W;
+        const long long tiles = (long long)ceil_div(M, 64) * ceil_div(IC, 64);
+        if (nw >= lim || ny >= lim || nx >= lim || tiles >= (long long)lim)
+            return CONVIMG_ERR_RANGE;
+        int dev = 0;
+        DeviceInfo *info = nullptr;
+        rc = current_device(&dev, &info);
+        if (rc != CONVIMG_OK)
+            return rc;
+        DgArgs g;
+        g.dy = dy;
+        g.w = w;
+        g.dx = dx;
+        g.N = N;
+        g.H = H;
+        g.W = W;
+        g.IC = IC;
+        g.OC = OC;
+        g.KH = KH;
+        g.KW = KW;
+        g.s = stride;
+        g.p = pad;
+        g.d = dilation;
+        g.OH = fwd.OH;
+        g.OW = fwd.OW;
+        g.M = (int)M;
+        g.K = KH * KW * OC;
+        g.tiles_m = ceil_div(M, 64);
+        g.dy_bytes = (unsigned)ny;
+        g.w_bytes = (unsigned)nw;
+        g.dx_bytes = (unsigned)nx;
+        g.div_oc = make_fast_div(OC);
+        g.div_kw = make_fast_div(KW);
+        g.div_hw = make_fast_div(H * W);
+        g.div_w = make_fast_div(W);
+        if (dtype == CONVIMG_BF16)
+            hipLaunchKernelGGL(igemm_dgrad_any<true>, dim3((unsigned)tiles), dim3(256), 0, stream, g);
+        else
+            hipLaunchKernelGGL(igemm_dgrad_any<false>, dim3((unsigned)tiles), dim3(256), 0, stream, g);
+        return hipGetLastError() == hipSuccess ? CONVIMG_OK : CONVIMG_ERR_LAUNCH;
+    }
     const int pt = dilation * (KH - 1) - pad;
     convimg_plan pl;
     rc = make_plan(N, fwd.OH, fwd.OW, OC, IC, KH, KW, 1, pt, dilation, dtype, 1, true, nullptr, &pl);

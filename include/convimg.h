@@ -47,7 +47,8 @@ extern "C" {
 #define CONVIMG_ERR_LAUNCH  7  /* the HIP runtime refused the launch */
 #define CONVIMG_ERR_DEVICE  8  /* no usable HIP device, or a device query failed */
 #define CONVIMG_ERR_TIMEOUT 9  /* a split-K wait gave up (reported by conv2d_fwd_status) */
-#define CONVIMG_ERR_UNSUPPORTED 10 /* conv2d_bwd_data: stride != 1, KH != KW or pad > dilation*(KH-1) */
+#define CONVIMG_ERR_UNSUPPORTED 10 /* no entry point returns it now: conv2d_bwd_data serves every
+                                      stride, window and padding, conv2d_bwd_weight fp32 storage */
 #define CONVIMG_ERR_WORKSPACE 11   /* conv2d_bwd_weight: ws_bytes below what it needs */
 #define CONVIMG_ERR_SCRATCH 12     /* conv2d_fwd_noalloc: the plan needs more semaphores than its scratch holds */
 
@@ -300,22 +301,27 @@ void conv2d_fwd_autotune_clear(void);
  * w itself and flips and transposes it in LDS: one launch, and `wt` is
  * left as it was.  A
  * caller whose weights do not change between calls may transform them once
- * and make that conv2d_fwd call itself.
+ * and make that conv2d_fwd call itself.  Every other problem (stride above
+ * 1, KH != KW, pad > dilation*(KH-1): the listing's fallback route) runs a
+ * general kernel that computes dx from the definition above as a GEMM over
+ * the input pixels, K = KH*KW*OC, gathering dY element by element with the
+ * divisibility test, fp32 products and sums (bf16 products are exact in
+ * fp32); `wt` is then left as it was.
  *
  *   dy    device, N x OH x OW x OC (NHWC) in `dtype`, OH/OW the forward
  *         output extents of H/W (the formula under conv2d_fwd)
  *   w     device, OC x KH x KW x IC (OHWI) in `dtype`: the forward weights
  *   wt    device, OC*KH*KW*IC elements of `dtype`, caller-owned workspace;
  *         receives IC x KH x KW x OC, the flipped and transposed weights,
- *         except on the in-LDS path above (then untouched)
+ *         except on the in-LDS path and the general kernel (then untouched)
  *   dx    device, fp32 N x H x W x IC (NHWC), fully overwritten
  *   N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype: the forward
  *         problem's arguments
  *
- * Errors: CONVIMG_ERR_UNSUPPORTED unless stride == 1, KH == KW and
- * pad <= dilation*(KH-1); the argument errors of conv2d_fwd for the forward
- * problem and for the one it maps to; CONVIMG_ERR_ALIAS if wt or dx overlaps
- * another buffer.  These are returned before any work is queued.  After the
+ * Errors: the argument errors of conv2d_fwd for the forward problem and
+ * (stride 1) for the one it maps to; CONVIMG_ERR_ALIAS if wt or dx overlaps
+ * another buffer; CONVIMG_ERR_RANGE (general kernel) for dy, w or dx of
+ * 2^31 bytes or more; CONVIMG_ERR_DEVICE without a usable device.  These are returned before any work is queued.  After the
  * transform is queued, CONVIMG_ERR_LAUNCH / CONVIMG_ERR_ALLOC may still come
  * back (wt then holds the transform).  Asynchronous on `stream`. */
 int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, int OC, int KH, int KW,

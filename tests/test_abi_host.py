@@ -292,10 +292,11 @@ def call_bwd(**kw):
     (dict(N=0), abi.CONVIMG_ERR_SHAPE),
     (dict(H=2, pad=0), abi.CONVIMG_ERR_SHAPE),
     (dict(dtype=2), abi.CONVIMG_ERR_DTYPE),
-    (dict(stride=2), abi.CONVIMG_ERR_UNSUPPORTED),
-    (dict(KW=5, pad=2), abi.CONVIMG_ERR_UNSUPPORTED),
-    (dict(pad=3), abi.CONVIMG_ERR_UNSUPPORTED),                # pad > dilation*(KH-1)
-    (dict(pad=5, dilation=2), abi.CONVIMG_ERR_UNSUPPORTED),
+    # the general kernel's problems (stride 2, KH != KW, pad beyond
+    # dilation*(KH-1)) check the same overlaps before any device work
+    (dict(stride=2, dx=0x1000000 + 64), abi.CONVIMG_ERR_ALIAS),
+    (dict(KW=5, pad=2, dx=0x2000000 - 64), abi.CONVIMG_ERR_ALIAS),
+    (dict(pad=3, dx=0x1000000 - 64), abi.CONVIMG_ERR_ALIAS),
     (dict(N=1 << 12, H=1 << 10, W=1 << 10), abi.CONVIMG_ERR_RANGE),
     # 90000 taps: more transform workgroups along one grid axis than HIP allows
     (dict(N=1, H=300, W=300, IC=1, OC=1, KH=300, KW=300, pad=0), abi.CONVIMG_ERR_RANGE),

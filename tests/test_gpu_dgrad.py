@@ -1,4 +1,4 @@
-"""GPU parity of the data backward (conv2d_bwd_data, stride 1) against the
+"""GPU parity of the data backward (conv2d_bwd_data) against the
 fp64 oracle's definition of the input gradient, element by element with the
 forward's bound |err| <= 1e-3*S + 1e-5 (S: the oracle's sum of |dy*w| over
 each element's terms).
@@ -10,7 +10,10 @@ sentinel guard (a write past the end fails).  Covered: the three stride-1
 named layers (ResNet-style, 512-channel, dilated) at full size, IC != OC with
 channel tails, 1x1, 5x5, edge paddings (0 and dilation*(K-1)), IC = 3 with a
 7x7 window, fp32 storage, and the torch wrapper; the weight transform alone
-on non-square windows, channel tails and misaligned buffers (element path).
+on non-square windows, channel tails and misaligned buffers (element path);
+and the general kernel for the problems the stride-1 mapping does not serve
+(strides 2 and 3, non-square windows, padding beyond dilation*(K-1), the
+stem layer at full size, fp32 storage).
 """
 import numpy as np
 import pytest
@@ -46,8 +49,8 @@ def upload(a, misalign=False):
 
 def bwd_parity(wl, dtype=None, seed=0, misalign=False):
     dtype = wl.dtype if dtype is None else dtype
-    OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, 1, wl.pad, wl.dilation)
-    OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, 1, wl.pad, wl.dilation)
+    OH = abi.conv2d_fwd_out_dim(wl.H, wl.KH, wl.stride, wl.pad, wl.dilation)
+    OW = abi.conv2d_fwd_out_dim(wl.W, wl.KW, wl.stride, wl.pad, wl.dilation)
     assert OH > 0 and OW > 0
     inp = make_grad_inputs(wl, OH, OW, seed=seed, dtype=dtype)
     dy, w = upload(inp.x_store, misalign), upload(inp.w_store, misalign)
@@ -64,7 +67,7 @@ def bwd_parity(wl, dtype=None, seed=0, misalign=False):
     dx[n_dx:] = SENTINEL
     log("dgrad %s dtype=%d" % (wl, dtype))
     rc = abi.conv2d_bwd_data(dy.data_ptr(), w.data_ptr(), wl.N, wl.H, wl.W, wl.IC, wl.OC, wl.KH,
-                             wl.KW, 1, wl.pad, wl.dilation, dtype, wt.data_ptr(), dx.data_ptr(),
+                             wl.KW, wl.stride, wl.pad, wl.dilation, dtype, wt.data_ptr(), dx.data_ptr(),
                              torch.cuda.current_stream().cuda_stream)
     assert rc == 0, abi.conv2d_strerror(rc)
     torch.cuda.synchronize()
@@ -81,7 +84,7 @@ def bwd_parity(wl, dtype=None, seed=0, misalign=False):
         got = raw.view(np.uint16) if dtype == BF16 else wt.cpu().numpy()
         assert np.array_equal(got.reshape(want.shape), want), "flipped weights differ"
     log("dgrad %s: %s" % (wl.name, "weights flipped in LDS" if untouched else "weights transformed into wt"))
-    yref, S = oracle.conv2d_bwd_data(inp.x32, inp.w32, wl.H, wl.W, 1, wl.pad, wl.dilation)
+    yref, S = oracle.conv2d_bwd_data(inp.x32, inp.w32, wl.H, wl.W, wl.stride, wl.pad, wl.dilation)
     ratio = check(y, yref, S, "dgrad %s" % (wl,))
     log("dgrad %s worst err/tol %.3g" % (wl.name, ratio))
     return y, yref, untouched
@@ -122,6 +125,28 @@ def test_dgrad_full_size(wl):
     bwd_parity(wl)
 
 
+# the general kernel: every problem the stride-1 mapping does not serve
+GENERAL = [
+    shape(2, 15, 17, 24, 40, 3, 3, 2, 1, 1, name="stride 2, channel tails"),
+    shape(2, 30, 30, 3, 64, 7, 7, 2, 3, 1, name="stride 2 7x7 IC 3"),
+    shape(2, 12, 14, 32, 48, 3, 5, 1, 2, 1, name="3x5 window"),
+    shape(1, 9, 9, 16, 16, 3, 3, 1, 3, 1, name="pad 3 > dilation*(K-1)"),
+    shape(1, 20, 22, 16, 24, 3, 3, 3, 2, 2, name="stride 3 dilation 2"),
+    shape(3, 10, 10, 64, 96, 1, 1, 2, 0, 1, name="1x1 stride 2"),
+    shape(2, 13, 11, 24, 40, 3, 3, 2, 1, 1, dtype=FP32, name="fp32 stride 2"),
+    shape(1, 5, 5, 8, 8, 5, 3, 2, 2, 1, dtype=FP32, name="fp32 5x3 stride 2"),
+    WORKLOADS["stem7x7"],
+]
+
+
+@pytest.mark.parametrize("wl", GENERAL, ids=lambda w: w.name)
+def test_dgrad_general_kernel(wl):
+    """Strides above 1, non-square windows and padding beyond dilation*(K-1)
+    run the general kernel (dx from its definition; wt untouched)."""
+    _, _, untouched = bwd_parity(wl)
+    assert untouched, "the general kernel does not use wt"
+
+
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
 def test_dgrad_shapes(wl):
     bwd_parity(wl)
@@ -140,9 +165,12 @@ def test_dgrad_torch_wrapper():
     torch.cuda.synchronize()
     yref, S = oracle.conv2d_bwd_data(inp.x32, inp.w32, 14, 14, 1, 1, 1)
     check(dx.cpu().numpy(), yref, S, "wrapper")
-    with pytest.raises(RuntimeError, match="stride 1"):
-        cig.conv2d_bwd_data_nhwc(upload(inp.x_store[:, ::2, ::2].copy()), w, 14, 14, stride=2,
-                                 pad=1)
+    # stride 2 (the general kernel): dy of the 7 x 7 forward output
+    dy2 = inp.x_store[:, ::2, ::2].copy()
+    dx2 = cig.conv2d_bwd_data_nhwc(upload(dy2), w, 14, 14, stride=2, pad=1)
+    torch.cuda.synchronize()
+    yref2, S2 = oracle.conv2d_bwd_data(inp.x32[:, ::2, ::2], inp.w32, 14, 14, 2, 1, 1)
+    check(dx2.cpu().numpy(), yref2, S2, "wrapper stride 2")
 
 
 @pytest.mark.parametrize("OC,KH,KW,IC,dtype,misalign", [
