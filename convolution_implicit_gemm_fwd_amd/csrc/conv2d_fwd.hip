@@ -1989,8 +1989,8 @@ int conv2d_bwd_weight(const void *x, const void *dy, int N, int H, int W, int IC
     if (splits > 1 && !inplace) {
         const int n = OC * wp.KKIC;
         const int vec = (n % 4 == 0 && ((uintptr_t)ws & 15) == 0 && ((uintptr_t)dw & 15) == 0) ? 1 : 0;
-        const int blocks = ceil_div(n, 4 * kWgRedCols);
-        if (wgrad_reduce_launch((const float *)ws, dw, n, splits, vec, blocks, stream) != hipSuccess)
+        if (wgrad_reduce_launch((const float *)ws, dw, n, splits, vec, wgrad_reduce_log2_groups(splits), stream)
+            != hipSuccess)
             return CONVIMG_ERR_LAUNCH;
     }
     return CONVIMG_OK;

@@ -57,10 +57,17 @@ hipError_t wgrad_f32_launch(const WgArgs &a, int grid, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
+hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int lg,
                                hipStream_t stream)
 {
-    hipLaunchKernelGGL(wgrad_reduce, dim3(blocks), dim3(kWgReduceThreads), 0, stream, part, dw, n, splits, vec);
+    static_assert(kWgRedMaxGroups == 32, "one instantiation a group count");
+    void (*const k[])(const float *, float *, int, int, int) = {wgrad_reduce<0>, wgrad_reduce<1>, wgrad_reduce<2>,
+                                                                 wgrad_reduce<3>, wgrad_reduce<4>, wgrad_reduce<5>};
+    if (lg < 0 || lg > 5)
+        return hipErrorInvalidValue;
+    const long long cols = kWgReduceThreads >> lg;
+    const int blocks = (int)(((long long)n + 4 * cols - 1) / (4 * cols));
+    hipLaunchKernelGGL(k[lg], dim3(blocks), dim3(kWgReduceThreads), 0, stream, part, dw, n, splits, vec);
     return hipGetLastError();
 }
 

@@ -45,9 +45,25 @@ constexpr int kWgRowBytes = kWgBK * 2 + 16;
 constexpr int kWgStageBytes = kWgRows * kWgRowBytes;
 constexpr int kWgLdsBytes = 2 * kWgStageBytes;
 constexpr int kWgReduceThreads = 256;
-constexpr int kWgRedCols = 16;                          // 4-element columns a reduce workgroup covers
-constexpr int kWgRedGroups = kWgReduceThreads / kWgRedCols;   // range groups per column
+constexpr int kWgRedMaxGroups = 32;                     // range groups per column, at most
 constexpr int kWgRedBatch = 8;                          // loads a thread issues before adding
+#ifndef CONVIMG_WG_RED_LOADS
+#define CONVIMG_WG_RED_LOADS 5
+#endif
+constexpr int kWgRedLoads = CONVIMG_WG_RED_LOADS;       // ranges a reduce thread loads, at most
+
+// Range groups for the reduce over `splits` ranges, as log2: the fewest (a
+// power of two, at most kWgRedMaxGroups) that leave each thread at most
+// kWgRedLoads ranges to load.  Measured: groups of about five ranges beat
+// both longer groups (fewer workgroups, each thread's loads in more
+// rounds) and shorter ones (more workgroups than are resident at once).
+inline int wgrad_reduce_log2_groups(int splits)
+{
+    int lg = 0;
+    while ((1 << lg) < kWgRedMaxGroups && (splits + (1 << lg) - 1) >> lg > kWgRedLoads)
+        ++lg;
+    return lg;
+}
 #ifndef CONVIMG_WG_PF
 #define CONVIMG_WG_PF 1
 #endif
@@ -901,23 +917,28 @@ __global__ __launch_bounds__(kWrThreads) void igemm_wgrad_row_bf16(WgArgs a)
 }
 
 // dw = the sum of the pixel ranges' partial tiles, part[s][i] for s < splits.
-// A workgroup covers kWgRedCols consecutive 4-element columns; thread t takes
-// column t % kWgRedCols and range group t / kWgRedCols (ranges split evenly
-// and in order over kWgRedGroups groups), loads all of its group's ranges
-// before adding them in order, and the groups' sums are then added in group
-// order through LDS: a fixed order, so every call gives the same bits, with
-// every load of the call in flight at once instead of a few rounds of them
-// per wave.  vec: n % 4 == 0 and both buffers 16-byte aligned (16-byte
-// accesses), else element by element.
+// A workgroup covers 256 >> LG consecutive 4-element columns; thread t takes
+// column t % cols and range group t / cols (ranges split evenly and in
+// order over 2^LG groups), loads all of its group's ranges before adding
+// them in order, and the groups' sums are then added in group order through
+// LDS: a fixed order for a given LG, so every call of a problem gives the
+// same bits.  LG is a compile-time constant so that every index here is a
+// shift and the groups' sums are read at once (a 64-bit division by a
+// run-time group count before the first load, and the sums read one after
+// another, measured 0.4 us slower on the ResNet-style layer).  vec: n % 4
+// == 0 and both buffers 16-byte aligned (16-byte accesses), else element by
+// element.
+template <int LG>
 __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__restrict__ part,
                                                                  float *__restrict__ dw, int n, int splits,
                                                                  int vec)
 {
-    __shared__ floatx4_t red[kWgRedGroups][kWgRedCols];
+    constexpr int LC = 8 - LG;                   // log2 of the columns a workgroup covers
+    __shared__ floatx4_t red[kWgReduceThreads];
     const int t = threadIdx.x;
-    const int col = t % kWgRedCols, g = t / kWgRedCols;
-    const int i = (blockIdx.x * kWgRedCols + col) * 4;
-    const int s0 = (int)((long long)splits * g / kWgRedGroups), s1 = (int)((long long)splits * (g + 1) / kWgRedGroups);
+    const int col = t & ((1 << LC) - 1), g = t >> LC;
+    const int i = (int)(((unsigned)blockIdx.x << LC) + (unsigned)col) * 4;
+    const int s0 = (int)(((long long)splits * g) >> LG), s1 = (int)(((long long)splits * (g + 1)) >> LG);
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (i < n) {
         if (vec) {
@@ -944,13 +965,13 @@ __global__ __launch_bounds__(kWgReduceThreads) void wgrad_reduce(const float *__
                     acc[e] += part[(size_t)s * n + i + e];
         }
     }
-    red[g][col] = acc;
+    red[t] = acc;
     __syncthreads();
     if (g == 0 && i < n) {
-        floatx4_t sum = red[0][col];
+        floatx4_t sum = red[col];
 #pragma unroll
-        for (int q = 1; q < kWgRedGroups; ++q)
-            sum += red[q][col];
+        for (int q = 1; q < (1 << LG); ++q)
+            sum += red[(q << LC) + col];
         if (vec) {
             *(floatx4_t *)(dw + i) = sum;
         } else {
@@ -1091,7 +1112,7 @@ hipError_t wgrad_launch(const WgArgs &a, bool vx, bool vdy, int grid, hipStream_
 hipError_t wgrad_tr_launch(const WgArgs &a, int grid, int stages, hipStream_t stream);
 hipError_t wgrad_row_launch(const WgArgs &a, int grid, int xi, int stages, hipStream_t stream);
 hipError_t wgrad_f32_launch(const WgArgs &a, int grid, hipStream_t stream);
-hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int blocks,
+hipError_t wgrad_reduce_launch(const float *part, float *dw, int n, int splits, int vec, int lg,
                                hipStream_t stream);
 
 }  // namespace convimg
