@@ -1795,6 +1795,58 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
         rc = current_device(&dev, &info);
         if (rc != CONVIMG_OK)
             return rc;
+        if (dtype == CONVIMG_BF16 && OC % 8 == 0 && ((uintptr_t)dy & 15) == 0) {
+            // bf16 with 16-byte runs of dy: the kernel by phases (only the
+            // taps that reach each phase of the stride)
+            int gsd = stride, r = dilation;
+            while (r != 0) {
+                const int t = gsd % r;
+                gsd = r;
+                r = t;
+            }
+            DgPhArgs q;
+            q.dy = dy;
+            q.w = w;
+            q.dx = dx;
+            q.N = N;
+            q.H = H;
+            q.W = W;
+            q.IC = IC;
+            q.OC = OC;
+            q.KH = KH;
+            q.KW = KW;
+            q.s = stride;
+            q.p = pad;
+            q.d = dilation;
+            q.OH = fwd.OH;
+            q.OW = fwd.OW;
+            q.dk = stride / gsd;
+            q.dq = dilation / gsd;
+            q.Hp = ceil_div(H, stride);
+            q.Wp = ceil_div(W, stride);
+            const long long Mp = (long long)N * q.Hp * q.Wp;
+            const long long tiles_p = ceil_div(Mp, 64);
+            const long long tiles_m = (long long)stride * stride * tiles_p;
+            const long long grid = tiles_m * ceil_div(IC, 64);
+            if (grid >= (long long)lim || Mp * 64 >= (long long)lim)
+                return CONVIMG_ERR_RANGE;
+            q.Mp = (int)Mp;
+            q.tiles_p = (int)tiles_p;
+            q.tiles_m = (int)tiles_m;
+            q.ob = ceil_div(OC, 64);
+            q.dy_bytes = (unsigned)ny;
+            q.w_bytes = (unsigned)nw;
+            q.dx_bytes = (unsigned)nx;
+            q.div_tp = make_fast_div(q.tiles_p);
+            q.div_hwp = make_fast_div(q.Hp * q.Wp);
+            q.div_wp = make_fast_div(q.Wp);
+            q.div_s = make_fast_div(stride);
+            if (IC % 8 == 0 && ((uintptr_t)w & 15) == 0)
+                hipLaunchKernelGGL(igemm_dgrad_phase_bf16<true>, dim3((unsigned)grid), dim3(256), 0, stream, q);
+            else
+                hipLaunchKernelGGL(igemm_dgrad_phase_bf16<false>, dim3((unsigned)grid), dim3(256), 0, stream, q);
+            return hipGetLastError() == hipSuccess ? CONVIMG_OK : CONVIMG_ERR_LAUNCH;
+        }
         DgArgs g;
         g.dy = dy;
         g.w = w;

@@ -262,4 +262,297 @@ __global__ __launch_bounds__(256) void igemm_dgrad_any(DgArgs a)
         }
 }
 
+// Data backward by phases (bf16 storage, OC % 8 == 0, dy 16-byte aligned;
+// any stride, kernel shape and padding).  The same sum as the general
+// kernel above, with the input pixels grouped by phase: the pixels with ih
+// = rh + s i and iw = rw + s j for one (rh, rw) in [0, s)^2.  For such a
+// pixel, oh = (ih + p - kh d) / s divides evenly exactly when kh d = rh + p
+// (mod s), i.e. for kh = kh0, kh0 + s/g, kh0 + 2 s/g, ... (g = gcd(s, d)),
+// and then oh = i + oh0 - a d/g for the a-th of those taps.  So the taps
+// that reach a phase are the same for all of its pixels, and along a phase
+// row they read consecutive dy pixels: a tile of 64 pixels of one phase
+// (N x Hp x Wp of them, Hp = ceil(H / s) rows a phase, rows past H masked)
+// loops over those taps only, nth x ntw of KH x KW (a quarter for a 3x3
+// kernel at stride 2), 64 output channels a step, and each step's operands
+// are 16-byte runs of dy (64 channels of one pixel) and of w (64 input
+// channels of one (oc, tap)).  A phase no tap reaches has zero steps: its
+// dx is 0.
+//
+// 64 (pixels) x 64 (input channels) tiles, four waves of 32 x 32 with
+// v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 sums).  LDS stage: A
+// (64 pixel rows of 64 dy channels) and B (64 output-channel rows of 64 w
+// input channels), 128-byte rows, chunk c of row r at c ^ swz(r).  A is read
+// as it lies (a lane's 8 consecutive k are one 16-byte chunk of its pixel's
+// row: swz(r) = (r >> 1) & 7 puts the 16 rows of one 128-bit read pass on 16
+// distinct bank groups); B is read with ds_read_b64_tr_b16 (lane r of a
+// 16-lane group points at k row kb + (r >> 2), column n0 + 4 (r & 3); lane l
+// then holds column n0 + l at k rows kb .. kb + 3, and two reads give the 8
+// consecutive k of a B operand; swz(r) = 2 bit1(r) + 4 bit3(r) keeps those
+// 4 rows x 32 bytes, and the next group's 8 rows on, on distinct banks).
+// VB (IC % 8 == 0, w 16-byte aligned): A and B arrive by direct-to-LDS
+// copies into a ring of three stages, two steps in flight; else A does and
+// B is gathered element by element into registers one step ahead and
+// written to LDS before the step's barrier.
+constexpr int kDgPhRegion = 64 * 128;           // bytes: 64 rows x 64 bf16
+constexpr int kDgPhStage = 2 * kDgPhRegion;     // A, then B
+constexpr int kDgPhStages = 3;
+constexpr int kDgPhCopies = 4;                  // copy instructions a wave issues per step (VB)
+
+struct DgPhArgs {
+    const void *dy, *w;
+    float *dx;
+    int N, H, W, IC, OC, KH, KW, s, p, d, OH, OW;
+    int dk, dq;                  // tap step between the taps of a phase (s / g) and dy step per tap (d / g)
+    int Hp, Wp, Mp;              // rows and columns a phase, pixels a phase (N Hp Wp)
+    int tiles_p, tiles_m, ob;    // m tiles a phase, m tiles in all (s^2 tiles_p), 64-channel blocks of OC
+    unsigned dy_bytes, w_bytes, dx_bytes;   // each below 2^31
+    FastDiv div_tp, div_hwp, div_wp, div_s;
+};
+
+__device__ __forceinline__ int dg_swz_a(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int dg_swz_b(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
+
+template <bool VB>
+__global__ __launch_bounds__(256) void igemm_dgrad_phase_bf16(DgPhArgs a)
+{
+    // one LDS variable per stage: the compiler can then tell a stage being
+    // copied into from the one the fragments are read from
+    __shared__ __align__(16) unsigned char lds0[kDgPhStage];
+    __shared__ __align__(16) unsigned char lds1[kDgPhStage];
+    __shared__ __align__(16) unsigned char lds2[VB ? kDgPhStage : 16];
+    __shared__ int pix[64];                       // dx element offset of each tile pixel, -1 past the phase
+    auto stage_base = [&](int stage) __attribute__((always_inline)) -> unsigned char * {
+        return stage == 0 ? lds0 : stage == 1 ? lds1 : lds2;
+    };
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int tn = bid / a.tiles_m, tmg = bid - tn * a.tiles_m;
+    const int ph = fast_div(tmg, a.div_tp), tm = tmg - ph * a.tiles_p;
+    const int rh = fast_div(ph, a.div_s), rw = ph - rh * a.s;
+    const int ic0 = tn * 64;
+    // the taps that reach this phase along h and along w (uniform)
+    int kh0 = -1, kw0 = -1;
+    for (int k = min(a.KH, a.dk) - 1; k >= 0; --k)
+        if ((rh + a.p - k * a.d) % a.s == 0)
+            kh0 = k;
+    for (int k = min(a.KW, a.dk) - 1; k >= 0; --k)
+        if ((rw + a.p - k * a.d) % a.s == 0)
+            kw0 = k;
+    const int nth = kh0 < 0 ? 0 : (a.KH - 1 - kh0) / a.dk + 1;
+    const int ntw = kw0 < 0 ? 0 : (a.KW - 1 - kw0) / a.dk + 1;
+    const int oh0 = kh0 < 0 ? 0 : (rh + a.p - kh0 * a.d) / a.s;
+    const int ow0 = kw0 < 0 ? 0 : (rw + a.p - kw0 * a.d) / a.s;
+    const int steps = nth * ntw * a.ob;
+
+    // this lane's two A rows (pixels 16 w + 8 q + (lane >> 3) of the tile)
+    // and, for the first 64 threads, the tile's dx offsets
+    int yb[2], pi[2], pj[2];
+    bool pv[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int m = tm * 64 + 16 * wave + 8 * q + (lane >> 3);
+        const int n = fast_div(m, a.div_hwp);
+        const int r = m - n * (a.Hp * a.Wp);
+        const int i = fast_div(r, a.div_wp);
+        pi[q] = i;
+        pj[q] = r - i * a.Wp;
+        yb[q] = n * a.OH;
+        pv[q] = m < a.Mp && rh + a.s * i < a.H && rw + a.s * pj[q] < a.W;
+    }
+    if (tid < 64) {
+        const int m = tm * 64 + tid;
+        const int n = fast_div(m, a.div_hwp);
+        const int r = m - n * (a.Hp * a.Wp);
+        const int i = fast_div(r, a.div_wp);
+        const int j = r - i * a.Wp;
+        const int ih = rh + a.s * i, iw = rw + a.s * j;
+        pix[tid] = (m < a.Mp && ih < a.H && iw < a.W) ? ((n * a.H + ih) * a.W + iw) * a.IC : -1;
+    }
+
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc((void *)a.dy, 0, a.dy_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.w, 0, a.w_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(a.dx, 0, a.dx_bytes, kRsrcWord3);
+    // copy lanes: row (lane >> 3) of an 8-row block, physical chunk lane & 7
+    const int pc = lane & 7;
+    int ca[2], cb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = 16 * wave + 8 * q + (lane >> 3);
+        ca[q] = pc ^ dg_swz_a(r);
+        cb[q] = pc ^ dg_swz_b(r);
+    }
+    // step st = tap (ah, aw) x channel block ob, ob fastest; the running
+    // position of the steps issued so far (issue() is called once per step,
+    // in order, also for the steps past the last, which copy zeros)
+    int nxt_ob = 0, nxt_aw = 0, nxt_ah = 0, nxt_st = 0;
+    unsigned vb[16];                              // B gathers of the next step (not VB): raw bf16 bits
+    auto issue = [&](unsigned char *sbase) __attribute__((always_inline)) {
+        const bool live = nxt_st < steps;
+        const int ob = nxt_ob, ah = nxt_ah, aw = nxt_aw;
+        // A: dy at (oh, ow) = (i + oh0 - ah dq, j + ow0 - aw dq), channels 64 ob + 8 c
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int oh = pi[q] + oh0 - ah * a.dq, ow = pj[q] + ow0 - aw * a.dq;
+            const int oc = 64 * ob + 8 * ca[q];
+            const bool ok = live && pv[q] && (unsigned)oh < (unsigned)a.OH && (unsigned)ow < (unsigned)a.OW
+                && oc < a.OC;
+            const unsigned off = ok ? 2u * ((unsigned)((yb[q] + oh) * a.OW + ow) * (unsigned)a.OC + (unsigned)oc)
+                                    : kOutOfRange;
+            dma16(rdy, (u32x4_t *)(sbase + (16 * wave + 8 * q) * 128), off);
+        }
+        // B: w[64 ob + row][kh][kw][ic0 + 8 c]
+        const int kh = kh0 + ah * a.dk, kw = kw0 + aw * a.dk;
+        const int tap = kh * a.KW + kw;
+        if constexpr (VB) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int oc = 64 * ob + 16 * wave + 8 * q + (lane >> 3);
+                const int ic = ic0 + 8 * cb[q];
+                const bool ok = live && oc < a.OC && ic < a.IC;
+                const unsigned off = ok
+                    ? 2u * ((unsigned)(oc * a.KH * a.KW + tap) * (unsigned)a.IC + (unsigned)ic) : kOutOfRange;
+                dma16(rw_, (u32x4_t *)(sbase + kDgPhRegion + (16 * wave + 8 * q) * 128), off);
+            }
+        } else {
+            // thread: column tid & 63, rows (tid >> 6) + 4 q
+            const int ic = ic0 + (tid & 63);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int oc = 64 * ob + (tid >> 6) + 4 * q;
+                const bool ok = live && oc < a.OC && ic < a.IC;
+                const unsigned off = ok
+                    ? 2u * ((unsigned)(oc * a.KH * a.KW + tap) * (unsigned)a.IC + (unsigned)ic) : kOutOfRange;
+                vb[q] = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(rw_, off, 0, 0);
+            }
+        }
+        ++nxt_st;
+        if (++nxt_ob == a.ob) {
+            nxt_ob = 0;
+            if (++nxt_aw == ntw) {
+                nxt_aw = 0;
+                ++nxt_ah;
+            }
+        }
+    };
+    auto put_b = [&](unsigned char *sbase) __attribute__((always_inline)) {
+        const int c = tid & 63;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int r = (tid >> 6) + 4 * q;
+            *(unsigned short *)(sbase + kDgPhRegion + r * 128 + 16 * ((c >> 3) ^ dg_swz_b(r)) + 2 * (c & 7)) =
+                (unsigned short)vb[q];
+        }
+    };
+
+    // fragments: wave (wm, wn) = pixels 32 wm .., input channels 32 wn ..
+    const int wm = wave & 1, wn = wave >> 1;
+    const int g16 = lane >> 4, r16 = lane & 15;
+    int aoff[2][2], boff[2][2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int r = 32 * wm + 16 * i + r16;
+            aoff[i][ks] = r * 128 + 16 * ((4 * ks + g16) ^ dg_swz_a(r));
+        }
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 32 * ks + 8 * g16 + 4 * h + (r16 >> 2);
+                const int n = 32 * wn + 16 * jb + 4 * (r16 & 3);
+                boff[jb][ks][h] = kDgPhRegion + r * 128 + 16 * ((n >> 3) ^ dg_swz_b(r)) + 2 * (n & 7);
+            }
+    floatx4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+            acc[i][jb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    auto tr = [&](const unsigned char *p) __attribute__((always_inline)) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+    };
+    auto compute = [&](const unsigned char *sbase) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8_t fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                fa[i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(sbase + aoff[i][ks]));
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const v4i16 lo = tr(sbase + boff[jb][ks][0]), hi = tr(sbase + boff[jb][ks][1]);
+                fb[jb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+                    acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
+        }
+    };
+
+    if constexpr (VB) {
+        // ring of three stages: step st's copies are issued after the
+        // barrier of step st - 2, which certifies every wave is done with
+        // step st - 3's stage.  The loop is unrolled by three so that every
+        // stage is a constant, and runs whole rounds of three steps with
+        // the copies, waits and barriers unconditional (only the MFMAs of
+        // the steps past the last are skipped): a branch around a step
+        // made the compiler wait for the copies of the step ahead before
+        // every fragment read.
+#pragma unroll
+        for (int q = 0; q < kDgPhStages - 1; ++q)
+            issue(stage_base(q));
+        for (int st0 = 0; st0 < steps; st0 += kDgPhStages) {
+#pragma unroll
+            for (int q = 0; q < kDgPhStages; ++q) {
+                wait_vmcnt<(kDgPhStages - 2) * kDgPhCopies>();   // step st0 + q landed (this wave's part)
+                lds_barrier();
+                issue(stage_base((q + kDgPhStages - 1) % kDgPhStages));
+                if (st0 + q < steps)
+                    compute(stage_base(q));
+            }
+        }
+        wait_vmcnt<0>();       // (the copies past the last step: done before the workgroup ends)
+    } else {
+        // two stages: step st + 1's copies and B gathers are issued after
+        // step st's barrier (every wave is then done with step st - 1's
+        // stage), the gathers written to LDS before step st + 1's barrier
+        issue(stage_base(0));
+        for (int st0 = 0; st0 < steps; st0 += 2) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (st0 + q < steps) {
+                    wait_vmcnt<0>();
+                    put_b(stage_base(q));
+                    __syncthreads();
+                    issue(stage_base(q ^ 1));
+                    compute(stage_base(q));
+                }
+            }
+        }
+        wait_vmcnt<0>();
+    }
+    __syncthreads();       // (pix was written by the first wave; a zero-step tile meets no barrier before)
+    // acc[i][jb]: lane holds pixels 32 wm + 16 i + 4 g16 + v of input channel
+    // ic0 + 32 wn + 16 jb + r16
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int ic = ic0 + 32 * wn + 16 * jb + r16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int base = pix[32 * wm + 16 * i + 4 * g16 + v];
+                const unsigned off = (base >= 0 && ic < a.IC) ? 4u * (unsigned)(base + ic) : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][jb][v]), rx, off, 0, kOutAux);
+            }
+        }
+}
+
 }  // namespace convimg

@@ -135,6 +135,12 @@ GENERAL = [
     shape(3, 10, 10, 64, 96, 1, 1, 2, 0, 1, name="1x1 stride 2"),
     shape(2, 13, 11, 24, 40, 3, 3, 2, 1, 1, dtype=FP32, name="fp32 stride 2"),
     shape(1, 5, 5, 8, 8, 5, 3, 2, 2, 1, dtype=FP32, name="fp32 5x3 stride 2"),
+    shape(1, 11, 9, 16, 12, 3, 3, 2, 1, 1, name="stride 2 OC 12 (element-wise kernel)"),
+    shape(1, 14, 15, 72, 136, 3, 3, 2, 1, 1, name="stride 2, two channel blocks each side"),
+    shape(1, 9, 9, 8, 8, 2, 2, 4, 0, 1, name="stride 4 > window: phases no tap reaches"),
+    shape(1, 10, 10, 16, 8, 3, 3, 2, 2, 2, name="stride 2 dilation 2"),
+    shape(2, 12, 12, 8, 16, 3, 3, 2, 0, 3, name="stride 2 dilation 3"),
+    shape(4, 56, 56, 128, 128, 3, 3, 2, 1, 1, name="ResNet-style stride-2 layer, N=4"),
     WORKLOADS["stem7x7"],
 ]
 
@@ -145,6 +151,13 @@ def test_dgrad_general_kernel(wl):
     run the general kernel (dx from its definition; wt untouched)."""
     _, _, untouched = bwd_parity(wl)
     assert untouched, "the general kernel does not use wt"
+
+
+def test_dgrad_general_misaligned():
+    """dy, w and dx off 16-byte alignment at stride 2: the element-wise
+    general kernel (the kernel by phases needs 16-byte runs of dy)."""
+    _, _, untouched = bwd_parity(shape(2, 13, 12, 24, 40, 3, 3, 2, 1, 1), misalign=True)
+    assert untouched
 
 
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
