@@ -302,25 +302,29 @@ void conv2d_fwd_autotune_clear(void);
  * left as it was.  A
  * caller whose weights do not change between calls may transform them once
  * and make that conv2d_fwd call itself.  Every other problem (stride above
- * 1, KH != KW, pad > dilation*(KH-1): the listing's fallback route) runs a
- * general kernel that computes dx from the definition above as a GEMM over
- * the input pixels, K = KH*KW*OC, gathering dY element by element with the
- * divisibility test, fp32 products and sums (bf16 products are exact in
- * fp32); `wt` is then left as it was.
+ * 1, KH != KW, pad > dilation*(KH-1): the listing's fallback route)
+ * computes dx from the definition above as a GEMM over the input pixels,
+ * K = (tap, oc), and leaves `wt` as it was: in bf16 with OC % 8 == 0 and a
+ * 16-byte aligned dy, a kernel that takes the input pixels by phase of the
+ * stride (ih % stride, iw % stride), so that each tile runs only the taps
+ * whose (ih + pad - kh*dilation) / stride divides evenly (bf16 MFMA, exact
+ * products, fp32 sums); otherwise a kernel that gathers dY element by
+ * element with the divisibility test (fp32 products and sums; bf16
+ * products are exact in fp32).
  *
  *   dy    device, N x OH x OW x OC (NHWC) in `dtype`, OH/OW the forward
  *         output extents of H/W (the formula under conv2d_fwd)
  *   w     device, OC x KH x KW x IC (OHWI) in `dtype`: the forward weights
  *   wt    device, OC*KH*KW*IC elements of `dtype`, caller-owned workspace;
  *         receives IC x KH x KW x OC, the flipped and transposed weights,
- *         except on the in-LDS path and the general kernel (then untouched)
+ *         except on the in-LDS path and the fallback route (then untouched)
  *   dx    device, fp32 N x H x W x IC (NHWC), fully overwritten
  *   N, H, W, IC, OC, KH, KW, stride, pad, dilation, dtype: the forward
  *         problem's arguments
  *
  * Errors: the argument errors of conv2d_fwd for the forward problem and
  * (stride 1) for the one it maps to; CONVIMG_ERR_ALIAS if wt or dx overlaps
- * another buffer; CONVIMG_ERR_RANGE (general kernel) for dy, w or dx of
+ * another buffer; CONVIMG_ERR_RANGE (fallback route) for dy, w or dx of
  * 2^31 bytes or more; CONVIMG_ERR_DEVICE without a usable device.  These are returned before any work is queued.  After the
  * transform is queued, CONVIMG_ERR_LAUNCH / CONVIMG_ERR_ALLOC may still come
  * back (wt then holds the transform).  Asynchronous on `stream`. */
