@@ -500,24 +500,30 @@ __global__ __launch_bounds__(256) void igemm_dgrad_phase_bf16(DgPhArgs a)
         // ring of three stages: step st's copies are issued after the
         // barrier of step st - 2, which certifies every wave is done with
         // step st - 3's stage.  The loop is unrolled by three so that every
-        // stage is a constant, and runs whole rounds of three steps with
-        // the copies, waits and barriers unconditional (only the MFMAs of
-        // the steps past the last are skipped): a branch around a step
-        // made the compiler wait for the copies of the step ahead before
-        // every fragment read.
+        // stage is a constant and runs whole rounds of three steps with no
+        // branch inside (a branch around each step made the compiler wait
+        // for the copies of the step ahead before most fragment reads),
+        // then the last partial round step by step.
+        static_assert(kDgPhStages == 3, "the rounds below are written for three stages");
+        auto step = [&](int q) __attribute__((always_inline)) {
+            wait_vmcnt<(kDgPhStages - 2) * kDgPhCopies>();   // this step landed (this wave's part)
+            lds_barrier();
+            issue(stage_base((q + kDgPhStages - 1) % kDgPhStages));
+            compute(stage_base(q));
+        };
 #pragma unroll
         for (int q = 0; q < kDgPhStages - 1; ++q)
             issue(stage_base(q));
-        for (int st0 = 0; st0 < steps; st0 += kDgPhStages) {
-#pragma unroll
-            for (int q = 0; q < kDgPhStages; ++q) {
-                wait_vmcnt<(kDgPhStages - 2) * kDgPhCopies>();   // step st0 + q landed (this wave's part)
-                lds_barrier();
-                issue(stage_base((q + kDgPhStages - 1) % kDgPhStages));
-                if (st0 + q < steps)
-                    compute(stage_base(q));
-            }
+        const int full = steps - steps % kDgPhStages;
+        for (int st0 = 0; st0 < full; st0 += kDgPhStages) {
+            step(0);
+            step(1);
+            step(2);
         }
+        if (full < steps)
+            step(0);
+        if (full + 1 < steps)
+            step(1);
         wait_vmcnt<0>();       // (the copies past the last step: done before the workgroup ends)
     } else {
         // two stages: step st + 1's copies and B gathers are issued after

@@ -644,18 +644,38 @@ __global__ __launch_bounds__(kWgThreads) void igemm_wgrad_tr_bf16(WgArgs a)
 #pragma unroll
     for (int q = 0; q < STAGES - 1; ++q)
         issue(q, q);
-    for (int st0 = 0; st0 < steps; st0 += STAGES) {
-#pragma unroll
-        for (int q = 0; q < STAGES; ++q) {
-            const int st = st0 + q;
-            if (st < steps) {
-                wait_vmcnt<(STAGES - 2) * kWtCopies>();    // step st has landed (this wave's part)
-                lds_barrier();
-                issue(st + STAGES - 1, (q + STAGES - 1) % STAGES);
-                compute(q);
-            }
-        }
+    // Whole rounds of STAGES steps with no branch inside (with a branch
+    // around each step the compiler waited for the copies of the steps
+    // ahead before the fragment reads of most steps), then the last partial
+    // round step by step.
+    auto step = [&](int st, auto q) __attribute__((always_inline)) {
+        wait_vmcnt<(STAGES - 2) * kWtCopies>();    // step st has landed (this wave's part)
+        lds_barrier();
+        issue(st + STAGES - 1, (decltype(q)::value + STAGES - 1) % STAGES);
+        compute(decltype(q)::value);
+    };
+    const int full = steps - steps % STAGES;
+    for (int st0 = 0; st0 < full; st0 += STAGES) {
+        step(st0, std::integral_constant<int, 0>{});
+        step(st0 + 1, std::integral_constant<int, 1>{});
+        if constexpr (STAGES > 2)
+            step(st0 + 2, std::integral_constant<int, 2>{});
+        if constexpr (STAGES > 3)
+            step(st0 + 3, std::integral_constant<int, 3>{});
+        if constexpr (STAGES > 4)
+            step(st0 + 4, std::integral_constant<int, 4>{});
     }
+    if (full < steps)
+        step(full, std::integral_constant<int, 0>{});
+    if constexpr (STAGES > 2)
+        if (full + 1 < steps)
+            step(full + 1, std::integral_constant<int, 1>{});
+    if constexpr (STAGES > 3)
+        if (full + 2 < steps)
+            step(full + 2, std::integral_constant<int, 2>{});
+    if constexpr (STAGES > 4)
+        if (full + 3 < steps)
+            step(full + 3, std::integral_constant<int, 3>{});
     wait_vmcnt<0>();       // (the copies past the last step: done before the workgroup ends)
 
     const int jc[3] = {j0 + 48 * wave, j0 + 48 * wave + 16, j0 + 48 * wave + 32};
