@@ -83,9 +83,9 @@ TRAFFIC = {
     # weight backward: the whole call (igemm_wgrad_row_bf16, + wgrad_reduce
     # where the ranges go through the workspace), as the --op wgrad roofline
     # times it; profiles/igemm_wgrad_*.md
-    "wgrad:resnet3x3": {"bytes": 36180125, "tile": -2, "kernel": "4bb0b58facb58f2e"},
-    "wgrad:largek": {"bytes": 44511574, "tile": -2, "kernel": "4bb0b58facb58f2e"},
-    "wgrad:dilated": {"bytes": 68869858, "tile": -2, "kernel": "4bb0b58facb58f2e"},
+    "wgrad:resnet3x3": {"bytes": 36188457, "tile": -2, "kernel": "cfddd831a25cdc45"},
+    "wgrad:largek": {"bytes": 44526942, "tile": -2, "kernel": "cfddd831a25cdc45"},
+    "wgrad:dilated": {"bytes": 68870308, "tile": -2, "kernel": "cfddd831a25cdc45"},
 }
 
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
