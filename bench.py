@@ -17,7 +17,8 @@ input): at stride 1 a step is the forward implicit GEMM it maps to, whose
 kernel flips and transposes the weights in LDS where it can (one launch),
 else the separate weight transform plus that GEMM (the roofline object then
 prices the GEMM kernel alone, timed in its own loop on the same buffers);
-other problems (the stem's stride 2) run the general kernel, one launch.
+other problems (the stem's stride 2) take the fallback route (the kernel
+by phases of the stride), one launch.
 
 --nchw f32|bf16 times conv2d_fwd_nchw on NCHW / OIHW copies of the same
 inputs (fp32 or bf16 NCHW output).
@@ -91,7 +92,7 @@ TRAFFIC = {
 # Sources each kernel family is compiled from (besides igemm_common.hpp).
 KIND_SOURCES = {
     -2: ("igemm_wgrad.hpp", "igemm_pipe.hpp", "conv2d_wgrad.hip"),   # weight backward
-    -3: ("igemm_dgrad.hpp",),                    # data backward, general kernel
+    -3: ("igemm_dgrad.hpp",),                    # data backward, fallback route
     -1: ("igemm_regs.hpp",),                     # fp32 storage
     0: ("igemm_regs.hpp",),                      # CONVIMG_KIND_REGS
     1: ("igemm_pipe.hpp",),                      # CONVIMG_KIND_PIPE
@@ -404,7 +405,7 @@ def main():
         assert rc == 0, abi.conv2d_strerror(rc)
         tuned = {"tile_id": t_tile, "splits": t_splits, "us_best": round(t_best, 3),
                  "us_static": round(t_default, 3)}
-    # the data backward's general kernel (stride > 1, KH != KW, pad beyond
+    # the data backward's fallback route (stride > 1, KH != KW, pad beyond
     # dilation*(KH-1)) maps to no forward problem
     general = dgrad and (wl.stride != 1 or wl.KH != wl.KW or wl.pad > wl.dilation * (wl.KH - 1))
     if general:

@@ -1777,8 +1777,9 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
     if (rc != CONVIMG_OK)
         return rc;
     if (stride != 1 || KH != KW || pad > dilation * (KH - 1)) {
-        // the general kernel: the gradient from its definition, any stride,
-        // kernel shape and padding (wt unused)
+        // the fallback route: the gradient from its definition, any stride,
+        // kernel shape and padding (wt unused), by phases of the stride or
+        // element by element
         const size_t esz = dtype == CONVIMG_BF16 ? 2 : 4;
         const size_t nw = (size_t)OC * KH * KW * IC * esz;
         const size_t ny = (size_t)fwd.M * OC * esz;
@@ -1828,7 +1829,7 @@ int conv2d_bwd_data(const void *dy, const void *w, int N, int H, int W, int IC, 
             const long long tiles_p = ceil_div(Mp, 64);
             const long long tiles_m = (long long)stride * stride * tiles_p;
             const long long grid = tiles_m * ceil_div(IC, 64);
-            if (grid >= (long long)lim || Mp * 64 >= (long long)lim)
+            if (grid >= (long long)lim || tiles_p * 64 >= (long long)lim)   // (pixel indices of a phase fit an int)
                 return CONVIMG_ERR_RANGE;
             q.Mp = (int)Mp;
             q.tiles_p = (int)tiles_p;

@@ -292,7 +292,7 @@ def call_bwd(**kw):
     (dict(N=0), abi.CONVIMG_ERR_SHAPE),
     (dict(H=2, pad=0), abi.CONVIMG_ERR_SHAPE),
     (dict(dtype=2), abi.CONVIMG_ERR_DTYPE),
-    # the general kernel's problems (stride 2, KH != KW, pad beyond
+    # the fallback route's problems (stride 2, KH != KW, pad beyond
     # dilation*(KH-1)) check the same overlaps before any device work
     (dict(stride=2, dx=0x1000000 + 64), abi.CONVIMG_ERR_ALIAS),
     (dict(KW=5, pad=2, dx=0x2000000 - 64), abi.CONVIMG_ERR_ALIAS),

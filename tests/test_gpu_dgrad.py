@@ -11,9 +11,11 @@ named layers (ResNet-style, 512-channel, dilated) at full size, IC != OC with
 channel tails, 1x1, 5x5, edge paddings (0 and dilation*(K-1)), IC = 3 with a
 7x7 window, fp32 storage, and the torch wrapper; the weight transform alone
 on non-square windows, channel tails and misaligned buffers (element path);
-and the general kernel for the problems the stride-1 mapping does not serve
-(strides 2 and 3, non-square windows, padding beyond dilation*(K-1), the
-stem layer at full size, fp32 storage).
+and the fallback route for the problems the stride-1 mapping does not
+serve (strides 2 to 4, dilations with stride, non-square windows, padding
+beyond dilation*(K-1), a ResNet-style stride-2 layer, the stem layer at
+full size: the kernel by phases of the stride; fp32 storage, OC % 8 != 0
+and misaligned buffers: the element-wise kernel).
 """
 import numpy as np
 import pytest
@@ -125,7 +127,7 @@ def test_dgrad_full_size(wl):
     bwd_parity(wl)
 
 
-# the general kernel: every problem the stride-1 mapping does not serve
+# the fallback route: every problem the stride-1 mapping does not serve
 GENERAL = [
     shape(2, 15, 17, 24, 40, 3, 3, 2, 1, 1, name="stride 2, channel tails"),
     shape(2, 30, 30, 3, 64, 7, 7, 2, 3, 1, name="stride 2 7x7 IC 3"),
@@ -148,14 +150,14 @@ GENERAL = [
 @pytest.mark.parametrize("wl", GENERAL, ids=lambda w: w.name)
 def test_dgrad_general_kernel(wl):
     """Strides above 1, non-square windows and padding beyond dilation*(K-1)
-    run the general kernel (dx from its definition; wt untouched)."""
+    take the fallback route (dx from its definition; wt untouched)."""
     _, _, untouched = bwd_parity(wl)
-    assert untouched, "the general kernel does not use wt"
+    assert untouched, "the fallback route does not use wt"
 
 
 def test_dgrad_general_misaligned():
     """dy, w and dx off 16-byte alignment at stride 2: the element-wise
-    general kernel (the kernel by phases needs 16-byte runs of dy)."""
+    kernel (the kernel by phases needs 16-byte runs of dy)."""
     _, _, untouched = bwd_parity(shape(2, 13, 12, 24, 40, 3, 3, 2, 1, 1), misalign=True)
     assert untouched
 
@@ -178,7 +180,7 @@ def test_dgrad_torch_wrapper():
     torch.cuda.synchronize()
     yref, S = oracle.conv2d_bwd_data(inp.x32, inp.w32, 14, 14, 1, 1, 1)
     check(dx.cpu().numpy(), yref, S, "wrapper")
-    # stride 2 (the general kernel): dy of the 7 x 7 forward output
+    # stride 2 (the fallback route): dy of the 7 x 7 forward output
     dy2 = inp.x_store[:, ::2, ::2].copy()
     dx2 = cig.conv2d_bwd_data_nhwc(upload(dy2), w, 14, 14, stride=2, pad=1)
     torch.cuda.synchronize()
