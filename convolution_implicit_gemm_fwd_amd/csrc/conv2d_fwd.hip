@@ -92,6 +92,7 @@ constexpr int kWindowTile = 32;           // the kWindow entry
 constexpr int kResidentTile = 33;         // the kResident entry
 constexpr int kImageTile = 34;            // the kImage entry
 constexpr int kTwoPerCuTile = 15;         // pipe32 128x128, 2 stages: two workgroups per CU
+constexpr int kSmallPipeTile = 20;        // pipe32 64x64, 4 stages: problems with few 128x128 tiles
 constexpr int kImgMaxMB = 8;              // image kernel: at most 8 blocks of 32 output pixels
 constexpr int kNumLoaders = 3;
 
@@ -700,13 +701,17 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
     const bool image_ok = pipe_ok && aligned && plan_image(N, H, W, IC, OC, KH, KW, p, OH, OW, &imp);
     int tile;
     if (pipe_ok) {
-        // 128x128 tiles two per CU when there are enough for that (one
-        // workgroup's copies overlap the other's MFMAs: measured 7 % faster
-        // than 256x128 on the dilated layer), else 256x128 one per CU, else
+        // 128x128 tiles, two workgroups per CU, wherever they give every CU
+        // at least one (one workgroup's copies overlap the other's MFMAs:
+        // measured 7 % faster than 256x128 on the dilated layer, and on a
+        // 1x1 stride-2 layer with 1.5 a CU 9.4 us against 14.9 for
+        // 128x64); fewer than that with OC > 64: 64x64 tiles, split over K
+        // up to the CU count (3x3 stride-2 layers with 16 images, 56x56x128,
+        // 28x28x256 and 14x14x512: 11.0 / 15.4 / 20.9 us against 16.9 /
+        // 28.2 / 57.6 for 128x64 with every resident slot split); else
         // 128x64 (with split-K where K is large)
-        const long long big = ((M + 255) / 256) * ((OC + 127) / 128);
         const long long mid = ((M + 127) / 128) * ((OC + 127) / 128);
-        tile = (OC > 64 && mid >= 2LL * num_cus) ? kTwoPerCuTile : (OC > 64 && big >= num_cus) ? 7 : 11;
+        tile = (OC > 64 && mid >= num_cus) ? kTwoPerCuTile : OC > 64 ? kSmallPipeTile : 11;
     } else if (OC <= 64) {
         tile = (M <= 64LL * num_cus) ? 3 : 0;
     } else {
@@ -819,7 +824,11 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
     const int resident = (occ ? occ[tile][loader] : lds_occupancy(tile)) * num_cus;
     int splits = 1;
     if (tiles < num_cus && ktiles >= 16) {
-        long long sc = resident / tiles;
+        // the 64x64 tile splits only until the CU count is reached (its
+        // serial turns cost more than the slots left idle: 14x14x512
+        // stride-2 layer 20.9 us with 2 splits, 24.2 us with 9); the others
+        // fill every resident slot
+        long long sc = tile == kSmallPipeTile ? (num_cus + tiles - 1) / tiles : resident / tiles;
         long long sk = ktiles / 8;
         splits = (int)(sc < sk ? sc : sk);
         if (splits > 16)
