@@ -1,4 +1,6 @@
-// igemm_dgrad.hpp -- weight transform for the data-backward pass.
+// igemm_dgrad.hpp -- the data-backward pass: the weight transform that maps
+// it onto the forward kernels at stride 1, and the two kernels of the
+// fallback route (by phases of the stride; element by element).
 //
 // For stride 1 the gradient with respect to the input is a forward
 // convolution of the output gradient (burn-cubecl "kernel/conv/base.rs"
