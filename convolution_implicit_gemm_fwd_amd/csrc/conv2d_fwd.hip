@@ -93,6 +93,7 @@ constexpr int kResidentTile = 33;         // the kResident entry
 constexpr int kImageTile = 34;            // the kImage entry
 constexpr int kTwoPerCuTile = 15;         // pipe32 128x128, 2 stages: two workgroups per CU
 constexpr int kSmallPipeTile = 20;        // pipe32 64x64, 4 stages: problems with few 128x128 tiles
+constexpr int kTallPipeTile = 4;          // pipe16 128x64, 3 stages: few 128x128 tiles but enough 128x64
 constexpr int kImgMaxMB = 8;              // image kernel: at most 8 blocks of 32 output pixels
 constexpr int kNumLoaders = 3;
 
@@ -705,13 +706,17 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
         // at least one (one workgroup's copies overlap the other's MFMAs:
         // measured 7 % faster than 256x128 on the dilated layer, and on a
         // 1x1 stride-2 layer with 1.5 a CU 9.4 us against 14.9 for
-        // 128x64); fewer than that with OC > 64: 64x64 tiles, split over K
-        // up to the CU count (3x3 stride-2 layers with 16 images, 56x56x128,
-        // 28x28x256 and 14x14x512: 11.0 / 15.4 / 20.9 us against 16.9 /
-        // 28.2 / 57.6 for 128x64 with every resident slot split); else
-        // 128x64 (with split-K where K is large)
+        // 128x64); fewer than that with OC > 64: 128x64 tiles (3 stages)
+        // where those fill the CUs (1x1 256 -> 1024 on 14x14: 7.1 us
+        // against 9.2 for 64x64), else 64x64 tiles, split over K up to the
+        // CU count (3x3 stride-2 layers with 16 images, 56x56x128, 28x28x256
+        // and 14x14x512: 11.0 / 15.4 / 20.9 us against 16.9 / 28.2 / 57.6
+        // for 128x64 with every resident slot split); OC <= 64: 128x64
+        // (with split-K where K is large)
         const long long mid = ((M + 127) / 128) * ((OC + 127) / 128);
-        tile = (OC > 64 && mid >= num_cus) ? kTwoPerCuTile : OC > 64 ? kSmallPipeTile : 11;
+        const long long tall = ((M + 127) / 128) * ((OC + 63) / 64);
+        tile = (OC > 64 && mid >= num_cus) ? kTwoPerCuTile
+             : OC > 64 ? (tall >= num_cus ? kTallPipeTile : kSmallPipeTile) : 11;
     } else if (OC <= 64) {
         tile = (M <= 64LL * num_cus) ? 3 : 0;
     } else {
@@ -824,12 +829,14 @@ int make_plan_uncached(int N, int H, int W, int IC, int OC, int KH, int KW, int 
     const int resident = (occ ? occ[tile][loader] : lds_occupancy(tile)) * num_cus;
     int splits = 1;
     if (tiles < num_cus && ktiles >= 16) {
-        // the 64x64 tile splits only until the CU count is reached (its
-        // serial turns cost more than the slots left idle: 14x14x512
-        // stride-2 layer 20.9 us with 2 splits, 24.2 us with 9); the others
-        // fill every resident slot
-        long long sc = tile == kSmallPipeTile ? (num_cus + tiles - 1) / tiles : resident / tiles;
-        long long sk = ktiles / 8;
+        // the 64x64 tile splits only until the CU count is reached and
+        // while each split keeps 16 K tiles (its serial turns cost more than
+        // the slots left idle: 14x14x512 stride-2 layer 20.9 us with 2
+        // splits, 24.2 us with 9; 1x1 1024 -> 256 on 14x14, 16 K tiles, 9.3
+        // us whole, 11.8 us in 2); the others fill every resident slot
+        const bool small = tile == kSmallPipeTile;
+        long long sc = small ? (num_cus + tiles - 1) / tiles : resident / tiles;
+        long long sk = ktiles / (small ? 16 : 8);
         splits = (int)(sc < sk ? sc : sk);
         if (splits > 16)
             splits = 16;
